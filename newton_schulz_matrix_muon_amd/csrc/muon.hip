@@ -1,0 +1,604 @@
+// Host side of the Muon C ABI: validation, the batched planner and the
+// launch sequence.  See include/muon.h for the contract.
+//
+// Planner (RFC-0023 方案 4, muon_batch_update / muon_batch_update_size):
+//  1. Every bank expands into NS units: each matrix, or each split_rows
+//     block of it (RFC-0023 split_head, fan_out = head size).  Within a bank
+//     the units sit at a uniform stride of rows_u*cols elements.
+//  2. Units are grouped by their exact shape (rows_u, cols) and gradient
+//     dtype; every group is cut into chunks of at most batch_update_size
+//     units (0 = no limit) and at most kMaxSeg bank segments.
+//  3. A chunk is one stacked pass: every kernel of the step runs once over
+//     all of its units (and the ten NS iterations run back to back), with the
+//     iterates laid out at a fixed stride in the caller's workspace.
+// The workspace is sized for the largest chunk and reused by every chunk.
+#include "../../include/muon.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <map>
+#include <new>
+#include <tuple>
+#include <vector>
+
+#include "kernels.hpp"
+
+using namespace muon_dev;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+struct Unitized {
+  int desc;            // caller bank index
+  int64_t n_units;     // units in the bank
+  int64_t rows_u;      // unit rows
+  int64_t cols;
+  int32_t gdtype;
+};
+
+struct SegRef {
+  int desc;
+  int64_t unit_begin;  // first unit inside the bank
+  int64_t count;
+};
+
+struct Chunk {
+  int64_t rows_u, cols;
+  int32_t gdtype;
+  int tile;             // 128 or 256
+  int64_t rows_pad, cols_pad, s_pad;
+  bool tall;            // rows_u > cols: the Gram is X^T X
+  int64_t n_units;
+  std::vector<SegRef> segs;
+  int rows_per_block, blocks_per_unit;   // momentum kernel
+  int64_t norm_vec_per_block; int norm_blocks_per_unit;
+};
+
+// Workspace carve-up of one chunk (byte offsets).
+struct Layout {
+  size_t x32[2], xb[2], a32, ab, bop, partials, inv_nu, flag, total;
+};
+
+Layout layout_of(const Chunk& c, bool bf16) {
+  Layout L{};
+  const size_t U = (size_t)c.n_units;
+  const size_t xs = (size_t)(c.rows_pad * c.cols_pad);
+  const size_t ss = (size_t)(c.s_pad * c.s_pad);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, kAlign); return o; };
+  L.x32[0] = take(U * xs * 4);
+  L.x32[1] = take(U * xs * 4);
+  if (bf16) {
+    L.xb[0] = take(U * xs * 2);
+    L.xb[1] = take(U * xs * 2);
+  }
+  L.a32 = take(U * ss * 4);
+  if (bf16) L.ab = take(U * ss * 2);
+  L.bop = take(U * ss * (bf16 ? 2 : 4));
+  L.partials = take(U * (size_t)c.blocks_per_unit * 8);
+  L.inv_nu = take(U * 4);
+  L.flag = take(U * 4);
+  L.total = off;
+  return L;
+}
+
+bool finite(float x) { return std::isfinite(x); }
+
+int validate_hyper(const muon_hyper* h) {
+  if (!h) return MUON_ERR_NULL;
+  if (!finite(h->lr) || !finite(h->mu) || !finite(h->weight_decay) || !finite(h->gamma))
+    return MUON_ERR_HYPER;
+  if (h->scale_mode != MUON_SCALE_SPECTRAL && h->scale_mode != MUON_SCALE_UNIT_RMS_NORM)
+    return MUON_ERR_DTYPE;
+  if (h->ns_precision != MUON_NS_FP32 && h->ns_precision != MUON_NS_BF16) return MUON_ERR_DTYPE;
+  if (h->batch_update_size < 0) return MUON_ERR_HYPER;
+  if (h->n_stages < 1 || h->n_stages > MUON_MAX_STAGES) return MUON_ERR_HYPER;
+  int64_t total = 0;
+  for (int i = 0; i < h->n_stages; ++i) {
+    const muon_ns_stage& s = h->stages[i];
+    if (s.steps < 0 || s.steps > 1000) return MUON_ERR_HYPER;
+    if (!finite(s.a) || !finite(s.b) || !finite(s.c)) return MUON_ERR_HYPER;
+    total += s.steps;
+  }
+  if (total < 1) return MUON_ERR_HYPER;
+  return MUON_OK;
+}
+
+// Shapes: rows, cols, batch >= 1; split divides rows; kernel index limits.
+int validate_descs(const muon_matrix_desc* mats, int64_t n, bool check_dtype) {
+  if (n < 0) return MUON_ERR_SHAPE;
+  if (n > 0 && !mats) return MUON_ERR_NULL;
+  const int64_t kMaxDim = (int64_t)1 << 30;
+  for (int64_t i = 0; i < n; ++i) {
+    const muon_matrix_desc& d = mats[i];
+    if (d.batch < 1 || d.rows < 1 || d.cols < 1 || d.split_rows < 0) return MUON_ERR_SHAPE;
+    if (d.rows > kMaxDim || d.cols > kMaxDim || d.batch > kMaxDim) return MUON_ERR_SHAPE;
+    if (d.split_rows > 0 && d.rows % d.split_rows != 0) return MUON_ERR_SHAPE;
+    if (d.reserved != 0) return MUON_ERR_SHAPE;
+    // Bytes of the largest caller bank must fit in int64 comfortably.
+    const double elems = (double)d.batch * (double)d.rows * (double)d.cols;
+    if (elems > 9.0e15) return MUON_ERR_SHAPE;
+    if (check_dtype && d.grad_dtype != MUON_DTYPE_F32 && d.grad_dtype != MUON_DTYPE_BF16)
+      return MUON_ERR_DTYPE;
+  }
+  return MUON_OK;
+}
+
+int pick_tile(int64_t rows_u, int64_t cols) {
+  return std::min(rows_u, cols) >= 256 ? 256 : 128;
+}
+
+// Group the banks' units by shape and cut the groups into chunks.
+int plan(const muon_matrix_desc* mats, int64_t n, const muon_hyper* h, bool step,
+         std::vector<Chunk>* chunks) {
+  std::vector<Unitized> us;
+  us.reserve((size_t)n);
+  for (int64_t i = 0; i < n; ++i) {
+    const muon_matrix_desc& d = mats[i];
+    Unitized u;
+    u.desc = (int)i;
+    u.rows_u = d.split_rows > 0 ? d.split_rows : d.rows;
+    u.n_units = d.batch * (d.rows / u.rows_u);
+    u.cols = d.cols;
+    u.gdtype = step ? d.grad_dtype : MUON_DTYPE_F32;
+    us.push_back(u);
+  }
+  // Group in order of first appearance.
+  std::map<std::tuple<int64_t, int64_t, int32_t>, int> gid;
+  std::vector<std::vector<int>> groups;
+  for (size_t i = 0; i < us.size(); ++i) {
+    auto key = std::make_tuple(us[i].rows_u, us[i].cols, us[i].gdtype);
+    auto it = gid.find(key);
+    if (it == gid.end()) {
+      gid.emplace(key, (int)groups.size());
+      groups.push_back({(int)i});
+    } else {
+      groups[it->second].push_back((int)i);
+    }
+  }
+  const int64_t cap = h->batch_update_size > 0 ? h->batch_update_size : INT64_MAX;
+  const int64_t kMaxUnitsPerChunk = (int64_t)1 << 24;  // grid-size guard
+  for (const auto& grp : groups) {
+    const Unitized& u0 = us[grp[0]];
+    Chunk proto;
+    proto.rows_u = u0.rows_u;
+    proto.cols = u0.cols;
+    proto.gdtype = u0.gdtype;
+    proto.tile = pick_tile(u0.rows_u, u0.cols);
+    proto.rows_pad = round_up(u0.rows_u, proto.tile);
+    proto.cols_pad = round_up(u0.cols, proto.tile);
+    proto.tall = u0.rows_u > u0.cols;
+    proto.s_pad = proto.tall ? proto.cols_pad : proto.rows_pad;
+    proto.n_units = 0;
+    // Momentum kernel: about 16K elements per block.
+    proto.rows_per_block = (int)std::max<int64_t>(1, std::min<int64_t>(u0.rows_u, 16384 / u0.cols));
+    proto.blocks_per_unit = (int)((u0.rows_u + proto.rows_per_block - 1) / proto.rows_per_block);
+    const int64_t nvec = proto.rows_pad * proto.cols_pad / 4;
+    proto.norm_vec_per_block = 4096;
+    proto.norm_blocks_per_unit = (int)((nvec + 4095) / 4096);
+    Chunk cur = proto;
+    for (int ui : grp) {
+      const Unitized& u = us[ui];
+      int64_t begin = 0;
+      while (begin < u.n_units) {
+        const int64_t room = std::min(cap, kMaxUnitsPerChunk) - cur.n_units;
+        if (room == 0 || (int)cur.segs.size() == kMaxSeg) {
+          chunks->push_back(cur);
+          cur = proto;
+          continue;
+        }
+        const int64_t take = std::min(room, u.n_units - begin);
+        cur.segs.push_back({u.desc, begin, take});
+        cur.n_units += take;
+        begin += take;
+      }
+    }
+    if (cur.n_units > 0) chunks->push_back(cur);
+  }
+  // Grid-size limits of the launches.
+  for (const Chunk& c : *chunks) {
+    const int64_t tiles = (c.s_pad / c.tile) * (std::max(c.rows_pad, c.cols_pad) / c.tile);
+    if (c.n_units * tiles > INT32_MAX / 2) return MUON_ERR_SHAPE;
+    if (c.n_units * (int64_t)c.blocks_per_unit > INT32_MAX / 2) return MUON_ERR_SHAPE;
+    if (c.n_units * (int64_t)c.norm_blocks_per_unit > INT32_MAX / 2) return MUON_ERR_SHAPE;
+  }
+  return MUON_OK;
+}
+
+size_t workspace_of(const std::vector<Chunk>& chunks, bool bf16) {
+  size_t need = 0;
+  for (const Chunk& c : chunks) need = std::max(need, layout_of(c, bf16).total);
+  return need;
+}
+
+double unit_scale(const Chunk& c, const muon_hyper* h) {
+  const double fo = (double)c.rows_u, fi = (double)c.cols;
+  if (h->scale_mode == MUON_SCALE_SPECTRAL) return std::sqrt(std::max(fo, fi)) * (double)h->gamma;
+  return std::sqrt(fo / fi);
+}
+
+bool misaligned(const void* p) { return ((uintptr_t)p & 15u) != 0; }
+
+struct Range {
+  uintptr_t lo, hi;
+  int owner;
+};
+
+// Overlap between any two written buffers, or between a written buffer and
+// an input of another bank.
+int check_alias(const std::vector<Range>& written, const std::vector<Range>& read) {
+  std::vector<Range> w = written;
+  std::sort(w.begin(), w.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+  for (size_t i = 1; i < w.size(); ++i)
+    if (w[i].lo < w[i - 1].hi) return MUON_ERR_ALIAS;
+  for (const Range& r : read)
+    for (const Range& x : w)
+      if (r.lo < x.hi && x.lo < r.hi && !(r.owner == x.owner && r.lo == x.lo && r.hi == x.hi))
+        return MUON_ERR_ALIAS;
+  return MUON_OK;
+}
+
+struct Tracer {
+  muon_trace* t;
+  hipStream_t s;
+  void before(int kind) {
+    if (t && t->kind == kind && t->count < t->capacity)
+      (void)hipEventRecord(t->events[2 * t->count], s);
+  }
+  void after(int kind) {
+    if (t && t->kind == kind) {
+      if (t->count < t->capacity) (void)hipEventRecord(t->events[2 * t->count + 1], s);
+      t->count++;
+    }
+  }
+};
+
+template <int PHASE, typename T, int TILE>
+void launch_gemm(bool akc, bool bkc, const GemmArgs& g, const ChunkArgs& ca, hipStream_t s) {
+  const int grid = g.n_units * g.tiles_m * g.tiles_n;
+  if (akc && bkc)
+    hipLaunchKernelGGL((ns_gemm<PHASE, T, TILE, true, true>), dim3(grid), dim3(kThreads), 0, s, g, ca);
+  else if (akc && !bkc)
+    hipLaunchKernelGGL((ns_gemm<PHASE, T, TILE, true, false>), dim3(grid), dim3(kThreads), 0, s, g, ca);
+  else
+    hipLaunchKernelGGL((ns_gemm<PHASE, T, TILE, false, false>), dim3(grid), dim3(kThreads), 0, s, g, ca);
+}
+
+template <int PHASE, typename T>
+void launch_gemm_t(int tile, bool akc, bool bkc, const GemmArgs& g, const ChunkArgs& ca,
+                   hipStream_t s) {
+  if (tile == 256)
+    launch_gemm<PHASE, T, 256>(akc, bkc, g, ca, s);
+  else
+    launch_gemm<PHASE, T, 128>(akc, bkc, g, ca, s);
+}
+
+template <int PHASE>
+void launch_phase(bool bf16, int tile, bool akc, bool bkc, const GemmArgs& g, const ChunkArgs& ca,
+                  hipStream_t s) {
+  if (bf16)
+    launch_gemm_t<PHASE, __bf16>(tile, akc, bkc, g, ca, s);
+  else
+    launch_gemm_t<PHASE, float>(tile, akc, bkc, g, ca, s);
+}
+
+// Runs one chunk: momentum (or NS-input copy), norms, normalisation and the
+// NS iterations with the fused final epilogue.
+int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs,
+              const void* const* ins, float* const* moms, const muon_matrix_desc* mats,
+              unsigned char* ws, hipStream_t s, Tracer& tr) {
+  const bool bf16 = h->ns_precision == MUON_NS_BF16;
+  const Layout L = layout_of(c, bf16);
+  ChunkArgs ca;
+  std::memset(&ca, 0, sizeof(ca));
+  ca.n_seg = (int32_t)c.segs.size();
+  ca.n_units = (int32_t)c.n_units;
+  ca.rows = (int32_t)c.rows_u;
+  ca.cols = (int32_t)c.cols;
+  ca.rows_pad = (int32_t)c.rows_pad;
+  ca.cols_pad = (int32_t)c.cols_pad;
+  ca.unit_elems = c.rows_u * c.cols;
+  ca.x_stride = c.rows_pad * c.cols_pad;
+  ca.mu = h->mu;
+  ca.decay = (float)(1.0 - (double)h->lr * (double)h->weight_decay);
+  ca.lr_scale = (float)((double)h->lr * unit_scale(c, h));
+  int32_t first = 0;
+  for (size_t i = 0; i < c.segs.size(); ++i) {
+    const SegRef& r = c.segs[i];
+    const int64_t off = r.unit_begin * c.rows_u * c.cols;  // elements
+    ca.seg[i].w = outs[r.desc] + off;
+    const size_t gsz = (step && mats[r.desc].grad_dtype == MUON_DTYPE_BF16) ? 2 : 4;
+    ca.seg[i].g = static_cast<const unsigned char*>(ins[r.desc]) + off * (int64_t)gsz;
+    ca.seg[i].m = step ? moms[r.desc] + off : nullptr;
+    ca.seg[i].first = first;
+    ca.seg[i].count = (int32_t)r.count;
+    first += (int32_t)r.count;
+  }
+
+  float* x32[2] = {reinterpret_cast<float*>(ws + L.x32[0]), reinterpret_cast<float*>(ws + L.x32[1])};
+  uint16_t* xb[2] = {bf16 ? reinterpret_cast<uint16_t*>(ws + L.xb[0]) : nullptr,
+                     bf16 ? reinterpret_cast<uint16_t*>(ws + L.xb[1]) : nullptr};
+  float* a32 = reinterpret_cast<float*>(ws + L.a32);
+  uint16_t* ab = bf16 ? reinterpret_cast<uint16_t*>(ws + L.ab) : nullptr;
+  void* bop = ws + L.bop;
+  double* partials = reinterpret_cast<double*>(ws + L.partials);
+  float* inv_nu = reinterpret_cast<float*>(ws + L.inv_nu);
+  int32_t* flag = reinterpret_cast<int32_t*>(ws + L.flag);
+
+  const int U = (int)c.n_units;
+  // 1. momentum + Nesterov + partial sums of squares.
+  tr.before(MUON_KERNEL_MOMENTUM);
+  {
+    const dim3 grid(U * c.blocks_per_unit);
+    if (!step)
+      hipLaunchKernelGGL(k_momentum<2>, grid, dim3(kThreads), 0, s, ca, x32[0], partials,
+                         c.rows_per_block, c.blocks_per_unit);
+    else if (c.gdtype == MUON_DTYPE_BF16)
+      hipLaunchKernelGGL(k_momentum<0>, grid, dim3(kThreads), 0, s, ca, x32[0], partials,
+                         c.rows_per_block, c.blocks_per_unit);
+    else
+      hipLaunchKernelGGL(k_momentum<1>, grid, dim3(kThreads), 0, s, ca, x32[0], partials,
+                         c.rows_per_block, c.blocks_per_unit);
+  }
+  tr.after(MUON_KERNEL_MOMENTUM);
+  // 2. norms and X0 = N / ||N||_F.
+  tr.before(MUON_KERNEL_NORMALIZE);
+  hipLaunchKernelGGL(k_norm_finish, dim3(U), dim3(64), 0, s, partials, c.blocks_per_unit, inv_nu,
+                     flag);
+  if (bf16)
+    hipLaunchKernelGGL(k_normalize<true>, dim3(U * c.norm_blocks_per_unit), dim3(kThreads), 0, s,
+                       ca, x32[0], xb[0], inv_nu, c.norm_vec_per_block, c.norm_blocks_per_unit);
+  else
+    hipLaunchKernelGGL(k_normalize<false>, dim3(U * c.norm_blocks_per_unit), dim3(kThreads), 0, s,
+                       ca, x32[0], nullptr, inv_nu, c.norm_vec_per_block, c.norm_blocks_per_unit);
+  tr.after(MUON_KERNEL_NORMALIZE);
+
+  // 3. Newton-Schulz iterations.
+  const int T = c.tile;
+  const int64_t xs = c.rows_pad * c.cols_pad;
+  const int64_t ss = c.s_pad * c.s_pad;
+  const int64_t sp = c.s_pad;
+  const void* xop[2] = {bf16 ? (const void*)xb[0] : (const void*)x32[0],
+                        bf16 ? (const void*)xb[1] : (const void*)x32[1]};
+  const void* aop = bf16 ? (const void*)ab : (const void*)a32;
+  int total = 0;
+  for (int i = 0; i < h->n_stages; ++i) total += h->stages[i].steps;
+  int it = 0;
+  for (int st = 0; st < h->n_stages; ++st) {
+    const muon_ns_stage& sg = h->stages[st];
+    for (int k = 0; k < sg.steps; ++k, ++it) {
+      const int cur = it & 1, nxt = cur ^ 1;
+      const bool last = (it == total - 1);
+      // Gram: A = X X^T (wide) or X^T X (tall), s_pad x s_pad.
+      GemmArgs g;
+      std::memset(&g, 0, sizeof(g));
+      g.n_units = U;
+      g.flag = flag;
+      g.a = xop[cur];
+      g.b = xop[cur];
+      g.a_ustride = g.b_ustride = xs;
+      g.lda = g.ldb = (int32_t)c.cols_pad;
+      g.M = g.N = (int32_t)sp;
+      g.K = (int32_t)(c.tall ? c.rows_pad : c.cols_pad);
+      g.tiles_m = g.tiles_n = (int32_t)(sp / T);
+      g.out32 = a32;
+      g.out16 = ab;
+      g.out_ustride = ss;
+      g.ldo = (int32_t)sp;
+      tr.before(MUON_KERNEL_GRAM);
+      launch_phase<GRAM>(bf16, T, !c.tall, !c.tall, g, ca, s);
+      tr.after(MUON_KERNEL_GRAM);
+      // Polynomial: B = b*A + c*A*A (A symmetric: both operands K-contiguous).
+      std::memset(&g, 0, sizeof(g));
+      g.n_units = U;
+      g.flag = flag;
+      g.a = aop;
+      g.b = aop;
+      g.a_ustride = g.b_ustride = ss;
+      g.lda = g.ldb = (int32_t)sp;
+      g.M = g.N = g.K = (int32_t)sp;
+      g.tiles_m = g.tiles_n = (int32_t)(sp / T);
+      g.out32 = bf16 ? nullptr : static_cast<float*>(bop);
+      g.out16 = bf16 ? bop : nullptr;
+      g.out_ustride = ss;
+      g.ldo = (int32_t)sp;
+      g.aux = a32;
+      g.aux_ustride = ss;
+      g.ldaux = (int32_t)sp;
+      g.cb = sg.b;
+      g.cc = sg.c;
+      tr.before(MUON_KERNEL_POLY);
+      launch_phase<POLY>(bf16, T, true, true, g, ca, s);
+      tr.after(MUON_KERNEL_POLY);
+      // Apply: X' = a*X + B*X (wide) or a*X + X*B (tall).
+      std::memset(&g, 0, sizeof(g));
+      g.n_units = U;
+      g.flag = flag;
+      g.M = (int32_t)c.rows_pad;
+      g.N = (int32_t)c.cols_pad;
+      g.K = (int32_t)sp;
+      g.tiles_m = (int32_t)(c.rows_pad / T);
+      g.tiles_n = (int32_t)(c.cols_pad / T);
+      bool akc, bkc;
+      if (!c.tall) {
+        g.a = bop;           // B[m][k], K-contiguous
+        g.a_ustride = ss;
+        g.lda = (int32_t)sp;
+        g.b = xop[cur];      // X[k][n], N-contiguous
+        g.b_ustride = xs;
+        g.ldb = (int32_t)c.cols_pad;
+        akc = true;
+        bkc = false;
+      } else {
+        g.a = xop[cur];      // X[m][k], K-contiguous
+        g.a_ustride = xs;
+        g.lda = (int32_t)c.cols_pad;
+        g.b = bop;           // B[k][n] = B[n][k], K-contiguous by symmetry
+        g.b_ustride = ss;
+        g.ldb = (int32_t)sp;
+        akc = true;
+        bkc = true;
+      }
+      g.out32 = x32[nxt];
+      g.out16 = bf16 ? (void*)xb[nxt] : nullptr;
+      g.out_ustride = xs;
+      g.ldo = (int32_t)c.cols_pad;
+      g.aux = x32[cur];
+      g.aux_ustride = xs;
+      g.ldaux = (int32_t)c.cols_pad;
+      g.ca = sg.a;
+      g.final_mode = last ? (step ? FINAL_STEP : FINAL_NSOUT) : FINAL_NONE;
+      tr.before(MUON_KERNEL_APPLY);
+      launch_phase<APPLY>(bf16, T, akc, bkc, g, ca, s);
+      tr.after(MUON_KERNEL_APPLY);
+    }
+  }
+  if (hipGetLastError() != hipSuccess) return MUON_ERR_HIP;
+  return MUON_OK;
+}
+
+int run(bool step, float* const* outs, const void* const* ins, float* const* moms,
+        const muon_matrix_desc* mats, int64_t n, const muon_hyper* h, void* ws, size_t ws_bytes,
+        hipStream_t stream, muon_trace* trace) {
+  try {
+    int st = validate_hyper(h);
+    if (st != MUON_OK) return st;
+    st = validate_descs(mats, n, step);
+    if (st != MUON_OK) return st;
+    if (n == 0) return MUON_OK;
+    if (!outs || !ins || (step && !moms)) return MUON_ERR_NULL;
+    std::vector<Range> written, read;
+    for (int64_t i = 0; i < n; ++i) {
+      const muon_matrix_desc& d = mats[i];
+      if (!outs[i] || !ins[i] || (step && !moms[i])) return MUON_ERR_NULL;
+      if (misaligned(outs[i]) || misaligned(ins[i]) || (step && misaligned(moms[i])))
+        return MUON_ERR_ALIGN;
+      const uintptr_t elems = (uintptr_t)(d.batch * d.rows * d.cols);
+      const uintptr_t gsz = (step && d.grad_dtype == MUON_DTYPE_BF16) ? 2 : 4;
+      written.push_back({(uintptr_t)outs[i], (uintptr_t)outs[i] + elems * 4, (int)i});
+      if (step) {
+        written.push_back({(uintptr_t)moms[i], (uintptr_t)moms[i] + elems * 4, (int)i});
+        read.push_back({(uintptr_t)ins[i], (uintptr_t)ins[i] + elems * gsz, -1 - (int)i});
+      } else {
+        // NS only: the input may be the bank's own output buffer, exactly.
+        read.push_back({(uintptr_t)ins[i], (uintptr_t)ins[i] + elems * 4, (int)i});
+      }
+    }
+    st = check_alias(written, read);
+    if (st != MUON_OK) return st;
+    std::vector<Chunk> chunks;
+    st = plan(mats, n, h, step, &chunks);
+    if (st != MUON_OK) return st;
+    const bool bf16 = h->ns_precision == MUON_NS_BF16;
+    const size_t need = workspace_of(chunks, bf16);
+    if (need > 0 && (!ws || ws_bytes < need)) return MUON_ERR_WORKSPACE;
+    if (((uintptr_t)ws & (kAlign - 1)) != 0) return MUON_ERR_ALIGN;
+    Tracer tr{trace, stream};
+    if (trace) trace->count = 0;
+    for (const Chunk& c : chunks) {
+      st = run_chunk(c, h, step, outs, ins, moms, mats, static_cast<unsigned char*>(ws), stream, tr);
+      if (st != MUON_OK) return st;
+    }
+    return MUON_OK;
+  } catch (const std::bad_alloc&) {
+    return MUON_ERR_SHAPE;
+  } catch (...) {
+    return MUON_ERR_HIP;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+void muon_hyper_default(muon_hyper* h) {
+  if (!h) return;
+  std::memset(h, 0, sizeof(*h));
+  h->lr = 2.7e-4f;
+  h->mu = 0.95f;
+  h->weight_decay = 0.1f;
+  h->gamma = 0.18f;
+  h->scale_mode = MUON_SCALE_SPECTRAL;
+  h->ns_precision = MUON_NS_BF16;
+  h->batch_update_size = 0;
+  h->n_stages = 2;
+  h->stages[0] = {8, 3.4445f, -4.7750f, 2.0315f};
+  h->stages[1] = {2, 2.0f, -1.5f, 0.5f};
+}
+
+int muon_workspace_size(const muon_matrix_desc* mats, int64_t n, const muon_hyper* h,
+                        size_t* bytes) {
+  try {
+    if (!bytes) return MUON_ERR_NULL;
+    int st = validate_hyper(h);
+    if (st != MUON_OK) return st;
+    st = validate_descs(mats, n, false);
+    if (st != MUON_OK) return st;
+    std::vector<Chunk> chunks;
+    st = plan(mats, n, h, true, &chunks);
+    if (st != MUON_OK) return st;
+    // Step and NS-only group the same units when dtypes agree; take the
+    // larger of the two plans so that one size serves both.
+    std::vector<Chunk> chunks_ns;
+    st = plan(mats, n, h, false, &chunks_ns);
+    if (st != MUON_OK) return st;
+    const bool bf16 = h->ns_precision == MUON_NS_BF16;
+    *bytes = std::max(workspace_of(chunks, bf16), workspace_of(chunks_ns, bf16));
+    return MUON_OK;
+  } catch (...) {
+    return MUON_ERR_SHAPE;
+  }
+}
+
+int muon_step_batched_traced(float* const* params, const void* const* grads, float* const* momenta,
+                             const muon_matrix_desc* mats, int64_t n, const muon_hyper* h,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream,
+                             muon_trace* trace) {
+  return run(true, params, grads, momenta, mats, n, h, workspace, workspace_bytes, stream, trace);
+}
+
+int muon_step_batched(float* const* params, const void* const* grads, float* const* momenta,
+                      const muon_matrix_desc* mats, int64_t n, const muon_hyper* h,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return run(true, params, grads, momenta, mats, n, h, workspace, workspace_bytes, stream, nullptr);
+}
+
+int muon_newton_schulz_batched_traced(const float* const* x_in, float* const* o_out,
+                                      const muon_matrix_desc* mats, int64_t n, const muon_hyper* h,
+                                      void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                      muon_trace* trace) {
+  return run(false, o_out, reinterpret_cast<const void* const*>(x_in), nullptr, mats, n, h,
+             workspace, workspace_bytes, stream, trace);
+}
+
+int muon_newton_schulz_batched(const float* const* x_in, float* const* o_out,
+                               const muon_matrix_desc* mats, int64_t n, const muon_hyper* h,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return muon_newton_schulz_batched_traced(x_in, o_out, mats, n, h, workspace, workspace_bytes,
+                                           stream, nullptr);
+}
+
+const char* muon_status_string(int status) {
+  switch (status) {
+    case MUON_OK: return "ok";
+    case MUON_ERR_NULL: return "a required pointer is NULL";
+    case MUON_ERR_SHAPE: return "invalid shape (rows/cols/batch < 1, split_rows does not divide rows, or too large)";
+    case MUON_ERR_DTYPE: return "unknown dtype, precision or scale mode";
+    case MUON_ERR_ALIGN: return "a data pointer is not 16-byte aligned (workspace: 256-byte)";
+    case MUON_ERR_WORKSPACE: return "workspace missing or smaller than muon_workspace_size()";
+    case MUON_ERR_HYPER: return "invalid hyper-parameters";
+    case MUON_ERR_HIP: return "HIP launch failed";
+    case MUON_ERR_ALIAS: return "input and output buffers overlap";
+    default: return "unknown status";
+  }
+}
+
+int muon_abi_version(void) { return 1; }
+
+}  // extern "C"

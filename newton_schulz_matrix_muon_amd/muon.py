@@ -1,0 +1,375 @@
+"""Python binding of the Muon C ABI (include/muon.h) via ctypes.
+
+Argument marshalling only: tensors are turned into device pointers and bank
+descriptors, the stream is torch's current stream, and the workspace is a
+cached torch byte tensor.  Every step of the computation runs in the HIP
+library; if it is missing this module raises on import.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass, field
+from typing import Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmuon.so")
+
+MUON_OK = 0
+STATUS_NAMES = {
+    0: "MUON_OK",
+    -1: "MUON_ERR_NULL",
+    -2: "MUON_ERR_SHAPE",
+    -3: "MUON_ERR_DTYPE",
+    -4: "MUON_ERR_ALIGN",
+    -5: "MUON_ERR_WORKSPACE",
+    -6: "MUON_ERR_HYPER",
+    -7: "MUON_ERR_HIP",
+    -8: "MUON_ERR_ALIAS",
+}
+DTYPE_F32, DTYPE_BF16 = 0, 1
+SCALE_SPECTRAL, SCALE_UNIT_RMS_NORM = 0, 1
+NS_FP32, NS_BF16 = 0, 1
+KERNEL_MOMENTUM, KERNEL_NORMALIZE, KERNEL_GRAM, KERNEL_POLY, KERNEL_APPLY = 1, 2, 3, 4, 5
+MAX_STAGES = 4
+
+EXPORTED = (
+    "muon_hyper_default",
+    "muon_workspace_size",
+    "muon_step_batched",
+    "muon_newton_schulz_batched",
+    "muon_step_batched_traced",
+    "muon_newton_schulz_batched_traced",
+    "muon_status_string",
+    "muon_abi_version",
+)
+
+
+class MatrixDesc(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64),
+        ("rows", ctypes.c_int64),
+        ("cols", ctypes.c_int64),
+        ("split_rows", ctypes.c_int64),
+        ("grad_dtype", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class NsStage(ctypes.Structure):
+    _fields_ = [
+        ("steps", ctypes.c_int32),
+        ("a", ctypes.c_float),
+        ("b", ctypes.c_float),
+        ("c", ctypes.c_float),
+    ]
+
+
+class HyperC(ctypes.Structure):
+    _fields_ = [
+        ("lr", ctypes.c_float),
+        ("mu", ctypes.c_float),
+        ("weight_decay", ctypes.c_float),
+        ("gamma", ctypes.c_float),
+        ("scale_mode", ctypes.c_int32),
+        ("ns_precision", ctypes.c_int32),
+        ("batch_update_size", ctypes.c_int32),
+        ("n_stages", ctypes.c_int32),
+        ("stages", NsStage * MAX_STAGES),
+    ]
+
+
+class TraceC(ctypes.Structure):
+    _fields_ = [
+        ("events", ctypes.POINTER(ctypes.c_void_p)),
+        ("capacity", ctypes.c_int32),
+        ("kind", ctypes.c_int32),
+        ("count", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+class MuonError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({status_string(status)})")
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python -m newton_schulz_matrix_muon_amd.build` (hipcc, gfx950)"
+        )
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    lib.muon_hyper_default.argtypes = [ctypes.POINTER(HyperC)]
+    lib.muon_hyper_default.restype = None
+    lib.muon_workspace_size.argtypes = [
+        ctypes.POINTER(MatrixDesc), ctypes.c_int64, ctypes.POINTER(HyperC),
+        ctypes.POINTER(ctypes.c_size_t),
+    ]
+    lib.muon_workspace_size.restype = ctypes.c_int
+    step_args = [
+        ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(MatrixDesc),
+        ctypes.c_int64, ctypes.POINTER(HyperC), P, ctypes.c_size_t, P,
+    ]
+    ns_args = [
+        ctypes.POINTER(P), ctypes.POINTER(P), ctypes.POINTER(MatrixDesc), ctypes.c_int64,
+        ctypes.POINTER(HyperC), P, ctypes.c_size_t, P,
+    ]
+    lib.muon_step_batched.argtypes = step_args
+    lib.muon_step_batched.restype = ctypes.c_int
+    lib.muon_step_batched_traced.argtypes = step_args + [ctypes.POINTER(TraceC)]
+    lib.muon_step_batched_traced.restype = ctypes.c_int
+    lib.muon_newton_schulz_batched.argtypes = ns_args
+    lib.muon_newton_schulz_batched.restype = ctypes.c_int
+    lib.muon_newton_schulz_batched_traced.argtypes = ns_args + [ctypes.POINTER(TraceC)]
+    lib.muon_newton_schulz_batched_traced.restype = ctypes.c_int
+    lib.muon_status_string.argtypes = [ctypes.c_int]
+    lib.muon_status_string.restype = ctypes.c_char_p
+    lib.muon_abi_version.argtypes = []
+    lib.muon_abi_version.restype = ctypes.c_int
+    return lib
+
+
+LIB = _load()
+
+
+def status_string(status: int) -> str:
+    return LIB.muon_status_string(status).decode()
+
+
+@dataclass
+class Hyper:
+    """Mirror of `muon_hyper`; defaults come from the library
+    (lr 2.7e-4, mu 0.95, wd 0.1, gamma 0.18, spectral, bf16 NS products,
+    8 x (3.4445, -4.7750, 2.0315) + 2 x (2, -1.5, 0.5))."""
+
+    lr: float = 2.7e-4
+    mu: float = 0.95
+    weight_decay: float = 0.1
+    gamma: float = 0.18
+    scale: str = "spectral"  # or "unit_rms_norm"
+    ns_precision: str = "bf16"  # or "fp32"
+    batch_update_size: int = 0
+    stages: Sequence[tuple[int, tuple[float, float, float]]] = field(
+        default_factory=lambda: ((8, (3.4445, -4.7750, 2.0315)), (2, (2.0, -1.5, 0.5)))
+    )
+
+    def to_c(self) -> HyperC:
+        h = HyperC()
+        h.lr, h.mu, h.weight_decay, h.gamma = self.lr, self.mu, self.weight_decay, self.gamma
+        h.scale_mode = {"spectral": SCALE_SPECTRAL, "unit_rms_norm": SCALE_UNIT_RMS_NORM}[self.scale]
+        h.ns_precision = {"fp32": NS_FP32, "bf16": NS_BF16}[self.ns_precision]
+        h.batch_update_size = self.batch_update_size
+        if not 1 <= len(self.stages) <= MAX_STAGES:
+            raise ValueError("between 1 and 4 NS stages")
+        h.n_stages = len(self.stages)
+        for i, (steps, (a, b, c)) in enumerate(self.stages):
+            h.stages[i].steps, h.stages[i].a, h.stages[i].b, h.stages[i].c = steps, a, b, c
+        return h
+
+
+def default_hyper_c() -> HyperC:
+    h = HyperC()
+    LIB.muon_hyper_default(ctypes.byref(h))
+    return h
+
+
+def _as3d(t: torch.Tensor) -> tuple[int, int, int]:
+    if t.dim() == 2:
+        return 1, t.shape[0], t.shape[1]
+    if t.dim() == 3:
+        return t.shape[0], t.shape[1], t.shape[2]
+    raise ValueError("expected a (rows, cols) or (batch, rows, cols) tensor")
+
+
+def _descs(tensors, split_rows, grad_dtypes) -> ctypes.Array:
+    arr = (MatrixDesc * max(1, len(tensors)))()
+    for i, t in enumerate(tensors):
+        b, r, c = _as3d(t)
+        arr[i].batch, arr[i].rows, arr[i].cols = b, r, c
+        arr[i].split_rows = int(split_rows[i] or 0)
+        arr[i].grad_dtype = grad_dtypes[i]
+        arr[i].reserved = 0
+    return arr
+
+
+def _ptrs(tensors) -> ctypes.Array:
+    arr = (ctypes.c_void_p * max(1, len(tensors)))()
+    for i, t in enumerate(tensors):
+        arr[i] = t.data_ptr()
+    return arr
+
+
+_WS: dict[int, torch.Tensor] = {}
+
+
+def workspace(nbytes: int, device: torch.device) -> torch.Tensor:
+    """A cached byte workspace of at least `nbytes` on `device`."""
+    key = device.index if device.index is not None else torch.cuda.current_device()
+    ws = _WS.get(key)
+    if ws is None or ws.numel() < nbytes:
+        _WS.pop(key, None)
+        ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        _WS[key] = ws
+    return ws
+
+
+def workspace_size(tensors, hyper: Hyper | HyperC, split_rows=None) -> int:
+    split_rows = split_rows or [0] * len(tensors)
+    d = _descs(tensors, split_rows, [DTYPE_F32] * len(tensors))
+    hc = hyper.to_c() if isinstance(hyper, Hyper) else hyper
+    out = ctypes.c_size_t(0)
+    st = LIB.muon_workspace_size(d, len(tensors), ctypes.byref(hc), ctypes.byref(out))
+    if st != MUON_OK:
+        raise MuonError(st, "muon_workspace_size")
+    return out.value
+
+
+def _check(ts, dtype, name, device):
+    for t in ts:
+        if t.device != device:
+            raise ValueError(f"{name}: all tensors must be on {device}")
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: tensors must be contiguous")
+
+
+def _stream_ptr(stream) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def _trace(kind: int, events) -> tuple[TraceC, ctypes.Array]:
+    arr = (ctypes.c_void_p * len(events))()
+    for i, e in enumerate(events):
+        arr[i] = e.cuda_event
+    tr = TraceC()
+    tr.events = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+    tr.capacity = len(events) // 2
+    tr.kind = kind
+    tr.count = 0
+    return tr, arr
+
+
+def step(
+    params: Sequence[torch.Tensor],
+    grads: Sequence[torch.Tensor],
+    momenta: Sequence[torch.Tensor],
+    hyper: Hyper | None = None,
+    split_rows: Sequence[int] | None = None,
+    stream=None,
+    ws: torch.Tensor | None = None,
+    trace: tuple[int, list] | None = None,
+) -> int:
+    """One Muon step, in place on `params` and `momenta` (muon_step_batched).
+
+    params/momenta: fp32 (rows, cols) or (batch, rows, cols) banks;
+    grads: bf16 or fp32 of the same shapes; split_rows: per bank, 0 or the
+    head size.  `trace = (kernel_kind, [events])` brackets every launch of
+    that kernel class with the given events (pairs).  Returns the number of
+    launches of the traced class (0 without a trace)."""
+    hyper = hyper or Hyper()
+    n = len(params)
+    if not (len(grads) == len(momenta) == n):
+        raise ValueError("params, grads and momenta must have the same length")
+    if n == 0:
+        return 0
+    dev = params[0].device
+    _check(params, torch.float32, "params", dev)
+    _check(momenta, torch.float32, "momenta", dev)
+    _check(grads, None, "grads", dev)
+    gd = []
+    for p, g, m in zip(params, grads, momenta):
+        if p.shape != g.shape or p.shape != m.shape:
+            raise ValueError("params, grads and momenta shapes differ")
+        if g.dtype == torch.bfloat16:
+            gd.append(DTYPE_BF16)
+        elif g.dtype == torch.float32:
+            gd.append(DTYPE_F32)
+        else:
+            raise TypeError(f"grads must be bf16 or fp32, got {g.dtype}")
+    split_rows = list(split_rows) if split_rows is not None else [0] * n
+    descs = _descs(params, split_rows, gd)
+    hc = hyper.to_c()
+    need = ctypes.c_size_t(0)
+    st = LIB.muon_workspace_size(descs, n, ctypes.byref(hc), ctypes.byref(need))
+    if st != MUON_OK:
+        raise MuonError(st, "muon_workspace_size")
+    if ws is None:
+        ws = workspace(need.value, dev)
+    args = (
+        _ptrs(params), _ptrs(grads), _ptrs(momenta), descs, n, ctypes.byref(hc),
+        ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()),
+        ctypes.c_void_p(_stream_ptr(stream)),
+    )
+    if trace is None:
+        st = LIB.muon_step_batched(*args)
+        count = 0
+    else:
+        tr, keep = _trace(trace[0], trace[1])
+        st = LIB.muon_step_batched_traced(*args, ctypes.byref(tr))
+        count = tr.count
+    if st != MUON_OK:
+        raise MuonError(st, "muon_step_batched")
+    return count
+
+
+def newton_schulz(
+    xs: Sequence[torch.Tensor],
+    outs: Sequence[torch.Tensor] | None = None,
+    hyper: Hyper | None = None,
+    split_rows: Sequence[int] | None = None,
+    stream=None,
+    ws: torch.Tensor | None = None,
+    trace: tuple[int, list] | None = None,
+):
+    """Hybrid Newton-Schulz only (muon_newton_schulz_batched): the unscaled
+    NS output of every unit of every fp32 bank in `xs`, written to `outs`
+    (new tensors when None).  Returns (outs, traced launch count)."""
+    hyper = hyper or Hyper()
+    n = len(xs)
+    if outs is None:
+        outs = [torch.empty_like(x) for x in xs]
+    if n == 0:
+        return outs, 0
+    dev = xs[0].device
+    _check(xs, torch.float32, "xs", dev)
+    _check(outs, torch.float32, "outs", dev)
+    split_rows = list(split_rows) if split_rows is not None else [0] * n
+    descs = _descs(xs, split_rows, [DTYPE_F32] * n)
+    hc = hyper.to_c()
+    need = ctypes.c_size_t(0)
+    st = LIB.muon_workspace_size(descs, n, ctypes.byref(hc), ctypes.byref(need))
+    if st != MUON_OK:
+        raise MuonError(st, "muon_workspace_size")
+    if ws is None:
+        ws = workspace(need.value, dev)
+    args = (
+        _ptrs(xs), _ptrs(outs), descs, n, ctypes.byref(hc), ctypes.c_void_p(ws.data_ptr()),
+        ctypes.c_size_t(ws.numel()), ctypes.c_void_p(_stream_ptr(stream)),
+    )
+    if trace is None:
+        st = LIB.muon_newton_schulz_batched(*args)
+        count = 0
+    else:
+        tr, keep = _trace(trace[0], trace[1])
+        st = LIB.muon_newton_schulz_batched_traced(*args, ctypes.byref(tr))
+        count = tr.count
+    if st != MUON_OK:
+        raise MuonError(st, "muon_newton_schulz_batched")
+    return outs, count
+
+
+def unit_scale(rows_u: int, cols: int, hyper: Hyper) -> float:
+    """The update scale the library applies to a unit (for reporting)."""
+    if hyper.scale == "spectral":
+        return math.sqrt(max(rows_u, cols)) * hyper.gamma
+    return math.sqrt(rows_u / cols)

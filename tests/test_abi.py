@@ -1,0 +1,140 @@
+"""The C ABI without a GPU: the library loads, exports every symbol that
+include/muon.h declares, fills the pages' defaults, sizes workspaces, and
+rejects invalid arguments before touching any memory (no launch happens on
+an error path, so fake device addresses are safe here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from newton_schulz_matrix_muon_amd import muon
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "muon.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(muon_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    names = header_functions()
+    assert set(names) == set(muon.EXPORTED)
+    for n in names:
+        assert hasattr(muon.LIB, n), n
+
+
+def test_defaults_are_the_pages_values():
+    h = muon.default_hyper_c()
+    assert h.lr == pytest.approx(2.7e-4) and h.mu == pytest.approx(0.95)
+    assert h.weight_decay == pytest.approx(0.1) and h.gamma == pytest.approx(0.18)
+    assert h.scale_mode == muon.SCALE_SPECTRAL and h.ns_precision == muon.NS_BF16
+    assert h.n_stages == 2
+    assert (h.stages[0].steps, h.stages[1].steps) == (8, 2)
+    assert (h.stages[0].a, h.stages[0].b, h.stages[0].c) == pytest.approx((3.4445, -4.7750, 2.0315))
+    assert (h.stages[1].a, h.stages[1].b, h.stages[1].c) == (2.0, -1.5, 0.5)
+
+
+def _desc(shapes):
+    arr = (muon.MatrixDesc * max(1, len(shapes)))()
+    for i, s in enumerate(shapes):
+        b, r, c, sp = s
+        arr[i].batch, arr[i].rows, arr[i].cols, arr[i].split_rows = b, r, c, sp
+        arr[i].grad_dtype = muon.DTYPE_BF16
+    return arr
+
+
+def ws_size(shapes, h=None):
+    h = h or muon.default_hyper_c()
+    out = ctypes.c_size_t(0)
+    st = muon.LIB.muon_workspace_size(_desc(shapes), len(shapes), ctypes.byref(h), ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_sizes():
+    mib = 1024 * 1024
+    st, n = ws_size([(32, 1024, 1024, 0)])
+    assert st == 0
+    # bf16 path: two fp32 + two bf16 iterates, fp32 + bf16 Gram, bf16
+    # polynomial = 20 bytes per element, plus per-unit norms
+    assert 32 * mib * 20 <= n < 32 * mib * 20 + mib
+    h = muon.default_hyper_c()
+    h.batch_update_size = 8
+    st, n8 = ws_size([(32, 1024, 1024, 0)], h)
+    assert st == 0 and 8 * mib * 20 <= n8 < 8 * mib * 20 + mib
+    h.ns_precision = muon.NS_FP32
+    st, nf = ws_size([(32, 1024, 1024, 0)], h)
+    # fp32 path: two fp32 iterates, fp32 Gram and polynomial = 16 bytes
+    assert st == 0 and 8 * mib * 16 <= nf < 8 * mib * 16 + mib
+    assert ws_size([])[0] == 0
+
+
+@pytest.mark.parametrize(
+    "shape,code",
+    [
+        ((1, 0, 5, 0), -2),
+        ((1, 5, 0, 0), -2),
+        ((0, 5, 5, 0), -2),
+        ((1, 10, 5, 3), -2),   # split does not divide rows
+        ((1, 10, 5, -1), -2),
+    ],
+)
+def test_bad_shapes_rejected(shape, code):
+    assert ws_size([shape])[0] == code
+
+
+def test_bad_hyper_rejected():
+    h = muon.default_hyper_c()
+    h.n_stages = 0
+    assert ws_size([(1, 4, 4, 0)], h)[0] == -6
+    h = muon.default_hyper_c()
+    h.lr = float("nan")
+    assert ws_size([(1, 4, 4, 0)], h)[0] == -6
+    h = muon.default_hyper_c()
+    h.scale_mode = 7
+    assert ws_size([(1, 4, 4, 0)], h)[0] == -3
+    h = muon.default_hyper_c()
+    h.stages[0].steps = 0
+    h.stages[1].steps = 0
+    assert ws_size([(1, 4, 4, 0)], h)[0] == -6
+
+
+def _step(ptrs_w, ptrs_g, ptrs_m, shapes, ws=0x10000000, ws_bytes=1 << 40, h=None):
+    n = len(shapes)
+    P = ctypes.c_void_p * max(1, n)
+    h = h or muon.default_hyper_c()
+    return muon.LIB.muon_step_batched(
+        P(*ptrs_w), P(*ptrs_g), P(*ptrs_m), _desc(shapes), n, ctypes.byref(h),
+        ctypes.c_void_p(ws), ctypes.c_size_t(ws_bytes), None,
+    )
+
+
+BASE = 0x7F0000000000
+
+
+def test_step_error_paths_touch_nothing():
+    s = [(1, 64, 128, 0)]
+    sz = 64 * 128 * 4
+    ok = ([BASE], [BASE + 2 * sz], [BASE + 4 * sz])
+    assert _step([0], ok[1], ok[2], s) == -1                      # NULL param
+    assert _step(ok[0], ok[1], ok[2], s, ws=0, ws_bytes=0) == -5   # no workspace
+    assert _step(ok[0], ok[1], ok[2], s, ws_bytes=16) == -5        # too small
+    assert _step([BASE + 4], ok[1], ok[2], s) == -4                # misaligned
+    assert _step(ok[0], ok[1], ok[2], s, ws=0x10000010) == -4      # workspace alignment
+    assert _step(ok[0], ok[1], [BASE + 112], s) == -8              # params overlap momenta
+    assert _step(ok[0], [BASE + 64], ok[2], s) == -8               # grads overlap params
+    assert _step(ok[0], ok[1], ok[2], [(1, 64, 128, 5)]) == -2     # bad split
+    h = muon.default_hyper_c()
+    h.ns_precision = 3
+    assert _step(ok[0], ok[1], ok[2], s, h=h) == -3
+    assert _step([], [], [], []) == 0                              # no-op
+
+
+def test_status_strings():
+    for code in range(-8, 1):
+        assert muon.status_string(code)
+    assert muon.status_string(12345) == "unknown status"
+    assert muon.LIB.muon_abi_version() == 1

@@ -1,0 +1,206 @@
+"""GPU parity of the HIP Muon path against the float64 oracle.
+
+Small cases run the oracle in full (several tiles, ragged tails, tall and
+wide units, split heads); the benchmark workload (32 x 1024^2, bf16
+gradients) is checked on sampled units over every step.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests.parity import TOL_M, TOL_NS, check_weight, f64, oracle_hyper, rel, say
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _seeded(shape, seed, scale=1.0):
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    return (torch.randn(shape, generator=g, dtype=torch.float32) * scale).to(DEV)
+
+
+# ------------------------------------------------------------ NS only -------
+NS_SHAPES = [
+    (64, 128),    # the single-matrix workload, one padded 128-tile
+    (128, 64),    # tall
+    (200, 300),   # ragged on both sides, 128 tiles
+    (300, 200),   # ragged tall
+    (1, 7),
+    (7, 1),
+    (1, 1),
+    (256, 512),   # 256 tiles
+    (600, 260),   # 256 tiles, ragged tall
+    (384, 1000),  # 256 tiles, ragged wide, several tiles each way
+]
+
+
+@pytest.mark.parametrize("prec", ["fp32", "bf16"])
+@pytest.mark.parametrize("shape", NS_SHAPES, ids=[f"{r}x{c}" for r, c in NS_SHAPES])
+def test_ns_only_matches_oracle(gpu_lib, shape, prec):
+    say(f"[ns] shape={shape} prec={prec}")
+    x = _seeded(shape, 1000 + shape[0] * 7 + shape[1])
+    h = gpu_lib.Hyper(ns_precision=prec)
+    outs, _ = gpu_lib.newton_schulz([x], hyper=h)
+    torch.cuda.synchronize()
+    o_ref = oracle.newton_schulz(f64(x))
+    e = rel(f64(outs[0]), o_ref)
+    say(f"   rel err {e:.3e}")
+    assert e <= TOL_NS[prec], f"rel err {e:.3e}"
+
+
+@pytest.mark.parametrize("prec", ["fp32", "bf16"])
+def test_ns_split_heads_and_banks(gpu_lib, prec):
+    # A (batch=3, 6*32, 96) bank split into 32-row heads: 18 units.
+    say(f"[ns split] prec={prec}")
+    x = _seeded((3, 192, 96), 77)
+    h = gpu_lib.Hyper(ns_precision=prec)
+    outs, _ = gpu_lib.newton_schulz([x], hyper=h, split_rows=[32])
+    torch.cuda.synchronize()
+    xo, oo = f64(x), f64(outs[0])
+    worst = 0.0
+    for b in range(3):
+        for hd in range(6):
+            blk = slice(hd * 32, (hd + 1) * 32)
+            worst = max(worst, rel(oo[b, blk], oracle.newton_schulz(xo[b, blk])))
+    say(f"   worst rel err {worst:.3e}")
+    assert worst <= TOL_NS[prec]
+
+
+def test_ns_zero_unit_gives_zero(gpu_lib):
+    x = _seeded((2, 64, 128), 5)
+    x[1].zero_()
+    outs, _ = gpu_lib.newton_schulz([x], hyper=gpu_lib.Hyper())
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(outs[0][1]).item() == 0
+    assert rel(f64(outs[0][0]), oracle.newton_schulz(f64(x[0]))) <= TOL_NS["bf16"]
+
+
+@pytest.mark.parametrize("prec", ["fp32", "bf16"])
+def test_batch_vs_single_bitwise(gpu_lib, prec):
+    # RFC-0023 risk list: stacking must not change results.  The kernels
+    # are deterministic and per-unit, so stacked, chunked and single runs
+    # must agree bit for bit.
+    say(f"[batch-vs-single] prec={prec}")
+    xs = _seeded((5, 200, 300), 11)
+    h = gpu_lib.Hyper(ns_precision=prec)
+    stacked, _ = gpu_lib.newton_schulz([xs], hyper=h)
+    h2 = gpu_lib.Hyper(ns_precision=prec, batch_update_size=2)
+    chunked, _ = gpu_lib.newton_schulz([xs], hyper=h2)
+    singles = [gpu_lib.newton_schulz([xs[i].clone()], hyper=h)[0][0] for i in range(5)]
+    torch.cuda.synchronize()
+    assert torch.equal(stacked[0], chunked[0])
+    for i in range(5):
+        assert torch.equal(stacked[0][i], singles[i])
+
+
+def test_ns_in_place(gpu_lib):
+    x = _seeded((96, 160), 21)
+    ref = oracle.newton_schulz(f64(x))
+    gpu_lib.newton_schulz([x], outs=[x], hyper=gpu_lib.Hyper(ns_precision="fp32"))
+    torch.cuda.synchronize()
+    assert rel(f64(x), ref) <= TOL_NS["fp32"]
+
+
+# -------------------------------------------------------------- step --------
+def _run_steps(gpu_lib, w0, grads, h, split_rows=0):
+    """Run len(grads) GPU steps and the oracle alongside; return per-step
+    (W_gpu, M_gpu, W_ref, M_ref)."""
+    w = w0.clone()
+    m = torch.zeros_like(w0)
+    hw = oracle_hyper(h)
+    w_ref = f64(w0)
+    m_ref = np.zeros_like(w_ref)
+    out = []
+    for t, g in enumerate(grads, start=1):
+        gpu_lib.step([w], [g], [m], hyper=h, split_rows=[split_rows])
+        torch.cuda.synchronize()
+        g64 = f64(g)
+        if w_ref.ndim == 3:
+            for b in range(w_ref.shape[0]):
+                w_ref[b], m_ref[b], _ = oracle.muon_step(w_ref[b], g64[b], m_ref[b], hw, split_rows, t)
+        else:
+            w_ref, m_ref, _ = oracle.muon_step(w_ref, g64, m_ref, hw, split_rows, t)
+        out.append((f64(w), f64(m), w_ref.copy(), m_ref.copy()))
+    return out
+
+
+@pytest.mark.parametrize("prec", ["fp32", "bf16"])
+def test_step_single_fp32_matrix_workload(gpu_lib, prec):
+    # 64x128 fp32 weight ~ N(0, 0.02), five steps of fp32 N(0, 1) grads,
+    # momentum from zero, spectral scale.
+    say(f"[step 64x128] prec={prec}")
+    wl = W.workload(1)
+    w0 = W.init_weight(wl, 0, (64, 128)).to(DEV)
+    grads = [W.grad_tensor(wl, t, 0, (64, 128), "fp32").to(DEV) for t in range(wl.steps)]
+    h = gpu_lib.Hyper(ns_precision=prec)
+    res = _run_steps(gpu_lib, w0, grads, h)
+    w0_64 = f64(w0)
+    for t, (wg, mg, wr, mr) in enumerate(res, start=1):
+        assert rel(mg, mr) <= TOL_M, f"step {t} momentum"
+        e = check_weight(wg, wr, w0_64, t, h, TOL_NS[prec], f"step {t}")
+        say(f"   step {t}: rel update err {e:.3e}")
+
+
+def test_step_zero_gradient_is_pure_decay(gpu_lib):
+    w0 = _seeded((2, 200, 300), 3, 0.02)
+    g = torch.zeros_like(w0, dtype=torch.bfloat16)
+    w = w0.clone()
+    m = torch.zeros_like(w0)
+    gpu_lib.step([w], [g], [m])
+    torch.cuda.synchronize()
+    d = np.float32(1.0 - np.float64(np.float32(2.7e-4)) * np.float64(np.float32(0.1)))
+    expect = f64(w0).astype(np.float32) * d
+    assert torch.count_nonzero(m).item() == 0
+    np.testing.assert_array_max_ulp(f64(w).astype(np.float32), expect, maxulp=1)
+
+
+def test_step_split_heads_bf16_studentt(gpu_lib):
+    # A fused 6-head QKV-like bank with 64-row heads, Student-t grads.
+    say("[step split heads]")
+    w0 = _seeded((384, 256), 8, 0.02)
+    grads = []
+    for t in range(3):
+        g = torch.Generator(device="cpu").manual_seed(900 + t)
+        z = torch.randn((384, 256), generator=g)
+        chi = sum(torch.randn((384, 256), generator=g) ** 2 for _ in range(3))
+        grads.append((z / torch.sqrt(chi / 3) * 1e-3).to(torch.bfloat16).to(DEV))
+    h = gpu_lib.Hyper()
+    res = _run_steps(gpu_lib, w0, grads, h, split_rows=64)
+    w0_64 = f64(w0)
+    for t, (wg, mg, wr, mr) in enumerate(res, start=1):
+        assert rel(mg, mr) <= TOL_M
+        for hd in range(6):
+            blk = slice(hd * 64, (hd + 1) * 64)
+            check_weight(wg[blk], wr[blk], w0_64[blk], t, h, TOL_NS["bf16"], f"step {t} head {hd}")
+
+
+@pytest.mark.parametrize("prec", ["bf16", "fp32"])
+def test_step_stacked_1024_workload_sampled(gpu_lib, prec):
+    # The benchmark workload: 32 stacked 1024x1024 fp32 weights, bf16 grads
+    # N(0, 1e-3), ten steps, spectral scale.  The GPU updates the whole
+    # stack; the oracle follows three sampled matrices through every step.
+    say(f"[step 32x1024^2] prec={prec}")
+    wl = W.workload(2)
+    w = W.bank_weights(wl, 0, DEV)
+    w0 = f64(w)
+    m = torch.zeros_like(w)
+    h = gpu_lib.Hyper(ns_precision=prec)
+    hw = oracle_hyper(h)
+    sample = [0, 13, 31]
+    w_ref = {i: w0[i].copy() for i in sample}
+    m_ref = {i: np.zeros((1024, 1024)) for i in sample}
+    steps = wl.steps if prec == "bf16" else 3
+    for t in range(1, steps + 1):
+        g = W.bank_grads(wl, t - 1, 0, DEV)
+        gpu_lib.step([w], [g], [m], hyper=h)
+        torch.cuda.synchronize()
+        for i in sample:
+            w_ref[i], m_ref[i], _ = oracle.muon_step(w_ref[i], f64(g[i]), m_ref[i], hw, 0, t)
+        for i in sample:
+            assert rel(f64(m[i]), m_ref[i]) <= TOL_M
+            e = check_weight(f64(w[i]), w_ref[i], w0[i], t, h, TOL_NS[prec], f"step {t} mat {i}")
+        say(f"   step {t}: last rel update err {e:.3e}")
