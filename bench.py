@@ -1,0 +1,262 @@
+"""Benchmark of the MI355X Muon step.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--ns bf16|fp32]
+
+A step is one Muon update (momentum, Nesterov, Frobenius normalisation, ten
+hybrid Newton-Schulz iterations, scale and decoupled weight decay) of every
+matrix of the workload, with inputs resident in HBM.  The default workload
+is 32 stacked 1024x1024 fp32 weights with bf16 gradients N(0, 1e-3),
+spectral scale, bf16 NS products (fp32 accumulation).
+
+Prints one JSON line with matrices/s (the metric), NS TFLOP/s and its
+fraction of the bf16 MFMA peak, the roofline of the dominant kernel class
+(timed live with HIP events around each of its launches on the step's
+stream), and a float64 CPU-oracle baseline on a bounded sample.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2516.6, "fp32": 157.3}  # MI355X dense MFMA
+HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--ns", default="bf16", choices=["bf16", "fp32"])
+    ap.add_argument("--batch-update-size", type=int, default=0)
+    ap.add_argument("--grad-sets", type=int, default=4, help="distinct resident gradient batches")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def build_inputs(wl, dev, grad_sets):
+    import torch
+
+    import workloads as W
+
+    params, moms, grads, splits = [], [], [], []
+    for i, spec in enumerate(wl.matrices):
+        params.append(W.bank_weights(wl, i, dev))
+        moms.append(torch.zeros((spec.batch, spec.rows, spec.cols), dtype=torch.float32, device=dev))
+        splits.append(spec.split_rows)
+    for k in range(grad_sets):
+        grads.append([W.bank_grads(wl, k, i, dev) for i in range(len(wl.matrices))])
+    return params, moms, grads, splits
+
+
+def nonzero_units(wl):
+    """(s, l, count) of every NS unit shape, excluding all-zero experts."""
+    import workloads as W
+
+    out = []
+    for spec in wl.matrices:
+        r, c = spec.unit_shape
+        n = spec.batch * spec.units_per_matrix
+        if wl.zero_fraction:
+            n -= len(W.zero_experts(wl, spec.batch)) * spec.units_per_matrix
+        out.append((min(r, c), max(r, c), n))
+    return out
+
+
+def kernel_flops(units):
+    """Algorithmic FLOPs of one launch of each NS kernel class, summed over
+    the workload's launches per iteration (one launch per shape group)."""
+    gram = sum(n * 2.0 * s * s * l for s, l, n in units)
+    poly = sum(n * 2.0 * s**3 for s, l, n in units)
+    apply = sum(n * 2.0 * s * s * l for s, l, n in units)
+    return {"gram": gram, "poly": poly, "apply": apply}
+
+
+def cpu_baseline(wl, hyper_o, seconds):
+    """The float64 oracle on a bounded sample of the workload's units."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        blas = [d for d in threadpool_info() if d.get("user_api") == "blas"]
+        threads = blas[0]["num_threads"] if blas else os.cpu_count()
+        blas_name = blas[0].get("internal_api", "?") if blas else "?"
+    except Exception:  # pragma: no cover
+        threads, blas_name = os.cpu_count(), "?"
+    spec = max(wl.matrices, key=lambda m: m.batch)
+    r, c = spec.unit_shape
+    rng = np.random.default_rng(0)
+    done, t0 = 0, time.perf_counter()
+    while True:
+        w = rng.standard_normal((r, c)) * 0.02
+        g = rng.standard_normal((r, c)) * 1e-3
+        oracle.muon_step(w, g, np.zeros((r, c)), hyper_o)
+        done += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {
+        "value": done / el,
+        "unit": "matrices/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{done} units of {r}x{c}, one float64 NumPy Muon step each ({el:.1f} s, {blas_name})",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(
+            f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+            "(the multi-GPU design shards whole matrices and is not built)",
+            file=sys.stderr,
+        )
+        sys.exit(2)
+
+    import torch
+
+    import workloads as W
+    from newton_schulz_matrix_muon_amd import muon
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = W.workload(args.config)
+    hyper = muon.Hyper(scale=wl.scale, ns_precision=args.ns, batch_update_size=args.batch_update_size)
+    params, moms, grads, splits = build_inputs(wl, dev, args.grad_sets)
+    ws_bytes = muon.workspace_size(params, hyper, splits)
+    ws = muon.workspace(ws_bytes, dev)
+    torch.cuda.synchronize()
+
+    units = nonzero_units(wl)
+    n_units = wl.units
+    ns_flops_step = wl.ns_flops() if not wl.zero_fraction else sum(
+        n * 10 * (4.0 * s * s * l + 2.0 * s**3) for s, l, n in units
+    )
+
+    def one_step(k, trace=None):
+        return muon.step(params, grads[k % len(grads)], moms, hyper=hyper, split_rows=splits,
+                         ws=ws, trace=trace)
+
+    iters = sum(s for s, _ in hyper.stages)
+    n_groups = len({(m.unit_shape, m.grad_dtype) for m in wl.matrices})
+    per_step = iters * n_groups * 64  # upper bound on launches of one class per step
+    s0 = torch.cuda.current_stream()
+
+    def make_events(n):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
+        for e in ev:  # create the underlying HIP events
+            e.record(s0)
+        return ev
+
+    def traced_ms(kind, k, ev):
+        cnt = one_step(k, trace=(kind, ev))
+        torch.cuda.synchronize()
+        n = min(cnt, len(ev) // 2)
+        return [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n)]
+
+    # Warm-up (untimed), then one traced step per kernel class to find the
+    # dominant NS class.
+    for k in range(args.warmup):
+        one_step(k)
+    ev1 = make_events(per_step)
+    torch.cuda.synchronize()
+    kinds = {"gram": muon.KERNEL_GRAM, "poly": muon.KERNEL_POLY, "apply": muon.KERNEL_APPLY}
+    per_kind = {name: sum(traced_ms(kind, 0, ev1)) for name, kind in kinds.items()}
+    mom_ms = traced_ms(muon.KERNEL_MOMENTUM, 0, ev1)
+    norm_ms = traced_ms(muon.KERNEL_NORMALIZE, 0, ev1)
+    dominant = max(per_kind, key=per_kind.get)
+
+    # Timed region: exactly `steps` steps; every launch of the dominant class
+    # is bracketed by HIP events on the step's stream, read back afterwards.
+    launches = one_step(0, trace=(kinds[dominant], ev1[:2]))  # launches per step
+    evs = [make_events(launches) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    counts = [one_step(k, trace=(kinds[dominant], evs[k])) for k in range(args.steps)]
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    sec_per_step = (t1 - t0) / args.steps
+    launch_ms = []
+    for ev, cnt in zip(evs, counts):
+        launch_ms += [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(min(cnt, len(ev) // 2))]
+
+    flops = kernel_flops(units)
+    avg_launch_ms = sum(launch_ms) / max(1, len(launch_ms))
+    # algorithmic FLOPs of one launch: the class's FLOPs per step (every
+    # iteration, every non-zero unit) over its launches per step
+    flops_per_launch = flops[dominant] * iters / launches
+    achieved = flops_per_launch / (avg_launch_ms * 1e-3) / 1e12
+    ns_ms = sum(per_kind.values())
+    ns_tflops = ns_flops_step / (ns_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[args.ns]
+    elem_bytes = sum(m.numel for m in wl.matrices) * (18 if wl.matrices[0].grad_dtype == "bf16" else 20)
+
+    line = {
+        "metric": "Muon matrices/sec + NS TFLOP/s (% of MI355X bf16 MFMA peak) per config",
+        "value": n_units / sec_per_step,
+        "unit": "matrices/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": sec_per_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": args.ns,
+        "data": "synthetic",
+        "config": {
+            "workload": wl.title,
+            "config_index": args.config,
+            "units": n_units,
+            "unit_shapes": sorted({f"{m.unit_shape[0]}x{m.unit_shape[1]}" for m in wl.matrices}),
+            "grad_dtype": wl.matrices[0].grad_dtype,
+            "scale": wl.scale,
+            "ns_path": args.ns,
+            "parallelism": "single GPU",
+        },
+        "ns_tflops": ns_tflops,
+        "ns_frac_of_peak": ns_tflops / peak,
+        "ns_ms_per_step": ns_ms,
+        "kernel_ms_per_step": {
+            **{k: round(v, 4) for k, v in per_kind.items()},
+            "momentum": round(sum(mom_ms), 4),
+            "normalize": round(sum(norm_ms), 4),
+        },
+        "elementwise_gbs": elem_bytes / (sum(mom_ms) * 1e-3) / 1e9 if mom_ms else None,
+        "roofline": {
+            "bound": "mfma",
+            "kernel": f"ns_gemm {dominant}",
+            "achieved": achieved,
+            "peak": peak,
+            "unit": "TFLOP/s",
+            "frac": achieved / peak,
+            "traffic": None,
+            "flops_per_launch": flops_per_launch,
+            "avg_launch_ms": avg_launch_ms,
+            "launches_timed": len(launch_ms),
+        },
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+
+        ho = oracle.Hyper(scale=wl.scale)
+        line["cpu_baseline"] = cpu_baseline(wl, ho, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -70,8 +70,10 @@ typedef enum { MUON_SCALE_SPECTRAL = 0, MUON_SCALE_UNIT_RMS_NORM = 1 } muon_scal
 
 /* Precision of the Newton-Schulz matrix products.  FP32: fp32 operands on
  * the fp32 matrix cores.  BF16: bf16 operands with fp32 accumulation; the
- * iterate X, the Gram A and every epilogue (b*A, a*X, the update) stay fp32,
- * only the operands of the three products are rounded (nearest-even). */
+ * iterate X and every epilogue (b*A + c*A^2, a*X + B*X, the update) are
+ * fp32, and what is rounded (nearest-even) to bf16 is what the products
+ * read: X, the Gram A (whose bf16 copy also feeds the b*A term) and the
+ * polynomial B. */
 typedef enum { MUON_NS_FP32 = 0, MUON_NS_BF16 = 1 } muon_ns_precision;
 
 /* A bank of `batch` equal-shape matrices stored back to back (stride

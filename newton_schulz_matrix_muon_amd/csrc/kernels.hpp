@@ -11,7 +11,8 @@
 //   k_normalize     X0 = N/||N||_F over the padded iterate (zeros in the
 //                   padding), plus the bf16 operand copy.
 //   ns_gemm<GRAM>   A = X X^T (or X^T X for a tall unit: the smaller side).
-//   ns_gemm<POLY>   B = b*A + c*A*A.
+//   ns_gemm<POLY>   B = b*A + c*A*A (on the bf16 path A is kept only as its
+//                   bf16 operand copy, which the b*A term also reads).
 //   ns_gemm<APPLY>  X' = a*X + B*X (or X*B); in the last iteration the
 //                   epilogue writes W <- W*(1 - lr*wd) - lr*scale*X' instead
 //                   (Algorithm 1's decoupled update) or the NS output.
@@ -77,7 +78,8 @@ struct GemmArgs {
   int64_t out_ustride;
   int32_t ldo;
   int32_t final_mode;
-  const float* aux;     // A (POLY) or X (APPLY), fp32, same layout as the output
+  const float* aux;     // fp32 A (POLY, fp32 path) or X (APPLY), laid out like the output
+  const void* aux16;    // bf16 A (POLY, bf16 path)
   int64_t aux_ustride;
   int32_t ldaux;
   float ca, cb, cc;     // quintic coefficients
@@ -271,12 +273,20 @@ __global__ __launch_bounds__(kThreads) void k_normalize(ChunkArgs ca, float* __r
 // ------------------------------------------------------------------ GEMM ---
 // Batched C = A_op * B_op over padded units, one TILE x TILE output tile per
 // workgroup of 4 waves (2 x 2, each TILE/2 x TILE/2 as 32x32 MFMA blocks).
-// Operands are staged through LDS with 128-byte rows (64 bf16 or 32 fp32 of
-// K), always K-contiguous in LDS; a K-contiguous global operand is copied
-// 16 bytes at a time, an MN-contiguous one is transposed in registers on the
-// way in.  16-byte chunks are XOR-swizzled so that both the row-wise stores
-// and the 32-row MFMA fragment reads avoid bank conflicts.  Two LDS stages:
-// the global loads of tile k+1 are in flight while tile k is multiplied.
+//
+// LDS holds, per stage, TILE rows of A_op and TILE rows of B_op, each row
+// 128 bytes of K (64 bf16 or 32 fp32) in eight 16-byte chunks, XOR-swizzled
+// (chunk ^ row%8 ^ (row/8)%8) so that 8 consecutive rows read at one logical
+// chunk hit distinct banks.  Two stages live in two separate LDS arrays.
+//  - A K-contiguous global operand is copied global -> LDS directly
+//    (buffer_load_dwordx4 ... lds: lane i of a wave lands at M0 + 16*i, so
+//    the swizzle is applied by choosing which global chunk each lane fetches).
+//  - An MN-contiguous operand is loaded into registers, transposed there in
+//    8x8 (bf16) or 4x4 (fp32) blocks and written to LDS.
+// MFMA fragments are double-buffered across the four K sub-steps of a tile.
+// The MFMA is issued as (B fragment, A fragment), so each lane accumulates
+// C[m][n..n+3] for one row m and 4 consecutive columns: the epilogue moves
+// 16-byte vectors.
 template <typename T>
 struct OpT;
 template <>
@@ -290,108 +300,99 @@ struct OpT<float> {
   static constexpr int kBK = 32;
 };
 
+typedef __attribute__((address_space(3))) void* lds_vptr;
+
 __device__ __forceinline__ int swz(int row, int chunk) {
   return chunk ^ (row & 7) ^ ((row >> 3) & 7);
 }
 
-// Global -> registers for one operand tile (TILE rows of the M or N side,
-// kBK of K).  KC: the operand is K-contiguous in global memory.
-template <typename T, int TILE, bool KC>
-struct TileLoader {
-  static constexpr int kChunks = TILE / 32;  // 16-byte chunks per thread (K-contiguous)
-  // Registers per thread: K-contiguous TILE/32 chunks; transposed bf16 one
-  // 8x8 block (8 chunks) per thread, fewer blocks than threads at TILE 128;
-  // transposed fp32 2*TILE/256 blocks of 4 chunks.
-  static constexpr int kRegs =
-      KC ? kChunks : (sizeof(T) == 2 ? 8 * ((TILE + kThreads - 1) / kThreads) : kChunks);
+// K-contiguous operand: TILE rows x 8 chunks, straight into LDS through a
+// buffer resource whose base is the tile's first row (so 32-bit offsets
+// cover TILE rows).  The MUBUF form (buffer_load ... lds) is used rather
+// than global_load_lds: the latter is a FLAT-encoded LDS writer, which makes
+// the compiler wait for all LDS reads at once while it is in flight.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base) {
+  // raw buffer, stride 0, 2 GiB range, 32-bit data format (gfx9 family)
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
+}
+
+template <typename T, int TILE>
+__device__ __forceinline__ void issue_direct(__amdgpu_buffer_rsrc_t rs, int ld, int k0,
+                                             u32x4* lds_stage) {
+  constexpr int kPerWave = TILE / 32;  // 64-lane instructions per wave
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+#pragma unroll
+  for (int i = 0; i < kPerWave; ++i) {
+    const int slot0 = (w * kPerWave + i) * 64;  // first 16-byte slot of this instruction
+    const int s = slot0 + lane;
+    const int row = s >> 3, pc = s & 7;
+    const int c = pc ^ (row & 7) ^ ((row >> 3) & 7);  // logical chunk stored at (row, pc)
+    const int voff = (row * ld + k0 + c * OpT<T>::kElems) * (int)sizeof(T);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_vptr)(lds_stage + slot0), 16, voff, 0, 0, 0);
+  }
+}
+
+// MN-contiguous operand: registers, transposed on the way to LDS.
+template <typename T, int TILE>
+struct TransLoader {
+  static constexpr bool kBF = sizeof(T) == 2;
+  static constexpr int kBlocks = kBF ? TILE : 2 * TILE;  // 8x8 bf16 or 4x4 fp32 blocks
+  static constexpr int kIters = (kBlocks + kThreads - 1) / kThreads;
+  static constexpr int kRegs = kIters * (kBF ? 8 : 4);
   u32x4 r[kRegs];
 
   __device__ __forceinline__ void load(const T* __restrict__ base, int ld, int mn0, int k0) {
     const int t = threadIdx.x;
-    if constexpr (KC) {
 #pragma unroll
-      for (int i = 0; i < kChunks; ++i) {
-        const int c = t + kThreads * i;
-        const int row = c >> 3, kc = c & 7;
-        r[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)(mn0 + row) * ld + k0 +
-                                                kc * OpT<T>::kElems);
-      }
-    } else if constexpr (sizeof(T) == 2) {
-      // 8 (k) x 8 (mn) bf16 blocks; TILE blocks per tile.
-      constexpr int kBlocks = TILE;
-#pragma unroll
-      for (int i = 0; i < (kBlocks + kThreads - 1) / kThreads; ++i) {
-        const int blk = t + kThreads * i;
-        if (kBlocks % kThreads == 0 || blk < kBlocks) {
+    for (int i = 0; i < kIters; ++i) {
+      const int blk = t + kThreads * i;
+      if (kBlocks % kThreads == 0 || blk < kBlocks) {
+        if constexpr (kBF) {
           const int mb = blk % (TILE / 8), kb = blk / (TILE / 8);
 #pragma unroll
           for (int rr = 0; rr < 8; ++rr)
             r[i * 8 + rr] = *reinterpret_cast<const u32x4*>(
                 base + (int64_t)(k0 + kb * 8 + rr) * ld + mn0 + mb * 8);
+        } else {
+          const int mb = blk % (TILE / 4), kb = blk / (TILE / 4);
+#pragma unroll
+          for (int rr = 0; rr < 4; ++rr)
+            r[i * 4 + rr] = *reinterpret_cast<const u32x4*>(
+                base + (int64_t)(k0 + kb * 4 + rr) * ld + mn0 + mb * 4);
         }
-      }
-    } else {
-      // 4 (k) x 4 (mn) fp32 blocks; 2*TILE blocks per tile.
-      constexpr int kBlocks = 2 * TILE;
-#pragma unroll
-      for (int i = 0; i < kBlocks / kThreads; ++i) {
-        const int blk = t + kThreads * i;
-        const int mb = blk % (TILE / 4), kb = blk / (TILE / 4);
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          r[i * 4 + rr] = *reinterpret_cast<const u32x4*>(
-              base + (int64_t)(k0 + kb * 4 + rr) * ld + mn0 + mb * 4);
       }
     }
   }
 
-  // Registers -> LDS stage (TILE rows x 8 chunks of 16 bytes).
   __device__ __forceinline__ void store(u32x4* __restrict__ lds) const {
     const int t = threadIdx.x;
-    if constexpr (KC) {
 #pragma unroll
-      for (int i = 0; i < kChunks; ++i) {
-        const int c = t + kThreads * i;
-        const int row = c >> 3, kc = c & 7;
-        lds[row * 8 + swz(row, kc)] = r[i];
-      }
-    } else if constexpr (sizeof(T) == 2) {
-      constexpr int kBlocks = TILE;
-#pragma unroll
-      for (int i = 0; i < (kBlocks + kThreads - 1) / kThreads; ++i) {
-        const int blk = t + kThreads * i;
-        if (kBlocks % kThreads == 0 || blk < kBlocks) {
+    for (int i = 0; i < kIters; ++i) {
+      const int blk = t + kThreads * i;
+      if (kBlocks % kThreads == 0 || blk < kBlocks) {
+        if constexpr (kBF) {
           const int mb = blk % (TILE / 8), kb = blk / (TILE / 8);
           const u32x4* v = &r[i * 8];
-          // v[rr] holds mn = mb*8 + 0..7 at k = kb*8 + rr.  Output row
-          // mn = mb*8 + e gets k = kb*8 + 0..7: dword j packs k = 2j, 2j+1.
+          // v[rr] holds mn = mb*8 + 0..7 at k = kb*8 + rr; LDS row
+          // mn = mb*8 + e takes k = kb*8 + 0..7 (dword j packs k = 2j, 2j+1).
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
             uint32_t d[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              const uint32_t lo = v[2 * j][e >> 1];
-              const uint32_t hi = v[2 * j + 1][e >> 1];
-              d[j] = __builtin_amdgcn_perm(hi, lo, sel);
-            }
+            for (int j = 0; j < 4; ++j)
+              d[j] = __builtin_amdgcn_perm(v[2 * j + 1][e >> 1], v[2 * j][e >> 1], sel);
             const int row = mb * 8 + e;
             lds[row * 8 + swz(row, kb)] = u32x4{d[0], d[1], d[2], d[3]};
           }
-        }
-      }
-    } else {
-      constexpr int kBlocks = 2 * TILE;
+        } else {
+          const int mb = blk % (TILE / 4), kb = blk / (TILE / 4);
+          const u32x4* v = &r[i * 4];
 #pragma unroll
-      for (int i = 0; i < kBlocks / kThreads; ++i) {
-        const int blk = t + kThreads * i;
-        const int mb = blk % (TILE / 4), kb = blk / (TILE / 4);
-        const u32x4* v = &r[i * 4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int row = mb * 4 + e;
-          const u32x4 o = u32x4{v[0][e], v[1][e], v[2][e], v[3][e]};
-          lds[row * 8 + swz(row, kb)] = o;
+          for (int e = 0; e < 4; ++e) {
+            const int row = mb * 4 + e;
+            lds[row * 8 + swz(row, kb)] = u32x4{v[0][e], v[1][e], v[2][e], v[3][e]};
+          }
         }
       }
     }
@@ -407,12 +408,43 @@ __device__ __forceinline__ int xcd_remap(int bid, int nb) {
   return x * q + min(x, rem) + i;
 }
 
+template <typename T, int FM>
+__device__ __forceinline__ void mfma_block(const u32x4 (&af)[FM], const u32x4 (&bf)[FM],
+                                           f32x16 (&acc)[FM][FM]) {
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FM; ++j) {
+      // (B, A): the lane owning C row m receives 4 consecutive columns.
+      if constexpr (sizeof(T) == 2) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+            __builtin_bit_cast(bf16x8, bf[j]), __builtin_bit_cast(bf16x8, af[i]), acc[i][j], 0, 0, 0);
+      } else {
+        const f32x4v a4 = __builtin_bit_cast(f32x4v, af[i]);
+        const f32x4v b4 = __builtin_bit_cast(f32x4v, bf[j]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(b4[q], a4[q], acc[i][j], 0, 0, 0);
+      }
+    }
+}
+
+__device__ __forceinline__ void store_bf16x4(void* base, int64_t idx, float a, float b, float c,
+                                             float d) {
+  uint2 p;
+  p.x = (uint32_t)to_bf16_bits(a) | ((uint32_t)to_bf16_bits(b) << 16);
+  p.y = (uint32_t)to_bf16_bits(c) | ((uint32_t)to_bf16_bits(d) << 16);
+  *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + idx) = p;
+}
+
 template <int PHASE, typename T, int TILE, bool AKC, bool BKC>
 __global__ __launch_bounds__(kThreads) void ns_gemm(GemmArgs g, ChunkArgs ca) {
   constexpr int WT = TILE / 2;   // wave tile
   constexpr int FM = WT / 32;    // 32x32 blocks per wave side
   constexpr bool kBF = sizeof(T) == 2;
-  __shared__ u32x4 lds[2 * 2 * TILE * 8];
+  constexpr int kOp = TILE * 8;  // 16-byte slots of one operand in one stage
+  __shared__ u32x4 lds0[2 * kOp];
+  __shared__ u32x4 lds1[2 * kOp];
 
   const int tiles_per_unit = g.tiles_m * g.tiles_n;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -428,11 +460,11 @@ __global__ __launch_bounds__(kThreads) void ns_gemm(GemmArgs g, ChunkArgs ca) {
     if (PHASE == APPLY && g.final_mode != FINAL_NONE) {
       // Zero unit: O' = 0, so the weight only decays / the output is zero.
       const SegView sg = find_seg(ca, u);
-      const int64_t uoff = (int64_t)(u - sg.first) * ca.unit_elems;
+      float* wout = sg.w + (int64_t)(u - sg.first) * ca.unit_elems;
       for (int idx = threadIdx.x; idx < TILE * TILE; idx += kThreads) {
         const int mm = m0 + idx / TILE, nn = n0 + idx % TILE;
         if (mm < ca.rows && nn < ca.cols) {
-          float* p = sg.w + uoff + (int64_t)mm * ca.cols + nn;
+          float* p = wout + (int64_t)mm * ca.cols + nn;
           *p = (g.final_mode == FINAL_STEP) ? (*p) * ca.decay : 0.0f;
         }
       }
@@ -442,8 +474,6 @@ __global__ __launch_bounds__(kThreads) void ns_gemm(GemmArgs g, ChunkArgs ca) {
 
   const T* A = static_cast<const T*>(g.a) + (int64_t)u * g.a_ustride;
   const T* B = static_cast<const T*>(g.b) + (int64_t)u * g.b_ustride;
-  // Stage st: A rows at lds + st*2*TILE*8, B rows right after them.
-  constexpr int kStage = 2 * TILE * 8;
 
   f32x16 acc[FM][FM];
 #pragma unroll
@@ -453,15 +483,31 @@ __global__ __launch_bounds__(kThreads) void ns_gemm(GemmArgs g, ChunkArgs ca) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  TileLoader<T, TILE, AKC> la;
-  TileLoader<T, TILE, BKC> lb;
+  TransLoader<T, TILE> ta, tb;
   constexpr int BK = OpT<T>::kBK;
   const int nk = g.K / BK;
 
-  la.load(A, g.lda, m0, 0);
-  lb.load(B, g.ldb, n0, 0);
-  la.store(lds);
-  lb.store(lds + TILE * 8);
+  const __amdgpu_buffer_rsrc_t rsa = tile_rsrc(A + (int64_t)m0 * g.lda);
+  const __amdgpu_buffer_rsrc_t rsb = tile_rsrc(B + (int64_t)n0 * g.ldb);
+  auto issue = [&](int kt, u32x4* stage) {
+    if constexpr (AKC) issue_direct<T, TILE>(rsa, g.lda, kt * BK, stage);
+    else ta.load(A, g.lda, m0, kt * BK);
+    if constexpr (BKC) issue_direct<T, TILE>(rsb, g.ldb, kt * BK, stage + kOp);
+    else tb.load(B, g.ldb, n0, kt * BK);
+  };
+  auto finish = [&](u32x4* stage) {
+    if constexpr (!AKC) ta.store(stage);
+    if constexpr (!BKC) tb.store(stage + kOp);
+  };
+
+  issue(0, lds0);
+  finish(lds0);
+  // Drain the scalar (kernel-argument) loads before the K loop: a scalar
+  // load still in flight would force every LDS wait in the loop to wait for
+  // everything, since scalar loads can return out of order.
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);
   __syncthreads();
 
   const int arow0 = wm * WT + (lane & 31);
@@ -469,92 +515,134 @@ __global__ __launch_bounds__(kThreads) void ns_gemm(GemmArgs g, ChunkArgs ca) {
   const int half = lane >> 5;
 
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) {
-      la.load(A, g.lda, m0, (kt + 1) * BK);
-      lb.load(B, g.ldb, n0, (kt + 1) * BK);
+    u32x4* cur = (kt & 1) ? lds1 : lds0;
+    u32x4* nxt = (kt & 1) ? lds0 : lds1;
+    if (kt + 1 < nk) issue(kt + 1, nxt);
+    const u32x4* As = cur;
+    const u32x4* Bs = cur + kOp;
+    u32x4 af[2][FM], bf[2][FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int ra = arow0 + i * 32, rb = brow0 + i * 32;
+      af[0][i] = As[ra * 8 + swz(ra, half)];
+      bf[0][i] = Bs[rb * 8 + swz(rb, half)];
     }
-    const u32x4* As = lds + cur * kStage;
-    const u32x4* Bs = As + TILE * 8;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      const int ch = 2 * kk + half;
-      u32x4 af[FM], bfr[FM];
+      // One scheduling region per sub-step: the fragment reads of sub-step
+      // kk+1 and the MFMAs of sub-step kk (which only read registers loaded
+      // in the previous region), so LDS latency hides under the MFMAs.
+      __builtin_amdgcn_sched_barrier(0);
+      if (kk < 3) {
+        const int ch = 2 * (kk + 1) + half;
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int ra = arow0 + i * 32;
-        af[i] = As[ra * 8 + swz(ra, ch)];
-        const int rb = brow0 + i * 32;
-        bfr[i] = Bs[rb * 8 + swz(rb, ch)];
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FM; ++j) {
-          if constexpr (kBF) {
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                __builtin_bit_cast(bf16x8, af[i]), __builtin_bit_cast(bf16x8, bfr[j]), acc[i][j],
-                0, 0, 0);
-          } else {
-            const f32x4v a4 = __builtin_bit_cast(f32x4v, af[i]);
-            const f32x4v b4 = __builtin_bit_cast(f32x4v, bfr[j]);
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(a4[q], b4[q], acc[i][j], 0, 0, 0);
-          }
+        for (int i = 0; i < FM; ++i) {
+          const int ra = arow0 + i * 32, rb = brow0 + i * 32;
+          af[(kk + 1) & 1][i] = As[ra * 8 + swz(ra, ch)];
+          bf[(kk + 1) & 1][i] = Bs[rb * 8 + swz(rb, ch)];
         }
+      }
+      mfma_block<T, FM>(af[kk & 1], bf[kk & 1], acc);
+      // Within the region: every fragment read first, then the MFMAs, so
+      // the reads have the whole region to land.
+      if (kk < 3) __builtin_amdgcn_sched_group_barrier(0x100, 2 * FM, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, FM * FM * (kBF ? 1 : 4), 0);
     }
-    if (kt + 1 < nk) {
-      la.store(lds + (cur ^ 1) * kStage);
-      lb.store(lds + (cur ^ 1) * kStage + TILE * 8);
-    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 1 < nk) finish(nxt);
     __syncthreads();
   }
 
-  // ---- epilogue: lane holds C[m][n] for n = lane%32 and
-  // m = 8*(r/4) + 4*(lane/32) + r%4 within each 32x32 block.
-  const int ncol = lane & 31;
-  const int mrow = 4 * half;
+  // ---- epilogue: lane holds C[m][n + 0..3] for m = .. + lane%32 and
+  // n = .. + 8*q + 4*(lane/32), q = r/4, within each 32x32 block.
   float* wout = nullptr;
   if (PHASE == APPLY && g.final_mode != FINAL_NONE) {
     const SegView sg = find_seg(ca, u);
     wout = sg.w + (int64_t)(u - sg.first) * ca.unit_elems;
   }
+  const bool vec_w = (ca.cols & 3) == 0;
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < FM; ++i) {
+    const int m = m0 + wm * WT + i * 32 + (lane & 31);
+    float4 aux[FM][4];
+    if constexpr (PHASE == POLY && kBF) {
+      // bf16 path: A exists only as the bf16 operand copy.
+      const uint16_t* ap = static_cast<const uint16_t*>(g.aux16) + (int64_t)u * g.aux_ustride +
+                           (int64_t)m * g.ldaux;
+#pragma unroll
+      for (int j = 0; j < FM; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint2 h = *reinterpret_cast<const uint2*>(ap + n0 + wn * WT + j * 32 + 8 * q + 4 * half);
+          aux[j][q] = make_float4(bf16_bits_to_f32(h.x & 0xffffu), bf16_bits_to_f32(h.x >> 16),
+                                  bf16_bits_to_f32(h.y & 0xffffu), bf16_bits_to_f32(h.y >> 16));
+        }
+    } else if constexpr (PHASE != GRAM) {
+      const float* ap = g.aux + (int64_t)u * g.aux_ustride + (int64_t)m * g.ldaux;
+#pragma unroll
+      for (int j = 0; j < FM; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          aux[j][q] = *reinterpret_cast<const float4*>(ap + n0 + wn * WT + j * 32 + 8 * q + 4 * half);
+    }
 #pragma unroll
     for (int j = 0; j < FM; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int m = m0 + wm * WT + i * 32 + 8 * (r >> 2) + mrow + (r & 3);
-        const int n = n0 + wn * WT + j * 32 + ncol;
-        const float v = acc[i][j][r];
+      for (int q = 0; q < 4; ++q) {
+        const int n = n0 + wn * WT + j * 32 + 8 * q + 4 * half;
+        const f32x16& c = acc[i][j];
+        float v0 = c[4 * q], v1 = c[4 * q + 1], v2 = c[4 * q + 2], v3 = c[4 * q + 3];
         const int64_t o = (int64_t)u * g.out_ustride + (int64_t)m * g.ldo + n;
         if constexpr (PHASE == GRAM) {
-          g.out32[o] = v;
-          if constexpr (kBF) static_cast<uint16_t*>(g.out16)[o] = to_bf16_bits(v);
-        } else if constexpr (PHASE == POLY) {
-          const float bv =
-              g.cb * g.aux[(int64_t)u * g.aux_ustride + (int64_t)m * g.ldaux + n] + g.cc * v;
           if constexpr (kBF)
-            static_cast<uint16_t*>(g.out16)[o] = to_bf16_bits(bv);
+            store_bf16x4(g.out16, o, v0, v1, v2, v3);
           else
-            g.out32[o] = bv;
+            *reinterpret_cast<float4*>(g.out32 + o) = make_float4(v0, v1, v2, v3);
+        } else if constexpr (PHASE == POLY) {
+          const float4 a = aux[j][q];
+          v0 = g.cb * a.x + g.cc * v0;
+          v1 = g.cb * a.y + g.cc * v1;
+          v2 = g.cb * a.z + g.cc * v2;
+          v3 = g.cb * a.w + g.cc * v3;
+          if constexpr (kBF)
+            store_bf16x4(g.out16, o, v0, v1, v2, v3);
+          else
+            *reinterpret_cast<float4*>(g.out32 + o) = make_float4(v0, v1, v2, v3);
         } else {
-          const float xv = __builtin_fmaf(
-              g.ca, g.aux[(int64_t)u * g.aux_ustride + (int64_t)m * g.ldaux + n], v);
+          const float4 a = aux[j][q];
+          v0 = __builtin_fmaf(g.ca, a.x, v0);
+          v1 = __builtin_fmaf(g.ca, a.y, v1);
+          v2 = __builtin_fmaf(g.ca, a.z, v2);
+          v3 = __builtin_fmaf(g.ca, a.w, v3);
           if (g.final_mode == FINAL_NONE) {
-            g.out32[o] = xv;
-            if constexpr (kBF) static_cast<uint16_t*>(g.out16)[o] = to_bf16_bits(xv);
+            *reinterpret_cast<float4*>(g.out32 + o) = make_float4(v0, v1, v2, v3);
+            if constexpr (kBF) store_bf16x4(g.out16, o, v0, v1, v2, v3);
           } else if (m < ca.rows && n < ca.cols) {
             float* p = wout + (int64_t)m * ca.cols + n;
-            if (g.final_mode == FINAL_STEP)
-              *p = __builtin_fmaf(-ca.lr_scale, xv, (*p) * ca.decay);
-            else
-              *p = xv;
+            const bool step = g.final_mode == FINAL_STEP;
+            if (vec_w && n + 3 < ca.cols) {
+              float4 wv = step ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
+              if (step) {
+                wv.x = __builtin_fmaf(-ca.lr_scale, v0, wv.x * ca.decay);
+                wv.y = __builtin_fmaf(-ca.lr_scale, v1, wv.y * ca.decay);
+                wv.z = __builtin_fmaf(-ca.lr_scale, v2, wv.z * ca.decay);
+                wv.w = __builtin_fmaf(-ca.lr_scale, v3, wv.w * ca.decay);
+              } else {
+                wv = make_float4(v0, v1, v2, v3);
+              }
+              *reinterpret_cast<float4*>(p) = wv;
+            } else {
+              const float vv[4] = {v0, v1, v2, v3};
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                if (n + e < ca.cols)
+                  p[e] = step ? __builtin_fmaf(-ca.lr_scale, vv[e], p[e] * ca.decay) : vv[e];
+              }
+            }
           }
         }
       }
+  }
 }
 
 }  // namespace muon_dev

@@ -78,8 +78,11 @@ Layout layout_of(const Chunk& c, bool bf16) {
     L.xb[0] = take(U * xs * 2);
     L.xb[1] = take(U * xs * 2);
   }
-  L.a32 = take(U * ss * 4);
-  if (bf16) L.ab = take(U * ss * 2);
+  // The Gram is stored once: fp32 on the fp32 path, bf16 on the bf16 path.
+  if (bf16)
+    L.ab = take(U * ss * 2);
+  else
+    L.a32 = take(U * ss * 4);
   L.bop = take(U * ss * (bf16 ? 2 : 4));
   L.partials = take(U * (size_t)c.blocks_per_unit * 8);
   L.inv_nu = take(U * 4);
@@ -201,8 +204,11 @@ int plan(const muon_matrix_desc* mats, int64_t n, const muon_hyper* h, bool step
     }
     if (cur.n_units > 0) chunks->push_back(cur);
   }
-  // Grid-size limits of the launches.
+  // Grid-size limits of the launches, and the 2 GiB reach of the per-tile
+  // buffer resources that stream K-contiguous operands (TILE rows of fp32).
   for (const Chunk& c : *chunks) {
+    if ((int64_t)c.tile * std::max(c.cols_pad, c.s_pad) * 4 >= ((int64_t)1 << 31))
+      return MUON_ERR_SHAPE;
     const int64_t tiles = (c.s_pad / c.tile) * (std::max(c.rows_pad, c.cols_pad) / c.tile);
     if (c.n_units * tiles > INT32_MAX / 2) return MUON_ERR_SHAPE;
     if (c.n_units * (int64_t)c.blocks_per_unit > INT32_MAX / 2) return MUON_ERR_SHAPE;
@@ -324,7 +330,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
   float* x32[2] = {reinterpret_cast<float*>(ws + L.x32[0]), reinterpret_cast<float*>(ws + L.x32[1])};
   uint16_t* xb[2] = {bf16 ? reinterpret_cast<uint16_t*>(ws + L.xb[0]) : nullptr,
                      bf16 ? reinterpret_cast<uint16_t*>(ws + L.xb[1]) : nullptr};
-  float* a32 = reinterpret_cast<float*>(ws + L.a32);
+  float* a32 = bf16 ? nullptr : reinterpret_cast<float*>(ws + L.a32);
   uint16_t* ab = bf16 ? reinterpret_cast<uint16_t*>(ws + L.ab) : nullptr;
   void* bop = ws + L.bop;
   double* partials = reinterpret_cast<double*>(ws + L.partials);
@@ -387,8 +393,8 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
       g.M = g.N = (int32_t)sp;
       g.K = (int32_t)(c.tall ? c.rows_pad : c.cols_pad);
       g.tiles_m = g.tiles_n = (int32_t)(sp / T);
-      g.out32 = a32;
-      g.out16 = ab;
+      g.out32 = a32;   // fp32 path
+      g.out16 = ab;    // bf16 path
       g.out_ustride = ss;
       g.ldo = (int32_t)sp;
       tr.before(MUON_KERNEL_GRAM);
@@ -409,6 +415,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
       g.out_ustride = ss;
       g.ldo = (int32_t)sp;
       g.aux = a32;
+      g.aux16 = ab;
       g.aux_ustride = ss;
       g.ldaux = (int32_t)sp;
       g.cb = sg.b;
