@@ -9,15 +9,21 @@
 //                   and the non-zero flag (notes section 2: Frobenius
 //                   normalisation, a zero matrix stays zero).
 //   k_normalize     X0 = N/||N||_F over the padded iterate (zeros in the
-//                   padding), plus the bf16 operand copy.
+//                   padding), plus the operand copies the products read: X0
+//                   in bf16 (bf16 path) and X0^T (bf16, or fp32 on the fp32
+//                   path), transposed through LDS.
 //   ns_gemm<GRAM>   A = X X^T (or X^T X for a tall unit: the smaller side).
 //   ns_gemm<POLY>   B = b*A + c*A*A (on the bf16 path A is kept only as its
 //                   bf16 operand copy, which the b*A term also reads).
-//   ns_gemm<APPLY>  X' = a*X + B*X (or X*B); in the last iteration the
-//                   epilogue writes W <- W*(1 - lr*wd) - lr*scale*X' instead
+//   ns_gemm<APPLY>  X' = a*X + B*X (or X*B), written with its operand copies
+//                   (X' in bf16, X'^T); in the last iteration the epilogue
+//                   writes W <- W*(1 - lr*wd) - lr*scale*X' instead
 //                   (Algorithm 1's decoupled update) or the NS output.
 // The three products are the quintic step a*X + b*(X X^T)X + c*(X X^T)^2 X of
-// the notes' section 2, grouped as (b*A + c*A^2)*X.
+// the notes' section 2, grouped as (b*A + c*A^2)*X.  Keeping X both as is and
+// transposed makes every product "A times B-transposed" with both operands
+// K-contiguous: Gram X X^T reads X twice (X^T X reads X^T twice), B*X reads B
+// and X^T, X*B reads X and B (B is symmetric).
 //
 // Padding: every iterate is stored as rows_pad x cols_pad with exact zeros
 // outside rows x cols, and every Gram / polynomial matrix as s_pad x s_pad.
@@ -77,6 +83,8 @@ struct GemmArgs {
   void* out16;          // bf16 output (unit 0) or nullptr
   int64_t out_ustride;
   int32_t ldo;
+  void* outt;           // APPLY: transposed operand copy of X' (T), or nullptr
+  int32_t ldt;          // its leading dimension (rows of X')
   int32_t final_mode;
   const float* aux;     // fp32 A (POLY, fp32 path) or X (APPLY), laid out like the output
   const void* aux16;    // bf16 A (POLY, bf16 path)
@@ -233,25 +241,29 @@ __global__ __launch_bounds__(64) void k_norm_finish(const double* __restrict__ p
   }
 }
 
-// X0 = N * (1/nu) over the whole padded iterate; zeros in the padding.
+// X0 = N * (1/nu) over the whole padded iterate (zeros in the padding), in
+// place in the fp32 buffer, plus X0 in bf16 (BF16) and X0^T (bf16 or fp32).
+// One 64x64 tile per workgroup; the transpose goes through LDS so that both
+// the row-major and the transposed writes are coalesced.
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void k_normalize(ChunkArgs ca, float* __restrict__ x32,
                                                          uint16_t* __restrict__ xb,
+                                                         void* __restrict__ xt,
                                                          const float* __restrict__ inv_nu,
-                                                         int64_t vec_per_block, int blocks_per_unit) {
-  const int u = blockIdx.x / blocks_per_unit;
-  const int bb = blockIdx.x - u * blocks_per_unit;
+                                                         int tiles_c, int tiles_per_unit) {
+  __shared__ float tile[64][65];
+  const int u = blockIdx.x / tiles_per_unit;
+  const int tt = blockIdx.x - u * tiles_per_unit;
+  const int r0 = (tt / tiles_c) * 64, c0 = (tt - (tt / tiles_c) * tiles_c) * 64;
   const float s = inv_nu[u];
-  const int64_t nvec = ca.x_stride >> 2;
-  const int64_t v0 = (int64_t)bb * vec_per_block;
-  const int64_t v1 = min(v0 + vec_per_block, nvec);
+  const int cp = ca.cols_pad, rp = ca.rows_pad;
   float* xu = x32 + (int64_t)u * ca.x_stride;
-  uint16_t* xbu = BF16 ? xb + (int64_t)u * ca.x_stride : nullptr;
-  const int cp = ca.cols_pad;
-  for (int64_t v = v0 + threadIdx.x; v < v1; v += kThreads) {
-    const int64_t e = v << 2;
-    const int r = (int)(e / cp);
-    const int c = (int)(e - (int64_t)r * cp);
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rr = t / 16 + 16 * i, cc = (t % 16) * 4;
+    const int r = r0 + rr, c = c0 + cc;
+    const int64_t e = (int64_t)r * cp + c;
     float4 val = make_float4(0.f, 0.f, 0.f, 0.f);
     if (r < ca.rows && c < ca.cols) {
       const float4 nv = *reinterpret_cast<const float4*>(xu + e);
@@ -265,136 +277,115 @@ __global__ __launch_bounds__(kThreads) void k_normalize(ChunkArgs ca, float* __r
       uint2 packed;
       packed.x = (uint32_t)to_bf16_bits(val.x) | ((uint32_t)to_bf16_bits(val.y) << 16);
       packed.y = (uint32_t)to_bf16_bits(val.z) | ((uint32_t)to_bf16_bits(val.w) << 16);
-      *reinterpret_cast<uint2*>(xbu + e) = packed;
+      *reinterpret_cast<uint2*>(xb + (int64_t)u * ca.x_stride + e) = packed;
+    }
+    tile[rr][cc] = val.x;
+    tile[rr][cc + 1] = val.y;
+    tile[rr][cc + 2] = val.z;
+    tile[rr][cc + 3] = val.w;
+  }
+  __syncthreads();
+  // X^T (cols_pad x rows_pad): row c takes tile column c - c0.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int cc = t / 16 + 16 * i, rr = (t % 16) * 4;
+    const int64_t e = (int64_t)u * ca.x_stride + (int64_t)(c0 + cc) * rp + r0 + rr;
+    const float a = tile[rr][cc], b = tile[rr + 1][cc], c = tile[rr + 2][cc], d = tile[rr + 3][cc];
+    if (BF16) {
+      uint2 packed;
+      packed.x = (uint32_t)to_bf16_bits(a) | ((uint32_t)to_bf16_bits(b) << 16);
+      packed.y = (uint32_t)to_bf16_bits(c) | ((uint32_t)to_bf16_bits(d) << 16);
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(xt) + e) = packed;
+    } else {
+      *reinterpret_cast<float4*>(static_cast<float*>(xt) + e) = make_float4(a, b, c, d);
     }
   }
 }
 
 // ------------------------------------------------------------------ GEMM ---
-// Batched C = A_op * B_op over padded units, one TILE x TILE output tile per
-// workgroup of 4 waves (2 x 2, each TILE/2 x TILE/2 as 32x32 MFMA blocks).
+// Batched C = A_op * B_op^T over padded units (both operands K-contiguous),
+// one TILE x TILE output tile per workgroup of 4 waves (2 x 2, each
+// TILE/2 x TILE/2 as 32x32 MFMA blocks).
 //
-// LDS holds, per stage, TILE rows of A_op and TILE rows of B_op, each row
-// 128 bytes of K (64 bf16 or 32 fp32) in eight 16-byte chunks, XOR-swizzled
-// (chunk ^ row%8 ^ (row/8)%8) so that 8 consecutive rows read at one logical
-// chunk hit distinct banks.  Two stages live in two separate LDS arrays.
-//  - A K-contiguous global operand is copied global -> LDS directly
-//    (buffer_load_dwordx4 ... lds: lane i of a wave lands at M0 + 16*i, so
-//    the swizzle is applied by choosing which global chunk each lane fetches).
-//  - An MN-contiguous operand is loaded into registers, transposed there in
-//    8x8 (bf16) or 4x4 (fp32) blocks and written to LDS.
-// MFMA fragments are double-buffered across the four K sub-steps of a tile.
-// The MFMA is issued as (B fragment, A fragment), so each lane accumulates
-// C[m][n..n+3] for one row m and 4 consecutive columns: the epilogue moves
-// 16-byte vectors.
+// LDS: kStages stages, each a separate array holding TILE rows of A_op and
+// TILE rows of B_op; a row is 64 bytes of K (32 bf16 or 16 fp32) in four
+// 16-byte chunks, XOR-swizzled by row so that the 32-row MFMA fragment reads
+// spread over the banks.  Operands stream global -> LDS directly, up to
+// kStages stages ahead of the MFMAs (buffer_load_dwordx4 ... lds: lane i of
+// a wave lands at M0 + 16*i, so the swizzle is applied by choosing which
+// global chunk each lane fetches).  Fragments are double-buffered across the
+// two K sub-steps of a stage, and the MFMA is issued as (B, A) so each lane
+// accumulates C[m][n..n+3] for one row m and four consecutive columns: the
+// epilogue moves 16-byte vectors.
 template <typename T>
 struct OpT;
 template <>
 struct OpT<__bf16> {
   static constexpr int kElems = 8;  // per 16-byte chunk
-  static constexpr int kBK = 64;    // K per LDS row
+  static constexpr int kBK = 32;    // K per LDS row (4 chunks)
 };
 template <>
 struct OpT<float> {
   static constexpr int kElems = 4;
-  static constexpr int kBK = 32;
+  static constexpr int kBK = 16;
 };
+
+constexpr int kStages = 4;
 
 typedef __attribute__((address_space(3))) void* lds_vptr;
 
+// Physical 16-byte chunk of logical chunk c in a 64-byte row.
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return chunk ^ (row & 7) ^ ((row >> 3) & 7);
+  return chunk ^ (((row >> 1) ^ (row >> 3)) & 3);
 }
 
-// K-contiguous operand: TILE rows x 8 chunks, straight into LDS through a
-// buffer resource whose base is the tile's first row (so 32-bit offsets
-// cover TILE rows).  The MUBUF form (buffer_load ... lds) is used rather
-// than global_load_lds: the latter is a FLAT-encoded LDS writer, which makes
-// the compiler wait for all LDS reads at once while it is in flight.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base) {
-  // raw buffer, stride 0, 2 GiB range, 32-bit data format (gfx9 family)
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, 0x7FFFFFFF, 0x00020000);
+// Buffer resource (4 SGPRs) for a raw buffer at `base`: stride 0, a 2 GiB
+// range and the 32-bit data format of the gfx9 family.
+__device__ __forceinline__ u32x4 tile_rsrc(const void* base) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  return u32x4{(uint32_t)b, (uint32_t)(b >> 32) & 0xFFFFu, 0x7FFFFFFFu, 0x00020000u};
 }
 
+// DMA instructions per wave for one operand of one stage.
+template <int TILE>
+constexpr int dma_per_wave() { return TILE / 64; }
+
+// One operand's share of a stage for this wave: TILE rows of the tile
+// (resource based at its first row) x 64 bytes of K.  `voff` holds the
+// stage-invariant per-lane byte offsets (row * ld + swizzled chunk), the K
+// position of the stage comes in as the scalar offset `koff`, and lds_op is
+// the LDS byte offset of the operand region.  Lane i of each instruction
+// lands at M0 + 16*i, so the swizzle is applied by choosing which global
+// chunk each lane fetches.
+//
+// The copy is issued as inline assembly so that the compiler does not see an
+// LDS writer: it cannot tell the stages apart and would otherwise wait for
+// every in-flight stage before each LDS read.  Completion is tracked with
+// explicit vmcnt waits (vmcnt counts every vector-memory instruction in
+// issue order) before the barrier that publishes a stage.
 template <typename T, int TILE>
-__device__ __forceinline__ void issue_direct(__amdgpu_buffer_rsrc_t rs, int ld, int k0,
-                                             u32x4* lds_stage) {
-  constexpr int kPerWave = TILE / 32;  // 64-lane instructions per wave
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+struct DmaPlan {
+  static constexpr int kN = dma_per_wave<TILE>();
+  int voff[kN];
+  __device__ __forceinline__ void init(int ld) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
 #pragma unroll
-  for (int i = 0; i < kPerWave; ++i) {
-    const int slot0 = (w * kPerWave + i) * 64;  // first 16-byte slot of this instruction
-    const int s = slot0 + lane;
-    const int row = s >> 3, pc = s & 7;
-    const int c = pc ^ (row & 7) ^ ((row >> 3) & 7);  // logical chunk stored at (row, pc)
-    const int voff = (row * ld + k0 + c * OpT<T>::kElems) * (int)sizeof(T);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_vptr)(lds_stage + slot0), 16, voff, 0, 0, 0);
-  }
-}
-
-// MN-contiguous operand: registers, transposed on the way to LDS.
-template <typename T, int TILE>
-struct TransLoader {
-  static constexpr bool kBF = sizeof(T) == 2;
-  static constexpr int kBlocks = kBF ? TILE : 2 * TILE;  // 8x8 bf16 or 4x4 fp32 blocks
-  static constexpr int kIters = (kBlocks + kThreads - 1) / kThreads;
-  static constexpr int kRegs = kIters * (kBF ? 8 : 4);
-  u32x4 r[kRegs];
-
-  __device__ __forceinline__ void load(const T* __restrict__ base, int ld, int mn0, int k0) {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int i = 0; i < kIters; ++i) {
-      const int blk = t + kThreads * i;
-      if (kBlocks % kThreads == 0 || blk < kBlocks) {
-        if constexpr (kBF) {
-          const int mb = blk % (TILE / 8), kb = blk / (TILE / 8);
-#pragma unroll
-          for (int rr = 0; rr < 8; ++rr)
-            r[i * 8 + rr] = *reinterpret_cast<const u32x4*>(
-                base + (int64_t)(k0 + kb * 8 + rr) * ld + mn0 + mb * 8);
-        } else {
-          const int mb = blk % (TILE / 4), kb = blk / (TILE / 4);
-#pragma unroll
-          for (int rr = 0; rr < 4; ++rr)
-            r[i * 4 + rr] = *reinterpret_cast<const u32x4*>(
-                base + (int64_t)(k0 + kb * 4 + rr) * ld + mn0 + mb * 4);
-        }
-      }
+    for (int i = 0; i < kN; ++i) {
+      const int sl = (w * kN + i) * 64 + lane;
+      const int row = sl >> 2, pc = sl & 3;
+      const int c = pc ^ (((row >> 1) ^ (row >> 3)) & 3);  // logical chunk stored at (row, pc)
+      voff[i] = (row * ld + c * OpT<T>::kElems) * (int)sizeof(T);
     }
   }
-
-  __device__ __forceinline__ void store(u32x4* __restrict__ lds) const {
-    const int t = threadIdx.x;
+  __device__ __forceinline__ void issue(const u32x4& rs, uint32_t koff, uint32_t lds_op) const {
+    const int w = threadIdx.x >> 6;
 #pragma unroll
-    for (int i = 0; i < kIters; ++i) {
-      const int blk = t + kThreads * i;
-      if (kBlocks % kThreads == 0 || blk < kBlocks) {
-        if constexpr (kBF) {
-          const int mb = blk % (TILE / 8), kb = blk / (TILE / 8);
-          const u32x4* v = &r[i * 8];
-          // v[rr] holds mn = mb*8 + 0..7 at k = kb*8 + rr; LDS row
-          // mn = mb*8 + e takes k = kb*8 + 0..7 (dword j packs k = 2j, 2j+1).
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-            uint32_t d[4];
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              d[j] = __builtin_amdgcn_perm(v[2 * j + 1][e >> 1], v[2 * j][e >> 1], sel);
-            const int row = mb * 8 + e;
-            lds[row * 8 + swz(row, kb)] = u32x4{d[0], d[1], d[2], d[3]};
-          }
-        } else {
-          const int mb = blk % (TILE / 4), kb = blk / (TILE / 4);
-          const u32x4* v = &r[i * 4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int row = mb * 4 + e;
-            lds[row * 8 + swz(row, kb)] = u32x4{v[0][e], v[1][e], v[2][e], v[3][e]};
-          }
-        }
-      }
+    for (int i = 0; i < kN; ++i) {
+      const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_op + (uint32_t)((w * kN + i) * 64) * 16u);
+      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                   :
+                   : "s"(m0v), "v"(voff[i]), "s"(rs), "s"(koff)
+                   : "memory", "m0");
     }
   }
 };
@@ -437,14 +428,27 @@ __device__ __forceinline__ void store_bf16x4(void* base, int64_t idx, float a, f
   *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + idx) = p;
 }
 
-template <int PHASE, typename T, int TILE, bool AKC, bool BKC>
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+template <int PHASE, typename T, int TILE>
 __global__ __launch_bounds__(kThreads) void ns_gemm(GemmArgs g, ChunkArgs ca) {
   constexpr int WT = TILE / 2;   // wave tile
   constexpr int FM = WT / 32;    // 32x32 blocks per wave side
   constexpr bool kBF = sizeof(T) == 2;
-  constexpr int kOp = TILE * 8;  // 16-byte slots of one operand in one stage
+  constexpr int kOp = TILE * 4;  // 16-byte slots of one operand in one stage
+  constexpr int BK = OpT<T>::kBK;
+  constexpr int P = 2 * dma_per_wave<TILE>();  // DMA instructions per wave per stage
+  constexpr int kMf = FM * FM * (kBF ? 1 : 4);  // MFMAs per K sub-step
   __shared__ u32x4 lds0[2 * kOp];
   __shared__ u32x4 lds1[2 * kOp];
+  __shared__ u32x4 lds2[2 * kOp];
+  __shared__ u32x4 lds3[2 * kOp];
 
   const int tiles_per_unit = g.tiles_m * g.tiles_n;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -474,6 +478,8 @@ __global__ __launch_bounds__(kThreads) void ns_gemm(GemmArgs g, ChunkArgs ca) {
 
   const T* A = static_cast<const T*>(g.a) + (int64_t)u * g.a_ustride;
   const T* B = static_cast<const T*>(g.b) + (int64_t)u * g.b_ustride;
+  const u32x4 rsa = tile_rsrc(A + (int64_t)m0 * g.lda);
+  const u32x4 rsb = tile_rsrc(B + (int64_t)n0 * g.ldb);
 
   f32x16 acc[FM][FM];
 #pragma unroll
@@ -483,74 +489,92 @@ __global__ __launch_bounds__(kThreads) void ns_gemm(GemmArgs g, ChunkArgs ca) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  TransLoader<T, TILE> ta, tb;
-  constexpr int BK = OpT<T>::kBK;
-  const int nk = g.K / BK;
-
-  const __amdgpu_buffer_rsrc_t rsa = tile_rsrc(A + (int64_t)m0 * g.lda);
-  const __amdgpu_buffer_rsrc_t rsb = tile_rsrc(B + (int64_t)n0 * g.ldb);
-  auto issue = [&](int kt, u32x4* stage) {
-    if constexpr (AKC) issue_direct<T, TILE>(rsa, g.lda, kt * BK, stage);
-    else ta.load(A, g.lda, m0, kt * BK);
-    if constexpr (BKC) issue_direct<T, TILE>(rsb, g.ldb, kt * BK, stage + kOp);
-    else tb.load(B, g.ldb, n0, kt * BK);
+  const int nk = g.K / BK;  // a multiple of kStages (K is a multiple of 128)
+  auto stage = [&](int st) -> u32x4* {
+    return st == 0 ? lds0 : st == 1 ? lds1 : st == 2 ? lds2 : lds3;
   };
-  auto finish = [&](u32x4* stage) {
-    if constexpr (!AKC) ta.store(stage);
-    if constexpr (!BKC) tb.store(stage + kOp);
+  // LDS byte offsets of the stages (casts of the arrays themselves fold to
+  // constants).
+  auto stage_off = [&](int st) -> uint32_t {
+    return st == 0   ? (uint32_t)(uintptr_t)(lds_vptr)lds0
+           : st == 1 ? (uint32_t)(uintptr_t)(lds_vptr)lds1
+           : st == 2 ? (uint32_t)(uintptr_t)(lds_vptr)lds2
+                     : (uint32_t)(uintptr_t)(lds_vptr)lds3;
+  };
+  DmaPlan<T, TILE> pa, pb;
+  pa.init(g.lda);
+  pb.init(g.ldb);
+  auto dma = [&](int kt, int st) {
+    const uint32_t koff = (uint32_t)(kt * BK * (int)sizeof(T));
+    pa.issue(rsa, koff, stage_off(st));
+    pb.issue(rsb, koff, stage_off(st) + kOp * 16u);
   };
 
-  issue(0, lds0);
-  finish(lds0);
-  // Drain the scalar (kernel-argument) loads before the K loop: a scalar
-  // load still in flight would force every LDS wait in the loop to wait for
-  // everything, since scalar loads can return out of order.
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-  __builtin_amdgcn_sched_barrier(0);
-  __syncthreads();
-
+  // Schedule of stage k (two K sub-steps kk0, kk1; buffers cycle mod 4):
+  //   region A: read kk1(k) fragments | MFMAs kk0(k)
+  //   wait for this wave's kk1(k) reads and its DMA of stage k+1; s_barrier
+  //   (stage k+1 is complete, and every wave is done reading stage k)
+  //   DMA stage k+4 into the buffer of stage k
+  //   region C: read kk0(k+1) fragments | MFMAs kk1(k)
+  // The barrier sits between MFMA groups whose operands are already in
+  // registers, so the fragment reads after it hide under MFMAs.
   const int arow0 = wm * WT + (lane & 31);
   const int brow0 = wn * WT + (lane & 31);
   const int half = lane >> 5;
-
-  for (int kt = 0; kt < nk; ++kt) {
-    u32x4* cur = (kt & 1) ? lds1 : lds0;
-    u32x4* nxt = (kt & 1) ? lds0 : lds1;
-    if (kt + 1 < nk) issue(kt + 1, nxt);
-    const u32x4* As = cur;
-    const u32x4* Bs = cur + kOp;
-    u32x4 af[2][FM], bf[2][FM];
+  u32x4 af[2][FM], bf[2][FM];
+  auto read_frags = [&](const u32x4* S, int kk, int slot) {
+    const int ch = 2 * kk + half;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int ra = arow0 + i * 32, rb = brow0 + i * 32;
-      af[0][i] = As[ra * 8 + swz(ra, half)];
-      bf[0][i] = Bs[rb * 8 + swz(rb, half)];
+      af[slot][i] = S[ra * 4 + swz(ra, ch)];
+      bf[slot][i] = S[kOp + rb * 4 + swz(rb, ch)];
     }
+  };
+
+  // Prologue: DMA of stages 0..3 (nk >= 4).  The scalar (kernel-argument)
+  // loads are drained as well: one still in flight would turn every LDS
+  // wait of the loop into a full wait.
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      // One scheduling region per sub-step: the fragment reads of sub-step
-      // kk+1 and the MFMAs of sub-step kk (which only read registers loaded
-      // in the previous region), so LDS latency hides under the MFMAs.
+  for (int st = 0; st < kStages; ++st) dma(st, st);
+  wait_vmcnt<3 * P>();
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
+  read_frags(stage(0), 0, 0);
+
+  for (int kt0 = 0; kt0 < nk; kt0 += kStages) {
+#pragma unroll
+    for (int sub = 0; sub < kStages; ++sub) {
+      const int k = kt0 + sub;
+      const u32x4* S = stage(sub);
       __builtin_amdgcn_sched_barrier(0);
-      if (kk < 3) {
-        const int ch = 2 * (kk + 1) + half;
-#pragma unroll
-        for (int i = 0; i < FM; ++i) {
-          const int ra = arow0 + i * 32, rb = brow0 + i * 32;
-          af[(kk + 1) & 1][i] = As[ra * 8 + swz(ra, ch)];
-          bf[(kk + 1) & 1][i] = Bs[rb * 8 + swz(rb, ch)];
-        }
-      }
-      mfma_block<T, FM>(af[kk & 1], bf[kk & 1], acc);
-      // Within the region: every fragment read first, then the MFMAs, so
-      // the reads have the whole region to land.
-      if (kk < 3) __builtin_amdgcn_sched_group_barrier(0x100, 2 * FM, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, FM * FM * (kBF ? 1 : 4), 0);
+      // region A
+      read_frags(S, 1, 1);
+      mfma_block<T, FM>(af[0], bf[0], acc);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * FM, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, kMf, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      // Publish stage k+1 (for the last stage this only drains the DMA; the
+      // reads below then touch a stale buffer whose values go unused, which
+      // keeps the MFMA block on a single control path).
+      const int ahead = nk - 2 - k;  // DMA stages issued after stage k+1
+      if (ahead >= 2)
+        wait_vmcnt<2 * P>();
+      else if (ahead == 1)
+        wait_vmcnt<P>();
+      else
+        wait_vmcnt<0>();
+      wait_lgkm0();
+      __builtin_amdgcn_s_barrier();
+      if (k + kStages < nk) dma(k + kStages, sub);
+      __builtin_amdgcn_sched_barrier(0);
+      // region C
+      read_frags(stage((sub + 1) % kStages), 0, 0);
+      mfma_block<T, FM>(af[1], bf[1], acc);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * FM, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, kMf, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    if (kt + 1 < nk) finish(nxt);
-    __syncthreads();
   }
 
   // ---- epilogue: lane holds C[m][n + 0..3] for m = .. + lane%32 and
@@ -617,6 +641,21 @@ __global__ __launch_bounds__(kThreads) void ns_gemm(GemmArgs g, ChunkArgs ca) {
           if (g.final_mode == FINAL_NONE) {
             *reinterpret_cast<float4*>(g.out32 + o) = make_float4(v0, v1, v2, v3);
             if constexpr (kBF) store_bf16x4(g.out16, o, v0, v1, v2, v3);
+            // X'^T: element (m, n+e) lands at row n+e, column m.
+            const int64_t ot = (int64_t)u * g.out_ustride + (int64_t)n * g.ldt + m;
+            if constexpr (kBF) {
+              uint16_t* pt = static_cast<uint16_t*>(g.outt) + ot;
+              pt[0] = to_bf16_bits(v0);
+              pt[g.ldt] = to_bf16_bits(v1);
+              pt[2 * (int64_t)g.ldt] = to_bf16_bits(v2);
+              pt[3 * (int64_t)g.ldt] = to_bf16_bits(v3);
+            } else {
+              float* pt = static_cast<float*>(g.outt) + ot;
+              pt[0] = v0;
+              pt[g.ldt] = v1;
+              pt[2 * (int64_t)g.ldt] = v2;
+              pt[3 * (int64_t)g.ldt] = v3;
+            }
           } else if (m < ca.rows && n < ca.cols) {
             float* p = wout + (int64_t)m * ca.cols + n;
             const bool step = g.final_mode == FINAL_STEP;

@@ -57,12 +57,12 @@ struct Chunk {
   int64_t n_units;
   std::vector<SegRef> segs;
   int rows_per_block, blocks_per_unit;   // momentum kernel
-  int64_t norm_vec_per_block; int norm_blocks_per_unit;
+  int norm_blocks_per_unit;              // 64x64 tiles of the padded iterate
 };
 
 // Workspace carve-up of one chunk (byte offsets).
 struct Layout {
-  size_t x32[2], xb[2], a32, ab, bop, partials, inv_nu, flag, total;
+  size_t x32[2], xb[2], xt[2], a32, ab, bop, partials, inv_nu, flag, total;
 };
 
 Layout layout_of(const Chunk& c, bool bf16) {
@@ -78,6 +78,9 @@ Layout layout_of(const Chunk& c, bool bf16) {
     L.xb[0] = take(U * xs * 2);
     L.xb[1] = take(U * xs * 2);
   }
+  // Transposed operand copies of the iterate (bf16, or fp32 on the fp32 path).
+  L.xt[0] = take(U * xs * (bf16 ? 2 : 4));
+  L.xt[1] = take(U * xs * (bf16 ? 2 : 4));
   // The Gram is stored once: fp32 on the fp32 path, bf16 on the bf16 path.
   if (bf16)
     L.ab = take(U * ss * 2);
@@ -182,9 +185,7 @@ int plan(const muon_matrix_desc* mats, int64_t n, const muon_hyper* h, bool step
     // Momentum kernel: about 16K elements per block.
     proto.rows_per_block = (int)std::max<int64_t>(1, std::min<int64_t>(u0.rows_u, 16384 / u0.cols));
     proto.blocks_per_unit = (int)((u0.rows_u + proto.rows_per_block - 1) / proto.rows_per_block);
-    const int64_t nvec = proto.rows_pad * proto.cols_pad / 4;
-    proto.norm_vec_per_block = 4096;
-    proto.norm_blocks_per_unit = (int)((nvec + 4095) / 4096);
+    proto.norm_blocks_per_unit = (int)((proto.rows_pad / 64) * (proto.cols_pad / 64));
     Chunk cur = proto;
     for (int ui : grp) {
       const Unitized& u = us[ui];
@@ -265,33 +266,21 @@ struct Tracer {
   }
 };
 
-template <int PHASE, typename T, int TILE>
-void launch_gemm(bool akc, bool bkc, const GemmArgs& g, const ChunkArgs& ca, hipStream_t s) {
-  const int grid = g.n_units * g.tiles_m * g.tiles_n;
-  if (akc && bkc)
-    hipLaunchKernelGGL((ns_gemm<PHASE, T, TILE, true, true>), dim3(grid), dim3(kThreads), 0, s, g, ca);
-  else if (akc && !bkc)
-    hipLaunchKernelGGL((ns_gemm<PHASE, T, TILE, true, false>), dim3(grid), dim3(kThreads), 0, s, g, ca);
-  else
-    hipLaunchKernelGGL((ns_gemm<PHASE, T, TILE, false, false>), dim3(grid), dim3(kThreads), 0, s, g, ca);
-}
-
 template <int PHASE, typename T>
-void launch_gemm_t(int tile, bool akc, bool bkc, const GemmArgs& g, const ChunkArgs& ca,
-                   hipStream_t s) {
+void launch_gemm(int tile, const GemmArgs& g, const ChunkArgs& ca, hipStream_t s) {
+  const int grid = g.n_units * g.tiles_m * g.tiles_n;
   if (tile == 256)
-    launch_gemm<PHASE, T, 256>(akc, bkc, g, ca, s);
+    hipLaunchKernelGGL((ns_gemm<PHASE, T, 256>), dim3(grid), dim3(kThreads), 0, s, g, ca);
   else
-    launch_gemm<PHASE, T, 128>(akc, bkc, g, ca, s);
+    hipLaunchKernelGGL((ns_gemm<PHASE, T, 128>), dim3(grid), dim3(kThreads), 0, s, g, ca);
 }
 
 template <int PHASE>
-void launch_phase(bool bf16, int tile, bool akc, bool bkc, const GemmArgs& g, const ChunkArgs& ca,
-                  hipStream_t s) {
+void launch_phase(bool bf16, int tile, const GemmArgs& g, const ChunkArgs& ca, hipStream_t s) {
   if (bf16)
-    launch_gemm_t<PHASE, __bf16>(tile, akc, bkc, g, ca, s);
+    launch_gemm<PHASE, __bf16>(tile, g, ca, s);
   else
-    launch_gemm_t<PHASE, float>(tile, akc, bkc, g, ca, s);
+    launch_gemm<PHASE, float>(tile, g, ca, s);
 }
 
 // Runs one chunk: momentum (or NS-input copy), norms, normalisation and the
@@ -330,6 +319,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
   float* x32[2] = {reinterpret_cast<float*>(ws + L.x32[0]), reinterpret_cast<float*>(ws + L.x32[1])};
   uint16_t* xb[2] = {bf16 ? reinterpret_cast<uint16_t*>(ws + L.xb[0]) : nullptr,
                      bf16 ? reinterpret_cast<uint16_t*>(ws + L.xb[1]) : nullptr};
+  void* xt[2] = {ws + L.xt[0], ws + L.xt[1]};
   float* a32 = bf16 ? nullptr : reinterpret_cast<float*>(ws + L.a32);
   uint16_t* ab = bf16 ? reinterpret_cast<uint16_t*>(ws + L.ab) : nullptr;
   void* bop = ws + L.bop;
@@ -357,12 +347,13 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
   tr.before(MUON_KERNEL_NORMALIZE);
   hipLaunchKernelGGL(k_norm_finish, dim3(U), dim3(64), 0, s, partials, c.blocks_per_unit, inv_nu,
                      flag);
+  const int tiles_c = (int)(c.cols_pad / 64);
   if (bf16)
     hipLaunchKernelGGL(k_normalize<true>, dim3(U * c.norm_blocks_per_unit), dim3(kThreads), 0, s,
-                       ca, x32[0], xb[0], inv_nu, c.norm_vec_per_block, c.norm_blocks_per_unit);
+                       ca, x32[0], xb[0], xt[0], inv_nu, tiles_c, c.norm_blocks_per_unit);
   else
     hipLaunchKernelGGL(k_normalize<false>, dim3(U * c.norm_blocks_per_unit), dim3(kThreads), 0, s,
-                       ca, x32[0], nullptr, inv_nu, c.norm_vec_per_block, c.norm_blocks_per_unit);
+                       ca, x32[0], nullptr, xt[0], inv_nu, tiles_c, c.norm_blocks_per_unit);
   tr.after(MUON_KERNEL_NORMALIZE);
 
   // 3. Newton-Schulz iterations.
@@ -370,6 +361,8 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
   const int64_t xs = c.rows_pad * c.cols_pad;
   const int64_t ss = c.s_pad * c.s_pad;
   const int64_t sp = c.s_pad;
+  // Operand copies of the iterate: X as is (bf16, or the fp32 iterate
+  // itself) and X^T (cols_pad x rows_pad).
   const void* xop[2] = {bf16 ? (const void*)xb[0] : (const void*)x32[0],
                         bf16 ? (const void*)xb[1] : (const void*)x32[1]};
   const void* aop = bf16 ? (const void*)ab : (const void*)a32;
@@ -386,10 +379,11 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
       std::memset(&g, 0, sizeof(g));
       g.n_units = U;
       g.flag = flag;
-      g.a = xop[cur];
-      g.b = xop[cur];
+      // wide: rows of X (K = cols); tall: rows of X^T (K = rows)
+      g.a = c.tall ? (const void*)xt[cur] : xop[cur];
+      g.b = g.a;
       g.a_ustride = g.b_ustride = xs;
-      g.lda = g.ldb = (int32_t)c.cols_pad;
+      g.lda = g.ldb = (int32_t)(c.tall ? c.rows_pad : c.cols_pad);
       g.M = g.N = (int32_t)sp;
       g.K = (int32_t)(c.tall ? c.rows_pad : c.cols_pad);
       g.tiles_m = g.tiles_n = (int32_t)(sp / T);
@@ -398,7 +392,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
       g.out_ustride = ss;
       g.ldo = (int32_t)sp;
       tr.before(MUON_KERNEL_GRAM);
-      launch_phase<GRAM>(bf16, T, !c.tall, !c.tall, g, ca, s);
+      launch_phase<GRAM>(bf16, T, g, ca, s);
       tr.after(MUON_KERNEL_GRAM);
       // Polynomial: B = b*A + c*A*A (A symmetric: both operands K-contiguous).
       std::memset(&g, 0, sizeof(g));
@@ -421,7 +415,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
       g.cb = sg.b;
       g.cc = sg.c;
       tr.before(MUON_KERNEL_POLY);
-      launch_phase<POLY>(bf16, T, true, true, g, ca, s);
+      launch_phase<POLY>(bf16, T, g, ca, s);
       tr.after(MUON_KERNEL_POLY);
       // Apply: X' = a*X + B*X (wide) or a*X + X*B (tall).
       std::memset(&g, 0, sizeof(g));
@@ -432,37 +426,34 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
       g.K = (int32_t)sp;
       g.tiles_m = (int32_t)(c.rows_pad / T);
       g.tiles_n = (int32_t)(c.cols_pad / T);
-      bool akc, bkc;
       if (!c.tall) {
-        g.a = bop;           // B[m][k], K-contiguous
+        g.a = bop;           // B[m][k]
         g.a_ustride = ss;
         g.lda = (int32_t)sp;
-        g.b = xop[cur];      // X[k][n], N-contiguous
+        g.b = xt[cur];       // X[k][n] read as X^T[n][k]
         g.b_ustride = xs;
-        g.ldb = (int32_t)c.cols_pad;
-        akc = true;
-        bkc = false;
+        g.ldb = (int32_t)c.rows_pad;
       } else {
-        g.a = xop[cur];      // X[m][k], K-contiguous
+        g.a = xop[cur];      // X[m][k]
         g.a_ustride = xs;
         g.lda = (int32_t)c.cols_pad;
-        g.b = bop;           // B[k][n] = B[n][k], K-contiguous by symmetry
+        g.b = bop;           // B[k][n] = B[n][k] (symmetric)
         g.b_ustride = ss;
         g.ldb = (int32_t)sp;
-        akc = true;
-        bkc = true;
       }
       g.out32 = x32[nxt];
       g.out16 = bf16 ? (void*)xb[nxt] : nullptr;
       g.out_ustride = xs;
       g.ldo = (int32_t)c.cols_pad;
+      g.outt = xt[nxt];
+      g.ldt = (int32_t)c.rows_pad;
       g.aux = x32[cur];
       g.aux_ustride = xs;
       g.ldaux = (int32_t)c.cols_pad;
       g.ca = sg.a;
       g.final_mode = last ? (step ? FINAL_STEP : FINAL_NSOUT) : FINAL_NONE;
       tr.before(MUON_KERNEL_APPLY);
-      launch_phase<APPLY>(bf16, T, akc, bkc, g, ca, s);
+      launch_phase<APPLY>(bf16, T, g, ca, s);
       tr.after(MUON_KERNEL_APPLY);
     }
   }

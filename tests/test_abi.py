@@ -58,17 +58,19 @@ def test_workspace_sizes():
     mib = 1024 * 1024
     st, n = ws_size([(32, 1024, 1024, 0)])
     assert st == 0
-    # bf16 path: two fp32 + two bf16 iterates, bf16 Gram, bf16 polynomial
-    # = 16 bytes per element, plus per-unit norms
-    assert 32 * mib * 16 <= n < 32 * mib * 16 + mib
+    # bf16 path: two fp32 iterates, two bf16 iterates and their two bf16
+    # transposes, bf16 Gram, bf16 polynomial = 20 bytes per element, plus
+    # per-unit norms
+    assert 32 * mib * 20 <= n < 32 * mib * 20 + mib
     h = muon.default_hyper_c()
     h.batch_update_size = 8
     st, n8 = ws_size([(32, 1024, 1024, 0)], h)
-    assert st == 0 and 8 * mib * 16 <= n8 < 8 * mib * 16 + mib
+    assert st == 0 and 8 * mib * 20 <= n8 < 8 * mib * 20 + mib
     h.ns_precision = muon.NS_FP32
     st, nf = ws_size([(32, 1024, 1024, 0)], h)
-    # fp32 path: two fp32 iterates, fp32 Gram and polynomial = 16 bytes
-    assert st == 0 and 8 * mib * 16 <= nf < 8 * mib * 16 + mib
+    # fp32 path: two fp32 iterates and their two transposes, fp32 Gram and
+    # polynomial = 24 bytes
+    assert st == 0 and 8 * mib * 24 <= nf < 8 * mib * 24 + mib
     assert ws_size([])[0] == 0
 
 
