@@ -577,110 +577,133 @@ __global__ __launch_bounds__(kThreads) void ns_gemm(GemmArgs g, ChunkArgs ca) {
     }
   }
 
-  // ---- epilogue: lane holds C[m][n + 0..3] for m = .. + lane%32 and
-  // n = .. + 8*q + 4*(lane/32), q = r/4, within each 32x32 block.
+  // ---- epilogue.  Each wave stages one 32-row block of its accumulators at
+  // a time in its own LDS region (lane (m, half) holds C[m][n..n+3]), then
+  // reads it back row-wise so that every global load and store covers whole
+  // row segments (WT/4 lanes per row, 16 bytes per lane); the transposed
+  // copy reads the staged block column-wise.
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();  // every wave is done with the stage buffers
+  float* ep = reinterpret_cast<float*>(wid == 0 ? lds0 : wid == 1 ? lds1 : wid == 2 ? lds2 : lds3);
+  constexpr int LDW = WT + 4;     // padded row stride (floats)
+  constexpr int LPR = WT / 4;     // lanes per row
+  constexpr int RPI = 64 / LPR;   // rows per instruction
+  constexpr int NIT = 32 / RPI;   // row-wise iterations per block
   float* wout = nullptr;
   if (PHASE == APPLY && g.final_mode != FINAL_NONE) {
     const SegView sg = find_seg(ca, u);
     wout = sg.w + (int64_t)(u - sg.first) * ca.unit_elems;
   }
   const bool vec_w = (ca.cols & 3) == 0;
+  const int rl = lane / LPR;            // row within an instruction
+  const int cl = (lane % LPR) * 4;      // first column of the lane
+  const int ncol = n0 + wn * WT + cl;   // global column of the lane's first element
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
-    const int m = m0 + wm * WT + i * 32 + (lane & 31);
-    float4 aux[FM][4];
+    const int mrow0 = m0 + wm * WT + i * 32;  // first global row of the block
+    // auxiliary input of the block, row-wise (issued before the staging)
+    float4 aux[NIT];
     if constexpr (PHASE == POLY && kBF) {
-      // bf16 path: A exists only as the bf16 operand copy.
-      const uint16_t* ap = static_cast<const uint16_t*>(g.aux16) + (int64_t)u * g.aux_ustride +
-                           (int64_t)m * g.ldaux;
+      const uint16_t* ap = static_cast<const uint16_t*>(g.aux16) + (int64_t)u * g.aux_ustride + ncol;
 #pragma unroll
-      for (int j = 0; j < FM; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint2 h = *reinterpret_cast<const uint2*>(ap + n0 + wn * WT + j * 32 + 8 * q + 4 * half);
-          aux[j][q] = make_float4(bf16_bits_to_f32(h.x & 0xffffu), bf16_bits_to_f32(h.x >> 16),
-                                  bf16_bits_to_f32(h.y & 0xffffu), bf16_bits_to_f32(h.y >> 16));
-        }
+      for (int it = 0; it < NIT; ++it) {
+        const uint2 h = *reinterpret_cast<const uint2*>(ap + (int64_t)(mrow0 + it * RPI + rl) * g.ldaux);
+        aux[it] = make_float4(bf16_bits_to_f32(h.x & 0xffffu), bf16_bits_to_f32(h.x >> 16),
+                              bf16_bits_to_f32(h.y & 0xffffu), bf16_bits_to_f32(h.y >> 16));
+      }
     } else if constexpr (PHASE != GRAM) {
-      const float* ap = g.aux + (int64_t)u * g.aux_ustride + (int64_t)m * g.ldaux;
+      const float* ap = g.aux + (int64_t)u * g.aux_ustride + ncol;
 #pragma unroll
-      for (int j = 0; j < FM; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          aux[j][q] = *reinterpret_cast<const float4*>(ap + n0 + wn * WT + j * 32 + 8 * q + 4 * half);
+      for (int it = 0; it < NIT; ++it)
+        aux[it] = *reinterpret_cast<const float4*>(ap + (int64_t)(mrow0 + it * RPI + rl) * g.ldaux);
     }
+    // stage the block
 #pragma unroll
     for (int j = 0; j < FM; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * WT + j * 32 + 8 * q + 4 * half;
         const f32x16& c = acc[i][j];
-        float v0 = c[4 * q], v1 = c[4 * q + 1], v2 = c[4 * q + 2], v3 = c[4 * q + 3];
-        const int64_t o = (int64_t)u * g.out_ustride + (int64_t)m * g.ldo + n;
-        if constexpr (PHASE == GRAM) {
-          if constexpr (kBF)
-            store_bf16x4(g.out16, o, v0, v1, v2, v3);
-          else
-            *reinterpret_cast<float4*>(g.out32 + o) = make_float4(v0, v1, v2, v3);
-        } else if constexpr (PHASE == POLY) {
-          const float4 a = aux[j][q];
-          v0 = g.cb * a.x + g.cc * v0;
-          v1 = g.cb * a.y + g.cc * v1;
-          v2 = g.cb * a.z + g.cc * v2;
-          v3 = g.cb * a.w + g.cc * v3;
-          if constexpr (kBF)
-            store_bf16x4(g.out16, o, v0, v1, v2, v3);
-          else
-            *reinterpret_cast<float4*>(g.out32 + o) = make_float4(v0, v1, v2, v3);
-        } else {
-          const float4 a = aux[j][q];
-          v0 = __builtin_fmaf(g.ca, a.x, v0);
-          v1 = __builtin_fmaf(g.ca, a.y, v1);
-          v2 = __builtin_fmaf(g.ca, a.z, v2);
-          v3 = __builtin_fmaf(g.ca, a.w, v3);
-          if (g.final_mode == FINAL_NONE) {
-            *reinterpret_cast<float4*>(g.out32 + o) = make_float4(v0, v1, v2, v3);
-            if constexpr (kBF) store_bf16x4(g.out16, o, v0, v1, v2, v3);
-            // X'^T: element (m, n+e) lands at row n+e, column m.
-            const int64_t ot = (int64_t)u * g.out_ustride + (int64_t)n * g.ldt + m;
-            if constexpr (kBF) {
-              uint16_t* pt = static_cast<uint16_t*>(g.outt) + ot;
-              pt[0] = to_bf16_bits(v0);
-              pt[g.ldt] = to_bf16_bits(v1);
-              pt[2 * (int64_t)g.ldt] = to_bf16_bits(v2);
-              pt[3 * (int64_t)g.ldt] = to_bf16_bits(v3);
-            } else {
-              float* pt = static_cast<float*>(g.outt) + ot;
-              pt[0] = v0;
-              pt[g.ldt] = v1;
-              pt[2 * (int64_t)g.ldt] = v2;
-              pt[3 * (int64_t)g.ldt] = v3;
-            }
-          } else if (m < ca.rows && n < ca.cols) {
-            float* p = wout + (int64_t)m * ca.cols + n;
-            const bool step = g.final_mode == FINAL_STEP;
-            if (vec_w && n + 3 < ca.cols) {
-              float4 wv = step ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
-              if (step) {
-                wv.x = __builtin_fmaf(-ca.lr_scale, v0, wv.x * ca.decay);
-                wv.y = __builtin_fmaf(-ca.lr_scale, v1, wv.y * ca.decay);
-                wv.z = __builtin_fmaf(-ca.lr_scale, v2, wv.z * ca.decay);
-                wv.w = __builtin_fmaf(-ca.lr_scale, v3, wv.w * ca.decay);
-              } else {
-                wv = make_float4(v0, v1, v2, v3);
-              }
-              *reinterpret_cast<float4*>(p) = wv;
-            } else {
-              const float vv[4] = {v0, v1, v2, v3};
+        *reinterpret_cast<float4*>(ep + (lane & 31) * LDW + j * 32 + 8 * q + 4 * half) =
+            make_float4(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
+      }
+    // row-wise pass (a wave's LDS accesses complete in order)
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                if (n + e < ca.cols)
-                  p[e] = step ? __builtin_fmaf(-ca.lr_scale, vv[e], p[e] * ca.decay) : vv[e];
-              }
+    for (int it = 0; it < NIT; ++it) {
+      const int r = it * RPI + rl;
+      const float4 cv = *reinterpret_cast<const float4*>(ep + r * LDW + cl);
+      const int m = mrow0 + r;
+      float v0 = cv.x, v1 = cv.y, v2 = cv.z, v3 = cv.w;
+      const int64_t o = (int64_t)u * g.out_ustride + (int64_t)m * g.ldo + ncol;
+      if constexpr (PHASE == GRAM) {
+        if constexpr (kBF)
+          store_bf16x4(g.out16, o, v0, v1, v2, v3);
+        else
+          *reinterpret_cast<float4*>(g.out32 + o) = make_float4(v0, v1, v2, v3);
+      } else if constexpr (PHASE == POLY) {
+        const float4 a = aux[it];
+        v0 = g.cb * a.x + g.cc * v0;
+        v1 = g.cb * a.y + g.cc * v1;
+        v2 = g.cb * a.z + g.cc * v2;
+        v3 = g.cb * a.w + g.cc * v3;
+        if constexpr (kBF)
+          store_bf16x4(g.out16, o, v0, v1, v2, v3);
+        else
+          *reinterpret_cast<float4*>(g.out32 + o) = make_float4(v0, v1, v2, v3);
+      } else {
+        const float4 a = aux[it];
+        v0 = __builtin_fmaf(g.ca, a.x, v0);
+        v1 = __builtin_fmaf(g.ca, a.y, v1);
+        v2 = __builtin_fmaf(g.ca, a.z, v2);
+        v3 = __builtin_fmaf(g.ca, a.w, v3);
+        if (g.final_mode == FINAL_NONE) {
+          *reinterpret_cast<float4*>(g.out32 + o) = make_float4(v0, v1, v2, v3);
+          if constexpr (kBF) store_bf16x4(g.out16, o, v0, v1, v2, v3);
+          // keep a*X + C for the transposed pass
+          *reinterpret_cast<float4*>(ep + r * LDW + cl) = make_float4(v0, v1, v2, v3);
+        } else if (m < ca.rows && ncol < ca.cols) {
+          const int n = ncol;
+          float* p = wout + (int64_t)m * ca.cols + n;
+          const bool step = g.final_mode == FINAL_STEP;
+          if (vec_w && n + 3 < ca.cols) {
+            float4 wv = step ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
+            if (step) {
+              wv.x = __builtin_fmaf(-ca.lr_scale, v0, wv.x * ca.decay);
+              wv.y = __builtin_fmaf(-ca.lr_scale, v1, wv.y * ca.decay);
+              wv.z = __builtin_fmaf(-ca.lr_scale, v2, wv.z * ca.decay);
+              wv.w = __builtin_fmaf(-ca.lr_scale, v3, wv.w * ca.decay);
+            } else {
+              wv = make_float4(v0, v1, v2, v3);
+            }
+            *reinterpret_cast<float4*>(p) = wv;
+          } else {
+            const float vv[4] = {v0, v1, v2, v3};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              if (n + e < ca.cols)
+                p[e] = step ? __builtin_fmaf(-ca.lr_scale, vv[e], p[e] * ca.decay) : vv[e];
             }
           }
         }
       }
+    }
+    if constexpr (PHASE == APPLY) {
+      if (g.final_mode == FINAL_NONE) {
+        // X'^T rows n0 + wn*WT .. +WT, columns mrow0 .. +32: 8 lanes per
+        // row, 4 consecutive columns (staged rows) per lane.
+        const int cm = (lane & 7) * 4;
+#pragma unroll
+        for (int it = 0; it < WT / 8; ++it) {
+          const int nn = it * 8 + (lane >> 3);
+          const float a0 = ep[(cm + 0) * LDW + nn], a1 = ep[(cm + 1) * LDW + nn];
+          const float a2 = ep[(cm + 2) * LDW + nn], a3 = ep[(cm + 3) * LDW + nn];
+          const int64_t ot = (int64_t)u * g.out_ustride + (int64_t)(n0 + wn * WT + nn) * g.ldt + mrow0 + cm;
+          if constexpr (kBF)
+            store_bf16x4(g.outt, ot, a0, a1, a2, a3);
+          else
+            *reinterpret_cast<float4*>(static_cast<float*>(g.outt) + ot) = make_float4(a0, a1, a2, a3);
+        }
+      }
+    }
   }
 }
 
