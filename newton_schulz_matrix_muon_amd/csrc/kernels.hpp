@@ -15,6 +15,8 @@
 //   ns_gemm<GRAM>   A = X X^T (or X^T X for a tall unit: the smaller side).
 //   ns_gemm<POLY>   B = b*A + c*A*A (on the bf16 path A is kept only as its
 //                   bf16 operand copy, which the b*A term also reads).
+//                   Both outputs are symmetric: only the upper-triangle tiles
+//                   are computed, each also written mirrored.
 //   ns_gemm<APPLY>  X' = a*X + B*X (or X*B), written with its operand copies
 //                   (X' in bf16, X'^T); in the last iteration the epilogue
 //                   writes W <- W*(1 - lr*wd) - lr*scale*X' instead
@@ -85,6 +87,8 @@ struct GemmArgs {
   int32_t ldo;
   void* outt;           // APPLY: transposed operand copy of X' (T), or nullptr
   int32_t ldt;          // its leading dimension (rows of X')
+  int32_t sym;          // GRAM/POLY: symmetric output; only tiles tm <= tn run
+                        // and each off-diagonal tile also writes its mirror
   int32_t final_mode;
   const float* aux;     // fp32 A (POLY, fp32 path) or X (APPLY), laid out like the output
   const void* aux16;    // bf16 A (POLY, bf16 path)
@@ -450,11 +454,25 @@ __global__ __launch_bounds__(kThreads) void ns_gemm(GemmArgs g, ChunkArgs ca) {
   __shared__ u32x4 lds2[2 * kOp];
   __shared__ u32x4 lds3[2 * kOp];
 
-  const int tiles_per_unit = g.tiles_m * g.tiles_n;
+  const int tiles_per_unit =
+      g.sym ? g.tiles_m * (g.tiles_m + 1) / 2 : g.tiles_m * g.tiles_n;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int u = logical / tiles_per_unit;
   const int tt = logical - u * tiles_per_unit;
-  const int tm = tt / g.tiles_n, tn = tt - (tt / g.tiles_n) * g.tiles_n;
+  int tm, tn;
+  if (g.sym) {
+    // upper triangle, row by row: row r holds tiles (r, r..T-1)
+    int r = 0, rem = tt;
+    while (rem >= g.tiles_m - r) {
+      rem -= g.tiles_m - r;
+      ++r;
+    }
+    tm = r;
+    tn = r + rem;
+  } else {
+    tm = tt / g.tiles_n;
+    tn = tt - tm * g.tiles_n;
+  }
   const int m0 = tm * TILE, n0 = tn * TILE;
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
@@ -634,17 +652,16 @@ __global__ __launch_bounds__(kThreads) void ns_gemm(GemmArgs g, ChunkArgs ca) {
       const int m = mrow0 + r;
       float v0 = cv.x, v1 = cv.y, v2 = cv.z, v3 = cv.w;
       const int64_t o = (int64_t)u * g.out_ustride + (int64_t)m * g.ldo + ncol;
-      if constexpr (PHASE == GRAM) {
-        if constexpr (kBF)
-          store_bf16x4(g.out16, o, v0, v1, v2, v3);
-        else
-          *reinterpret_cast<float4*>(g.out32 + o) = make_float4(v0, v1, v2, v3);
-      } else if constexpr (PHASE == POLY) {
-        const float4 a = aux[it];
-        v0 = g.cb * a.x + g.cc * v0;
-        v1 = g.cb * a.y + g.cc * v1;
-        v2 = g.cb * a.z + g.cc * v2;
-        v3 = g.cb * a.w + g.cc * v3;
+      if constexpr (PHASE == GRAM || PHASE == POLY) {
+        if constexpr (PHASE == POLY) {
+          const float4 a = aux[it];
+          v0 = g.cb * a.x + g.cc * v0;
+          v1 = g.cb * a.y + g.cc * v1;
+          v2 = g.cb * a.z + g.cc * v2;
+          v3 = g.cb * a.w + g.cc * v3;
+          // the mirror pass below reads the final values
+          *reinterpret_cast<float4*>(ep + r * LDW + cl) = make_float4(v0, v1, v2, v3);
+        }
         if constexpr (kBF)
           store_bf16x4(g.out16, o, v0, v1, v2, v3);
         else
@@ -683,6 +700,24 @@ __global__ __launch_bounds__(kThreads) void ns_gemm(GemmArgs g, ChunkArgs ca) {
                 p[e] = step ? __builtin_fmaf(-ca.lr_scale, vv[e], p[e] * ca.decay) : vv[e];
             }
           }
+        }
+      }
+    }
+    if constexpr (PHASE == GRAM || PHASE == POLY) {
+      if (g.sym && tm != tn) {
+        // mirror tile: rows n0 + wn*WT .. +WT, columns mrow0 .. +32, read
+        // column-wise from the staged block (8 lanes per row, 4 columns each)
+        const int cm = (lane & 7) * 4;
+#pragma unroll
+        for (int it = 0; it < WT / 8; ++it) {
+          const int nn = it * 8 + (lane >> 3);
+          const float a0 = ep[(cm + 0) * LDW + nn], a1 = ep[(cm + 1) * LDW + nn];
+          const float a2 = ep[(cm + 2) * LDW + nn], a3 = ep[(cm + 3) * LDW + nn];
+          const int64_t om = (int64_t)u * g.out_ustride + (int64_t)(n0 + wn * WT + nn) * g.ldo + mrow0 + cm;
+          if constexpr (kBF)
+            store_bf16x4(g.out16, om, a0, a1, a2, a3);
+          else
+            *reinterpret_cast<float4*>(g.out32 + om) = make_float4(a0, a1, a2, a3);
         }
       }
     }

@@ -268,7 +268,8 @@ struct Tracer {
 
 template <int PHASE, typename T>
 void launch_gemm(int tile, const GemmArgs& g, const ChunkArgs& ca, hipStream_t s) {
-  const int grid = g.n_units * g.tiles_m * g.tiles_n;
+  const int per_unit = g.sym ? g.tiles_m * (g.tiles_m + 1) / 2 : g.tiles_m * g.tiles_n;
+  const int grid = g.n_units * per_unit;
   if (tile == 256)
     hipLaunchKernelGGL((ns_gemm<PHASE, T, 256>), dim3(grid), dim3(kThreads), 0, s, g, ca);
   else
@@ -387,6 +388,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
       g.M = g.N = (int32_t)sp;
       g.K = (int32_t)(c.tall ? c.rows_pad : c.cols_pad);
       g.tiles_m = g.tiles_n = (int32_t)(sp / T);
+      g.sym = 1;       // A is symmetric: upper-triangle tiles, mirrored
       g.out32 = a32;   // fp32 path
       g.out16 = ab;    // bf16 path
       g.out_ustride = ss;
@@ -404,6 +406,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
       g.lda = g.ldb = (int32_t)sp;
       g.M = g.N = g.K = (int32_t)sp;
       g.tiles_m = g.tiles_n = (int32_t)(sp / T);
+      g.sym = 1;       // B = b*A + c*A*A is symmetric as well
       g.out32 = bf16 ? nullptr : static_cast<float*>(bop);
       g.out16 = bf16 ? bop : nullptr;
       g.out_ustride = ss;
