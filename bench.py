@@ -38,10 +38,54 @@ def parse():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--ns", default="bf16", choices=["bf16", "fp32"])
     ap.add_argument("--batch-update-size", type=int, default=0)
+    ap.add_argument("--schedule", default="persistent", choices=["persistent", "launches"],
+                    help="NS launch schedule: one persistent launch per pass, or one per product")
     ap.add_argument("--grad-sets", type=int, default=4, help="distinct resident gradient batches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="after the timed region, run one plain copy kernel over this many MiB "
+                         "(int32 bitwise-not, read once and written once) for counter calibration")
     return ap.parse_args()
+
+
+def kernel_sources_sha256():
+    """Digest of the HIP sources, tying a stored counter record to the
+    kernels it was taken on."""
+    import hashlib
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "newton_schulz_matrix_muon_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".hpp", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(kernel, workload, ns):
+    """HBM bytes per launch from a committed rocprofv3 counter summary
+    (FETCH_SIZE and WRITE_SIZE runs, scaled by a copy kernel of known size),
+    or None when there is none for this kernel and workload or the kernel
+    sources have changed since it was taken."""
+    pdir = os.path.join(ROOT, "profiles")
+    if not os.path.isdir(pdir):
+        return None
+    digest = kernel_sources_sha256()
+    for name in sorted(os.listdir(pdir)):
+        if not name.endswith(".md"):
+            continue
+        with open(os.path.join(pdir, name), encoding="utf-8") as f:
+            for line in f:
+                if not line.startswith("traffic_record: "):
+                    continue
+                rec = json.loads(line[len("traffic_record: "):])
+                if (rec.get("kernel"), rec.get("workload"), rec.get("ns")) != (kernel, workload, ns):
+                    continue
+                if rec.get("sources_sha256") != digest:
+                    return None
+                return rec
+    return None
 
 
 def build_inputs(wl, dev, grad_sets):
@@ -74,12 +118,21 @@ def nonzero_units(wl):
 
 
 def kernel_flops(units):
-    """Algorithmic FLOPs of one launch of each NS kernel class, summed over
-    the workload's launches per iteration (one launch per shape group)."""
+    """Algorithmic FLOPs of each NS kernel class per iteration, summed over
+    the workload's shape groups: X X^T and A*A as full products (2 s^2 l and
+    2 s^3), B*X as 2 s^2 l."""
     gram = sum(n * 2.0 * s * s * l for s, l, n in units)
     poly = sum(n * 2.0 * s**3 for s, l, n in units)
     apply = sum(n * 2.0 * s * s * l for s, l, n in units)
     return {"gram": gram, "poly": poly, "apply": apply}
+
+
+def executed_fraction(s):
+    """Share of a symmetric s x s product's tiles that run (upper triangle
+    of the tile grid; tiles are 256, or 128 when s < 256)."""
+    tile = 256 if s >= 256 else 128
+    t = -(-s // tile)
+    return (t * (t + 1) / 2) / (t * t)
 
 
 def cpu_baseline(wl, hyper_o, seconds):
@@ -135,7 +188,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     wl = W.workload(args.config)
-    hyper = muon.Hyper(scale=wl.scale, ns_precision=args.ns, batch_update_size=args.batch_update_size)
+    hyper = muon.Hyper(scale=wl.scale, ns_precision=args.ns, batch_update_size=args.batch_update_size,
+                       schedule=args.schedule)
     params, moms, grads, splits = build_inputs(wl, dev, args.grad_sets)
     ws_bytes = muon.workspace_size(params, hyper, splits)
     ws = muon.workspace(ws_bytes, dev)
@@ -174,7 +228,10 @@ def main():
         one_step(k)
     ev1 = make_events(per_step)
     torch.cuda.synchronize()
-    kinds = {"gram": muon.KERNEL_GRAM, "poly": muon.KERNEL_POLY, "apply": muon.KERNEL_APPLY}
+    if args.schedule == "persistent":
+        kinds = {"ns": muon.KERNEL_NS}
+    else:
+        kinds = {"gram": muon.KERNEL_GRAM, "poly": muon.KERNEL_POLY, "apply": muon.KERNEL_APPLY}
     per_kind = {name: sum(traced_ms(kind, 0, ev1)) for name, kind in kinds.items()}
     mom_ms = traced_ms(muon.KERNEL_MOMENTUM, 0, ev1)
     norm_ms = traced_ms(muon.KERNEL_NORMALIZE, 0, ev1)
@@ -195,6 +252,7 @@ def main():
         launch_ms += [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(min(cnt, len(ev) // 2))]
 
     flops = kernel_flops(units)
+    flops["ns"] = flops["gram"] + flops["poly"] + flops["apply"]
     avg_launch_ms = sum(launch_ms) / max(1, len(launch_ms))
     # algorithmic FLOPs of one launch: the class's FLOPs per step (every
     # iteration, every non-zero unit) over its launches per step
@@ -203,7 +261,25 @@ def main():
     ns_ms = sum(per_kind.values())
     ns_tflops = ns_flops_step / (ns_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[args.ns]
-    elem_bytes = sum(m.numel for m in wl.matrices) * (18 if wl.matrices[0].grad_dtype == "bf16" else 20)
+    # momentum kernel: G read (2 or 4 B), M read and written (8 B), the fp32
+    # look-ahead written (4 B)
+    elem_bytes = sum(m.numel * (14 if m.grad_dtype == "bf16" else 16) for m in wl.matrices)
+    sym_exec = {
+        "gram": sum(n * 2.0 * s * s * l * executed_fraction(s) for s, l, n in units) * iters,
+        "poly": sum(n * 2.0 * s**3 * executed_fraction(s) for s, l, n in units) * iters,
+        "apply": flops["apply"] * iters,
+    }
+    sym_exec["ns"] = sym_exec["gram"] + sym_exec["poly"] + sym_exec["apply"]
+    kernel_name = "ns_persistent" if dominant == "ns" else f"ns_gemm {dominant}"
+    traffic = stored_traffic(kernel_name, wl.title, args.ns)
+    if args.calibrate_copy_mib > 0:
+        n = args.calibrate_copy_mib * (1 << 20) // 4
+        src = torch.zeros(n, dtype=torch.int32, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        torch.bitwise_not(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     line = {
         "metric": "Muon matrices/sec + NS TFLOP/s (% of MI355X bf16 MFMA peak) per config",
@@ -226,6 +302,7 @@ def main():
             "grad_dtype": wl.matrices[0].grad_dtype,
             "scale": wl.scale,
             "ns_path": args.ns,
+            "schedule": args.schedule,
             "parallelism": "single GPU",
         },
         "ns_tflops": ns_tflops,
@@ -236,15 +313,20 @@ def main():
             "momentum": round(sum(mom_ms), 4),
             "normalize": round(sum(norm_ms), 4),
         },
+        # FLOPs the kernels execute: the symmetric products run only their
+        # upper-triangle tiles
+        "kernel_tflops_executed": {
+            k: round(sym_exec[k] / (per_kind[k] * 1e-3) / 1e12, 2) for k in per_kind
+        },
         "elementwise_gbs": elem_bytes / (sum(mom_ms) * 1e-3) / 1e9 if mom_ms else None,
         "roofline": {
             "bound": "mfma",
-            "kernel": f"ns_gemm {dominant}",
+            "kernel": kernel_name,
             "achieved": achieved,
             "peak": peak,
             "unit": "TFLOP/s",
             "frac": achieved / peak,
-            "traffic": None,
+            "traffic": traffic["bytes_per_launch"] if traffic else None,
             "flops_per_launch": flops_per_launch,
             "avg_launch_ms": avg_launch_ms,
             "launches_timed": len(launch_ms),

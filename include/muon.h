@@ -61,7 +61,9 @@ typedef enum {
   MUON_ERR_WORKSPACE = -5, /* workspace NULL or smaller than muon_workspace_size() */
   MUON_ERR_HYPER = -6,     /* invalid hyper-parameters (non-finite, bad stage table) */
   MUON_ERR_HIP = -7,       /* a HIP call failed; outputs are undefined */
-  MUON_ERR_ALIAS = -8      /* overlapping input/output buffers where not allowed */
+  MUON_ERR_ALIAS = -8,     /* overlapping input/output buffers where not allowed */
+  MUON_ERR_SCHEDULE = -9   /* the persistent NS schedule stopped (reported by
+                              muon_workspace_status); outputs are undefined */
 } muon_status;
 
 typedef enum { MUON_DTYPE_F32 = 0, MUON_DTYPE_BF16 = 1 } muon_dtype;
@@ -75,6 +77,18 @@ typedef enum { MUON_SCALE_SPECTRAL = 0, MUON_SCALE_UNIT_RMS_NORM = 1 } muon_scal
  * read: X, the Gram A (whose bf16 copy also feeds the b*A term) and the
  * polynomial B. */
 typedef enum { MUON_NS_FP32 = 0, MUON_NS_BF16 = 1 } muon_ns_precision;
+
+/* How the Newton-Schulz products of a stacked pass are launched; both give
+ * bit-identical results.
+ * PERSISTENT: one launch runs every iteration of the pass.  Workgroups claim
+ *   output tiles in order (for each iteration: the Gram tiles of every
+ *   unit, then the polynomial tiles, then the apply tiles) and each tile
+ *   waits until its unit has finished the products before it, so tiles of
+ *   different units and products overlap.  A wait is bounded (a few seconds
+ *   of wall clock); if one ever runs out the launch stops and
+ *   muon_workspace_status reports MUON_ERR_SCHEDULE.
+ * LAUNCHES: one launch per product and iteration, in stream order. */
+typedef enum { MUON_SCHEDULE_PERSISTENT = 0, MUON_SCHEDULE_LAUNCHES = 1 } muon_schedule;
 
 /* A bank of `batch` equal-shape matrices stored back to back (stride
  * rows*cols elements).  rows = fan_out, cols = fan_in.  split_rows = 0: each
@@ -107,19 +121,24 @@ typedef struct {
   int32_t batch_update_size; /* max NS units per stacked pass; 0 = whole shape group */
   int32_t n_stages;          /* 1..MUON_MAX_STAGES */
   muon_ns_stage stages[MUON_MAX_STAGES];
+  int32_t schedule;          /* muon_schedule */
+  int32_t reserved;          /* must be 0 */
 } muon_hyper;
 
 /* Fill `h` with the pages' values: lr 2.7e-4, mu 0.95, weight_decay 0.1,
  * gamma 0.18, spectral scale, bf16 NS products, whole-group batches, and the
  * hybrid schedule 8 x (3.4445, -4.7750, 2.0315) + 2 x (2, -1.5, 0.5)
- * (DeepSeek tech notes "Muon 优化器" sections 1-3).  NULL is ignored. */
+ * (DeepSeek tech notes "Muon 优化器" sections 1-3); persistent launch
+ * schedule.  NULL is ignored. */
 void muon_hyper_default(muon_hyper* h);
 
 /* Bytes of device workspace that muon_step_batched / muon_newton_schulz_batched
  * need for these matrices and hyper-parameters (the same value for both).
- * The workspace holds the NS iterates, Gram and polynomial matrices of the
- * largest stacked pass and the per-unit norms; it is scratch, owned by the
- * caller, and may be reused freely between calls on the same stream.
+ * The workspace holds a status word, the NS iterates, Gram and polynomial
+ * matrices of the largest stacked pass, the per-unit norms and the schedule
+ * counters; it is scratch, owned by the caller, and may be reused freely
+ * between calls on the same stream (calls that share a workspace must not
+ * run concurrently).
  * Errors: MUON_ERR_NULL, MUON_ERR_SHAPE, MUON_ERR_DTYPE, MUON_ERR_HYPER. */
 int muon_workspace_size(const muon_matrix_desc* mats, int64_t n_mats, const muon_hyper* h,
                         size_t* bytes);
@@ -155,7 +174,9 @@ typedef enum {
   MUON_KERNEL_NORMALIZE = 2,/* norm finish + scaling of the NS input */
   MUON_KERNEL_GRAM = 3,     /* A = X X^T on the smaller side */
   MUON_KERNEL_POLY = 4,     /* B = b*A + c*A*A */
-  MUON_KERNEL_APPLY = 5     /* X <- a*X + B*X (last one: the weight update) */
+  MUON_KERNEL_APPLY = 5,    /* X <- a*X + B*X (last one: the weight update) */
+  MUON_KERNEL_NS = 6        /* every NS product of a pass in one launch
+                               (MUON_SCHEDULE_PERSISTENT) */
 } muon_kernel_kind;
 
 /* Timing hook: when passed to the *_traced entry points, every launch of
@@ -184,10 +205,16 @@ int muon_newton_schulz_batched_traced(const float* const* x_in, float* const* o_
                                       size_t workspace_bytes, hipStream_t stream,
                                       muon_trace* trace);
 
+/* Waits for `stream`, then reads the status word that the last call on this
+ * workspace left: MUON_OK, or MUON_ERR_SCHEDULE if a persistent NS launch
+ * stopped early.  Errors: MUON_ERR_NULL, MUON_ERR_WORKSPACE (fewer than 256
+ * bytes), MUON_ERR_ALIGN, MUON_ERR_HIP. */
+int muon_workspace_status(const void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Static description of a status code (never NULL). */
 const char* muon_status_string(int status);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2. */
 int muon_abi_version(void);
 
 #ifdef __cplusplus

@@ -21,6 +21,10 @@
 //                   (X' in bf16, X'^T); in the last iteration the epilogue
 //                   writes W <- W*(1 - lr*wd) - lr*scale*X' instead
 //                   (Algorithm 1's decoupled update) or the NS output.
+//   ns_persistent   the three products of every iteration in one launch:
+//                   workgroups claim tiles in order and wait on per-unit
+//                   completion counts, so tiles of different units and
+//                   phases overlap (no launch boundary between products).
 // The three products are the quintic step a*X + b*(X X^T)X + c*(X X^T)^2 X of
 // the notes' section 2, grouped as (b*A + c*A^2)*X.  Keeping X both as is and
 // transposed makes every product "A times B-transposed" with both operands
@@ -229,9 +233,14 @@ __global__ __launch_bounds__(kThreads) void k_momentum(ChunkArgs ca, float* __re
 }
 
 // One wave per unit: fixed-order sum of the partials.
+// It also clears the persistent schedule's per-unit counts and claim
+// counter (when given), and the error word (when given).
 __global__ __launch_bounds__(64) void k_norm_finish(const double* __restrict__ partials,
                                                     int blocks_per_unit, float* __restrict__ inv_nu,
-                                                    int32_t* __restrict__ flag) {
+                                                    int32_t* __restrict__ flag,
+                                                    uint32_t* __restrict__ sched_done,
+                                                    uint32_t* __restrict__ sched_queue,
+                                                    uint32_t* __restrict__ err) {
   const int u = blockIdx.x;
   double s = 0.0;
   for (int i = threadIdx.x; i < blocks_per_unit; i += 64)
@@ -242,6 +251,9 @@ __global__ __launch_bounds__(64) void k_norm_finish(const double* __restrict__ p
     const bool zero = (s == 0.0);
     flag[u] = zero ? 0 : 1;
     inv_nu[u] = zero ? 0.0f : (float)(1.0 / sqrt(s));
+    if (sched_done) sched_done[u] = 0u;
+    if (u == 0 && sched_queue) *sched_queue = 0u;
+    if (u == 0 && err) *err = 0u;
   }
 }
 
@@ -345,9 +357,13 @@ __device__ __forceinline__ int swz(int row, int chunk) {
 
 // Buffer resource (4 SGPRs) for a raw buffer at `base`: stride 0, a 2 GiB
 // range and the 32-bit data format of the gfx9 family.
+// The base is uniform across the workgroup; readfirstlane keeps the
+// descriptor in scalar registers whatever the compiler can prove.
 __device__ __forceinline__ u32x4 tile_rsrc(const void* base) {
   const uint64_t b = reinterpret_cast<uint64_t>(base);
-  return u32x4{(uint32_t)b, (uint32_t)(b >> 32) & 0xFFFFu, 0x7FFFFFFFu, 0x00020000u};
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  return u32x4{lo, hi & 0xFFFFu, 0x7FFFFFFFu, 0x00020000u};
 }
 
 // DMA instructions per wave for one operand of one stage.
@@ -440,8 +456,41 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+// LDS stage buffers of the GEMM tile (kStages of them, each TILE rows of
+// both operands x 64 bytes).  Declared once per tile size, so a kernel that
+// runs several tile phases holds a single set.
+template <int TILE>
+__shared__ u32x4 lds_st0[2 * TILE * 4];
+template <int TILE>
+__shared__ u32x4 lds_st1[2 * TILE * 4];
+template <int TILE>
+__shared__ u32x4 lds_st2[2 * TILE * 4];
+template <int TILE>
+__shared__ u32x4 lds_st3[2 * TILE * 4];
+
+// Zero unit in the last iteration: O' = 0, so the weight only decays (step)
+// or the NS output is zero, over the TILE x TILE block at (m0, n0).
+template <int TILE>
+__device__ __forceinline__ void zero_unit_tile(const ChunkArgs& ca, int final_mode, int u, int m0,
+                                               int n0) {
+  const SegView sg = find_seg(ca, u);
+  float* wout = sg.w + (int64_t)(u - sg.first) * ca.unit_elems;
+  for (int idx = threadIdx.x; idx < TILE * TILE; idx += kThreads) {
+    const int mm = m0 + idx / TILE, nn = n0 + idx % TILE;
+    if (mm < ca.rows && nn < ca.cols) {
+      float* p = wout + (int64_t)mm * ca.cols + nn;
+      *p = (final_mode == FINAL_STEP) ? (*p) * ca.decay : 0.0f;
+    }
+  }
+}
+
+// One TILE x TILE output tile (tm, tn) of unit u.  Every wave of the
+// workgroup calls it; it starts by overwriting the LDS stage buffers, so the
+// caller makes sure no wave still reads them (a barrier after the previous
+// tile's epilogue).
 template <int PHASE, typename T, int TILE>
-__global__ __launch_bounds__(kThreads) void ns_gemm(GemmArgs g, ChunkArgs ca) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca, int u, int tm,
+                                          int tn) {
   constexpr int WT = TILE / 2;   // wave tile
   constexpr int FM = WT / 32;    // 32x32 blocks per wave side
   constexpr bool kBF = sizeof(T) == 2;
@@ -449,50 +498,14 @@ __global__ __launch_bounds__(kThreads) void ns_gemm(GemmArgs g, ChunkArgs ca) {
   constexpr int BK = OpT<T>::kBK;
   constexpr int P = 2 * dma_per_wave<TILE>();  // DMA instructions per wave per stage
   constexpr int kMf = FM * FM * (kBF ? 1 : 4);  // MFMAs per K sub-step
-  __shared__ u32x4 lds0[2 * kOp];
-  __shared__ u32x4 lds1[2 * kOp];
-  __shared__ u32x4 lds2[2 * kOp];
-  __shared__ u32x4 lds3[2 * kOp];
-
-  const int tiles_per_unit =
-      g.sym ? g.tiles_m * (g.tiles_m + 1) / 2 : g.tiles_m * g.tiles_n;
-  const int logical = xcd_remap(blockIdx.x, gridDim.x);
-  const int u = logical / tiles_per_unit;
-  const int tt = logical - u * tiles_per_unit;
-  int tm, tn;
-  if (g.sym) {
-    // upper triangle, row by row: row r holds tiles (r, r..T-1)
-    int r = 0, rem = tt;
-    while (rem >= g.tiles_m - r) {
-      rem -= g.tiles_m - r;
-      ++r;
-    }
-    tm = r;
-    tn = r + rem;
-  } else {
-    tm = tt / g.tiles_n;
-    tn = tt - tm * g.tiles_n;
-  }
+  u32x4* const lds0 = lds_st0<TILE>;
+  u32x4* const lds1 = lds_st1<TILE>;
+  u32x4* const lds2 = lds_st2<TILE>;
+  u32x4* const lds3 = lds_st3<TILE>;
   const int m0 = tm * TILE, n0 = tn * TILE;
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
   const int wm = wid >> 1, wn = wid & 1;
-
-  if (!g.flag[u]) {
-    if (PHASE == APPLY && g.final_mode != FINAL_NONE) {
-      // Zero unit: O' = 0, so the weight only decays / the output is zero.
-      const SegView sg = find_seg(ca, u);
-      float* wout = sg.w + (int64_t)(u - sg.first) * ca.unit_elems;
-      for (int idx = threadIdx.x; idx < TILE * TILE; idx += kThreads) {
-        const int mm = m0 + idx / TILE, nn = n0 + idx % TILE;
-        if (mm < ca.rows && nn < ca.cols) {
-          float* p = wout + (int64_t)mm * ca.cols + nn;
-          *p = (g.final_mode == FINAL_STEP) ? (*p) * ca.decay : 0.0f;
-        }
-      }
-    }
-    return;
-  }
 
   const T* A = static_cast<const T*>(g.a) + (int64_t)u * g.a_ustride;
   const T* B = static_cast<const T*>(g.b) + (int64_t)u * g.b_ustride;
@@ -514,10 +527,10 @@ __global__ __launch_bounds__(kThreads) void ns_gemm(GemmArgs g, ChunkArgs ca) {
   // LDS byte offsets of the stages (casts of the arrays themselves fold to
   // constants).
   auto stage_off = [&](int st) -> uint32_t {
-    return st == 0   ? (uint32_t)(uintptr_t)(lds_vptr)lds0
-           : st == 1 ? (uint32_t)(uintptr_t)(lds_vptr)lds1
-           : st == 2 ? (uint32_t)(uintptr_t)(lds_vptr)lds2
-                     : (uint32_t)(uintptr_t)(lds_vptr)lds3;
+    return st == 0   ? (uint32_t)(uintptr_t)(lds_vptr)lds_st0<TILE>
+           : st == 1 ? (uint32_t)(uintptr_t)(lds_vptr)lds_st1<TILE>
+           : st == 2 ? (uint32_t)(uintptr_t)(lds_vptr)lds_st2<TILE>
+                     : (uint32_t)(uintptr_t)(lds_vptr)lds_st3<TILE>;
   };
   DmaPlan<T, TILE> pa, pb;
   pa.init(g.lda);
@@ -740,6 +753,209 @@ __global__ __launch_bounds__(kThreads) void ns_gemm(GemmArgs g, ChunkArgs ca) {
       }
     }
   }
+}
+
+// Upper-triangle tile t (row by row: row r holds tiles (r, r..T-1)) of a
+// T x T tile grid.
+__device__ __forceinline__ void sym_tile(int t, int T, int& tm, int& tn) {
+  int r = 0;
+  while (t >= T - r) {
+    t -= T - r;
+    ++r;
+  }
+  tm = r;
+  tn = r + t;
+}
+
+// One launch per product: workgroup -> (unit, tile), XCD-aware.
+template <int PHASE, typename T, int TILE>
+__global__ __launch_bounds__(kThreads) void ns_gemm(GemmArgs g, ChunkArgs ca) {
+  const int tiles_per_unit = g.sym ? g.tiles_m * (g.tiles_m + 1) / 2 : g.tiles_m * g.tiles_n;
+  const int logical = xcd_remap(blockIdx.x, gridDim.x);
+  const int u = logical / tiles_per_unit;
+  const int tt = logical - u * tiles_per_unit;
+  int tm, tn;
+  if (g.sym) {
+    sym_tile(tt, g.tiles_m, tm, tn);
+  } else {
+    tm = tt / g.tiles_n;
+    tn = tt - tm * g.tiles_n;
+  }
+  if (!g.flag[u]) {
+    if (PHASE == APPLY && g.final_mode != FINAL_NONE)
+      zero_unit_tile<TILE>(ca, g.final_mode, u, tm * TILE, tn * TILE);
+    return;
+  }
+  gemm_tile<PHASE, T, TILE>(g, ca, u, tm, tn);
+}
+
+// ------------------------------------------------------ persistent NS ------
+// All Newton-Schulz iterations of a chunk in one launch.  Work items, in
+// claim order: for each iteration, the Gram tiles of every unit, then the
+// polynomial tiles, then the apply tiles (unit-major within a phase).  A
+// workgroup claims the next item from an atomic counter, waits until the
+// item's unit has finished every item of the phases before it (a per-unit
+// count of finished items), runs the tile and adds one to the count.  An
+// item only waits for items that precede it in claim order, and those were
+// claimed by running workgroups, so the schedule always makes progress; the
+// wait is still bounded by a wall-clock limit, after which the launch stops
+// and reports through `err`.
+struct NsSched {
+  GemmArgs gram, poly, apply;     // cur-independent fields of each product
+  const void* gram_op[2];         // Gram operand (both sides) for X in buffer cur
+  const void* app_a[2];           // apply operands for X in buffer cur
+  const void* app_b[2];
+  float* app_out32[2];            // apply outputs (buffer cur ^ 1)
+  void* app_out16[2];
+  void* app_outt[2];
+  const float* app_aux[2];        // the iterate X (buffer cur)
+  int32_t final_mode;             // of the last iteration's apply
+  int32_t n_iter;
+  int32_t n_stages;
+  int32_t stage_begin[4];         // first iteration of each stage
+  float sa[4], sb[4], sc[4];      // coefficients of each stage
+  int32_t tg;                     // tiles per unit of a symmetric product
+  int32_t ta;                     // tiles per unit of the apply product
+  int32_t n_items;
+  uint32_t* queue;                // next item to claim
+  uint32_t* done;                 // per unit: finished items
+  uint32_t* err;                  // set when a wait timed out
+  uint64_t timeout_ticks;         // wall-clock ticks
+};
+
+template <typename T, int TILE>
+__global__ __launch_bounds__(kThreads) void ns_persistent(NsSched p, ChunkArgs ca) {
+  // Every branch below is uniform across the workgroup or across a wave:
+  // the scheduling work (claim, completion count, dependency wait) is done
+  // by all of wave 0 with only lane 0 contributing to the atomics, never
+  // under a per-lane condition.  A per-lane branch around it lets the
+  // compiler thread the tail of one iteration into the head of the next for
+  // that lane alone, and the other lanes would then reach the barriers on
+  // stale state.
+  __shared__ int s_item, s_go;
+  const int per_unit = 2 * p.tg + p.ta;
+  const int per_iter = ca.n_units * per_unit;
+  const int ug = ca.n_units * p.tg;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t one = (threadIdx.x & 63) == 0 ? 1u : 0u;  // lane 0's share
+  int pending = -1;  // unit whose finished tile wave 0 has yet to count
+  for (;;) {
+    if (wave == 0) {
+      if (pending >= 0) {
+        // Every wave's stores are complete (the barrier that ended the
+        // tile): release at agent scope, then count the tile.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __hip_atomic_fetch_add(p.done + pending, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      int item = __builtin_amdgcn_readfirstlane(
+          (int)__hip_atomic_fetch_add(p.queue, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      const uint32_t e = __builtin_amdgcn_readfirstlane(
+          __hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+      if (e != 0u) item = p.n_items;
+      s_item = item;  // every lane writes the same value
+    }
+    pending = -1;
+    __syncthreads();
+    const int item = __builtin_amdgcn_readfirstlane(s_item);
+    if (item >= p.n_items) break;
+    const int it = item / per_iter;
+    int r = item - it * per_iter;
+    int phase, u, t;
+    if (r < ug) {
+      phase = GRAM;
+    } else if (r < 2 * ug) {
+      phase = POLY;
+      r -= ug;
+    } else {
+      phase = APPLY;
+      r -= 2 * ug;
+    }
+    const int tpu = phase == APPLY ? p.ta : p.tg;
+    u = r / tpu;
+    t = r - u * tpu;
+    const bool live = __builtin_amdgcn_readfirstlane(p.gram.flag[u]) != 0;
+    // A zero unit computes nothing, so its items wait for nothing.
+    const uint32_t need =
+        (uint32_t)(it * per_unit + (phase == GRAM ? 0 : phase == POLY ? p.tg : 2 * p.tg));
+    if (wave == 0) {
+      int go = 1;
+      if (live && need > 0u) {
+        const uint64_t t0 = wall_clock64();
+        uint32_t d = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(p.done + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        while (d < need) {
+          const uint32_t e = __builtin_amdgcn_readfirstlane(
+              __hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+          if (e != 0u || wall_clock64() - t0 > p.timeout_ticks) {
+            __hip_atomic_store(p.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            go = 0;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(2);
+          d = __builtin_amdgcn_readfirstlane(
+              __hip_atomic_load(p.done + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        }
+      }
+      s_go = go;
+    }
+    __syncthreads();
+    if (!__builtin_amdgcn_readfirstlane(s_go)) break;
+    // Make the other workgroups' results visible to this wave's loads.
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    const int cur = it & 1;
+    if (phase == GRAM) {
+      if (live) {
+        GemmArgs g = p.gram;
+        g.a = g.b = cur ? p.gram_op[1] : p.gram_op[0];
+        int tm, tn;
+        sym_tile(t, g.tiles_m, tm, tn);
+        gemm_tile<GRAM, T, TILE>(g, ca, u, tm, tn);
+      }
+    } else if (phase == POLY) {
+      if (live) {
+        GemmArgs g = p.poly;
+        float cb = p.sb[0], cc = p.sc[0];
+#pragma unroll
+        for (int s = 1; s < 4; ++s)
+          if (s < p.n_stages && it >= p.stage_begin[s]) {
+            cb = p.sb[s];
+            cc = p.sc[s];
+          }
+        g.cb = cb;
+        g.cc = cc;
+        int tm, tn;
+        sym_tile(t, g.tiles_m, tm, tn);
+        gemm_tile<POLY, T, TILE>(g, ca, u, tm, tn);
+      }
+    } else {
+      const int fm = it == p.n_iter - 1 ? p.final_mode : (int)FINAL_NONE;
+      const int tm = t / p.apply.tiles_n, tn = t - (t / p.apply.tiles_n) * p.apply.tiles_n;
+      if (live) {
+        GemmArgs g = p.apply;
+        float a = p.sa[0];
+#pragma unroll
+        for (int s = 1; s < 4; ++s)
+          if (s < p.n_stages && it >= p.stage_begin[s]) a = p.sa[s];
+        g.ca = a;
+        g.final_mode = fm;
+        g.a = cur ? p.app_a[1] : p.app_a[0];
+        g.b = cur ? p.app_b[1] : p.app_b[0];
+        g.out32 = cur ? p.app_out32[1] : p.app_out32[0];
+        g.out16 = cur ? p.app_out16[1] : p.app_out16[0];
+        g.outt = cur ? p.app_outt[1] : p.app_outt[0];
+        g.aux = cur ? p.app_aux[1] : p.app_aux[0];
+        gemm_tile<APPLY, T, TILE>(g, ca, u, tm, tn);
+      } else if (fm != FINAL_NONE) {
+        zero_unit_tile<TILE>(ca, fm, u, tm * TILE, tn * TILE);
+      }
+    }
+    // Every wave's stores of the tile complete before the barrier; wave 0
+    // counts the tile at the top of the next iteration.
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (live) pending = u;
+  }
+  // Every exit passes the claim first, which counts the pending tile.
 }
 
 }  // namespace muon_dev

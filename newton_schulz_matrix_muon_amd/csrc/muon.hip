@@ -11,7 +11,8 @@
 //  3. A chunk is one stacked pass: every kernel of the step runs once over
 //     all of its units (and the ten NS iterations run back to back), with the
 //     iterates laid out at a fixed stride in the caller's workspace.
-// The workspace is sized for the largest chunk and reused by every chunk.
+// The workspace is a 256-byte status header (word 0: the schedule error
+// word) followed by the carve-up of the largest chunk, reused by every chunk.
 #include "../../include/muon.h"
 
 #include <algorithm>
@@ -19,6 +20,7 @@
 #include <cstdint>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <new>
 #include <tuple>
 #include <vector>
@@ -62,15 +64,17 @@ struct Chunk {
 
 // Workspace carve-up of one chunk (byte offsets).
 struct Layout {
-  size_t x32[2], xb[2], xt[2], a32, ab, bop, partials, inv_nu, flag, total;
+  size_t x32[2], xb[2], xt[2], a32, ab, bop, partials, inv_nu, flag, done, queue, total;
 };
+
+constexpr size_t kHeader = 256;  // status header at the start of the workspace
 
 Layout layout_of(const Chunk& c, bool bf16) {
   Layout L{};
   const size_t U = (size_t)c.n_units;
   const size_t xs = (size_t)(c.rows_pad * c.cols_pad);
   const size_t ss = (size_t)(c.s_pad * c.s_pad);
-  size_t off = 0;
+  size_t off = kHeader;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, kAlign); return o; };
   L.x32[0] = take(U * xs * 4);
   L.x32[1] = take(U * xs * 4);
@@ -90,6 +94,8 @@ Layout layout_of(const Chunk& c, bool bf16) {
   L.partials = take(U * (size_t)c.blocks_per_unit * 8);
   L.inv_nu = take(U * 4);
   L.flag = take(U * 4);
+  L.done = take(U * 4);   // persistent schedule: finished items per unit
+  L.queue = take(4);      // persistent schedule: next item to claim
   L.total = off;
   return L;
 }
@@ -102,6 +108,9 @@ int validate_hyper(const muon_hyper* h) {
     return MUON_ERR_HYPER;
   if (h->scale_mode != MUON_SCALE_SPECTRAL && h->scale_mode != MUON_SCALE_UNIT_RMS_NORM)
     return MUON_ERR_DTYPE;
+  if (h->schedule != MUON_SCHEDULE_PERSISTENT && h->schedule != MUON_SCHEDULE_LAUNCHES)
+    return MUON_ERR_HYPER;
+  if (h->reserved != 0) return MUON_ERR_HYPER;
   if (h->ns_precision != MUON_NS_FP32 && h->ns_precision != MUON_NS_BF16) return MUON_ERR_DTYPE;
   if (h->batch_update_size < 0) return MUON_ERR_HYPER;
   if (h->n_stages < 1 || h->n_stages > MUON_MAX_STAGES) return MUON_ERR_HYPER;
@@ -219,7 +228,7 @@ int plan(const muon_matrix_desc* mats, int64_t n, const muon_hyper* h, bool step
 }
 
 size_t workspace_of(const std::vector<Chunk>& chunks, bool bf16) {
-  size_t need = 0;
+  size_t need = kHeader;
   for (const Chunk& c : chunks) need = std::max(need, layout_of(c, bf16).total);
   return need;
 }
@@ -266,6 +275,51 @@ struct Tracer {
   }
 };
 
+// Per-device facts the persistent launch needs: resident workgroups of each
+// kernel variant and the wall-clock rate.
+struct DeviceInfo {
+  bool ready = false;
+  int cus = 0;
+  int wall_khz = 0;
+  int resident[2][2] = {{0, 0}, {0, 0}};  // [bf16][tile 256]
+};
+
+constexpr int kMaxDevices = 64;
+std::mutex g_dev_mu;
+DeviceInfo g_dev[kMaxDevices];
+
+template <typename T, int TILE>
+int resident_of(int cus) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ns_persistent<T, TILE>, kThreads, 0) !=
+          hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  return per_cu * cus;
+}
+
+int device_info(DeviceInfo* out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MUON_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_dev_mu);
+  DeviceInfo& d = g_dev[dev];
+  if (!d.ready) {
+    if (hipDeviceGetAttribute(&d.cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipDeviceGetAttribute(&d.wall_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
+        d.cus < 1 || d.wall_khz < 1)
+      return MUON_ERR_HIP;
+    d.resident[0][0] = resident_of<float, 128>(d.cus);
+    d.resident[0][1] = resident_of<float, 256>(d.cus);
+    d.resident[1][0] = resident_of<__bf16, 128>(d.cus);
+    d.resident[1][1] = resident_of<__bf16, 256>(d.cus);
+    d.ready = true;
+  }
+  *out = d;
+  return MUON_OK;
+}
+
+constexpr double kWaitLimitSeconds = 5.0;  // bound of one dependency wait
+
 template <int PHASE, typename T>
 void launch_gemm(int tile, const GemmArgs& g, const ChunkArgs& ca, hipStream_t s) {
   const int per_unit = g.sym ? g.tiles_m * (g.tiles_m + 1) / 2 : g.tiles_m * g.tiles_n;
@@ -288,7 +342,7 @@ void launch_phase(bool bf16, int tile, const GemmArgs& g, const ChunkArgs& ca, h
 // NS iterations with the fused final epilogue.
 int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs,
               const void* const* ins, float* const* moms, const muon_matrix_desc* mats,
-              unsigned char* ws, hipStream_t s, Tracer& tr) {
+              unsigned char* ws, hipStream_t s, Tracer& tr, bool first_chunk) {
   const bool bf16 = h->ns_precision == MUON_NS_BF16;
   const Layout L = layout_of(c, bf16);
   ChunkArgs ca;
@@ -346,8 +400,11 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
   tr.after(MUON_KERNEL_MOMENTUM);
   // 2. norms and X0 = N / ||N||_F.
   tr.before(MUON_KERNEL_NORMALIZE);
+  uint32_t* done = reinterpret_cast<uint32_t*>(ws + L.done);
+  uint32_t* queue = reinterpret_cast<uint32_t*>(ws + L.queue);
+  uint32_t* err = reinterpret_cast<uint32_t*>(ws);
   hipLaunchKernelGGL(k_norm_finish, dim3(U), dim3(64), 0, s, partials, c.blocks_per_unit, inv_nu,
-                     flag);
+                     flag, done, queue, first_chunk ? err : nullptr);
   const int tiles_c = (int)(c.cols_pad / 64);
   if (bf16)
     hipLaunchKernelGGL(k_normalize<true>, dim3(U * c.norm_blocks_per_unit), dim3(kThreads), 0, s,
@@ -369,6 +426,119 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
   const void* aop = bf16 ? (const void*)ab : (const void*)a32;
   int total = 0;
   for (int i = 0; i < h->n_stages; ++i) total += h->stages[i].steps;
+  if (total == 0) return hipGetLastError() == hipSuccess ? MUON_OK : MUON_ERR_HIP;
+  const int tg = (int)((sp / T) * (sp / T + 1) / 2);
+  const int ta = (int)((c.rows_pad / T) * (c.cols_pad / T));
+  const int64_t n_items = (int64_t)total * U * (2 * tg + ta);
+  if (h->schedule == MUON_SCHEDULE_PERSISTENT && n_items < INT32_MAX / 2) {
+    DeviceInfo di;
+    const int dst = device_info(&di);
+    if (dst != MUON_OK) return dst;
+    NsSched p;
+    std::memset(&p, 0, sizeof(p));
+    // Gram: A = X X^T (wide, rows of X) or X^T X (tall, rows of X^T).
+    GemmArgs& gg = p.gram;
+    gg.n_units = U;
+    gg.flag = flag;
+    gg.a_ustride = gg.b_ustride = xs;
+    gg.lda = gg.ldb = (int32_t)(c.tall ? c.rows_pad : c.cols_pad);
+    gg.M = gg.N = (int32_t)sp;
+    gg.K = (int32_t)(c.tall ? c.rows_pad : c.cols_pad);
+    gg.tiles_m = gg.tiles_n = (int32_t)(sp / T);
+    gg.sym = 1;
+    gg.out32 = a32;
+    gg.out16 = ab;
+    gg.out_ustride = ss;
+    gg.ldo = (int32_t)sp;
+    for (int k = 0; k < 2; ++k) p.gram_op[k] = c.tall ? (const void*)xt[k] : xop[k];
+    // Polynomial: B = b*A + c*A*A.
+    GemmArgs& gp = p.poly;
+    gp.n_units = U;
+    gp.flag = flag;
+    gp.a = gp.b = aop;
+    gp.a_ustride = gp.b_ustride = ss;
+    gp.lda = gp.ldb = (int32_t)sp;
+    gp.M = gp.N = gp.K = (int32_t)sp;
+    gp.tiles_m = gp.tiles_n = (int32_t)(sp / T);
+    gp.sym = 1;
+    gp.out32 = bf16 ? nullptr : static_cast<float*>(bop);
+    gp.out16 = bf16 ? bop : nullptr;
+    gp.out_ustride = ss;
+    gp.ldo = (int32_t)sp;
+    gp.aux = a32;
+    gp.aux16 = ab;
+    gp.aux_ustride = ss;
+    gp.ldaux = (int32_t)sp;
+    // Apply: X' = a*X + B*X (wide) or a*X + X*B (tall).
+    GemmArgs& ga = p.apply;
+    ga.n_units = U;
+    ga.flag = flag;
+    ga.M = (int32_t)c.rows_pad;
+    ga.N = (int32_t)c.cols_pad;
+    ga.K = (int32_t)sp;
+    ga.tiles_m = (int32_t)(c.rows_pad / T);
+    ga.tiles_n = (int32_t)(c.cols_pad / T);
+    if (!c.tall) {
+      ga.a_ustride = ss;
+      ga.lda = (int32_t)sp;
+      ga.b_ustride = xs;
+      ga.ldb = (int32_t)c.rows_pad;
+    } else {
+      ga.a_ustride = xs;
+      ga.lda = (int32_t)c.cols_pad;
+      ga.b_ustride = ss;
+      ga.ldb = (int32_t)sp;
+    }
+    ga.out_ustride = xs;
+    ga.ldo = (int32_t)c.cols_pad;
+    ga.ldt = (int32_t)c.rows_pad;
+    ga.aux_ustride = xs;
+    ga.ldaux = (int32_t)c.cols_pad;
+    for (int k = 0; k < 2; ++k) {
+      const int nx = k ^ 1;
+      p.app_a[k] = c.tall ? xop[k] : (const void*)bop;
+      p.app_b[k] = c.tall ? (const void*)bop : (const void*)xt[k];
+      p.app_out32[k] = x32[nx];
+      p.app_out16[k] = bf16 ? (void*)xb[nx] : nullptr;
+      p.app_outt[k] = xt[nx];
+      p.app_aux[k] = x32[k];
+    }
+    p.final_mode = step ? FINAL_STEP : FINAL_NSOUT;
+    p.n_iter = total;
+    p.n_stages = h->n_stages;
+    int begin = 0;
+    for (int i = 0; i < h->n_stages; ++i) {
+      p.stage_begin[i] = begin;
+      begin += h->stages[i].steps;
+      p.sa[i] = h->stages[i].a;
+      p.sb[i] = h->stages[i].b;
+      p.sc[i] = h->stages[i].c;
+    }
+    // A stage with zero steps begins where the next one does; the kernel
+    // takes the last stage whose beginning it has reached.
+    p.tg = tg;
+    p.ta = ta;
+    p.n_items = (int32_t)n_items;
+    p.queue = queue;
+    p.done = done;
+    p.err = err;
+    p.timeout_ticks = (uint64_t)(kWaitLimitSeconds * 1e3 * (double)di.wall_khz);
+    const int grid = (int)std::min<int64_t>(n_items, di.resident[bf16 ? 1 : 0][T == 256 ? 1 : 0]);
+    tr.before(MUON_KERNEL_NS);
+    if (bf16) {
+      if (T == 256)
+        hipLaunchKernelGGL((ns_persistent<__bf16, 256>), dim3(grid), dim3(kThreads), 0, s, p, ca);
+      else
+        hipLaunchKernelGGL((ns_persistent<__bf16, 128>), dim3(grid), dim3(kThreads), 0, s, p, ca);
+    } else {
+      if (T == 256)
+        hipLaunchKernelGGL((ns_persistent<float, 256>), dim3(grid), dim3(kThreads), 0, s, p, ca);
+      else
+        hipLaunchKernelGGL((ns_persistent<float, 128>), dim3(grid), dim3(kThreads), 0, s, p, ca);
+    }
+    tr.after(MUON_KERNEL_NS);
+    return hipGetLastError() == hipSuccess ? MUON_OK : MUON_ERR_HIP;
+  }
   int it = 0;
   for (int st = 0; st < h->n_stages; ++st) {
     const muon_ns_stage& sg = h->stages[st];
@@ -503,7 +673,8 @@ int run(bool step, float* const* outs, const void* const* ins, float* const* mom
     Tracer tr{trace, stream};
     if (trace) trace->count = 0;
     for (const Chunk& c : chunks) {
-      st = run_chunk(c, h, step, outs, ins, moms, mats, static_cast<unsigned char*>(ws), stream, tr);
+      st = run_chunk(c, h, step, outs, ins, moms, mats, static_cast<unsigned char*>(ws), stream, tr,
+                     &c == &chunks.front());
       if (st != MUON_OK) return st;
     }
     return MUON_OK;
@@ -596,10 +767,22 @@ const char* muon_status_string(int status) {
     case MUON_ERR_HYPER: return "invalid hyper-parameters";
     case MUON_ERR_HIP: return "HIP launch failed";
     case MUON_ERR_ALIAS: return "input and output buffers overlap";
+    case MUON_ERR_SCHEDULE: return "a persistent NS launch stopped: a dependency wait ran out of time";
     default: return "unknown status";
   }
 }
 
-int muon_abi_version(void) { return 1; }
+int muon_workspace_status(const void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!workspace) return MUON_ERR_NULL;
+  if (workspace_bytes < kHeader) return MUON_ERR_WORKSPACE;
+  if (((uintptr_t)workspace & (kAlign - 1)) != 0) return MUON_ERR_ALIGN;
+  if (hipStreamSynchronize(stream) != hipSuccess) return MUON_ERR_HIP;
+  uint32_t word = 0;
+  if (hipMemcpy(&word, workspace, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess)
+    return MUON_ERR_HIP;
+  return word == 0u ? MUON_OK : MUON_ERR_SCHEDULE;
+}
+
+int muon_abi_version(void) { return 2; }
 
 }  // extern "C"

@@ -30,11 +30,14 @@ STATUS_NAMES = {
     -6: "MUON_ERR_HYPER",
     -7: "MUON_ERR_HIP",
     -8: "MUON_ERR_ALIAS",
+    -9: "MUON_ERR_SCHEDULE",
 }
 DTYPE_F32, DTYPE_BF16 = 0, 1
 SCALE_SPECTRAL, SCALE_UNIT_RMS_NORM = 0, 1
 NS_FP32, NS_BF16 = 0, 1
 KERNEL_MOMENTUM, KERNEL_NORMALIZE, KERNEL_GRAM, KERNEL_POLY, KERNEL_APPLY = 1, 2, 3, 4, 5
+KERNEL_NS = 6
+SCHEDULE_PERSISTENT, SCHEDULE_LAUNCHES = 0, 1
 MAX_STAGES = 4
 
 EXPORTED = (
@@ -44,6 +47,7 @@ EXPORTED = (
     "muon_newton_schulz_batched",
     "muon_step_batched_traced",
     "muon_newton_schulz_batched_traced",
+    "muon_workspace_status",
     "muon_status_string",
     "muon_abi_version",
 )
@@ -80,6 +84,8 @@ class HyperC(ctypes.Structure):
         ("batch_update_size", ctypes.c_int32),
         ("n_stages", ctypes.c_int32),
         ("stages", NsStage * MAX_STAGES),
+        ("schedule", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -130,6 +136,8 @@ def _load() -> ctypes.CDLL:
     lib.muon_newton_schulz_batched.restype = ctypes.c_int
     lib.muon_newton_schulz_batched_traced.argtypes = ns_args + [ctypes.POINTER(TraceC)]
     lib.muon_newton_schulz_batched_traced.restype = ctypes.c_int
+    lib.muon_workspace_status.argtypes = [P, ctypes.c_size_t, P]
+    lib.muon_workspace_status.restype = ctypes.c_int
     lib.muon_status_string.argtypes = [ctypes.c_int]
     lib.muon_status_string.restype = ctypes.c_char_p
     lib.muon_abi_version.argtypes = []
@@ -148,7 +156,8 @@ def status_string(status: int) -> str:
 class Hyper:
     """Mirror of `muon_hyper`; defaults come from the library
     (lr 2.7e-4, mu 0.95, wd 0.1, gamma 0.18, spectral, bf16 NS products,
-    8 x (3.4445, -4.7750, 2.0315) + 2 x (2, -1.5, 0.5))."""
+    8 x (3.4445, -4.7750, 2.0315) + 2 x (2, -1.5, 0.5), persistent NS
+    launch schedule)."""
 
     lr: float = 2.7e-4
     mu: float = 0.95
@@ -160,6 +169,7 @@ class Hyper:
     stages: Sequence[tuple[int, tuple[float, float, float]]] = field(
         default_factory=lambda: ((8, (3.4445, -4.7750, 2.0315)), (2, (2.0, -1.5, 0.5)))
     )
+    schedule: str = "persistent"  # or "launches"
 
     def to_c(self) -> HyperC:
         h = HyperC()
@@ -167,6 +177,8 @@ class Hyper:
         h.scale_mode = {"spectral": SCALE_SPECTRAL, "unit_rms_norm": SCALE_UNIT_RMS_NORM}[self.scale]
         h.ns_precision = {"fp32": NS_FP32, "bf16": NS_BF16}[self.ns_precision]
         h.batch_update_size = self.batch_update_size
+        h.schedule = {"persistent": SCHEDULE_PERSISTENT, "launches": SCHEDULE_LAUNCHES}[self.schedule]
+        h.reserved = 0
         if not 1 <= len(self.stages) <= MAX_STAGES:
             raise ValueError("between 1 and 4 NS stages")
         h.n_stages = len(self.stages)
@@ -219,6 +231,15 @@ def workspace(nbytes: int, device: torch.device) -> torch.Tensor:
         ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         _WS[key] = ws
     return ws
+
+
+def workspace_status(ws: torch.Tensor, stream=None) -> None:
+    """Waits for the stream and raises MuonError if the last call on `ws`
+    stopped early (muon_workspace_status)."""
+    st = LIB.muon_workspace_status(ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()),
+                                   ctypes.c_void_p(_stream_ptr(stream)))
+    if st != MUON_OK:
+        raise MuonError(st, "muon_workspace_status")
 
 
 def workspace_size(tensors, hyper: Hyper | HyperC, split_rows=None) -> int:

@@ -36,6 +36,7 @@ def test_defaults_are_the_pages_values():
     assert (h.stages[0].steps, h.stages[1].steps) == (8, 2)
     assert (h.stages[0].a, h.stages[0].b, h.stages[0].c) == pytest.approx((3.4445, -4.7750, 2.0315))
     assert (h.stages[1].a, h.stages[1].b, h.stages[1].c) == (2.0, -1.5, 0.5)
+    assert h.schedule == muon.SCHEDULE_PERSISTENT and h.reserved == 0
 
 
 def _desc(shapes):
@@ -60,7 +61,7 @@ def test_workspace_sizes():
     assert st == 0
     # bf16 path: two fp32 iterates, two bf16 iterates and their two bf16
     # transposes, bf16 Gram, bf16 polynomial = 20 bytes per element, plus
-    # per-unit norms
+    # the status header, per-unit norms and schedule counters
     assert 32 * mib * 20 <= n < 32 * mib * 20 + mib
     h = muon.default_hyper_c()
     h.batch_update_size = 8
@@ -102,6 +103,15 @@ def test_bad_hyper_rejected():
     h.stages[0].steps = 0
     h.stages[1].steps = 0
     assert ws_size([(1, 4, 4, 0)], h)[0] == -6
+    h = muon.default_hyper_c()
+    h.schedule = 2
+    assert ws_size([(1, 4, 4, 0)], h)[0] == -6
+    h = muon.default_hyper_c()
+    h.reserved = 1
+    assert ws_size([(1, 4, 4, 0)], h)[0] == -6
+    h = muon.default_hyper_c()
+    h.schedule = muon.SCHEDULE_LAUNCHES
+    assert ws_size([(1, 4, 4, 0)], h)[0] == 0
 
 
 def _step(ptrs_w, ptrs_g, ptrs_m, shapes, ws=0x10000000, ws_bytes=1 << 40, h=None):
@@ -135,8 +145,15 @@ def test_step_error_paths_touch_nothing():
     assert _step([], [], [], []) == 0                              # no-op
 
 
+def test_workspace_status_argument_errors():
+    st = muon.LIB.muon_workspace_status
+    assert st(None, 1 << 20, None) == -1
+    assert st(ctypes.c_void_p(0x10000000), 128, None) == -5
+    assert st(ctypes.c_void_p(0x10000010), 1 << 20, None) == -4
+
+
 def test_status_strings():
-    for code in range(-8, 1):
-        assert muon.status_string(code)
+    for code in range(-9, 1):
+        assert muon.status_string(code) != "unknown status"
     assert muon.status_string(12345) == "unknown status"
-    assert muon.LIB.muon_abi_version() == 1
+    assert muon.LIB.muon_abi_version() == 2

@@ -1,0 +1,85 @@
+"""The persistent NS launch (one launch per stacked pass, workgroups
+claiming tiles and waiting on per-unit completion counts) against one launch
+per product: both run the same tile code on the same inputs, so their
+results must agree bit for bit, and the persistent launch must report a
+clean status."""
+
+import pytest
+import torch
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+# (banks as (batch, rows, cols, split_rows), grad dtype, NS precision)
+CASES = [
+    ([(6, 256, 384, 0)], "bf16", "bf16"),            # 256 tiles, ragged
+    ([(4, 100, 200, 0), (3, 300, 200, 0)], "fp32", "bf16"),  # 128 tiles, wide and tall
+    ([(2, 512, 256, 128)], "bf16", "bf16"),           # split heads
+    ([(3, 640, 256, 0)], "bf16", "fp32"),             # tall, fp32 products
+    ([(5, 256, 256, 0)], "fp32", "fp32"),             # fp32 path, 256 tiles
+    ([(1, 1024, 2048, 0)], "bf16", "bf16"),           # one unit, many tiles
+]
+
+
+def _bank(shape, seed, gdtype):
+    b, r, c, _ = shape
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    w = (torch.randn((b, r, c), generator=g) * 0.02).to(DEV)
+    gr = (torch.randn((b, r, c), generator=g) * 1e-3).to(DEV)
+    if b > 1:
+        gr[b // 2].zero_()  # one all-zero unit per bank
+    return w, gr.to(torch.bfloat16 if gdtype == "bf16" else torch.float32)
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_step_schedules_agree_bitwise(gpu_lib, case):
+    banks, gdtype, prec = CASES[case]
+    print(f"[schedule] case {case}: {banks} grads {gdtype} products {prec}", flush=True)
+    splits = [s[3] for s in banks]
+    inputs = [_bank(s, 100 + 17 * i, gdtype) for i, s in enumerate(banks)]
+    out = {}
+    for sched in ("launches", "persistent"):
+        h = gpu_lib.Hyper(ns_precision=prec, schedule=sched)
+        params = [w.clone() for w, _ in inputs]
+        moms = [torch.zeros_like(w) for w, _ in inputs]
+        ws = gpu_lib.workspace(gpu_lib.workspace_size(params, h, splits), torch.device(DEV))
+        for t in range(2):  # two steps: the second starts from a live momentum
+            gpu_lib.step(params, [g for _, g in inputs], moms, hyper=h, split_rows=splits, ws=ws)
+        gpu_lib.workspace_status(ws)
+        out[sched] = (params, moms)
+    for i in range(len(banks)):
+        assert torch.equal(out["launches"][0][i], out["persistent"][0][i]), f"params of bank {i}"
+        assert torch.equal(out["launches"][1][i], out["persistent"][1][i]), f"momenta of bank {i}"
+
+
+@pytest.mark.parametrize("prec", ["bf16", "fp32"])
+def test_ns_only_schedules_agree_bitwise(gpu_lib, prec):
+    print(f"[schedule ns] prec {prec}", flush=True)
+    g = torch.Generator(device="cpu").manual_seed(9)
+    xs = [torch.randn((7, 384, 256), generator=g).to(DEV), torch.randn((2, 130, 700), generator=g).to(DEV)]
+    res = {}
+    for sched in ("launches", "persistent"):
+        h = gpu_lib.Hyper(ns_precision=prec, schedule=sched)
+        outs, _ = gpu_lib.newton_schulz(xs, hyper=h)
+        torch.cuda.synchronize()
+        res[sched] = outs
+    for a, b in zip(res["launches"], res["persistent"]):
+        assert torch.equal(a, b)
+
+
+def test_persistent_trace_brackets_one_launch_per_pass(gpu_lib):
+    print("[schedule trace]", flush=True)
+    x = torch.randn((4, 256, 256), device=DEV)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
+    for e in ev:
+        e.record()
+    h = gpu_lib.Hyper(schedule="persistent")
+    _, n = gpu_lib.newton_schulz([x], hyper=h, trace=(gpu_lib.KERNEL_NS, ev))
+    torch.cuda.synchronize()
+    assert n == 1
+    assert ev[0].elapsed_time(ev[1]) > 0
+    h = gpu_lib.Hyper(schedule="launches")
+    _, n = gpu_lib.newton_schulz([x], hyper=h, trace=(gpu_lib.KERNEL_APPLY, ev))
+    torch.cuda.synchronize()
+    assert n == 10
