@@ -240,6 +240,7 @@ __global__ __launch_bounds__(64) void k_norm_finish(const double* __restrict__ p
                                                     int32_t* __restrict__ flag,
                                                     uint32_t* __restrict__ sched_done,
                                                     uint32_t* __restrict__ sched_queue,
+                                                    int n_queue_words,
                                                     uint32_t* __restrict__ err) {
   const int u = blockIdx.x;
   double s = 0.0;
@@ -252,7 +253,8 @@ __global__ __launch_bounds__(64) void k_norm_finish(const double* __restrict__ p
     flag[u] = zero ? 0 : 1;
     inv_nu[u] = zero ? 0.0f : (float)(1.0 / sqrt(s));
     if (sched_done) sched_done[u] = 0u;
-    if (u == 0 && sched_queue) *sched_queue = 0u;
+    if (u == 0 && sched_queue)
+      for (int i = 0; i < n_queue_words; ++i) sched_queue[i] = 0u;
     if (u == 0 && err) *err = 0u;
   }
 }
@@ -397,16 +399,19 @@ struct DmaPlan {
       voff[i] = (row * ld + c * OpT<T>::kElems) * (int)sizeof(T);
     }
   }
-  __device__ __forceinline__ void issue(const u32x4& rs, uint32_t koff, uint32_t lds_op) const {
+  // Instruction i of this wave's share.
+  __device__ __forceinline__ void issue_one(const u32x4& rs, uint32_t koff, uint32_t lds_op,
+                                            int i) const {
     const int w = threadIdx.x >> 6;
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_op + (uint32_t)((w * kN + i) * 64) * 16u);
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(m0v), "v"(voff[i]), "s"(rs), "s"(koff)
+                 : "memory", "m0");
+  }
+  __device__ __forceinline__ void issue(const u32x4& rs, uint32_t koff, uint32_t lds_op) const {
 #pragma unroll
-    for (int i = 0; i < kN; ++i) {
-      const uint32_t m0v = __builtin_amdgcn_readfirstlane(lds_op + (uint32_t)((w * kN + i) * 64) * 16u);
-      asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                   :
-                   : "s"(m0v), "v"(voff[i]), "s"(rs), "s"(koff)
-                   : "memory", "m0");
-    }
+    for (int i = 0; i < kN; ++i) issue_one(rs, koff, lds_op, i);
   }
 };
 
@@ -419,25 +424,29 @@ __device__ __forceinline__ int xcd_remap(int bid, int nb) {
   return x * q + min(x, rem) + i;
 }
 
+// One 32x32 block over one 16-byte K chunk: a single bf16 MFMA, or four
+// fp32 ones.  Issued as (B, A): the lane owning C row m receives 4
+// consecutive columns.
+template <typename T>
+__device__ __forceinline__ void mfma_one(const u32x4& af, const u32x4& bf, f32x16& acc) {
+  if constexpr (sizeof(T) == 2) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, bf),
+                                                  __builtin_bit_cast(bf16x8, af), acc, 0, 0, 0);
+  } else {
+    const f32x4v a4 = __builtin_bit_cast(f32x4v, af);
+    const f32x4v b4 = __builtin_bit_cast(f32x4v, bf);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(b4[q], a4[q], acc, 0, 0, 0);
+  }
+}
+
 template <typename T, int FM>
 __device__ __forceinline__ void mfma_block(const u32x4 (&af)[FM], const u32x4 (&bf)[FM],
                                            f32x16 (&acc)[FM][FM]) {
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FM; ++j) {
-      // (B, A): the lane owning C row m receives 4 consecutive columns.
-      if constexpr (sizeof(T) == 2) {
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-            __builtin_bit_cast(bf16x8, bf[j]), __builtin_bit_cast(bf16x8, af[i]), acc[i][j], 0, 0, 0);
-      } else {
-        const f32x4v a4 = __builtin_bit_cast(f32x4v, af[i]);
-        const f32x4v b4 = __builtin_bit_cast(f32x4v, bf[j]);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x2f32(b4[q], a4[q], acc[i][j], 0, 0, 0);
-      }
-    }
+    for (int j = 0; j < FM; ++j) mfma_one<T>(af[i], bf[j], acc[i][j]);
 }
 
 __device__ __forceinline__ void store_bf16x4(void* base, int64_t idx, float a, float b, float c,
@@ -597,14 +606,45 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
         wait_vmcnt<0>();
       wait_lgkm0();
       __builtin_amdgcn_s_barrier();
-      if (k + kStages < nk) dma(k + kStages, sub);
       __builtin_amdgcn_sched_barrier(0);
-      // region C
-      read_frags(stage((sub + 1) % kStages), 0, 0);
-      mfma_block<T, FM>(af[1], bf[1], acc);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * FM, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, kMf, 0);
-      __builtin_amdgcn_sched_barrier(0);
+      // region C: the copy of stage k+4 into the buffer of stage k (no wave
+      // reads it any more), the fragment reads of kk0(k+1) and the MFMAs of
+      // kk1(k), interleaved in 2*FM chunks of one copy instruction, one
+      // fragment read and FM/2 MFMA blocks, so that the copies drain
+      // through the memory pipeline while the matrix cores run instead of
+      // holding up the wave's first MFMAs.
+      {
+        const bool more = k + kStages < nk;
+        const uint32_t koff = (uint32_t)((k + kStages) * BK * (int)sizeof(T));
+        const uint32_t so = stage_off(sub);
+        const u32x4* Sn = stage((sub + 1) % kStages);
+        constexpr int kN = DmaPlan<T, TILE>::kN;  // copy instructions per operand (= FM)
+        static_assert(kN == FM, "one copy instruction and one fragment read per chunk");
+        constexpr int kPerChunk = FM / 2;         // MFMA blocks per chunk
+        const int ch = half;                      // K chunk of kk0
+#pragma unroll
+        for (int c = 0; c < 2 * FM; ++c) {
+          if (more) {
+            if (c < kN)
+              pa.issue_one(rsa, koff, so, c);
+            else
+              pb.issue_one(rsb, koff, so + kOp * 16u, c - kN);
+          }
+          if (c < FM) {
+            const int ra = arow0 + c * 32;
+            af[0][c] = Sn[ra * 4 + swz(ra, ch)];
+          } else {
+            const int rb = brow0 + (c - FM) * 32;
+            bf[0][c - FM] = Sn[kOp + rb * 4 + swz(rb, ch)];
+          }
+#pragma unroll
+          for (int q = 0; q < kPerChunk; ++q) {
+            const int m = c * kPerChunk + q;
+            mfma_one<T>(af[1][m / FM], bf[1][m % FM], acc[m / FM][m % FM]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
     }
   }
 
@@ -800,6 +840,15 @@ __global__ __launch_bounds__(kThreads) void ns_gemm(GemmArgs g, ChunkArgs ca) {
 // claimed by running workgroups, so the schedule always makes progress; the
 // wait is still bounded by a wall-clock limit, after which the launch stops
 // and reports through `err`.
+//
+// Queues.  With one queue any workgroup may run any tile, so a tile's
+// results are published at agent scope (the L2 written back before the
+// count).  With one queue per XCC, unit u belongs to queue u % n_queues and
+// only workgroups running on that XCC claim from it: every tile of a unit
+// is then produced and consumed through the same L2, so publishing only
+// needs the stores to have completed.  Readers acquire at agent scope in
+// both cases.  The last workgroup to leave runs, on its own, any queue that
+// no workgroup ever claimed from (an XCC that received none).
 struct NsSched {
   GemmArgs gram, poly, apply;     // cur-independent fields of each product
   const void* gram_op[2];         // Gram operand (both sides) for X in buffer cur
@@ -816,12 +865,18 @@ struct NsSched {
   float sa[4], sb[4], sc[4];      // coefficients of each stage
   int32_t tg;                     // tiles per unit of a symmetric product
   int32_t ta;                     // tiles per unit of the apply product
-  int32_t n_items;
-  uint32_t* queue;                // next item to claim
+  int32_t n_queues;               // 1, or one queue per XCC (see below)
+  uint32_t* queue;                // per queue: next item to claim; then the
+                                  // count of workgroups that have left
   uint32_t* done;                 // per unit: finished items
   uint32_t* err;                  // set when a wait timed out
   uint64_t timeout_ticks;         // wall-clock ticks
 };
+
+// The XCC (accelerator die, with its own L2) the workgroup runs on.
+__device__ __forceinline__ int xcc_id() {
+  return __builtin_amdgcn_readfirstlane(__builtin_amdgcn_s_getreg((3 << 11) | 20)) & 15;
+}
 
 template <typename T, int TILE>
 __global__ __launch_bounds__(kThreads) void ns_persistent(NsSched p, ChunkArgs ca) {
@@ -834,30 +889,64 @@ __global__ __launch_bounds__(kThreads) void ns_persistent(NsSched p, ChunkArgs c
   // stale state.
   __shared__ int s_item, s_go;
   const int per_unit = 2 * p.tg + p.ta;
-  const int per_iter = ca.n_units * per_unit;
-  const int ug = ca.n_units * p.tg;
+  const int nq = p.n_queues;
+  const bool local = nq > 1;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t one = (threadIdx.x & 63) == 0 ? 1u : 0u;  // lane 0's share
-  int pending = -1;  // unit whose finished tile wave 0 has yet to count
+  uint32_t* const left = p.queue + nq;                    // workgroups that have left
+  // units of queue qq: qq, qq + nq, ...
+  auto units_of = [&](int qq) { return ca.n_units > qq ? (ca.n_units - qq + nq - 1) / nq : 0; };
+  int q = local ? xcc_id() % nq : 0;
+  int uq = units_of(q);
+  int pending = -1;      // unit whose finished tile wave 0 has yet to count
+  bool alone = false;    // running unclaimed queues after every other workgroup left
   for (;;) {
     if (wave == 0) {
       if (pending >= 0) {
         // Every wave's stores are complete (the barrier that ended the
-        // tile): release at agent scope, then count the tile.
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        // tile); with one queue they are written back to memory first.
+        if (!local) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         __hip_atomic_fetch_add(p.done + pending, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       int item = __builtin_amdgcn_readfirstlane(
-          (int)__hip_atomic_fetch_add(p.queue, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+          (int)__hip_atomic_fetch_add(p.queue + q, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
       const uint32_t e = __builtin_amdgcn_readfirstlane(
           __hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-      if (e != 0u) item = p.n_items;
+      if (e != 0u) item = -1;
       s_item = item;  // every lane writes the same value
     }
     pending = -1;
     __syncthreads();
     const int item = __builtin_amdgcn_readfirstlane(s_item);
-    if (item >= p.n_items) break;
+    const int per_iter = uq * per_unit;
+    if (item < 0) break;  // stopped
+    if (item >= p.n_iter * per_iter) {
+      // This queue is drained.
+      if (!local) break;
+      if (!alone) {
+        // Count this workgroup out; the last one continues alone.
+        __syncthreads();
+        if (wave == 0)
+          s_go = __builtin_amdgcn_readfirstlane((int)__hip_atomic_fetch_add(
+                     left, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == (int)gridDim.x - 1;
+        __syncthreads();
+        if (!__builtin_amdgcn_readfirstlane(s_go)) break;
+        alone = true;
+      }
+      // Every other workgroup has left, so a queue that nobody claimed from
+      // has no workgroup on its XCC: run it here, one tile after another.
+      int next = -1;
+      for (int qq = 0; qq < nq; ++qq) {
+        const uint32_t head = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(p.queue + qq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        if (next < 0 && head == 0u && units_of(qq) > 0) next = qq;
+      }
+      if (next < 0) break;
+      q = next;
+      uq = units_of(q);
+      continue;
+    }
+    const int ug = uq * p.tg;
     const int it = item / per_iter;
     int r = item - it * per_iter;
     int phase, u, t;
@@ -873,6 +962,7 @@ __global__ __launch_bounds__(kThreads) void ns_persistent(NsSched p, ChunkArgs c
     const int tpu = phase == APPLY ? p.ta : p.tg;
     u = r / tpu;
     t = r - u * tpu;
+    u = q + nq * u;
     const bool live = __builtin_amdgcn_readfirstlane(p.gram.flag[u]) != 0;
     // A zero unit computes nothing, so its items wait for nothing.
     const uint32_t need =
@@ -900,7 +990,9 @@ __global__ __launch_bounds__(kThreads) void ns_persistent(NsSched p, ChunkArgs c
     }
     __syncthreads();
     if (!__builtin_amdgcn_readfirstlane(s_go)) break;
-    // Make the other workgroups' results visible to this wave's loads.
+    // Make the other workgroups' results visible to this wave's loads
+    // (acquire at agent scope: the L1 must be dropped in any case, and a
+    // workgroup-scope invalidate does not reach it).
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     const int cur = it & 1;
     if (phase == GRAM) {

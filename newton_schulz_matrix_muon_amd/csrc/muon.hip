@@ -18,6 +18,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -68,6 +69,7 @@ struct Layout {
 };
 
 constexpr size_t kHeader = 256;  // status header at the start of the workspace
+constexpr int kMaxQueues = 16;   // persistent schedule: at most one queue per XCC
 
 Layout layout_of(const Chunk& c, bool bf16) {
   Layout L{};
@@ -95,7 +97,7 @@ Layout layout_of(const Chunk& c, bool bf16) {
   L.inv_nu = take(U * 4);
   L.flag = take(U * 4);
   L.done = take(U * 4);   // persistent schedule: finished items per unit
-  L.queue = take(4);      // persistent schedule: next item to claim
+  L.queue = take(4 * (kMaxQueues + 1));  // persistent schedule: claim counters, leavers
   L.total = off;
   return L;
 }
@@ -281,6 +283,7 @@ struct DeviceInfo {
   bool ready = false;
   int cus = 0;
   int wall_khz = 0;
+  int xccs = 1;
   int resident[2][2] = {{0, 0}, {0, 0}};  // [bf16][tile 256]
 };
 
@@ -308,6 +311,10 @@ int device_info(DeviceInfo* out) {
         hipDeviceGetAttribute(&d.wall_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
         d.cus < 1 || d.wall_khz < 1)
       return MUON_ERR_HIP;
+    if (hipDeviceGetAttribute(&d.xccs, hipDeviceAttributeNumberOfXccs, dev) != hipSuccess ||
+        d.xccs < 1)
+      d.xccs = 1;
+    d.xccs = std::min(d.xccs, kMaxQueues);
     d.resident[0][0] = resident_of<float, 128>(d.cus);
     d.resident[0][1] = resident_of<float, 256>(d.cus);
     d.resident[1][0] = resident_of<__bf16, 128>(d.cus);
@@ -404,7 +411,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
   uint32_t* queue = reinterpret_cast<uint32_t*>(ws + L.queue);
   uint32_t* err = reinterpret_cast<uint32_t*>(ws);
   hipLaunchKernelGGL(k_norm_finish, dim3(U), dim3(64), 0, s, partials, c.blocks_per_unit, inv_nu,
-                     flag, done, queue, first_chunk ? err : nullptr);
+                     flag, done, queue, kMaxQueues + 1, first_chunk ? err : nullptr);
   const int tiles_c = (int)(c.cols_pad / 64);
   if (bf16)
     hipLaunchKernelGGL(k_normalize<true>, dim3(U * c.norm_blocks_per_unit), dim3(kThreads), 0, s,
@@ -518,12 +525,22 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
     // takes the last stage whose beginning it has reached.
     p.tg = tg;
     p.ta = ta;
-    p.n_items = (int32_t)n_items;
+    // One queue per XCC when the units spread over the XCCs with at most
+    // an eighth of the slots idle; one queue otherwise.
+    const int nx = di.xccs;
+    const int64_t slots = (U + nx - 1) / nx * (int64_t)nx;
+    p.n_queues = (nx > 1 && U >= nx && 8 * (slots - U) <= slots) ? nx : 1;
     p.queue = queue;
     p.done = done;
     p.err = err;
     p.timeout_ticks = (uint64_t)(kWaitLimitSeconds * 1e3 * (double)di.wall_khz);
-    const int grid = (int)std::min<int64_t>(n_items, di.resident[bf16 ? 1 : 0][T == 256 ? 1 : 0]);
+    int grid = (int)std::min<int64_t>(n_items, di.resident[bf16 ? 1 : 0][T == 256 ? 1 : 0]);
+    // Test hook: MUON_PERSISTENT_WORKGROUPS caps the grid, so that tests can
+    // run the schedule with XCCs that receive no workgroup.
+    if (const char* cap = std::getenv("MUON_PERSISTENT_WORKGROUPS")) {
+      const int c = std::atoi(cap);
+      if (c > 0) grid = std::min(grid, c);
+    }
     tr.before(MUON_KERNEL_NS);
     if (bf16) {
       if (T == 256)

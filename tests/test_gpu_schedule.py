@@ -83,3 +83,24 @@ def test_persistent_trace_brackets_one_launch_per_pass(gpu_lib):
     _, n = gpu_lib.newton_schulz([x], hyper=h, trace=(gpu_lib.KERNEL_APPLY, ev))
     torch.cuda.synchronize()
     assert n == 10
+
+
+@pytest.mark.parametrize("workgroups", [1, 3])
+def test_persistent_with_xccs_left_without_workgroups(gpu_lib, workgroups, monkeypatch):
+    # 16 units spread over one queue per XCC; a capped grid leaves most XCCs
+    # without a workgroup, and the last workgroup to leave runs their queues.
+    print(f"[schedule orphan] workgroups {workgroups}", flush=True)
+    inputs = [_bank((16, 256, 256, 0), 321, "bf16")]
+    out = {}
+    for sched in ("launches", "persistent"):
+        if sched == "persistent":
+            monkeypatch.setenv("MUON_PERSISTENT_WORKGROUPS", str(workgroups))
+        h = gpu_lib.Hyper(schedule=sched)
+        params = [w.clone() for w, _ in inputs]
+        moms = [torch.zeros_like(w) for w, _ in inputs]
+        ws = gpu_lib.workspace(gpu_lib.workspace_size(params, h, [0]), torch.device(DEV))
+        gpu_lib.step(params, [g for _, g in inputs], moms, hyper=h, split_rows=[0], ws=ws)
+        gpu_lib.workspace_status(ws)
+        out[sched] = params[0]
+    monkeypatch.delenv("MUON_PERSISTENT_WORKGROUPS")
+    assert torch.equal(out["launches"], out["persistent"])
