@@ -63,15 +63,15 @@ def kernel_sources_sha256():
     return h.hexdigest()
 
 
-def stored_traffic(kernel, workload, ns):
+def stored_traffic(kernel, workload, ns, pdir=None, digest=None):
     """HBM bytes per launch from a committed rocprofv3 counter summary
     (FETCH_SIZE and WRITE_SIZE runs, scaled by a copy kernel of known size),
     or None when there is none for this kernel and workload or the kernel
     sources have changed since it was taken."""
-    pdir = os.path.join(ROOT, "profiles")
+    pdir = pdir or os.path.join(ROOT, "profiles")
     if not os.path.isdir(pdir):
         return None
-    digest = kernel_sources_sha256()
+    digest = digest or kernel_sources_sha256()
     for name in sorted(os.listdir(pdir)):
         if not name.endswith(".md"):
             continue

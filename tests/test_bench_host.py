@@ -1,0 +1,55 @@
+"""Host-side pieces of bench.py (no GPU): the workload FLOP counts, the
+executed share of the symmetric products and the stored-traffic lookup."""
+
+import json
+
+import bench
+import workloads as W
+
+
+def test_kernel_flops_match_the_workload_total():
+    wl = W.workload(2)
+    units = bench.nonzero_units(wl)
+    f = bench.kernel_flops(units)
+    iters = 10
+    # one NS iteration: X X^T (2 s^2 l) + A A (2 s^3) + B X (2 s^2 l)
+    assert (f["gram"] + f["poly"] + f["apply"]) * iters == wl.ns_flops()
+
+
+def test_executed_fraction_of_symmetric_tiles():
+    assert bench.executed_fraction(1024) == 10 / 16   # 4 x 4 tiles of 256
+    assert bench.executed_fraction(256) == 1.0
+    assert bench.executed_fraction(128) == 1.0        # one 128 tile
+    assert bench.executed_fraction(4096) == (16 * 17 / 2) / 256
+
+
+def test_stored_traffic_lookup(tmp_path):
+    rec = {"kernel": "ns_persistent", "workload": "w", "ns": "bf16", "sources_sha256": "abc",
+           "bytes_per_launch": 123}
+    (tmp_path / "x_traffic.md").write_text("# t\n\ntraffic_record: " + json.dumps(rec) + "\n")
+    got = bench.stored_traffic("ns_persistent", "w", "bf16", pdir=str(tmp_path), digest="abc")
+    assert got["bytes_per_launch"] == 123
+    # other kernel, other workload, or changed sources: no figure
+    assert bench.stored_traffic("ns_gemm apply", "w", "bf16", pdir=str(tmp_path), digest="abc") is None
+    assert bench.stored_traffic("ns_persistent", "v", "bf16", pdir=str(tmp_path), digest="abc") is None
+    assert bench.stored_traffic("ns_persistent", "w", "bf16", pdir=str(tmp_path), digest="def") is None
+
+
+def test_committed_traffic_records_are_well_formed():
+    import os
+
+    pdir = os.path.join(bench.ROOT, "profiles")
+    for name in os.listdir(pdir):
+        for line in open(os.path.join(pdir, name), encoding="utf-8"):
+            if line.startswith("traffic_record: "):
+                rec = json.loads(line[len("traffic_record: "):])
+                assert rec["bytes_per_launch"] == rec["fetch_bytes_per_launch"] + rec["write_bytes_per_launch"]
+                assert len(rec["sources_sha256"]) == 64
+
+
+def test_multi_gpu_request_exits_with_a_message(capsys):
+    import subprocess
+    import sys
+
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True)
+    assert r.returncode == 2 and "one GPU" in r.stderr
