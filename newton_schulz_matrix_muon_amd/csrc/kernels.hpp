@@ -325,37 +325,41 @@ __global__ __launch_bounds__(kThreads) void k_normalize(ChunkArgs ca, float* __r
 // one TILE x TILE output tile per workgroup of 4 waves (2 x 2, each
 // TILE/2 x TILE/2 as 32x32 MFMA blocks).
 //
-// LDS: kStages stages, each a separate array holding TILE rows of A_op and
-// TILE rows of B_op; a row is 64 bytes of K (32 bf16 or 16 fp32) in four
-// 16-byte chunks, XOR-swizzled by row so that the 32-row MFMA fragment reads
-// spread over the banks.  Operands stream global -> LDS directly, up to
-// kStages stages ahead of the MFMAs (buffer_load_dwordx4 ... lds: lane i of
-// a wave lands at M0 + 16*i, so the swizzle is applied by choosing which
-// global chunk each lane fetches).  Fragments are double-buffered across the
-// two K sub-steps of a stage, and the MFMA is issued as (B, A) so each lane
-// accumulates C[m][n..n+3] for one row m and four consecutive columns: the
-// epilogue moves 16-byte vectors.
+// LDS: a ring of kSlots half-stages; a half-stage holds TILE rows of one
+// operand, a row being 128 bytes of K (64 bf16 or 32 fp32) in eight 16-byte
+// chunks, XOR-swizzled by row so that the 32-row MFMA fragment reads spread
+// over the banks.  Rows of 128 bytes make every global request a whole
+// line: the L2 serves a fixed number of requests per clock, and with
+// 64-byte rows the copies, not the matrix cores, set the pace.  Operands
+// stream global -> LDS directly, 1.5 to 2.5 stages ahead of the MFMAs
+// (buffer_load_dwordx4 ... lds: lane i of a wave lands at M0 + 16*i, so the
+// swizzle is applied by choosing which global chunk each lane fetches).
+// Fragments are double-buffered across the four K sub-steps of a stage, and
+// the MFMA is issued as (B, A) so each lane accumulates C[m][n..n+3] for
+// one row m and four consecutive columns: the epilogue moves 16-byte
+// vectors.
 template <typename T>
 struct OpT;
 template <>
 struct OpT<__bf16> {
   static constexpr int kElems = 8;  // per 16-byte chunk
-  static constexpr int kBK = 32;    // K per LDS row (4 chunks)
+  static constexpr int kBK = 64;    // K per 128-byte LDS row (8 chunks)
 };
 template <>
 struct OpT<float> {
   static constexpr int kElems = 4;
-  static constexpr int kBK = 16;
+  static constexpr int kBK = 32;
 };
 
-constexpr int kStages = 4;
+constexpr int kRowChunks = 8;  // 16-byte chunks per 128-byte LDS row
+constexpr int kSlots = 5;      // ring of half-stages (one operand each)
 
 typedef __attribute__((address_space(3))) void* lds_vptr;
 
-// Physical 16-byte chunk of logical chunk c in a 64-byte row.
-__device__ __forceinline__ int swz(int row, int chunk) {
-  return chunk ^ (((row >> 1) ^ (row >> 3)) & 3);
-}
+// Physical 16-byte chunk of logical chunk c in a 128-byte row: 16
+// consecutive rows read at one logical chunk hit 16 distinct 4-bank groups
+// (two rows per 256-byte bank line, eight chunk positions per parity).
+__device__ __forceinline__ int swz(int row, int chunk) { return chunk ^ ((row >> 1) & 7); }
 
 // Buffer resource (4 SGPRs) for a raw buffer at `base`: stride 0, a 2 GiB
 // range and the 32-bit data format of the gfx9 family.
@@ -368,21 +372,22 @@ __device__ __forceinline__ u32x4 tile_rsrc(const void* base) {
   return u32x4{lo, hi & 0xFFFFu, 0x7FFFFFFFu, 0x00020000u};
 }
 
-// DMA instructions per wave for one operand of one stage.
+// Copy instructions per wave for one half-stage (TILE rows x 128 bytes).
 template <int TILE>
-constexpr int dma_per_wave() { return TILE / 64; }
+constexpr int dma_per_wave() { return TILE / 32; }
 
-// One operand's share of a stage for this wave: TILE rows of the tile
-// (resource based at its first row) x 64 bytes of K.  `voff` holds the
+// One operand's share of a half-stage for this wave: TILE rows of the tile
+// (resource based at its first row) x 128 bytes of K, eight lanes per row so
+// that every request is a whole 128-byte line.  `voff` holds the
 // stage-invariant per-lane byte offsets (row * ld + swizzled chunk), the K
-// position of the stage comes in as the scalar offset `koff`, and lds_op is
-// the LDS byte offset of the operand region.  Lane i of each instruction
-// lands at M0 + 16*i, so the swizzle is applied by choosing which global
-// chunk each lane fetches.
+// position comes in as the scalar offset `koff`, and lds_op is the LDS byte
+// offset of the ring slot.  Lane i of each instruction lands at M0 + 16*i,
+// so the swizzle is applied by choosing which global chunk each lane
+// fetches.
 //
 // The copy is issued as inline assembly so that the compiler does not see an
-// LDS writer: it cannot tell the stages apart and would otherwise wait for
-// every in-flight stage before each LDS read.  Completion is tracked with
+// LDS writer: it cannot tell the slots apart and would otherwise wait for
+// every copy in flight before each LDS read.  Completion is tracked with
 // explicit vmcnt waits (vmcnt counts every vector-memory instruction in
 // issue order) before the barrier that publishes a stage.
 template <typename T, int TILE>
@@ -394,8 +399,8 @@ struct DmaPlan {
 #pragma unroll
     for (int i = 0; i < kN; ++i) {
       const int sl = (w * kN + i) * 64 + lane;
-      const int row = sl >> 2, pc = sl & 3;
-      const int c = pc ^ (((row >> 1) ^ (row >> 3)) & 3);  // logical chunk stored at (row, pc)
+      const int row = sl >> 3, pc = sl & 7;
+      const int c = pc ^ ((row >> 1) & 7);  // logical chunk stored at (row, pc)
       voff[i] = (row * ld + c * OpT<T>::kElems) * (int)sizeof(T);
     }
   }
@@ -408,10 +413,6 @@ struct DmaPlan {
                  :
                  : "s"(m0v), "v"(voff[i]), "s"(rs), "s"(koff)
                  : "memory", "m0");
-  }
-  __device__ __forceinline__ void issue(const u32x4& rs, uint32_t koff, uint32_t lds_op) const {
-#pragma unroll
-    for (int i = 0; i < kN; ++i) issue_one(rs, koff, lds_op, i);
   }
 };
 
@@ -465,17 +466,12 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// LDS stage buffers of the GEMM tile (kStages of them, each TILE rows of
-// both operands x 64 bytes).  Declared once per tile size, so a kernel that
-// runs several tile phases holds a single set.
+// LDS of the GEMM tile: a ring of kSlots half-stages, each TILE rows of
+// one operand x 128 bytes of K (160 KB at TILE 256).  Declared once per tile
+// size, so a kernel that runs several tile phases holds a single ring; the
+// epilogue stages its blocks in it too.
 template <int TILE>
-__shared__ u32x4 lds_st0[2 * TILE * 4];
-template <int TILE>
-__shared__ u32x4 lds_st1[2 * TILE * 4];
-template <int TILE>
-__shared__ u32x4 lds_st2[2 * TILE * 4];
-template <int TILE>
-__shared__ u32x4 lds_st3[2 * TILE * 4];
+__shared__ u32x4 lds_ring[kSlots * TILE * kRowChunks];
 
 // Zero unit in the last iteration: O' = 0, so the weight only decays (step)
 // or the NS output is zero, over the TILE x TILE block at (m0, n0).
@@ -503,14 +499,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
   constexpr int WT = TILE / 2;   // wave tile
   constexpr int FM = WT / 32;    // 32x32 blocks per wave side
   constexpr bool kBF = sizeof(T) == 2;
-  constexpr int kOp = TILE * 4;  // 16-byte slots of one operand in one stage
   constexpr int BK = OpT<T>::kBK;
-  constexpr int P = 2 * dma_per_wave<TILE>();  // DMA instructions per wave per stage
-  constexpr int kMf = FM * FM * (kBF ? 1 : 4);  // MFMAs per K sub-step
-  u32x4* const lds0 = lds_st0<TILE>;
-  u32x4* const lds1 = lds_st1<TILE>;
-  u32x4* const lds2 = lds_st2<TILE>;
-  u32x4* const lds3 = lds_st3<TILE>;
+  constexpr int NI = dma_per_wave<TILE>();     // copies per wave per half-stage
+  constexpr int kSlot = TILE * kRowChunks;     // 16-byte slots per ring slot
+  constexpr int kMf = FM * FM * (kBF ? 1 : 4); // MFMAs per K sub-step
+  u32x4* const ring = lds_ring<TILE>;
+  const uint32_t ring_off = (uint32_t)(uintptr_t)(lds_vptr)lds_ring<TILE>;
   const int m0 = tm * TILE, n0 = tn * TILE;
   const int lane = threadIdx.x & 63;
   const int wid = threadIdx.x >> 6;
@@ -529,123 +523,125 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  const int nk = g.K / BK;  // a multiple of kStages (K is a multiple of 128)
-  auto stage = [&](int st) -> u32x4* {
-    return st == 0 ? lds0 : st == 1 ? lds1 : st == 2 ? lds2 : lds3;
-  };
-  // LDS byte offsets of the stages (casts of the arrays themselves fold to
-  // constants).
-  auto stage_off = [&](int st) -> uint32_t {
-    return st == 0   ? (uint32_t)(uintptr_t)(lds_vptr)lds_st0<TILE>
-           : st == 1 ? (uint32_t)(uintptr_t)(lds_vptr)lds_st1<TILE>
-           : st == 2 ? (uint32_t)(uintptr_t)(lds_vptr)lds_st2<TILE>
-                     : (uint32_t)(uintptr_t)(lds_vptr)lds_st3<TILE>;
-  };
+  // Stages of BK along K, each two half-stages: 2k holds A_op's rows, 2k+1
+  // B_op's.  Half-stage h lives in ring slot h % kSlots.
+  const int nk = g.K / BK;  // >= 2 (K is a multiple of 128)
+  const int nh = 2 * nk;
   DmaPlan<T, TILE> pa, pb;
   pa.init(g.lda);
   pb.init(g.ldb);
-  auto dma = [&](int kt, int st) {
-    const uint32_t koff = (uint32_t)(kt * BK * (int)sizeof(T));
-    pa.issue(rsa, koff, stage_off(st));
-    pb.issue(rsb, koff, stage_off(st) + kOp * 16u);
+  auto issue_half = [&](int h, int i) {  // copy instruction i of half-stage h
+    const uint32_t koff = (uint32_t)((h >> 1) * BK * (int)sizeof(T));
+    const uint32_t so = ring_off + (uint32_t)((h % kSlots) * kSlot) * 16u;
+    if (h & 1)
+      pb.issue_one(rsb, koff, so, i);
+    else
+      pa.issue_one(rsa, koff, so, i);
   };
 
-  // Schedule of stage k (two K sub-steps kk0, kk1; buffers cycle mod 4):
-  //   region A: read kk1(k) fragments | MFMAs kk0(k)
-  //   wait for this wave's kk1(k) reads and its DMA of stage k+1; s_barrier
-  //   (stage k+1 is complete, and every wave is done reading stage k)
-  //   DMA stage k+4 into the buffer of stage k
-  //   region C: read kk0(k+1) fragments | MFMAs kk1(k)
+  // Schedule of stage k (four K sub-steps kk0..kk3 of 16 bf16 / 8 fp32):
+  //   sub-steps 0-2: read the fragments of kk(s+1) | MFMAs of kk(s)
+  //   wait for this wave's copies of stage k+1 (half-stage 2k+4, if any,
+  //   may stay in flight); s_barrier: stage k+1 is complete and every wave
+  //   is done reading stage k
+  //   sub-step 3: copies of half-stages 2k+5 and 2k+6 into stage k's slots,
+  //   interleaved with the reads of kk0(k+1) and the MFMAs of kk3(k)
   // The barrier sits between MFMA groups whose operands are already in
-  // registers, so the fragment reads after it hide under MFMAs.
+  // registers, so the fragment reads after it hide under MFMAs, and 1.5 to
+  // 2.5 stages of copies stay in flight.
   const int arow0 = wm * WT + (lane & 31);
   const int brow0 = wn * WT + (lane & 31);
   const int half = lane >> 5;
   u32x4 af[2][FM], bf[2][FM];
-  auto read_frags = [&](const u32x4* S, int kk, int slot) {
-    const int ch = 2 * kk + half;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int ra = arow0 + i * 32, rb = brow0 + i * 32;
-      af[slot][i] = S[ra * 4 + swz(ra, ch)];
-      bf[slot][i] = S[kOp + rb * 4 + swz(rb, ch)];
-    }
+  auto read_a = [&](const u32x4* S, int kk, int slot, int i) {
+    const int r = arow0 + i * 32;
+    af[slot][i] = S[r * kRowChunks + swz(r, 2 * kk + half)];
+  };
+  auto read_b = [&](const u32x4* S, int kk, int slot, int i) {
+    const int r = brow0 + i * 32;
+    bf[slot][i] = S[r * kRowChunks + swz(r, 2 * kk + half)];
   };
 
-  // Prologue: DMA of stages 0..3 (nk >= 4).  The scalar (kernel-argument)
-  // loads are drained as well: one still in flight would turn every LDS
-  // wait of the loop into a full wait.
+  // Prologue: half-stages 0..4.  The scalar (kernel-argument) loads are
+  // drained as well: one still in flight would turn every LDS wait of the
+  // loop into a full wait.
 #pragma unroll
-  for (int st = 0; st < kStages; ++st) dma(st, st);
-  wait_vmcnt<3 * P>();
+  for (int h = 0; h < kSlots; ++h)
+    if (h < nh)
+#pragma unroll
+      for (int i = 0; i < NI; ++i) issue_half(h, i);
+  if (nh >= 5)
+    wait_vmcnt<3 * NI>();
+  else
+    wait_vmcnt<2 * NI>();  // nh == 4
   wait_lgkm0();
   __builtin_amdgcn_s_barrier();
-  read_frags(stage(0), 0, 0);
-
-  for (int kt0 = 0; kt0 < nk; kt0 += kStages) {
 #pragma unroll
-    for (int sub = 0; sub < kStages; ++sub) {
-      const int k = kt0 + sub;
-      const u32x4* S = stage(sub);
+  for (int i = 0; i < FM; ++i) {
+    read_a(ring, 0, 0, i);
+    read_b(ring + kSlot, 0, 0, i);
+  }
+
+  int sa = 0, sb = 1;  // ring slots of stage k
+  for (int k = 0; k < nk; ++k) {
+    const u32x4* SA = ring + sa * kSlot;
+    const u32x4* SB = ring + sb * kSlot;
+    const int na = sa + 2 >= kSlots ? sa + 2 - kSlots : sa + 2;
+    const int nb = sb + 2 >= kSlots ? sb + 2 - kSlots : sb + 2;
+#pragma unroll
+    for (int ss = 0; ss < 3; ++ss) {
       __builtin_amdgcn_sched_barrier(0);
-      // region A
-      read_frags(S, 1, 1);
-      mfma_block<T, FM>(af[0], bf[0], acc);
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        read_a(SA, ss + 1, (ss + 1) & 1, i);
+        read_b(SB, ss + 1, (ss + 1) & 1, i);
+      }
+      mfma_block<T, FM>(af[ss & 1], bf[ss & 1], acc);
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * FM, 0);
       __builtin_amdgcn_sched_group_barrier(0x008, kMf, 0);
       __builtin_amdgcn_sched_barrier(0);
-      // Publish stage k+1 (for the last stage this only drains the DMA; the
-      // reads below then touch a stale buffer whose values go unused, which
-      // keeps the MFMA block on a single control path).
-      const int ahead = nk - 2 - k;  // DMA stages issued after stage k+1
-      if (ahead >= 2)
-        wait_vmcnt<2 * P>();
-      else if (ahead == 1)
-        wait_vmcnt<P>();
-      else
-        wait_vmcnt<0>();
-      wait_lgkm0();
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      // region C: the copy of stage k+4 into the buffer of stage k (no wave
-      // reads it any more), the fragment reads of kk0(k+1) and the MFMAs of
-      // kk1(k), interleaved in 2*FM chunks of one copy instruction, one
-      // fragment read and FM/2 MFMA blocks, so that the copies drain
-      // through the memory pipeline while the matrix cores run instead of
-      // holding up the wave's first MFMAs.
-      {
-        const bool more = k + kStages < nk;
-        const uint32_t koff = (uint32_t)((k + kStages) * BK * (int)sizeof(T));
-        const uint32_t so = stage_off(sub);
-        const u32x4* Sn = stage((sub + 1) % kStages);
-        constexpr int kN = DmaPlan<T, TILE>::kN;  // copy instructions per operand (= FM)
-        static_assert(kN == FM, "one copy instruction and one fragment read per chunk");
-        constexpr int kPerChunk = FM / 2;         // MFMA blocks per chunk
-        const int ch = half;                      // K chunk of kk0
+    }
+    // Publish stage k+1 (for the last stage this only drains the copies;
+    // the reads below then touch stale slots whose values go unused, which
+    // keeps the MFMA block on a single control path).
+    if (k + 3 <= nk)
+      wait_vmcnt<NI>();
+    else
+      wait_vmcnt<0>();
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      const int h0 = 2 * k + 5, h1 = 2 * k + 6;
+      const bool more0 = h0 < nh, more1 = h1 < nh;
+      const u32x4* NA = ring + na * kSlot;
+      const u32x4* NB = ring + nb * kSlot;
+      constexpr int C = 2 * NI;      // chunks: one copy instruction each
+      constexpr int R = 2 * FM;      // fragment reads
+      constexpr int M = FM * FM;     // MFMA blocks
+      static_assert(C % R == 0, "reads spread evenly over the chunks");
 #pragma unroll
-        for (int c = 0; c < 2 * FM; ++c) {
-          if (more) {
-            if (c < kN)
-              pa.issue_one(rsa, koff, so, c);
-            else
-              pb.issue_one(rsb, koff, so + kOp * 16u, c - kN);
-          }
-          if (c < FM) {
-            const int ra = arow0 + c * 32;
-            af[0][c] = Sn[ra * 4 + swz(ra, ch)];
-          } else {
-            const int rb = brow0 + (c - FM) * 32;
-            bf[0][c - FM] = Sn[kOp + rb * 4 + swz(rb, ch)];
-          }
-#pragma unroll
-          for (int q = 0; q < kPerChunk; ++q) {
-            const int m = c * kPerChunk + q;
-            mfma_one<T>(af[1][m / FM], bf[1][m % FM], acc[m / FM][m % FM]);
-          }
-          __builtin_amdgcn_sched_barrier(0);
+      for (int c = 0; c < C; ++c) {
+        if (c < NI) {
+          if (more0) issue_half(h0, c);
+        } else {
+          if (more1) issue_half(h1, c - NI);
         }
+        if (c % (C / R) == 0) {
+          const int r = c / (C / R);
+          if (r < FM)
+            read_a(NA, 0, 0, r);
+          else
+            read_b(NB, 0, 0, r - FM);
+        }
+#pragma unroll
+        for (int m = c * M / C; m < (c + 1) * M / C; ++m)
+          mfma_one<T>(af[1][m / FM], bf[1][m % FM], acc[m / FM][m % FM]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
+    sa = na;
+    sb = nb;
   }
 
   // ---- epilogue.  Each wave stages one 32-row block of its accumulators at
@@ -653,22 +649,22 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
   // reads it back row-wise so that every global load and store covers whole
   // row segments (WT/4 lanes per row, 16 bytes per lane); the transposed
   // copy reads the staged block column-wise.
-  wait_lgkm0();
-  __builtin_amdgcn_s_barrier();  // every wave is done with the stage buffers
-  float* ep = reinterpret_cast<float*>(wid == 0 ? lds0 : wid == 1 ? lds1 : wid == 2 ? lds2 : lds3);
   constexpr int LDW = WT + 4;     // padded row stride (floats)
   constexpr int LPR = WT / 4;     // lanes per row
   constexpr int RPI = 64 / LPR;   // rows per instruction
   constexpr int NIT = 32 / RPI;   // row-wise iterations per block
+  const int rl = lane / LPR;            // row within an instruction
+  const int cl = (lane % LPR) * 4;      // first column of the lane
+  const int ncol = n0 + wn * WT + cl;   // global column of the lane's first element
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();  // every wave is done with the stage buffers
+  float* ep = reinterpret_cast<float*>(ring) + wid * (32 * LDW);
   float* wout = nullptr;
   if (PHASE == APPLY && g.final_mode != FINAL_NONE) {
     const SegView sg = find_seg(ca, u);
     wout = sg.w + (int64_t)(u - sg.first) * ca.unit_elems;
   }
   const bool vec_w = (ca.cols & 3) == 0;
-  const int rl = lane / LPR;            // row within an instruction
-  const int cl = (lane % LPR) * 4;      // first column of the lane
-  const int ncol = n0 + wn * WT + cl;   // global column of the lane's first element
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int mrow0 = m0 + wm * WT + i * 32;  // first global row of the block
@@ -887,7 +883,11 @@ __global__ __launch_bounds__(kThreads) void ns_persistent(NsSched p, ChunkArgs c
   // compiler thread the tail of one iteration into the head of the next for
   // that lane alone, and the other lanes would then reach the barriers on
   // stale state.
-  __shared__ int s_item, s_go;
+  // Broadcast words live in the tile ring (which fills the LDS).  They are
+  // written only after the barrier that ends a tile, and the barrier that
+  // follows their last read comes before the next tile's first copy.
+  int& s_item = reinterpret_cast<int*>(lds_ring<TILE>)[0];
+  int& s_go = reinterpret_cast<int*>(lds_ring<TILE>)[1];
   const int per_unit = 2 * p.tg + p.ta;
   const int nq = p.n_queues;
   const bool local = nq > 1;
@@ -989,7 +989,9 @@ __global__ __launch_bounds__(kThreads) void ns_persistent(NsSched p, ChunkArgs c
       s_go = go;
     }
     __syncthreads();
-    if (!__builtin_amdgcn_readfirstlane(s_go)) break;
+    const int go = __builtin_amdgcn_readfirstlane(s_go);
+    __syncthreads();  // every wave has read the broadcast words
+    if (!go) break;
     // Make the other workgroups' results visible to this wave's loads
     // (acquire at agent scope: the L1 must be dropped in any case, and a
     // workgroup-scope invalidate does not reach it).
