@@ -6,6 +6,7 @@
  *
  *   M <- mu*M + G                          classic SGD momentum
  *   N  = mu*M + G                          Nesterov look-ahead on the new M
+ *                                          (or the EMA style, see below)
  *   O' = HybridNewtonSchulz(N)             per NS unit (see below)
  *   W <- W*(1 - lr*wd) - lr*scale*O'       decoupled weight decay
  *
@@ -90,6 +91,14 @@ typedef enum { MUON_NS_FP32 = 0, MUON_NS_BF16 = 1 } muon_ns_precision;
  * LAUNCHES: one launch per product and iteration, in stream order. */
 typedef enum { MUON_SCHEDULE_PERSISTENT = 0, MUON_SCHEDULE_LAUNCHES = 1 } muon_schedule;
 
+/* Momentum and look-ahead rule (RFC-0023 方案 1, both styles):
+ * SGD: M <- mu*M + G;            N = mu*M + G (on the updated M)
+ * EMA: M <- mu*M + (1 - mu)*G;   N = mu*bc(M, t+1) + (1 - mu)*bc(G, t),
+ *      bc(x, k) = x / (1 - mu^k), t = muon_hyper.step (1-based), 0 <= mu < 1.
+ * NS is invariant to the scale of its input, so the EMA style differs from
+ * the SGD style only through the bias corrections. */
+typedef enum { MUON_NESTEROV_SGD = 0, MUON_NESTEROV_EMA = 1 } muon_nesterov_style;
+
 /* A bank of `batch` equal-shape matrices stored back to back (stride
  * rows*cols elements).  rows = fan_out, cols = fan_in.  split_rows = 0: each
  * matrix is one NS unit; otherwise rows % split_rows == 0 and every block of
@@ -122,14 +131,16 @@ typedef struct {
   int32_t n_stages;          /* 1..MUON_MAX_STAGES */
   muon_ns_stage stages[MUON_MAX_STAGES];
   int32_t schedule;          /* muon_schedule */
+  int32_t nesterov_style;    /* muon_nesterov_style */
+  int32_t step;              /* 1-based index of this step (EMA style only) */
   int32_t reserved;          /* must be 0 */
 } muon_hyper;
 
 /* Fill `h` with the pages' values: lr 2.7e-4, mu 0.95, weight_decay 0.1,
  * gamma 0.18, spectral scale, bf16 NS products, whole-group batches, and the
  * hybrid schedule 8 x (3.4445, -4.7750, 2.0315) + 2 x (2, -1.5, 0.5)
- * (DeepSeek tech notes "Muon 优化器" sections 1-3); persistent launch
- * schedule.  NULL is ignored. */
+ * (DeepSeek tech notes "Muon 优化器" sections 1-3); SGD-style momentum,
+ * step 1, persistent launch schedule.  NULL is ignored. */
 void muon_hyper_default(muon_hyper* h);
 
 /* Bytes of device workspace that muon_step_batched / muon_newton_schulz_batched
@@ -145,7 +156,7 @@ int muon_workspace_size(const muon_matrix_desc* mats, int64_t n_mats, const muon
 
 /* One Muon step over `n_mats` banks (DeepSeek tech notes "Muon 优化器"
  * section 1 Algorithm 1 with the section-2 hybrid Newton-Schulz; RFC-0023
- * 方案 1 momentum, split_head and 方案 4 batching; Megatron-LM PR "Scaling
+ * 方案 1 momentum (either style), split_head and 方案 4 batching; Megatron-LM PR "Scaling
  * for MuP over Muon optimizer" scale modes).
  *   params[i]  : float*  (batch, rows, cols)   W, updated in place
  *   grads[i]   : bf16 or fp32 (batch, rows, cols), read only
@@ -214,7 +225,7 @@ int muon_workspace_status(const void* workspace, size_t workspace_bytes, hipStre
 /* Static description of a status code (never NULL). */
 const char* muon_status_string(int status);
 
-/* ABI version of this header: 2. */
+/* ABI version of this header: 3. */
 int muon_abi_version(void);
 
 #ifdef __cplusplus

@@ -2,7 +2,9 @@
 //
 // Kernels, in launch order for one stacked pass ("chunk") of equal-shape NS
 // units:
-//   k_momentum      M <- mu*M + G, N = mu*M + G into the fp32 iterate buffer,
+//   k_momentum      M <- mu*M + G, N = mu*M + G into the fp32 iterate buffer
+//                   (or the EMA style with bias corrections: two coefficient
+//                   pairs from the host, exact for the SGD style's 1s),
 //                   per-block fp64 partial sums of N^2 (DeepSeek tech notes
 //                   "Muon 优化器" section 1 Algorithm 1; RFC-0023 方案 1).
 //   k_norm_finish   per unit: fixed-order fp64 sum of the partials, 1/||N||_F
@@ -67,7 +69,8 @@ struct ChunkArgs {
   int32_t rows_pad, cols_pad;  // padded iterate shape
   int64_t unit_elems;          // rows * cols
   int64_t x_stride;            // rows_pad * cols_pad
-  float mu;
+  float ma, mb;                // M <- ma*M + mb*G
+  float la, lb;                // N  = la*M + lb*G (on the updated M)
   float decay;                 // 1 - lr * weight_decay
   float lr_scale;              // lr * scale
   int32_t pad0;
@@ -168,7 +171,7 @@ __global__ __launch_bounds__(kThreads) void k_momentum(ChunkArgs ca, float* __re
   const int cols = ca.cols;
   const int r0 = bb * rows_per_block;
   const int r1 = min(r0 + rows_per_block, ca.rows);
-  const float mu = ca.mu;
+  const float ma = ca.ma, mb = ca.mb, la = ca.la, lb = ca.lb;
   float* xu = x32 + (int64_t)u * ca.x_stride;
   double ss = 0.0;
   const bool vec = (cols & 3) == 0;
@@ -199,8 +202,8 @@ __global__ __launch_bounds__(kThreads) void k_momentum(ChunkArgs ca, float* __re
           float m[4] = {mv.x, mv.y, mv.z, mv.w};
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            m[i] = __builtin_fmaf(mu, m[i], g[i]);
-            n[i] = __builtin_fmaf(mu, m[i], g[i]);
+            m[i] = __builtin_fmaf(ma, m[i], mb * g[i]);
+            n[i] = __builtin_fmaf(la, m[i], lb * g[i]);
           }
           *mp = make_float4(m[0], m[1], m[2], m[3]);
         }
@@ -219,9 +222,9 @@ __global__ __launch_bounds__(kThreads) void k_momentum(ChunkArgs ca, float* __re
         if (GK == 2) {
           n = g;
         } else {
-          float m = __builtin_fmaf(mu, sg.m[base + c], g);
+          float m = __builtin_fmaf(ma, sg.m[base + c], mb * g);
           sg.m[base + c] = m;
-          n = __builtin_fmaf(mu, m, g);
+          n = __builtin_fmaf(la, m, lb * g);
         }
         xr[c] = n;
         ss = __builtin_fma((double)n, (double)n, ss);

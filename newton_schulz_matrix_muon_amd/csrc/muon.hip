@@ -113,6 +113,10 @@ int validate_hyper(const muon_hyper* h) {
   if (h->schedule != MUON_SCHEDULE_PERSISTENT && h->schedule != MUON_SCHEDULE_LAUNCHES)
     return MUON_ERR_HYPER;
   if (h->reserved != 0) return MUON_ERR_HYPER;
+  if (h->nesterov_style != MUON_NESTEROV_SGD && h->nesterov_style != MUON_NESTEROV_EMA)
+    return MUON_ERR_HYPER;
+  if (h->nesterov_style == MUON_NESTEROV_EMA && (h->step < 1 || !(h->mu >= 0.0f && h->mu < 1.0f)))
+    return MUON_ERR_HYPER;
   if (h->ns_precision != MUON_NS_FP32 && h->ns_precision != MUON_NS_BF16) return MUON_ERR_DTYPE;
   if (h->batch_update_size < 0) return MUON_ERR_HYPER;
   if (h->n_stages < 1 || h->n_stages > MUON_MAX_STAGES) return MUON_ERR_HYPER;
@@ -233,6 +237,25 @@ size_t workspace_of(const std::vector<Chunk>& chunks, bool bf16) {
   size_t need = kHeader;
   for (const Chunk& c : chunks) need = std::max(need, layout_of(c, bf16).total);
   return need;
+}
+
+// M <- ma*M + mb*G and N = la*M + lb*G (RFC-0023 方案 1).  SGD style: mu, 1,
+// mu, 1.  EMA style: mu, 1 - mu, mu/(1 - mu^(t+1)), (1 - mu)/(1 - mu^t), the
+// bias corrections evaluated in double.
+void momentum_coefficients(const muon_hyper* h, float* ma, float* mb, float* la, float* lb) {
+  const double mu = h->mu;
+  if (h->nesterov_style == MUON_NESTEROV_EMA) {
+    const double t = (double)h->step;
+    *ma = (float)mu;
+    *mb = (float)(1.0 - mu);
+    *la = (float)(mu / (1.0 - std::pow(mu, t + 1.0)));
+    *lb = (float)((1.0 - mu) / (1.0 - std::pow(mu, t)));
+  } else {
+    *ma = h->mu;
+    *mb = 1.0f;
+    *la = h->mu;
+    *lb = 1.0f;
+  }
 }
 
 double unit_scale(const Chunk& c, const muon_hyper* h) {
@@ -362,7 +385,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
   ca.cols_pad = (int32_t)c.cols_pad;
   ca.unit_elems = c.rows_u * c.cols;
   ca.x_stride = c.rows_pad * c.cols_pad;
-  ca.mu = h->mu;
+  momentum_coefficients(h, &ca.ma, &ca.mb, &ca.la, &ca.lb);
   ca.decay = (float)(1.0 - (double)h->lr * (double)h->weight_decay);
   ca.lr_scale = (float)((double)h->lr * unit_scale(c, h));
   int32_t first = 0;
@@ -716,6 +739,9 @@ void muon_hyper_default(muon_hyper* h) {
   h->scale_mode = MUON_SCALE_SPECTRAL;
   h->ns_precision = MUON_NS_BF16;
   h->batch_update_size = 0;
+  h->schedule = MUON_SCHEDULE_PERSISTENT;
+  h->nesterov_style = MUON_NESTEROV_SGD;
+  h->step = 1;
   h->n_stages = 2;
   h->stages[0] = {8, 3.4445f, -4.7750f, 2.0315f};
   h->stages[1] = {2, 2.0f, -1.5f, 0.5f};
@@ -800,6 +826,6 @@ int muon_workspace_status(const void* workspace, size_t workspace_bytes, hipStre
   return word == 0u ? MUON_OK : MUON_ERR_SCHEDULE;
 }
 
-int muon_abi_version(void) { return 2; }
+int muon_abi_version(void) { return 3; }
 
 }  // extern "C"

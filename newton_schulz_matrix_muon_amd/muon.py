@@ -38,6 +38,7 @@ NS_FP32, NS_BF16 = 0, 1
 KERNEL_MOMENTUM, KERNEL_NORMALIZE, KERNEL_GRAM, KERNEL_POLY, KERNEL_APPLY = 1, 2, 3, 4, 5
 KERNEL_NS = 6
 SCHEDULE_PERSISTENT, SCHEDULE_LAUNCHES = 0, 1
+NESTEROV_SGD, NESTEROV_EMA = 0, 1
 MAX_STAGES = 4
 
 EXPORTED = (
@@ -85,6 +86,8 @@ class HyperC(ctypes.Structure):
         ("n_stages", ctypes.c_int32),
         ("stages", NsStage * MAX_STAGES),
         ("schedule", ctypes.c_int32),
+        ("nesterov_style", ctypes.c_int32),
+        ("step", ctypes.c_int32),
         ("reserved", ctypes.c_int32),
     ]
 
@@ -170,6 +173,8 @@ class Hyper:
         default_factory=lambda: ((8, (3.4445, -4.7750, 2.0315)), (2, (2.0, -1.5, 0.5)))
     )
     schedule: str = "persistent"  # or "launches"
+    nesterov_style: str = "sgd"  # or "ema" (bias-corrected; needs `step`)
+    step: int = 1  # 1-based index of this step (EMA style only)
 
     def to_c(self) -> HyperC:
         h = HyperC()
@@ -178,6 +183,8 @@ class Hyper:
         h.ns_precision = {"fp32": NS_FP32, "bf16": NS_BF16}[self.ns_precision]
         h.batch_update_size = self.batch_update_size
         h.schedule = {"persistent": SCHEDULE_PERSISTENT, "launches": SCHEDULE_LAUNCHES}[self.schedule]
+        h.nesterov_style = {"sgd": NESTEROV_SGD, "ema": NESTEROV_EMA}[self.nesterov_style]
+        h.step = self.step
         h.reserved = 0
         if not 1 <= len(self.stages) <= MAX_STAGES:
             raise ValueError("between 1 and 4 NS stages")

@@ -43,6 +43,7 @@ def oracle_hyper(h) -> oracle.Hyper:
     return oracle.Hyper(
         lr=h.lr, mu=h.mu, weight_decay=h.weight_decay, gamma=h.gamma, scale=h.scale,
         schedule=tuple((s, tuple(c)) for s, c in h.stages),
+        nesterov_style=h.nesterov_style,
     )
 
 

@@ -37,6 +37,7 @@ def test_defaults_are_the_pages_values():
     assert (h.stages[0].a, h.stages[0].b, h.stages[0].c) == pytest.approx((3.4445, -4.7750, 2.0315))
     assert (h.stages[1].a, h.stages[1].b, h.stages[1].c) == (2.0, -1.5, 0.5)
     assert h.schedule == muon.SCHEDULE_PERSISTENT and h.reserved == 0
+    assert h.nesterov_style == muon.NESTEROV_SGD and h.step == 1
 
 
 def _desc(shapes):
@@ -112,6 +113,17 @@ def test_bad_hyper_rejected():
     h = muon.default_hyper_c()
     h.schedule = muon.SCHEDULE_LAUNCHES
     assert ws_size([(1, 4, 4, 0)], h)[0] == 0
+    h = muon.default_hyper_c()
+    h.nesterov_style = 2
+    assert ws_size([(1, 4, 4, 0)], h)[0] == -6
+    h = muon.default_hyper_c()
+    h.nesterov_style = muon.NESTEROV_EMA
+    assert ws_size([(1, 4, 4, 0)], h)[0] == 0
+    h.step = 0                       # the bias corrections need t >= 1
+    assert ws_size([(1, 4, 4, 0)], h)[0] == -6
+    h.step = 3
+    h.mu = 1.0                       # 1 - mu^t would be 0
+    assert ws_size([(1, 4, 4, 0)], h)[0] == -6
 
 
 def _step(ptrs_w, ptrs_g, ptrs_m, shapes, ws=0x10000000, ws_bytes=1 << 40, h=None):
@@ -156,4 +168,4 @@ def test_status_strings():
     for code in range(-9, 1):
         assert muon.status_string(code) != "unknown status"
     assert muon.status_string(12345) == "unknown status"
-    assert muon.LIB.muon_abi_version() == 2
+    assert muon.LIB.muon_abi_version() == 3

@@ -5,6 +5,8 @@ wide units, split heads); the benchmark workload (32 x 1024^2, bf16
 gradients) is checked on sampled units over every step.
 """
 
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -116,7 +118,8 @@ def _run_steps(gpu_lib, w0, grads, h, split_rows=0):
     m_ref = np.zeros_like(w_ref)
     out = []
     for t, g in enumerate(grads, start=1):
-        gpu_lib.step([w], [g], [m], hyper=h, split_rows=[split_rows])
+        ht = dataclasses.replace(h, step=t)  # the EMA style's bias corrections use the step index
+        gpu_lib.step([w], [g], [m], hyper=ht, split_rows=[split_rows])
         torch.cuda.synchronize()
         g64 = f64(g)
         if w_ref.ndim == 3:
@@ -143,6 +146,29 @@ def test_step_single_fp32_matrix_workload(gpu_lib, prec):
         assert rel(mg, mr) <= TOL_M, f"step {t} momentum"
         e = check_weight(wg, wr, w0_64, t, h, TOL_NS[prec], f"step {t}")
         say(f"   step {t}: rel update err {e:.3e}")
+
+
+@pytest.mark.parametrize("prec", ["fp32", "bf16"])
+def test_step_ema_nesterov_style(gpu_lib, prec):
+    # The EMA look-ahead with bias corrections (RFC-0023 方案 1, optax
+    # style), four steps, split heads and one all-zero unit in the bank.
+    say(f"[step ema] prec={prec}")
+    w0 = _seeded((3, 256, 384), 41, 0.02)
+    grads = []
+    for t in range(4):
+        g = _seeded((3, 256, 384), 500 + t, 1e-3)
+        g[1, 128:].zero_()  # the second head of matrix 1 stays zero
+        grads.append(g.to(torch.bfloat16))
+    h = gpu_lib.Hyper(ns_precision=prec, nesterov_style="ema")
+    res = _run_steps(gpu_lib, w0, grads, h, split_rows=128)
+    w0_64 = f64(w0)
+    for t, (wg, mg, wr, mr) in enumerate(res, start=1):
+        assert rel(mg, mr) <= TOL_M, f"step {t} momentum"
+        for b in range(3):
+            for hd in range(2):
+                blk = slice(hd * 128, (hd + 1) * 128)
+                check_weight(wg[b, blk], wr[b, blk], w0_64[b, blk], t, h, TOL_NS[prec],
+                             f"step {t} matrix {b} head {hd}")
 
 
 def test_step_zero_gradient_is_pure_decay(gpu_lib):

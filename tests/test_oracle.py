@@ -275,3 +275,19 @@ def test_ema_without_bias_correction_is_scaled_sgd():
         la_ema = beta * m_ema + (1 - beta) * g
         np.testing.assert_allclose(la_ema, (1 - beta) * la_sgd, rtol=1e-13)
         assert rel(oracle.newton_schulz(la_ema), oracle.newton_schulz(la_sgd)) < 1e-12
+
+
+def test_ema_bias_correction_recovers_a_constant_gradient():
+    # From a zero buffer the EMA after t equal gradients is (1 - beta^t) g,
+    # so the bias correction with count t returns g exactly (an off-by-one
+    # in the count would not); and both corrections tend to 1, so the
+    # look-ahead tends to beta*mu + (1-beta)*g.
+    beta = 0.95
+    g = np.array([[1.5, -2.0], [0.25, 3.0]])
+    m = np.zeros_like(g)
+    for t in range(1, 7):
+        m = oracle.ema_momentum(m, g, beta)
+        np.testing.assert_allclose(oracle.bias_correction(m, beta, t), g, rtol=1e-14)
+    m_late = oracle.ema_momentum(np.full_like(g, 0.3), g, beta)
+    look = oracle.ema_lookahead(m_late, g, beta, 4000)
+    np.testing.assert_allclose(look, beta * m_late + (1 - beta) * g, rtol=1e-12)
