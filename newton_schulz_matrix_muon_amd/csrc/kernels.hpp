@@ -23,6 +23,9 @@
 //                   (X' in bf16, X'^T); in the last iteration the epilogue
 //                   writes W <- W*(1 - lr*wd) - lr*scale*X' instead
 //                   (Algorithm 1's decoupled update) or the NS output.
+//   k_ns_small      the whole NS of a wide unit with at most 128 rows in one
+//                   workgroup, A and B on chip, one pass over X per
+//                   iteration (bf16 products).
 //   ns_persistent   the three products of every iteration in one launch:
 //                   workgroups claim tiles in order and wait on per-unit
 //                   completion counts, so tiles of different units and
@@ -826,6 +829,272 @@ __global__ __launch_bounds__(kThreads) void ns_gemm(GemmArgs g, ChunkArgs ca) {
     return;
   }
   gemm_tile<PHASE, T, TILE>(g, ca, u, tm, tn);
+}
+
+// -------------------------------------------------------- small-s NS -------
+// Whole Newton-Schulz of a wide unit with at most 128 rows (a split head, a
+// small matrix) in one workgroup, bf16 products.  A and B never leave the
+// chip: A lives in the accumulators, its bf16 copy and B's in LDS.  Per
+// iteration one pass streams X (fp32, rows padded to 128) in 128-column
+// blocks X_j and, for each block,
+//   X'_j = a*X_j + B*X_j          (B*X_j: B rows x X_j^T rows from LDS)
+//   A'  += X'_j X'_j^T            (the next iteration's Gram)
+// so X makes one round trip per iteration and the Gram, polynomial and apply
+// of the notes' section 2 quintic step need no separate passes.  The
+// roundings match the general path (bf16 operands of every product, fp32
+// accumulation, fp32 iterate); the b*A term uses A's fp32 accumulator.
+// Iteration 0 reads the look-ahead N straight from the momentum kernel and
+// scales it by 1/||N||_F, masking the padding.
+struct NsSmallArgs {
+  float* x32[2];          // ping-pong iterates (unit 0), rows 128 x ldx
+  int64_t x_stride;       // elements per unit
+  int32_t ldx;            // padded columns (multiple of 128)
+  int32_t n_iter;
+  int32_t n_stages;
+  int32_t stage_begin[4];
+  float sa[4], sb[4], sc[4];
+  int32_t final_mode;     // FINAL_STEP or FINAL_NSOUT
+  const float* inv_nu;    // per unit: 1/||N||_F
+  const int32_t* flag;    // per unit: nonzero norm
+};
+
+constexpr int kSmall = 128;  // padded rows (= Gram size) of the small path
+
+// bf16 element (row, k) of a 128 x 128 operand in LDS: 256-byte rows of 16
+// chunks, chunk index XOR-ed with the row so that 32-row fragment reads and
+// the transposed writes spread over the banks.
+__device__ __forceinline__ int sm_at(int row, int k) {
+  return row * kSmall + ((((k >> 3) ^ (row & 15)) << 3) | (k & 7));
+}
+
+// C[m][n] += sum_k L1[m][k] * L2[n][k] over K = 128 for this wave's 64 x 64
+// quadrant (2 x 2 blocks of 32 x 32).
+__device__ __forceinline__ void sm_mma(const uint16_t* L1, const uint16_t* L2, f32x16 (&acc)[2][2],
+                                       int wm, int wn, int lane) {
+  const u32x4* A = reinterpret_cast<const u32x4*>(L1);
+  const u32x4* B = reinterpret_cast<const u32x4*>(L2);
+  const int half = lane >> 5;
+#pragma unroll
+  for (int kk = 0; kk < kSmall / 16; ++kk) {
+    const int ch = 2 * kk + half;
+    u32x4 af[2], bf[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int ra = wm * 64 + i * 32 + (lane & 31);
+      const int rb = wn * 64 + i * 32 + (lane & 31);
+      af[i] = A[ra * 16 + (ch ^ (ra & 15))];
+      bf[i] = B[rb * 16 + (ch ^ (rb & 15))];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) mfma_one<__bf16>(af[i], bf[j], acc[i][j]);
+  }
+}
+
+// Accumulator-layout values (lane (m, half) of block (i, j) holds row
+// wm*64 + i*32 + m, columns wn*64 + j*32 + 8q + 4*half + e) into LDS as bf16,
+// row-major (L[row][col]) or transposed (L[col][row]).
+__device__ __forceinline__ void sm_put_rows(uint16_t* L, const float (&v)[2][2][16], int wm, int wn,
+                                            int lane) {
+  const int m = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = wm * 64 + i * 32 + m;
+        const int col = wn * 64 + j * 32 + 8 * q + 4 * half;
+        uint2 pk;
+        pk.x = (uint32_t)to_bf16_bits(v[i][j][4 * q]) | ((uint32_t)to_bf16_bits(v[i][j][4 * q + 1]) << 16);
+        pk.y = (uint32_t)to_bf16_bits(v[i][j][4 * q + 2]) | ((uint32_t)to_bf16_bits(v[i][j][4 * q + 3]) << 16);
+        *reinterpret_cast<uint2*>(L + sm_at(row, col)) = pk;
+      }
+}
+
+__device__ __forceinline__ void sm_put_cols(uint16_t* L, const float (&v)[2][2][16], int wm, int wn,
+                                            int lane) {
+  const int m = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = wm * 64 + i * 32 + m;
+        const int col = wn * 64 + j * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        L[sm_at(col, row)] = to_bf16_bits(v[i][j][r]);
+      }
+}
+
+__global__ __launch_bounds__(kThreads) void k_ns_small(NsSmallArgs p, ChunkArgs ca) {
+  __shared__ __attribute__((aligned(16))) uint16_t LA[kSmall * kSmall];  // A, then B
+  __shared__ __attribute__((aligned(16))) uint16_t LX[kSmall * kSmall];  // X_j^T
+  __shared__ __attribute__((aligned(16))) uint16_t LR[kSmall * kSmall];  // X'_j (or X_0j), row-major
+  const int u = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wid = threadIdx.x >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+  const int m = lane & 31, half = lane >> 5;
+  const int nb = p.ldx / kSmall;
+
+  const SegView sg = find_seg(ca, u);
+  float* const wout = sg.w + (int64_t)(u - sg.first) * ca.unit_elems;
+  if (!p.flag[u]) {
+    // Zero unit: O' = 0, so the weight only decays / the output is zero.
+    for (int64_t e = threadIdx.x; e < ca.unit_elems; e += kThreads)
+      wout[e] = (p.final_mode == FINAL_STEP) ? wout[e] * ca.decay : 0.0f;
+    return;
+  }
+  const float inv0 = p.inv_nu[u];
+
+  // Block j of the iterate, in accumulator layout (iteration 0: the masked,
+  // scaled look-ahead).  Two register sets: block j+1 is loaded while block
+  // j is processed.
+  typedef float Blk[2][2][16];
+  Blk xbuf[2];
+  auto load_x = [&](Blk& xv, const float* X, int j, bool first) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = wm * 64 + i * 32 + m;
+          const int col = j * kSmall + wn * 64 + jj * 32 + 8 * q + 4 * half;
+          float4 x = *reinterpret_cast<const float4*>(X + (int64_t)row * p.ldx + col);
+          if (first) {
+            const bool rin = row < ca.rows;
+            x.x = (rin && col + 0 < ca.cols) ? x.x * inv0 : 0.0f;
+            x.y = (rin && col + 1 < ca.cols) ? x.y * inv0 : 0.0f;
+            x.z = (rin && col + 2 < ca.cols) ? x.z * inv0 : 0.0f;
+            x.w = (rin && col + 3 < ca.cols) ? x.w * inv0 : 0.0f;
+          }
+          xv[i][jj][4 * q] = x.x;
+          xv[i][jj][4 * q + 1] = x.y;
+          xv[i][jj][4 * q + 2] = x.z;
+          xv[i][jj][4 * q + 3] = x.w;
+        }
+  };
+  auto zero = [](f32x16 (&a)[2][2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) a[i][j][r] = 0.0f;
+  };
+  auto as_vals = [](const f32x16 (&a)[2][2], float (&v)[2][2][16]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[i][j][r] = a[i][j][r];
+  };
+
+  // Gram of iteration 0.
+  f32x16 accA[2][2], accC[2][2];
+  zero(accA);
+  const float* X0 = p.x32[0] + (int64_t)u * p.x_stride;
+  auto gram_block = [&](Blk& xv, Blk& xnext, int j) {
+    if (j + 1 < nb) load_x(xnext, X0, j + 1, true);
+    __syncthreads();  // LR is free
+    sm_put_rows(LR, xv, wm, wn, lane);
+    __syncthreads();
+    sm_mma(LR, LR, accA, wm, wn, lane);
+  };
+  load_x(xbuf[0], X0, 0, true);
+  for (int j = 0; j < nb; j += 2) {  // unrolled by two: the register sets alternate
+    gram_block(xbuf[0], xbuf[1], j);
+    if (j + 1 < nb) gram_block(xbuf[1], xbuf[0], j + 1);
+  }
+
+  for (int it = 0; it < p.n_iter; ++it) {
+    float ca_ = p.sa[0], cb = p.sb[0], cc = p.sc[0];
+#pragma unroll
+    for (int s = 1; s < 4; ++s)
+      if (s < p.n_stages && it >= p.stage_begin[s]) {
+        ca_ = p.sa[s];
+        cb = p.sb[s];
+        cc = p.sc[s];
+      }
+    const bool last = it == p.n_iter - 1;
+    const float* X = p.x32[it & 1] + (int64_t)u * p.x_stride;
+    float* Xn = p.x32[(it & 1) ^ 1] + (int64_t)u * p.x_stride;
+
+    // B = b*A + c*A*A (A symmetric), into LA as the apply's operand.
+    float av[2][2][16];
+    as_vals(accA, av);
+    __syncthreads();  // every wave is done with LA and LR
+    sm_put_rows(LA, av, wm, wn, lane);
+    __syncthreads();
+    zero(accC);
+    sm_mma(LA, LA, accC, wm, wn, lane);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) av[i][j][r] = cb * av[i][j][r] + cc * accC[i][j][r];
+    __syncthreads();  // every wave has read A
+    sm_put_rows(LA, av, wm, wn, lane);
+
+    // Apply pass, with the next Gram accumulated on the way.
+    zero(accA);
+    auto apply_block = [&](Blk& xv, Blk& xnext, int j) {
+      if (j + 1 < nb) load_x(xnext, X, j + 1, it == 0);
+      __syncthreads();  // LA complete; LX and LR free
+      sm_put_cols(LX, xv, wm, wn, lane);
+      __syncthreads();
+      zero(accC);
+      sm_mma(LA, LX, accC, wm, wn, lane);  // (B X_j)[m][n] = sum_k B[m][k] X_j[k][n]
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) xv[i][jj][r] = __builtin_fmaf(ca_, xv[i][jj][r], accC[i][jj][r]);
+      if (last) {
+        // O' block: the decoupled update (or the NS output), masked.
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int row = wm * 64 + i * 32 + m;
+              const int col = j * kSmall + wn * 64 + jj * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+              if (row < ca.rows && col < ca.cols) {
+                float* q = wout + (int64_t)row * ca.cols + col;
+                *q = (p.final_mode == FINAL_STEP) ? __builtin_fmaf(-ca.lr_scale, xv[i][jj][r], *q * ca.decay)
+                                                   : xv[i][jj][r];
+              }
+            }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int row = wm * 64 + i * 32 + m;
+              const int col = j * kSmall + wn * 64 + jj * 32 + 8 * q + 4 * half;
+              *reinterpret_cast<float4*>(Xn + (int64_t)row * p.ldx + col) =
+                  make_float4(xv[i][jj][4 * q], xv[i][jj][4 * q + 1], xv[i][jj][4 * q + 2], xv[i][jj][4 * q + 3]);
+            }
+        sm_put_rows(LR, xv, wm, wn, lane);
+        __syncthreads();
+        sm_mma(LR, LR, accA, wm, wn, lane);
+      }
+    };
+    load_x(xbuf[0], X, 0, it == 0);
+    for (int j = 0; j < nb; j += 2) {  // unrolled by two: the register sets alternate
+      apply_block(xbuf[0], xbuf[1], j);
+      if (j + 1 < nb) apply_block(xbuf[1], xbuf[0], j + 1);
+    }
+  }
 }
 
 // ------------------------------------------------------ persistent NS ------

@@ -435,6 +435,36 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
   uint32_t* err = reinterpret_cast<uint32_t*>(ws);
   hipLaunchKernelGGL(k_norm_finish, dim3(U), dim3(64), 0, s, partials, c.blocks_per_unit, inv_nu,
                      flag, done, queue, kMaxQueues + 1, first_chunk ? err : nullptr);
+  // Small wide units (at most 128 rows, bf16 products): the whole NS in one
+  // workgroup per unit, reading N itself (no normalisation pass).
+  if (bf16 && !c.tall && c.rows_u <= kSmall && c.rows_pad == kSmall) {
+    int total_it = 0;
+    for (int i = 0; i < h->n_stages; ++i) total_it += h->stages[i].steps;
+    NsSmallArgs p;
+    std::memset(&p, 0, sizeof(p));
+    p.x32[0] = x32[0];
+    p.x32[1] = x32[1];
+    p.x_stride = c.rows_pad * c.cols_pad;
+    p.ldx = (int32_t)c.cols_pad;
+    p.n_iter = total_it;
+    p.n_stages = h->n_stages;
+    int begin = 0;
+    for (int i = 0; i < h->n_stages; ++i) {
+      p.stage_begin[i] = begin;
+      begin += h->stages[i].steps;
+      p.sa[i] = h->stages[i].a;
+      p.sb[i] = h->stages[i].b;
+      p.sc[i] = h->stages[i].c;
+    }
+    p.final_mode = step ? FINAL_STEP : FINAL_NSOUT;
+    p.inv_nu = inv_nu;
+    p.flag = flag;
+    tr.after(MUON_KERNEL_NORMALIZE);
+    tr.before(MUON_KERNEL_NS);
+    hipLaunchKernelGGL(k_ns_small, dim3(U), dim3(kThreads), 0, s, p, ca);
+    tr.after(MUON_KERNEL_NS);
+    return hipGetLastError() == hipSuccess ? MUON_OK : MUON_ERR_HIP;
+  }
   const int tiles_c = (int)(c.cols_pad / 64);
   if (bf16)
     hipLaunchKernelGGL(k_normalize<true>, dim3(U * c.norm_blocks_per_unit), dim3(kThreads), 0, s,

@@ -37,6 +37,8 @@ NS_SHAPES = [
     (256, 512),   # 256 tiles
     (600, 260),   # 256 tiles, ragged tall
     (384, 1000),  # 256 tiles, ragged wide, several tiles each way
+    (128, 300),   # small-unit path (whole NS on chip): 128 rows, ragged columns
+    (100, 1000),  # small-unit path: ragged rows, eight 128-column blocks
 ]
 
 
