@@ -38,8 +38,9 @@ def parse():
     ap.add_argument("--config", type=int, default=2)
     ap.add_argument("--ns", default="bf16", choices=["bf16", "fp32"])
     ap.add_argument("--batch-update-size", type=int, default=0)
-    ap.add_argument("--schedule", default="persistent", choices=["persistent", "launches"],
-                    help="NS launch schedule: one persistent launch per pass, or one per product")
+    ap.add_argument("--schedule", default="auto", choices=["auto", "persistent", "launches"],
+                    help="NS schedule: the library's choice per pass, or force one persistent "
+                         "launch per pass, or one launch per product")
     ap.add_argument("--grad-sets", type=int, default=4, help="distinct resident gradient batches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -103,23 +104,42 @@ def build_inputs(wl, dev, grad_sets):
     return params, moms, grads, splits
 
 
-def nonzero_units(wl):
-    """(s, l, count) of every NS unit shape, excluding all-zero experts."""
+def unit_groups(wl):
+    """(rows, cols, units, non-zero units) of every NS unit shape, banks of
+    one unit shape merged as the library stacks them; all-zero experts are
+    excluded from the second count."""
     import workloads as W
 
-    out = []
+    out = {}
     for spec in wl.matrices:
         r, c = spec.unit_shape
         n = spec.batch * spec.units_per_matrix
+        nz = n
         if wl.zero_fraction:
-            n -= len(W.zero_experts(wl, spec.batch)) * spec.units_per_matrix
-        out.append((min(r, c), max(r, c), n))
-    return out
+            nz -= len(W.zero_experts(wl, spec.batch)) * spec.units_per_matrix
+        a, b = out.get((r, c), (0, 0))
+        out[(r, c)] = (a + n, b + nz)
+    return [(r, c, n, nz) for (r, c), (n, nz) in out.items()]
+
+
+def ns_route(rows, cols, n_units, ns, schedule, cus):
+    """Kernel class that runs the NS of a stacked pass: "ns" (one launch per
+    pass: the on-chip small-unit kernel or the persistent kernel) or
+    "launches" (one launch per product).  Mirrors the library's AUTO rule
+    for attributing FLOPs to the traced kernel classes."""
+    if schedule == "persistent":
+        return "ns"
+    if schedule == "launches":
+        return "launches"
+    if ns == "bf16" and rows <= cols and rows <= 128:
+        if -(-cols // 128) <= 8 or 2 * n_units >= cus:
+            return "ns"
+    return "ns" if min(rows, cols) >= 256 else "launches"
 
 
 def kernel_flops(units):
     """Algorithmic FLOPs of each NS kernel class per iteration, summed over
-    the workload's shape groups: X X^T and A*A as full products (2 s^2 l and
+    (s, l, count) shape groups: X X^T and A*A as full products (2 s^2 l and
     2 s^3), B*X as 2 s^2 l."""
     gram = sum(n * 2.0 * s * s * l for s, l, n in units)
     poly = sum(n * 2.0 * s**3 for s, l, n in units)
@@ -133,6 +153,28 @@ def executed_fraction(s):
     tile = 256 if s >= 256 else 128
     t = -(-s // tile)
     return (t * (t + 1) / 2) / (t * t)
+
+
+def class_flops(groups, ns, schedule, cus):
+    """Per NS kernel class ("ns", "gram", "poly", "apply"): algorithmic FLOPs
+    per iteration, and the FLOPs the kernels execute (symmetric products run
+    their upper-triangle tiles only; the on-chip small-unit kernel runs
+    whole 128 x 128 products)."""
+    alg = dict.fromkeys(("ns", "gram", "poly", "apply"), 0.0)
+    exe = dict(alg)
+    for r, c, n, nz in groups:
+        s, l = min(r, c), max(r, c)
+        f = kernel_flops([(s, l, nz)])
+        frac = executed_fraction(s)
+        e = {"gram": f["gram"] * frac, "poly": f["poly"] * frac, "apply": f["apply"]}
+        if ns_route(r, c, n, ns, schedule, cus) == "ns":
+            alg["ns"] += sum(f.values())
+            exe["ns"] += sum(e.values())
+        else:
+            for k in ("gram", "poly", "apply"):
+                alg[k] += f[k]
+                exe[k] += e[k]
+    return alg, exe
 
 
 def cpu_baseline(wl, hyper_o, seconds):
@@ -195,11 +237,9 @@ def main():
     ws = muon.workspace(ws_bytes, dev)
     torch.cuda.synchronize()
 
-    units = nonzero_units(wl)
+    groups = unit_groups(wl)
     n_units = wl.units
-    ns_flops_step = wl.ns_flops() if not wl.zero_fraction else sum(
-        n * 10 * (4.0 * s * s * l + 2.0 * s**3) for s, l, n in units
-    )
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
 
     def one_step(k, trace=None):
         return muon.step(params, grads[k % len(grads)], moms, hyper=hyper, split_rows=splits,
@@ -228,11 +268,13 @@ def main():
         one_step(k)
     ev1 = make_events(per_step)
     torch.cuda.synchronize()
-    if args.schedule == "persistent":
-        kinds = {"ns": muon.KERNEL_NS}
-    else:
-        kinds = {"gram": muon.KERNEL_GRAM, "poly": muon.KERNEL_POLY, "apply": muon.KERNEL_APPLY}
-    per_kind = {name: sum(traced_ms(kind, 0, ev1)) for name, kind in kinds.items()}
+    kinds = {"ns": muon.KERNEL_NS, "gram": muon.KERNEL_GRAM, "poly": muon.KERNEL_POLY,
+             "apply": muon.KERNEL_APPLY}
+    per_kind = {}
+    for name, kind in kinds.items():
+        ms = traced_ms(kind, 0, ev1)
+        if ms:
+            per_kind[name] = sum(ms)
     mom_ms = traced_ms(muon.KERNEL_MOMENTUM, 0, ev1)
     norm_ms = traced_ms(muon.KERNEL_NORMALIZE, 0, ev1)
     dominant = max(per_kind, key=per_kind.get)
@@ -251,8 +293,8 @@ def main():
     for ev, cnt in zip(evs, counts):
         launch_ms += [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(min(cnt, len(ev) // 2))]
 
-    flops = kernel_flops(units)
-    flops["ns"] = flops["gram"] + flops["poly"] + flops["apply"]
+    flops, exe = class_flops(groups, args.ns, args.schedule, cus)
+    ns_flops_step = sum(flops.values()) * iters
     avg_launch_ms = sum(launch_ms) / max(1, len(launch_ms))
     # algorithmic FLOPs of one launch: the class's FLOPs per step (every
     # iteration, every non-zero unit) over its launches per step
@@ -264,13 +306,13 @@ def main():
     # momentum kernel: G read (2 or 4 B), M read and written (8 B), the fp32
     # look-ahead written (4 B)
     elem_bytes = sum(m.numel * (14 if m.grad_dtype == "bf16" else 16) for m in wl.matrices)
-    sym_exec = {
-        "gram": sum(n * 2.0 * s * s * l * executed_fraction(s) for s, l, n in units) * iters,
-        "poly": sum(n * 2.0 * s**3 * executed_fraction(s) for s, l, n in units) * iters,
-        "apply": flops["apply"] * iters,
-    }
-    sym_exec["ns"] = sym_exec["gram"] + sym_exec["poly"] + sym_exec["apply"]
-    kernel_name = "ns_persistent" if dominant == "ns" else f"ns_gemm {dominant}"
+    if dominant != "ns":
+        kernel_name = f"ns_gemm {dominant}"
+    elif any(ns_route(r, c, n, args.ns, args.schedule, cus) == "ns" and min(r, c) < 256
+             for r, c, n, _ in groups):
+        kernel_name = "k_ns_small" if all(min(r, c) < 256 for r, c, _, _ in groups) else "ns"
+    else:
+        kernel_name = "ns_persistent"
     traffic = stored_traffic(kernel_name, wl.title, args.ns)
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib * (1 << 20) // 4
@@ -316,7 +358,7 @@ def main():
         # FLOPs the kernels execute: the symmetric products run only their
         # upper-triangle tiles
         "kernel_tflops_executed": {
-            k: round(sym_exec[k] / (per_kind[k] * 1e-3) / 1e12, 2) for k in per_kind
+            k: round(exe[k] * iters / (per_kind[k] * 1e-3) / 1e12, 2) for k in per_kind
         },
         "elementwise_gbs": elem_bytes / (sum(mom_ms) * 1e-3) / 1e9 if mom_ms else None,
         "roofline": {

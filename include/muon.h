@@ -79,8 +79,8 @@ typedef enum { MUON_SCALE_SPECTRAL = 0, MUON_SCALE_UNIT_RMS_NORM = 1 } muon_scal
  * polynomial B. */
 typedef enum { MUON_NS_FP32 = 0, MUON_NS_BF16 = 1 } muon_ns_precision;
 
-/* How the Newton-Schulz products of a stacked pass are launched; both give
- * bit-identical results.
+/* How the Newton-Schulz of a stacked pass is run.  PERSISTENT and LAUNCHES
+ * run the same tiled products and give bit-identical results.
  * PERSISTENT: one launch runs every iteration of the pass.  Workgroups claim
  *   output tiles in order (for each iteration: the Gram tiles of every
  *   unit, then the polynomial tiles, then the apply tiles) and each tile
@@ -88,8 +88,19 @@ typedef enum { MUON_NS_FP32 = 0, MUON_NS_BF16 = 1 } muon_ns_precision;
  *   different units and products overlap.  A wait is bounded (a few seconds
  *   of wall clock); if one ever runs out the launch stops and
  *   muon_workspace_status reports MUON_ERR_SCHEDULE.
- * LAUNCHES: one launch per product and iteration, in stream order. */
-typedef enum { MUON_SCHEDULE_PERSISTENT = 0, MUON_SCHEDULE_LAUNCHES = 1 } muon_schedule;
+ * LAUNCHES: one launch per product and iteration, in stream order.
+ * AUTO (default): per pass, whichever is faster on the MI355X.  Wide units
+ *   with at most 128 rows and bf16 products run their whole NS in one
+ *   workgroup each (A and B on chip, one pass over X per iteration) when
+ *   they span at most eight 128-column blocks or number at least half the
+ *   CUs; other passes of units with min(rows, cols) < 256 use LAUNCHES,
+ *   the rest PERSISTENT.  The on-chip path rounds like the tiled one except
+ *   that b*A uses A's fp32 accumulator, so results agree to rounding. */
+typedef enum {
+  MUON_SCHEDULE_AUTO = 0,
+  MUON_SCHEDULE_PERSISTENT = 1,
+  MUON_SCHEDULE_LAUNCHES = 2
+} muon_schedule;
 
 /* Momentum and look-ahead rule (RFC-0023 方案 1, both styles):
  * SGD: M <- mu*M + G;            N = mu*M + G (on the updated M)
@@ -140,7 +151,7 @@ typedef struct {
  * gamma 0.18, spectral scale, bf16 NS products, whole-group batches, and the
  * hybrid schedule 8 x (3.4445, -4.7750, 2.0315) + 2 x (2, -1.5, 0.5)
  * (DeepSeek tech notes "Muon 优化器" sections 1-3); SGD-style momentum,
- * step 1, persistent launch schedule.  NULL is ignored. */
+ * step 1, AUTO schedule.  NULL is ignored. */
 void muon_hyper_default(muon_hyper* h);
 
 /* Bytes of device workspace that muon_step_batched / muon_newton_schulz_batched
@@ -187,7 +198,8 @@ typedef enum {
   MUON_KERNEL_POLY = 4,     /* B = b*A + c*A*A */
   MUON_KERNEL_APPLY = 5,    /* X <- a*X + B*X (last one: the weight update) */
   MUON_KERNEL_NS = 6        /* every NS product of a pass in one launch
-                               (MUON_SCHEDULE_PERSISTENT) */
+                               (the persistent or the on-chip small-unit
+                               kernel) */
 } muon_kernel_kind;
 
 /* Timing hook: when passed to the *_traced entry points, every launch of
@@ -225,7 +237,7 @@ int muon_workspace_status(const void* workspace, size_t workspace_bytes, hipStre
 /* Static description of a status code (never NULL). */
 const char* muon_status_string(int status);
 
-/* ABI version of this header: 3. */
+/* ABI version of this header: 4. */
 int muon_abi_version(void);
 
 #ifdef __cplusplus

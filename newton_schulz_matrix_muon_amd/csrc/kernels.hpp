@@ -1172,6 +1172,13 @@ __global__ __launch_bounds__(kThreads) void ns_persistent(NsSched p, ChunkArgs c
   int uq = units_of(q);
   int pending = -1;      // unit whose finished tile wave 0 has yet to count
   bool alone = false;    // running unclaimed queues after every other workgroup left
+  // Wave 0 claims the next item (and reads the error word) as soon as the
+  // current one may start, so the round trip overlaps the tile.  Holding
+  // one claimed item ahead cannot stall the schedule: the earliest
+  // unfinished item in claim order is always some workgroup's current one
+  // (a held item comes after its holder's current, unfinished item).
+  bool have_next = false;
+  uint32_t next_raw = 0u, err_raw = 0u;
   for (;;) {
     if (wave == 0) {
       if (pending >= 0) {
@@ -1180,13 +1187,15 @@ __global__ __launch_bounds__(kThreads) void ns_persistent(NsSched p, ChunkArgs c
         if (!local) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         __hip_atomic_fetch_add(p.done + pending, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      int item = __builtin_amdgcn_readfirstlane(
-          (int)__hip_atomic_fetch_add(p.queue + q, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-      const uint32_t e = __builtin_amdgcn_readfirstlane(
-          __hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-      if (e != 0u) item = -1;
+      if (!have_next) {
+        next_raw = __hip_atomic_fetch_add(p.queue + q, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        err_raw = __hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      int item = __builtin_amdgcn_readfirstlane((int)next_raw);
+      if (__builtin_amdgcn_readfirstlane(err_raw) != 0u) item = -1;
       s_item = item;  // every lane writes the same value
     }
+    have_next = false;
     pending = -1;
     __syncthreads();
     const int item = __builtin_amdgcn_readfirstlane(s_item);
@@ -1268,6 +1277,11 @@ __global__ __launch_bounds__(kThreads) void ns_persistent(NsSched p, ChunkArgs c
     // (acquire at agent scope: the L1 must be dropped in any case, and a
     // workgroup-scope invalidate does not reach it).
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    if (wave == 0) {
+      next_raw = __hip_atomic_fetch_add(p.queue + q, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      err_raw = __hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      have_next = true;
+    }
     const int cur = it & 1;
     if (phase == GRAM) {
       if (live) {

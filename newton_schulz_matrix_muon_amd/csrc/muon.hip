@@ -110,7 +110,8 @@ int validate_hyper(const muon_hyper* h) {
     return MUON_ERR_HYPER;
   if (h->scale_mode != MUON_SCALE_SPECTRAL && h->scale_mode != MUON_SCALE_UNIT_RMS_NORM)
     return MUON_ERR_DTYPE;
-  if (h->schedule != MUON_SCHEDULE_PERSISTENT && h->schedule != MUON_SCHEDULE_LAUNCHES)
+  if (h->schedule != MUON_SCHEDULE_AUTO && h->schedule != MUON_SCHEDULE_PERSISTENT &&
+      h->schedule != MUON_SCHEDULE_LAUNCHES)
     return MUON_ERR_HYPER;
   if (h->reserved != 0) return MUON_ERR_HYPER;
   if (h->nesterov_style != MUON_NESTEROV_SGD && h->nesterov_style != MUON_NESTEROV_EMA)
@@ -435,9 +436,21 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
   uint32_t* err = reinterpret_cast<uint32_t*>(ws);
   hipLaunchKernelGGL(k_norm_finish, dim3(U), dim3(64), 0, s, partials, c.blocks_per_unit, inv_nu,
                      flag, done, queue, kMaxQueues + 1, first_chunk ? err : nullptr);
-  // Small wide units (at most 128 rows, bf16 products): the whole NS in one
-  // workgroup per unit, reading N itself (no normalisation pass).
-  if (bf16 && !c.tall && c.rows_u <= kSmall && c.rows_pad == kSmall) {
+  // Small wide units (at most 128 rows, bf16 products, AUTO schedule): the
+  // whole NS in one workgroup per unit, reading N itself (no normalisation
+  // pass).  A unit's workgroup walks its column blocks in sequence, so the
+  // path is taken for short units (up to eight 128-column blocks) or when
+  // the units number at least half the CUs; a few long units go to the
+  // tiled products, which spread each unit over many CUs.
+  bool small = h->schedule == MUON_SCHEDULE_AUTO && bf16 && !c.tall && c.rows_u <= kSmall &&
+               c.rows_pad == kSmall;
+  if (small && c.cols_pad / kSmall > 8) {
+    DeviceInfo di;
+    const int dst = device_info(&di);
+    if (dst != MUON_OK) return dst;
+    small = 2 * U >= di.cus;
+  }
+  if (small) {
     int total_it = 0;
     for (int i = 0; i < h->n_stages; ++i) total_it += h->stages[i].steps;
     NsSmallArgs p;
@@ -490,7 +503,11 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
   const int tg = (int)((sp / T) * (sp / T + 1) / 2);
   const int ta = (int)((c.rows_pad / T) * (c.cols_pad / T));
   const int64_t n_items = (int64_t)total * U * (2 * tg + ta);
-  if (h->schedule == MUON_SCHEDULE_PERSISTENT && n_items < INT32_MAX / 2) {
+  // AUTO: persistent for 256-tile passes; 128-tile passes (short K) run
+  // faster as separate launches than as claimed tiles.
+  const bool persistent = h->schedule == MUON_SCHEDULE_PERSISTENT ||
+                          (h->schedule == MUON_SCHEDULE_AUTO && T == 256);
+  if (persistent && n_items < INT32_MAX / 2) {
     DeviceInfo di;
     const int dst = device_info(&di);
     if (dst != MUON_OK) return dst;
@@ -769,7 +786,7 @@ void muon_hyper_default(muon_hyper* h) {
   h->scale_mode = MUON_SCALE_SPECTRAL;
   h->ns_precision = MUON_NS_BF16;
   h->batch_update_size = 0;
-  h->schedule = MUON_SCHEDULE_PERSISTENT;
+  h->schedule = MUON_SCHEDULE_AUTO;
   h->nesterov_style = MUON_NESTEROV_SGD;
   h->step = 1;
   h->n_stages = 2;
@@ -856,6 +873,6 @@ int muon_workspace_status(const void* workspace, size_t workspace_bytes, hipStre
   return word == 0u ? MUON_OK : MUON_ERR_SCHEDULE;
 }
 
-int muon_abi_version(void) { return 3; }
+int muon_abi_version(void) { return 4; }
 
 }  // extern "C"

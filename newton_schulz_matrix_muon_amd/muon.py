@@ -37,7 +37,7 @@ SCALE_SPECTRAL, SCALE_UNIT_RMS_NORM = 0, 1
 NS_FP32, NS_BF16 = 0, 1
 KERNEL_MOMENTUM, KERNEL_NORMALIZE, KERNEL_GRAM, KERNEL_POLY, KERNEL_APPLY = 1, 2, 3, 4, 5
 KERNEL_NS = 6
-SCHEDULE_PERSISTENT, SCHEDULE_LAUNCHES = 0, 1
+SCHEDULE_AUTO, SCHEDULE_PERSISTENT, SCHEDULE_LAUNCHES = 0, 1, 2
 NESTEROV_SGD, NESTEROV_EMA = 0, 1
 MAX_STAGES = 4
 
@@ -159,8 +159,8 @@ def status_string(status: int) -> str:
 class Hyper:
     """Mirror of `muon_hyper`; defaults come from the library
     (lr 2.7e-4, mu 0.95, wd 0.1, gamma 0.18, spectral, bf16 NS products,
-    8 x (3.4445, -4.7750, 2.0315) + 2 x (2, -1.5, 0.5), persistent NS
-    launch schedule)."""
+    8 x (3.4445, -4.7750, 2.0315) + 2 x (2, -1.5, 0.5), AUTO NS
+    schedule)."""
 
     lr: float = 2.7e-4
     mu: float = 0.95
@@ -172,7 +172,7 @@ class Hyper:
     stages: Sequence[tuple[int, tuple[float, float, float]]] = field(
         default_factory=lambda: ((8, (3.4445, -4.7750, 2.0315)), (2, (2.0, -1.5, 0.5)))
     )
-    schedule: str = "persistent"  # or "launches"
+    schedule: str = "auto"  # or "persistent" / "launches" (tiled products only)
     nesterov_style: str = "sgd"  # or "ema" (bias-corrected; needs `step`)
     step: int = 1  # 1-based index of this step (EMA style only)
 
@@ -182,7 +182,8 @@ class Hyper:
         h.scale_mode = {"spectral": SCALE_SPECTRAL, "unit_rms_norm": SCALE_UNIT_RMS_NORM}[self.scale]
         h.ns_precision = {"fp32": NS_FP32, "bf16": NS_BF16}[self.ns_precision]
         h.batch_update_size = self.batch_update_size
-        h.schedule = {"persistent": SCHEDULE_PERSISTENT, "launches": SCHEDULE_LAUNCHES}[self.schedule]
+        h.schedule = {"auto": SCHEDULE_AUTO, "persistent": SCHEDULE_PERSISTENT,
+                      "launches": SCHEDULE_LAUNCHES}[self.schedule]
         h.nesterov_style = {"sgd": NESTEROV_SGD, "ema": NESTEROV_EMA}[self.nesterov_style]
         h.step = self.step
         h.reserved = 0

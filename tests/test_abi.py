@@ -36,7 +36,7 @@ def test_defaults_are_the_pages_values():
     assert (h.stages[0].steps, h.stages[1].steps) == (8, 2)
     assert (h.stages[0].a, h.stages[0].b, h.stages[0].c) == pytest.approx((3.4445, -4.7750, 2.0315))
     assert (h.stages[1].a, h.stages[1].b, h.stages[1].c) == (2.0, -1.5, 0.5)
-    assert h.schedule == muon.SCHEDULE_PERSISTENT and h.reserved == 0
+    assert h.schedule == muon.SCHEDULE_AUTO and h.reserved == 0
     assert h.nesterov_style == muon.NESTEROV_SGD and h.step == 1
 
 
@@ -105,7 +105,7 @@ def test_bad_hyper_rejected():
     h.stages[1].steps = 0
     assert ws_size([(1, 4, 4, 0)], h)[0] == -6
     h = muon.default_hyper_c()
-    h.schedule = 2
+    h.schedule = 3
     assert ws_size([(1, 4, 4, 0)], h)[0] == -6
     h = muon.default_hyper_c()
     h.reserved = 1
@@ -168,4 +168,4 @@ def test_status_strings():
     for code in range(-9, 1):
         assert muon.status_string(code) != "unknown status"
     assert muon.status_string(12345) == "unknown status"
-    assert muon.LIB.muon_abi_version() == 3
+    assert muon.LIB.muon_abi_version() == 4

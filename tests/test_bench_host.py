@@ -9,7 +9,7 @@ import workloads as W
 
 def test_kernel_flops_match_the_workload_total():
     wl = W.workload(2)
-    units = bench.nonzero_units(wl)
+    units = [(min(r, c), max(r, c), nz) for r, c, _, nz in bench.unit_groups(wl)]
     f = bench.kernel_flops(units)
     iters = 10
     # one NS iteration: X X^T (2 s^2 l) + A A (2 s^3) + B X (2 s^2 l)
@@ -21,6 +21,37 @@ def test_executed_fraction_of_symmetric_tiles():
     assert bench.executed_fraction(256) == 1.0
     assert bench.executed_fraction(128) == 1.0        # one 128 tile
     assert bench.executed_fraction(4096) == (16 * 17 / 2) / 256
+
+
+def test_unit_groups_merge_heads_of_one_shape():
+    wl = W.workload(3)  # Q, K and V heads are all 128 x 4096
+    g = {(r, c): (n, nz) for r, c, n, nz in bench.unit_groups(wl)}
+    assert g[(128, 4096)] == (48, 48)
+    assert sum(n for n, _ in g.values()) == wl.units
+
+
+def test_ns_route_follows_the_auto_rule():
+    r = bench.ns_route
+    assert r(1024, 1024, 32, "bf16", "auto", 256) == "ns"            # 256 tiles: persistent
+    assert r(128, 4096, 48, "bf16", "auto", 256) == "launches"       # few long heads
+    assert r(128, 4096, 128, "bf16", "auto", 256) == "ns"            # many heads: on chip
+    assert r(64, 128, 1, "bf16", "auto", 256) == "ns"                # short: on chip
+    assert r(64, 128, 1, "fp32", "auto", 256) == "launches"          # fp32 products: tiled
+    assert r(300, 128, 4, "bf16", "auto", 256) == "launches"         # tall
+    assert r(128, 4096, 512, "bf16", "launches", 256) == "launches"
+    assert r(64, 128, 1, "bf16", "persistent", 256) == "ns"
+
+
+def test_class_flops_split_by_route():
+    groups = [(1024, 1024, 4, 4), (128, 4096, 48, 40)]
+    alg, exe = bench.class_flops(groups, "bf16", "auto", 256)
+    big = bench.kernel_flops([(1024, 1024, 4)])
+    heads = bench.kernel_flops([(128, 4096, 40)])
+    assert alg["ns"] == sum(big.values())
+    for k in ("gram", "poly", "apply"):
+        assert alg[k] == heads[k]
+    assert exe["ns"] < alg["ns"]                     # symmetric tiles of 1024 squares
+    assert exe["gram"] == alg["gram"]                # one 128 tile
 
 
 def test_stored_traffic_lookup(tmp_path):

@@ -56,6 +56,25 @@ def test_ns_only_matches_oracle(gpu_lib, shape, prec):
     assert e <= TOL_NS[prec], f"rel err {e:.3e}"
 
 
+# Wide units of at most 128 rows and more than eight 128-column blocks: the
+# default schedule runs a few of them as tiled products and many of them
+# (at least half the CUs) on chip; the forced schedules always tile.
+@pytest.mark.parametrize("sched", ["auto", "persistent", "launches"])
+@pytest.mark.parametrize("batch,rows,cols", [(12, 128, 1100), (160, 96, 1100)],
+                         ids=["few-long", "many-long"])
+def test_ns_long_small_units_every_schedule(gpu_lib, sched, batch, rows, cols):
+    say(f"[ns long small units] {batch}x{rows}x{cols} schedule={sched}")
+    x = _seeded((batch, rows, cols), 4242 + batch)
+    h = gpu_lib.Hyper(ns_precision="bf16", schedule=sched)
+    outs, _ = gpu_lib.newton_schulz([x], hyper=h)
+    torch.cuda.synchronize()
+    worst = 0.0
+    for i in sorted({0, batch // 2, batch - 1}):
+        worst = max(worst, rel(f64(outs[0][i]), oracle.newton_schulz(f64(x[i]))))
+    say(f"   worst rel err {worst:.3e}")
+    assert worst <= TOL_NS["bf16"]
+
+
 @pytest.mark.parametrize("prec", ["fp32", "bf16"])
 def test_ns_split_heads_and_banks(gpu_lib, prec):
     # A (batch=3, 6*32, 96) bank split into 32-row heads: 18 units.
