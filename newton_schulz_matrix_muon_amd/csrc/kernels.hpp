@@ -11,16 +11,19 @@
 //                   and the non-zero flag (notes section 2: Frobenius
 //                   normalisation, a zero matrix stays zero).
 //   k_normalize     X0 = N/||N||_F over the padded iterate (zeros in the
-//                   padding), plus the operand copies the products read: X0
-//                   in bf16 (bf16 path) and X0^T (bf16, or fp32 on the fp32
-//                   path), transposed through LDS.
+//                   padding) as the operand copies the products read: X0
+//                   and X0^T, in bf16 on the bf16 path (X0 is then held
+//                   only in bf16) or fp32, transposed through LDS.
 //   ns_gemm<GRAM>   A = X X^T (or X^T X for a tall unit: the smaller side).
 //   ns_gemm<POLY>   B = b*A + c*A*A (on the bf16 path A is kept only as its
 //                   bf16 operand copy, which the b*A term also reads).
 //                   Both outputs are symmetric: only the upper-triangle tiles
 //                   are computed, each also written mirrored.
-//   ns_gemm<APPLY>  X' = a*X + B*X (or X*B), written with its operand copies
-//                   (X' in bf16, X'^T); in the last iteration the epilogue
+//   ns_gemm<APPLY>  X' = a*X + B*X (or X*B), written as its operand copies
+//                   X' and X'^T.  On the bf16 path the iterate exists only
+//                   as these bf16 copies: the a*X term reads the same
+//                   rounded X that the products read.  In the last
+//                   iteration the epilogue
 //                   writes W <- W*(1 - lr*wd) - lr*scale*X' instead
 //                   (Algorithm 1's decoupled update) or the NS output.
 //   k_ns_small      the whole NS of a wide unit with at most 128 rows in one
@@ -100,8 +103,8 @@ struct GemmArgs {
   int32_t sym;          // GRAM/POLY: symmetric output; only tiles tm <= tn run
                         // and each off-diagonal tile also writes its mirror
   int32_t final_mode;
-  const float* aux;     // fp32 A (POLY, fp32 path) or X (APPLY), laid out like the output
-  const void* aux16;    // bf16 A (POLY, bf16 path)
+  const float* aux;     // fp32 A (POLY) or X (APPLY) on the fp32 path, laid out like the output
+  const void* aux16;    // bf16 A (POLY) or X (APPLY) on the bf16 path
   int64_t aux_ustride;
   int32_t ldaux;
   float ca, cb, cc;     // quintic coefficients
@@ -158,6 +161,11 @@ __device__ __forceinline__ uint16_t to_bf16_bits(float f) {
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
   return __builtin_bit_cast(float, h << 16);
+}
+
+// f rounded to bf16 (round to nearest even), as fp32.
+__device__ __forceinline__ float bf16_round(float f) {
+  return bf16_bits_to_f32(to_bf16_bits(f));
 }
 
 // ------------------------------------------------------------- momentum ----
@@ -265,8 +273,8 @@ __global__ __launch_bounds__(64) void k_norm_finish(const double* __restrict__ p
   }
 }
 
-// X0 = N * (1/nu) over the whole padded iterate (zeros in the padding), in
-// place in the fp32 buffer, plus X0 in bf16 (BF16) and X0^T (bf16 or fp32).
+// X0 = N * (1/nu) over the whole padded iterate (zeros in the padding):
+// in bf16 (BF16) or in place in the fp32 buffer, and X0^T in the same type.
 // One 64x64 tile per workgroup; the transpose goes through LDS so that both
 // the row-major and the transposed writes are coalesced.
 template <bool BF16>
@@ -296,12 +304,13 @@ __global__ __launch_bounds__(kThreads) void k_normalize(ChunkArgs ca, float* __r
       val.z = (c + 2 < ca.cols) ? nv.z * s : 0.f;
       val.w = (c + 3 < ca.cols) ? nv.w * s : 0.f;
     }
-    *reinterpret_cast<float4*>(xu + e) = val;
     if (BF16) {
       uint2 packed;
       packed.x = (uint32_t)to_bf16_bits(val.x) | ((uint32_t)to_bf16_bits(val.y) << 16);
       packed.y = (uint32_t)to_bf16_bits(val.z) | ((uint32_t)to_bf16_bits(val.w) << 16);
       *reinterpret_cast<uint2*>(xb + (int64_t)u * ca.x_stride + e) = packed;
+    } else {
+      *reinterpret_cast<float4*>(xu + e) = val;
     }
     tile[rr][cc] = val.x;
     tile[rr][cc + 1] = val.y;
@@ -676,7 +685,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
     const int mrow0 = m0 + wm * WT + i * 32;  // first global row of the block
     // auxiliary input of the block, row-wise (issued before the staging)
     float4 aux[NIT];
-    if constexpr (PHASE == POLY && kBF) {
+    if constexpr (PHASE != GRAM && kBF) {
       const uint16_t* ap = static_cast<const uint16_t*>(g.aux16) + (int64_t)u * g.aux_ustride + ncol;
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
@@ -728,8 +737,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
         v2 = __builtin_fmaf(g.ca, a.z, v2);
         v3 = __builtin_fmaf(g.ca, a.w, v3);
         if (g.final_mode == FINAL_NONE) {
-          *reinterpret_cast<float4*>(g.out32 + o) = make_float4(v0, v1, v2, v3);
-          if constexpr (kBF) store_bf16x4(g.out16, o, v0, v1, v2, v3);
+          if constexpr (kBF)
+            store_bf16x4(g.out16, o, v0, v1, v2, v3);
+          else
+            *reinterpret_cast<float4*>(g.out32 + o) = make_float4(v0, v1, v2, v3);
           // keep a*X + C for the transposed pass
           *reinterpret_cast<float4*>(ep + r * LDW + cl) = make_float4(v0, v1, v2, v3);
         } else if (m < ca.rows && ncol < ca.cols) {
@@ -846,7 +857,8 @@ __global__ __launch_bounds__(kThreads) void ns_gemm(GemmArgs g, ChunkArgs ca) {
 // Iteration 0 reads the look-ahead N straight from the momentum kernel and
 // scales it by 1/||N||_F, masking the padding.
 struct NsSmallArgs {
-  float* x32[2];          // ping-pong iterates (unit 0), rows 128 x ldx
+  const float* n32;       // the look-ahead N (unit 0), rows 128 x ldx
+  uint16_t* xb[2];        // ping-pong bf16 iterates (unit 0), rows 128 x ldx
   int64_t x_stride;       // elements per unit
   int32_t ldx;            // padded columns (multiple of 128)
   int32_t n_iter;
@@ -949,12 +961,15 @@ __global__ __launch_bounds__(kThreads) void k_ns_small(NsSmallArgs p, ChunkArgs 
   }
   const float inv0 = p.inv_nu[u];
 
-  // Block j of the iterate, in accumulator layout (iteration 0: the masked,
-  // scaled look-ahead).  Two register sets: block j+1 is loaded while block
-  // j is processed.
+  // Block j of the iterate, in accumulator layout, with bf16-rounded
+  // values: iteration 0 rounds the masked, scaled look-ahead, later ones
+  // read the bf16 iterate (the iterate is held in bf16 as on the tiled
+  // path).  Two register sets: block j+1 is loaded while block j is
+  // processed.
   typedef float Blk[2][2][16];
   Blk xbuf[2];
-  auto load_x = [&](Blk& xv, const float* X, int j, bool first) {
+  auto load_x0 = [&](Blk& xv, int j) {
+    const float* N = p.n32 + (int64_t)u * p.x_stride;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -963,18 +978,28 @@ __global__ __launch_bounds__(kThreads) void k_ns_small(NsSmallArgs p, ChunkArgs 
         for (int q = 0; q < 4; ++q) {
           const int row = wm * 64 + i * 32 + m;
           const int col = j * kSmall + wn * 64 + jj * 32 + 8 * q + 4 * half;
-          float4 x = *reinterpret_cast<const float4*>(X + (int64_t)row * p.ldx + col);
-          if (first) {
-            const bool rin = row < ca.rows;
-            x.x = (rin && col + 0 < ca.cols) ? x.x * inv0 : 0.0f;
-            x.y = (rin && col + 1 < ca.cols) ? x.y * inv0 : 0.0f;
-            x.z = (rin && col + 2 < ca.cols) ? x.z * inv0 : 0.0f;
-            x.w = (rin && col + 3 < ca.cols) ? x.w * inv0 : 0.0f;
-          }
-          xv[i][jj][4 * q] = x.x;
-          xv[i][jj][4 * q + 1] = x.y;
-          xv[i][jj][4 * q + 2] = x.z;
-          xv[i][jj][4 * q + 3] = x.w;
+          const float4 x = *reinterpret_cast<const float4*>(N + (int64_t)row * p.ldx + col);
+          const bool rin = row < ca.rows;
+          xv[i][jj][4 * q] = bf16_round((rin && col + 0 < ca.cols) ? x.x * inv0 : 0.0f);
+          xv[i][jj][4 * q + 1] = bf16_round((rin && col + 1 < ca.cols) ? x.y * inv0 : 0.0f);
+          xv[i][jj][4 * q + 2] = bf16_round((rin && col + 2 < ca.cols) ? x.z * inv0 : 0.0f);
+          xv[i][jj][4 * q + 3] = bf16_round((rin && col + 3 < ca.cols) ? x.w * inv0 : 0.0f);
+        }
+  };
+  auto load_x = [&](Blk& xv, const uint16_t* X, int j) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int row = wm * 64 + i * 32 + m;
+          const int col = j * kSmall + wn * 64 + jj * 32 + 8 * q + 4 * half;
+          const uint2 h = *reinterpret_cast<const uint2*>(X + (int64_t)row * p.ldx + col);
+          xv[i][jj][4 * q] = bf16_bits_to_f32(h.x & 0xffffu);
+          xv[i][jj][4 * q + 1] = bf16_bits_to_f32(h.x >> 16);
+          xv[i][jj][4 * q + 2] = bf16_bits_to_f32(h.y & 0xffffu);
+          xv[i][jj][4 * q + 3] = bf16_bits_to_f32(h.y >> 16);
         }
   };
   auto zero = [](f32x16 (&a)[2][2]) {
@@ -997,15 +1022,14 @@ __global__ __launch_bounds__(kThreads) void k_ns_small(NsSmallArgs p, ChunkArgs 
   // Gram of iteration 0.
   f32x16 accA[2][2], accC[2][2];
   zero(accA);
-  const float* X0 = p.x32[0] + (int64_t)u * p.x_stride;
   auto gram_block = [&](Blk& xv, Blk& xnext, int j) {
-    if (j + 1 < nb) load_x(xnext, X0, j + 1, true);
+    if (j + 1 < nb) load_x0(xnext, j + 1);
     __syncthreads();  // LR is free
     sm_put_rows(LR, xv, wm, wn, lane);
     __syncthreads();
     sm_mma(LR, LR, accA, wm, wn, lane);
   };
-  load_x(xbuf[0], X0, 0, true);
+  load_x0(xbuf[0], 0);
   for (int j = 0; j < nb; j += 2) {  // unrolled by two: the register sets alternate
     gram_block(xbuf[0], xbuf[1], j);
     if (j + 1 < nb) gram_block(xbuf[1], xbuf[0], j + 1);
@@ -1021,8 +1045,8 @@ __global__ __launch_bounds__(kThreads) void k_ns_small(NsSmallArgs p, ChunkArgs 
         cc = p.sc[s];
       }
     const bool last = it == p.n_iter - 1;
-    const float* X = p.x32[it & 1] + (int64_t)u * p.x_stride;
-    float* Xn = p.x32[(it & 1) ^ 1] + (int64_t)u * p.x_stride;
+    const uint16_t* X = p.xb[it & 1] + (int64_t)u * p.x_stride;
+    uint16_t* Xn = p.xb[(it & 1) ^ 1] + (int64_t)u * p.x_stride;
 
     // B = b*A + c*A*A (A symmetric), into LA as the apply's operand.
     float av[2][2][16];
@@ -1044,7 +1068,12 @@ __global__ __launch_bounds__(kThreads) void k_ns_small(NsSmallArgs p, ChunkArgs 
     // Apply pass, with the next Gram accumulated on the way.
     zero(accA);
     auto apply_block = [&](Blk& xv, Blk& xnext, int j) {
-      if (j + 1 < nb) load_x(xnext, X, j + 1, it == 0);
+      if (j + 1 < nb) {
+        if (it == 0)
+          load_x0(xnext, j + 1);
+        else
+          load_x(xnext, X, j + 1);
+      }
       __syncthreads();  // LA complete; LX and LR free
       sm_put_cols(LX, xv, wm, wn, lane);
       __syncthreads();
@@ -1081,15 +1110,18 @@ __global__ __launch_bounds__(kThreads) void k_ns_small(NsSmallArgs p, ChunkArgs 
             for (int q = 0; q < 4; ++q) {
               const int row = wm * 64 + i * 32 + m;
               const int col = j * kSmall + wn * 64 + jj * 32 + 8 * q + 4 * half;
-              *reinterpret_cast<float4*>(Xn + (int64_t)row * p.ldx + col) =
-                  make_float4(xv[i][jj][4 * q], xv[i][jj][4 * q + 1], xv[i][jj][4 * q + 2], xv[i][jj][4 * q + 3]);
+              store_bf16x4(Xn, (int64_t)row * p.ldx + col, xv[i][jj][4 * q], xv[i][jj][4 * q + 1],
+                           xv[i][jj][4 * q + 2], xv[i][jj][4 * q + 3]);
             }
         sm_put_rows(LR, xv, wm, wn, lane);
         __syncthreads();
         sm_mma(LR, LR, accA, wm, wn, lane);
       }
     };
-    load_x(xbuf[0], X, 0, it == 0);
+    if (it == 0)
+      load_x0(xbuf[0], 0);
+    else
+      load_x(xbuf[0], X, 0);
     for (int j = 0; j < nb; j += 2) {  // unrolled by two: the register sets alternate
       apply_block(xbuf[0], xbuf[1], j);
       if (j + 1 < nb) apply_block(xbuf[1], xbuf[0], j + 1);
@@ -1125,7 +1157,8 @@ struct NsSched {
   float* app_out32[2];            // apply outputs (buffer cur ^ 1)
   void* app_out16[2];
   void* app_outt[2];
-  const float* app_aux[2];        // the iterate X (buffer cur)
+  const float* app_aux[2];        // the iterate X (buffer cur): fp32 path
+  const void* app_aux16[2];       // the same, bf16 path
   int32_t final_mode;             // of the last iteration's apply
   int32_t n_iter;
   int32_t n_stages;
@@ -1324,6 +1357,7 @@ __global__ __launch_bounds__(kThreads) void ns_persistent(NsSched p, ChunkArgs c
         g.out16 = cur ? p.app_out16[1] : p.app_out16[0];
         g.outt = cur ? p.app_outt[1] : p.app_outt[0];
         g.aux = cur ? p.app_aux[1] : p.app_aux[0];
+        g.aux16 = cur ? p.app_aux16[1] : p.app_aux16[0];
         gemm_tile<APPLY, T, TILE>(g, ca, u, tm, tn);
       } else if (fm != FINAL_NONE) {
         zero_unit_tile<TILE>(ca, fm, u, tm * TILE, tn * TILE);

@@ -78,8 +78,10 @@ Layout layout_of(const Chunk& c, bool bf16) {
   const size_t ss = (size_t)(c.s_pad * c.s_pad);
   size_t off = kHeader;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, kAlign); return o; };
+  // fp32 iterates: N (and X0) in the first; the second only on the fp32
+  // path (the bf16 path keeps the iterate as its bf16 operand copies).
   L.x32[0] = take(U * xs * 4);
-  L.x32[1] = take(U * xs * 4);
+  if (!bf16) L.x32[1] = take(U * xs * 4);
   if (bf16) {
     L.xb[0] = take(U * xs * 2);
     L.xb[1] = take(U * xs * 2);
@@ -402,7 +404,8 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
     first += (int32_t)r.count;
   }
 
-  float* x32[2] = {reinterpret_cast<float*>(ws + L.x32[0]), reinterpret_cast<float*>(ws + L.x32[1])};
+  float* x32[2] = {reinterpret_cast<float*>(ws + L.x32[0]),
+                   bf16 ? nullptr : reinterpret_cast<float*>(ws + L.x32[1])};
   uint16_t* xb[2] = {bf16 ? reinterpret_cast<uint16_t*>(ws + L.xb[0]) : nullptr,
                      bf16 ? reinterpret_cast<uint16_t*>(ws + L.xb[1]) : nullptr};
   void* xt[2] = {ws + L.xt[0], ws + L.xt[1]};
@@ -455,8 +458,9 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
     for (int i = 0; i < h->n_stages; ++i) total_it += h->stages[i].steps;
     NsSmallArgs p;
     std::memset(&p, 0, sizeof(p));
-    p.x32[0] = x32[0];
-    p.x32[1] = x32[1];
+    p.n32 = x32[0];
+    p.xb[0] = xb[0];
+    p.xb[1] = xb[1];
     p.x_stride = c.rows_pad * c.cols_pad;
     p.ldx = (int32_t)c.cols_pad;
     p.n_iter = total_it;
@@ -575,10 +579,11 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
       const int nx = k ^ 1;
       p.app_a[k] = c.tall ? xop[k] : (const void*)bop;
       p.app_b[k] = c.tall ? (const void*)bop : (const void*)xt[k];
-      p.app_out32[k] = x32[nx];
+      p.app_out32[k] = bf16 ? nullptr : x32[nx];
       p.app_out16[k] = bf16 ? (void*)xb[nx] : nullptr;
       p.app_outt[k] = xt[nx];
-      p.app_aux[k] = x32[k];
+      p.app_aux[k] = bf16 ? nullptr : x32[k];
+      p.app_aux16[k] = bf16 ? (const void*)xb[k] : nullptr;
     }
     p.final_mode = step ? FINAL_STEP : FINAL_NSOUT;
     p.n_iter = total;
@@ -701,13 +706,14 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
         g.b_ustride = ss;
         g.ldb = (int32_t)sp;
       }
-      g.out32 = x32[nxt];
+      g.out32 = bf16 ? nullptr : x32[nxt];
       g.out16 = bf16 ? (void*)xb[nxt] : nullptr;
       g.out_ustride = xs;
       g.ldo = (int32_t)c.cols_pad;
       g.outt = xt[nxt];
       g.ldt = (int32_t)c.rows_pad;
-      g.aux = x32[cur];
+      g.aux = bf16 ? nullptr : x32[cur];
+      g.aux16 = bf16 ? (const void*)xb[cur] : nullptr;
       g.aux_ustride = xs;
       g.ldaux = (int32_t)c.cols_pad;
       g.ca = sg.a;
