@@ -481,6 +481,17 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+// Workgroup barrier for LDS broadcasts: waits for this wave's LDS (and
+// scalar) accesses only, not for its global stores and atomics in flight,
+// which a __syncthreads() fence would drain first.  The signal fences keep
+// the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  wait_lgkm0();
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // LDS of the GEMM tile: a ring of kSlots half-stages, each TILE rows of
 // one operand x 128 bytes of K (160 KB at TILE 256).  Declared once per tile
 // size, so a kernel that runs several tile phases holds a single ring; the
@@ -521,8 +532,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
   u32x4* const ring = lds_ring<TILE>;
   const uint32_t ring_off = (uint32_t)(uintptr_t)(lds_vptr)lds_ring<TILE>;
   const int m0 = tm * TILE, n0 = tn * TILE;
-  const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
+  // Lane-dependent values are recomputed for every tile (see the copy
+  // offsets below): an opaque copy of the lane index keeps the compiler
+  // from hoisting each phase's per-lane addressing out of a persistent loop.
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wid >> 1, wn = wid & 1;
 
   const T* A = static_cast<const T*>(g.a) + (int64_t)u * g.a_ustride;
@@ -542,9 +557,14 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
   // B_op's.  Half-stage h lives in ring slot h % kSlots.
   const int nk = g.K / BK;  // >= 2 (K is a multiple of 128)
   const int nh = 2 * nk;
+  // The per-lane copy offsets are recomputed for every tile: an opaque copy
+  // of the leading dimensions keeps the compiler from hoisting them out of
+  // a persistent tile loop, where they would stay live for every phase.
+  int lda = g.lda, ldb = g.ldb;
+  asm volatile("" : "+s"(lda), "+s"(ldb));
   DmaPlan<T, TILE> pa, pb;
-  pa.init(g.lda);
-  pb.init(g.ldb);
+  pa.init(lda);
+  pb.init(ldb);
   auto issue_half = [&](int h, int i) {  // copy instruction i of half-stage h
     const uint32_t koff = (uint32_t)((h >> 1) * BK * (int)sizeof(T));
     const uint32_t so = ring_off + (uint32_t)((h % kSlots) * kSlot) * 16u;
@@ -680,19 +700,36 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
     wout = sg.w + (int64_t)(u - sg.first) * ca.unit_elems;
   }
   const bool vec_w = (ca.cols & 3) == 0;
+  // bf16 auxiliary input (A for POLY, X for APPLY), row-wise, two blocks
+  // ahead: blocks 0 and 1 are issued here and block i + 2 once block i has
+  // taken its values, so the load latency is paid about once per tile.
+  constexpr bool kAuxB = PHASE != GRAM && kBF;
+  uint2 auxr[kAuxB ? 2 : 1][NIT];
+  const uint16_t* const aux_p =
+      kAuxB ? static_cast<const uint16_t*>(g.aux16) + (int64_t)u * g.aux_ustride + ncol : nullptr;
+  auto load_aux = [&](int i) {
+#pragma unroll
+    for (int it = 0; it < NIT; ++it)
+      auxr[i & 1][it] = *reinterpret_cast<const uint2*>(
+          aux_p + (int64_t)(m0 + wm * WT + i * 32 + it * RPI + rl) * g.ldaux);
+  };
+  if constexpr (kAuxB) {
+    load_aux(0);
+    if (FM > 1) load_aux(1);
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
     const int mrow0 = m0 + wm * WT + i * 32;  // first global row of the block
-    // auxiliary input of the block, row-wise (issued before the staging)
+    // auxiliary input of the block, row-wise (fp32: issued before the staging)
     float4 aux[NIT];
-    if constexpr (PHASE != GRAM && kBF) {
-      const uint16_t* ap = static_cast<const uint16_t*>(g.aux16) + (int64_t)u * g.aux_ustride + ncol;
+    if constexpr (kAuxB) {
 #pragma unroll
       for (int it = 0; it < NIT; ++it) {
-        const uint2 h = *reinterpret_cast<const uint2*>(ap + (int64_t)(mrow0 + it * RPI + rl) * g.ldaux);
+        const uint2 h = auxr[i & 1][it];
         aux[it] = make_float4(bf16_bits_to_f32(h.x & 0xffffu), bf16_bits_to_f32(h.x >> 16),
                               bf16_bits_to_f32(h.y & 0xffffu), bf16_bits_to_f32(h.y >> 16));
       }
+      if (i + 2 < FM) load_aux(i + 2);
     } else if constexpr (PHASE != GRAM) {
       const float* ap = g.aux + (int64_t)u * g.aux_ustride + ncol;
 #pragma unroll
@@ -1214,12 +1251,6 @@ __global__ __launch_bounds__(kThreads) void ns_persistent(NsSched p, ChunkArgs c
   uint32_t next_raw = 0u, err_raw = 0u;
   for (;;) {
     if (wave == 0) {
-      if (pending >= 0) {
-        // Every wave's stores are complete (the barrier that ended the
-        // tile); with one queue they are written back to memory first.
-        if (!local) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        __hip_atomic_fetch_add(p.done + pending, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
       if (!have_next) {
         next_raw = __hip_atomic_fetch_add(p.queue + q, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         err_raw = __hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1227,10 +1258,18 @@ __global__ __launch_bounds__(kThreads) void ns_persistent(NsSched p, ChunkArgs c
       int item = __builtin_amdgcn_readfirstlane((int)next_raw);
       if (__builtin_amdgcn_readfirstlane(err_raw) != 0u) item = -1;
       s_item = item;  // every lane writes the same value
+      // Count the finished tile after reading the claim, so that the wait
+      // for the claim's value does not also wait for this atomic.
+      if (pending >= 0) {
+        // Every wave's stores are complete (the barrier that ended the
+        // tile); with one queue they are written back to memory first.
+        if (!local) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        __hip_atomic_fetch_add(p.done + pending, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
     have_next = false;
     pending = -1;
-    __syncthreads();
+    lds_barrier();
     const int item = __builtin_amdgcn_readfirstlane(s_item);
     const int per_iter = uq * per_unit;
     if (item < 0) break;  // stopped
@@ -1302,9 +1341,9 @@ __global__ __launch_bounds__(kThreads) void ns_persistent(NsSched p, ChunkArgs c
       }
       s_go = go;
     }
-    __syncthreads();
+    lds_barrier();
     const int go = __builtin_amdgcn_readfirstlane(s_go);
-    __syncthreads();  // every wave has read the broadcast words
+    lds_barrier();  // every wave has read the broadcast words
     if (!go) break;
     // Make the other workgroups' results visible to this wave's loads
     // (acquire at agent scope: the L1 must be dropped in any case, and a
