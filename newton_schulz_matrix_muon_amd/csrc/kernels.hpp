@@ -337,8 +337,12 @@ __global__ __launch_bounds__(kThreads) void k_normalize(ChunkArgs ca, float* __r
 
 // ------------------------------------------------------------------ GEMM ---
 // Batched C = A_op * B_op^T over padded units (both operands K-contiguous),
-// one TILE x TILE output tile per workgroup of 4 waves (2 x 2, each
-// TILE/2 x TILE/2 as 32x32 MFMA blocks).
+// one TILE x TILE output tile per workgroup.  256 tiles take 8 waves in a
+// 4 x 2 grid (64 x 128 each), two per SIMD: a copy instruction holds up the
+// issue of its wave for tens of cycles, and the other wave of the SIMD
+// keeps the matrix core busy meanwhile (with one wave per SIMD the copies'
+// issue time adds to the MFMA time).  128 tiles take 4 waves (2 x 2, 64 x
+// 64 each).  Each wave's share is a grid of 32x32 MFMA blocks.
 //
 // LDS: a ring of kSlots half-stages; a half-stage holds TILE rows of one
 // operand, a row being 128 bytes of K (64 bf16 or 32 fp32) in eight 16-byte
@@ -387,9 +391,15 @@ __device__ __forceinline__ u32x4 tile_rsrc(const void* base) {
   return u32x4{lo, hi & 0xFFFFu, 0x7FFFFFFFu, 0x00020000u};
 }
 
+// Waves and threads of a GEMM workgroup.
+template <int TILE>
+constexpr int gemm_waves() { return TILE == 256 ? 8 : 4; }
+template <int TILE>
+constexpr int gemm_threads() { return 64 * gemm_waves<TILE>(); }
+
 // Copy instructions per wave for one half-stage (TILE rows x 128 bytes).
 template <int TILE>
-constexpr int dma_per_wave() { return TILE / 32; }
+constexpr int dma_per_wave() { return TILE * kRowChunks / (64 * gemm_waves<TILE>()); }
 
 // One operand's share of a half-stage for this wave: TILE rows of the tile
 // (resource based at its first row) x 128 bytes of K, eight lanes per row so
@@ -456,15 +466,6 @@ __device__ __forceinline__ void mfma_one(const u32x4& af, const u32x4& bf, f32x1
   }
 }
 
-template <typename T, int FM>
-__device__ __forceinline__ void mfma_block(const u32x4 (&af)[FM], const u32x4 (&bf)[FM],
-                                           f32x16 (&acc)[FM][FM]) {
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FM; ++j) mfma_one<T>(af[i], bf[j], acc[i][j]);
-}
-
 __device__ __forceinline__ void store_bf16x4(void* base, int64_t idx, float a, float b, float c,
                                              float d) {
   uint2 p;
@@ -506,7 +507,7 @@ __device__ __forceinline__ void zero_unit_tile(const ChunkArgs& ca, int final_mo
                                                int n0) {
   const SegView sg = find_seg(ca, u);
   float* wout = sg.w + (int64_t)(u - sg.first) * ca.unit_elems;
-  for (int idx = threadIdx.x; idx < TILE * TILE; idx += kThreads) {
+  for (int idx = threadIdx.x; idx < TILE * TILE; idx += gemm_threads<TILE>()) {
     const int mm = m0 + idx / TILE, nn = n0 + idx % TILE;
     if (mm < ca.rows && nn < ca.cols) {
       float* p = wout + (int64_t)mm * ca.cols + nn;
@@ -519,16 +520,25 @@ __device__ __forceinline__ void zero_unit_tile(const ChunkArgs& ca, int final_mo
 // workgroup calls it; it starts by overwriting the LDS stage buffers, so the
 // caller makes sure no wave still reads them (a barrier after the previous
 // tile's epilogue).
-template <int PHASE, typename T, int TILE>
+struct NoHook {
+  __device__ __forceinline__ void operator()() const {}
+};
+
+// `issued` runs once the prologue's copies are in flight (the persistent
+// schedule claims its next item there, so that the claim's round trip
+// overlaps the copies' latency).
+template <int PHASE, typename T, int TILE, typename Hook = NoHook>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca, int u, int tm,
-                                          int tn) {
-  constexpr int WT = TILE / 2;   // wave tile
-  constexpr int FM = WT / 32;    // 32x32 blocks per wave side
+                                          int tn, const Hook& issued = Hook()) {
+  constexpr int NW = gemm_waves<TILE>();
+  constexpr int WM = TILE / (NW / 2);  // wave tile rows (waves in a (NW/2) x 2 grid)
+  constexpr int WN = TILE / 2;         // wave tile columns
+  constexpr int FA = WM / 32;          // 32x32 blocks per wave: FA rows x FB columns
+  constexpr int FB = WN / 32;
   constexpr bool kBF = sizeof(T) == 2;
   constexpr int BK = OpT<T>::kBK;
   constexpr int NI = dma_per_wave<TILE>();     // copies per wave per half-stage
   constexpr int kSlot = TILE * kRowChunks;     // 16-byte slots per ring slot
-  constexpr int kMf = FM * FM * (kBF ? 1 : 4); // MFMAs per K sub-step
   u32x4* const ring = lds_ring<TILE>;
   const uint32_t ring_off = (uint32_t)(uintptr_t)(lds_vptr)lds_ring<TILE>;
   const int m0 = tm * TILE, n0 = tn * TILE;
@@ -545,11 +555,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
   const u32x4 rsa = tile_rsrc(A + (int64_t)m0 * g.lda);
   const u32x4 rsb = tile_rsrc(B + (int64_t)n0 * g.ldb);
 
-  f32x16 acc[FM][FM];
+  f32x16 acc[FA][FB];
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < FA; ++i)
 #pragma unroll
-    for (int j = 0; j < FM; ++j)
+    for (int j = 0; j < FB; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
@@ -575,19 +585,28 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
   };
 
   // Schedule of stage k (four K sub-steps kk0..kk3 of 16 bf16 / 8 fp32):
-  //   sub-steps 0-2: read the fragments of kk(s+1) | MFMAs of kk(s)
-  //   wait for this wave's copies of stage k+1 (half-stage 2k+4, if any,
-  //   may stay in flight); s_barrier: stage k+1 is complete and every wave
-  //   is done reading stage k
-  //   sub-step 3: copies of half-stages 2k+5 and 2k+6 into stage k's slots,
-  //   interleaved with the reads of kk0(k+1) and the MFMAs of kk3(k)
-  // The barrier sits between MFMA groups whose operands are already in
-  // registers, so the fragment reads after it hide under MFMAs, and 1.5 to
-  // 2.5 stages of copies stay in flight.
-  const int arow0 = wm * WT + (lane & 31);
-  const int brow0 = wn * WT + (lane & 31);
+  //   sub-steps 0-2: read the fragments of kk(s+1) | MFMAs of kk(s), with
+  //   the copies of half-stage 2k+4 (A of stage k+2) spread over them, into
+  //   the slot of half 2k-1, which the previous stage's barrier released
+  //   wait for this wave's copies of stage k+1 (half-stage 2k+4 may stay in
+  //   flight); s_barrier: stage k+1 is complete and every wave is done
+  //   reading stage k
+  //   sub-step 3: copies of half-stage 2k+5 (B of stage k+2) into the slot
+  //   of half 2k, interleaved with the reads of kk0(k+1) and the MFMAs of
+  //   kk3(k)
+  // A copy instruction holds up its wave's issue until the address unit
+  // takes it, so the copies are spread over the whole stage rather than
+  // bunched after the barrier.  The barrier sits between MFMA groups whose
+  // operands are already in registers, so the fragment reads after it hide
+  // under MFMAs.
+  const int arow0 = wm * WM + (lane & 31);
+  const int brow0 = wn * WN + (lane & 31);
   const int half = lane >> 5;
-  u32x4 af[2][FM], bf[2][FM];
+  // Waves w and w + 4 share a SIMD: the second one issues its copies half
+  // a copy interval later, so that the two do not wait on the address unit
+  // at the same time.
+  const bool second = NW == 8 && wid >= 4;
+  u32x4 af[2][FA], bf[2][FB];
   auto read_a = [&](const u32x4* S, int kk, int slot, int i) {
     const int r = arow0 + i * 32;
     af[slot][i] = S[r * kRowChunks + swz(r, 2 * kk + half)];
@@ -597,25 +616,25 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
     bf[slot][i] = S[r * kRowChunks + swz(r, 2 * kk + half)];
   };
 
-  // Prologue: half-stages 0..4.  The scalar (kernel-argument) loads are
-  // drained as well: one still in flight would turn every LDS wait of the
-  // loop into a full wait.
+  // Prologue: half-stages 0..3 (nh >= 4).  The scalar (kernel-argument)
+  // loads are drained as well: one still in flight would turn every LDS
+  // wait of the loop into a full wait.
 #pragma unroll
-  for (int h = 0; h < kSlots; ++h)
-    if (h < nh)
+  for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int i = 0; i < NI; ++i) issue_half(h, i);
-  if (nh >= 5)
-    wait_vmcnt<3 * NI>();
-  else
-    wait_vmcnt<2 * NI>();  // nh == 4
+    for (int i = 0; i < NI; ++i) issue_half(h, i);
+  issued();
+#pragma unroll
+  for (int h = 2; h < 4; ++h)
+#pragma unroll
+    for (int i = 0; i < NI; ++i) issue_half(h, i);
+  wait_vmcnt<2 * NI>();
   wait_lgkm0();
   __builtin_amdgcn_s_barrier();
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    read_a(ring, 0, 0, i);
-    read_b(ring + kSlot, 0, 0, i);
-  }
+  for (int i = 0; i < FA; ++i) read_a(ring, 0, 0, i);
+#pragma unroll
+  for (int j = 0; j < FB; ++j) read_b(ring + kSlot, 0, 0, j);
 
   int sa = 0, sb = 1;  // ring slots of stage k
   for (int k = 0; k < nk; ++k) {
@@ -623,18 +642,31 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
     const u32x4* SB = ring + sb * kSlot;
     const int na = sa + 2 >= kSlots ? sa + 2 - kSlots : sa + 2;
     const int nb = sb + 2 >= kSlots ? sb + 2 - kSlots : sb + 2;
+    const int ha = 2 * k + 4;
+    const bool more_a = ha < nh;
 #pragma unroll
     for (int ss = 0; ss < 3; ++ss) {
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        read_a(SA, ss + 1, (ss + 1) & 1, i);
-        read_b(SB, ss + 1, (ss + 1) & 1, i);
-      }
-      mfma_block<T, FM>(af[ss & 1], bf[ss & 1], acc);
-      __builtin_amdgcn_sched_group_barrier(0x100, 2 * FM, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, kMf, 0);
+      for (int i = 0; i < FA; ++i) read_a(SA, ss + 1, (ss + 1) & 1, i);
+#pragma unroll
+      for (int j = 0; j < FB; ++j) read_b(SB, ss + 1, (ss + 1) & 1, j);
       __builtin_amdgcn_sched_barrier(0);
+      // this sub-step's share of the copies of half-stage ha, spread over
+      // its MFMA blocks
+      constexpr int M = FA * FB;
+      const int c0 = ss * NI / 3, c1 = (ss + 1) * NI / 3;
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+#pragma unroll
+        for (int c = c0; c < c1; ++c) {
+          const int at = (c - c0) * M / (c1 - c0);
+          const int later = at + M / (c1 - c0) / 2;
+          if (more_a && ((!second && m == at) || (second && m == later))) issue_half(ha, c);
+        }
+        mfma_one<T>(af[ss & 1][m / FB], bf[ss & 1][m % FB], acc[m / FB][m % FB]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
     // Publish stage k+1 (for the last stage this only drains the copies;
     // the reads below then touch stale slots whose values go unused, which
@@ -647,31 +679,31 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     {
-      const int h0 = 2 * k + 5, h1 = 2 * k + 6;
-      const bool more0 = h0 < nh, more1 = h1 < nh;
+      const int h0 = 2 * k + 5;
+      const bool more0 = h0 < nh;
       const u32x4* NA = ring + na * kSlot;
       const u32x4* NB = ring + nb * kSlot;
-      constexpr int C = 2 * NI;      // chunks: one copy instruction each
-      constexpr int R = 2 * FM;      // fragment reads
-      constexpr int M = FM * FM;     // MFMA blocks
-      static_assert(C % R == 0, "reads spread evenly over the chunks");
+      constexpr int C = NI;          // copy instructions
+      constexpr int R = FA + FB;     // fragment reads
+      constexpr int M = FA * FB;     // MFMA blocks
+      static_assert(M >= C && M >= R, "at most one copy and one read per MFMA block");
 #pragma unroll
-      for (int c = 0; c < C; ++c) {
-        if (c < NI) {
-          if (more0) issue_half(h0, c);
-        } else {
-          if (more1) issue_half(h1, c - NI);
-        }
-        if (c % (C / R) == 0) {
-          const int r = c / (C / R);
-          if (r < FM)
-            read_a(NA, 0, 0, r);
-          else
-            read_b(NB, 0, 0, r - FM);
+      for (int m = 0; m < M; ++m) {
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+          const int at = c * M / C, later = at + M / C / 2;
+          if (more0 && ((!second && m == at) || (second && m == later))) issue_half(h0, c);
         }
 #pragma unroll
-        for (int m = c * M / C; m < (c + 1) * M / C; ++m)
-          mfma_one<T>(af[1][m / FM], bf[1][m % FM], acc[m / FM][m % FM]);
+        for (int r = 0; r < R; ++r) {
+          if (m == r * M / R) {
+            if (r < FA)
+              read_a(NA, 0, 0, r);
+            else
+              read_b(NB, 0, 0, r - FA);
+          }
+        }
+        mfma_one<T>(af[1][m / FB], bf[1][m % FB], acc[m / FB][m % FB]);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -682,15 +714,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
   // ---- epilogue.  Each wave stages one 32-row block of its accumulators at
   // a time in its own LDS region (lane (m, half) holds C[m][n..n+3]), then
   // reads it back row-wise so that every global load and store covers whole
-  // row segments (WT/4 lanes per row, 16 bytes per lane); the transposed
+  // row segments (WN/4 lanes per row, 16 bytes per lane); the transposed
   // copy reads the staged block column-wise.
-  constexpr int LDW = WT + 4;     // padded row stride (floats)
-  constexpr int LPR = WT / 4;     // lanes per row
+  constexpr int LDW = WN + 4;     // padded row stride (floats)
+  constexpr int LPR = WN / 4;     // lanes per row
   constexpr int RPI = 64 / LPR;   // rows per instruction
   constexpr int NIT = 32 / RPI;   // row-wise iterations per block
   const int rl = lane / LPR;            // row within an instruction
   const int cl = (lane % LPR) * 4;      // first column of the lane
-  const int ncol = n0 + wn * WT + cl;   // global column of the lane's first element
+  const int ncol = n0 + wn * WN + cl;   // global column of the lane's first element
   wait_lgkm0();
   __builtin_amdgcn_s_barrier();  // every wave is done with the stage buffers
   float* ep = reinterpret_cast<float*>(ring) + wid * (32 * LDW);
@@ -711,26 +743,28 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
 #pragma unroll
     for (int it = 0; it < NIT; ++it)
       auxr[i & 1][it] = *reinterpret_cast<const uint2*>(
-          aux_p + (int64_t)(m0 + wm * WT + i * 32 + it * RPI + rl) * g.ldaux);
+          aux_p + (int64_t)(m0 + wm * WM + i * 32 + it * RPI + rl) * g.ldaux);
   };
   if constexpr (kAuxB) {
     load_aux(0);
-    if (FM > 1) load_aux(1);
+    if (FA > 1) load_aux(1);
   }
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int mrow0 = m0 + wm * WT + i * 32;  // first global row of the block
-    // auxiliary input of the block, row-wise (fp32: issued before the staging)
-    float4 aux[NIT];
-    if constexpr (kAuxB) {
-#pragma unroll
-      for (int it = 0; it < NIT; ++it) {
+  for (int i = 0; i < FA; ++i) {
+    const int mrow0 = m0 + wm * WM + i * 32;  // first global row of the block
+    // auxiliary input of the block, row-wise (fp32: issued before the
+    // staging; bf16: converted as the row pass uses it)
+    float4 aux[(PHASE != GRAM && !kBF) ? NIT : 1];
+    auto aux_at = [&](int it) -> float4 {
+      if constexpr (kAuxB) {
         const uint2 h = auxr[i & 1][it];
-        aux[it] = make_float4(bf16_bits_to_f32(h.x & 0xffffu), bf16_bits_to_f32(h.x >> 16),
-                              bf16_bits_to_f32(h.y & 0xffffu), bf16_bits_to_f32(h.y >> 16));
+        return make_float4(bf16_bits_to_f32(h.x & 0xffffu), bf16_bits_to_f32(h.x >> 16),
+                           bf16_bits_to_f32(h.y & 0xffffu), bf16_bits_to_f32(h.y >> 16));
+      } else {
+        return aux[(PHASE != GRAM && !kBF) ? it : 0];
       }
-      if (i + 2 < FM) load_aux(i + 2);
-    } else if constexpr (PHASE != GRAM) {
+    };
+    if constexpr (PHASE != GRAM && !kBF) {
       const float* ap = g.aux + (int64_t)u * g.aux_ustride + ncol;
 #pragma unroll
       for (int it = 0; it < NIT; ++it)
@@ -738,7 +772,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
     }
     // stage the block
 #pragma unroll
-    for (int j = 0; j < FM; ++j)
+    for (int j = 0; j < FB; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         const f32x16& c = acc[i][j];
@@ -755,7 +789,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
       const int64_t o = (int64_t)u * g.out_ustride + (int64_t)m * g.ldo + ncol;
       if constexpr (PHASE == GRAM || PHASE == POLY) {
         if constexpr (PHASE == POLY) {
-          const float4 a = aux[it];
+          const float4 a = aux_at(it);
           v0 = g.cb * a.x + g.cc * v0;
           v1 = g.cb * a.y + g.cc * v1;
           v2 = g.cb * a.z + g.cc * v2;
@@ -768,7 +802,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
         else
           *reinterpret_cast<float4*>(g.out32 + o) = make_float4(v0, v1, v2, v3);
       } else {
-        const float4 a = aux[it];
+        const float4 a = aux_at(it);
         v0 = __builtin_fmaf(g.ca, a.x, v0);
         v1 = __builtin_fmaf(g.ca, a.y, v1);
         v2 = __builtin_fmaf(g.ca, a.z, v2);
@@ -806,17 +840,20 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
         }
       }
     }
+    if constexpr (kAuxB) {
+      if (i + 2 < FA) load_aux(i + 2);  // the row pass has taken block i's values
+    }
     if constexpr (PHASE == GRAM || PHASE == POLY) {
       if (g.sym && tm != tn) {
-        // mirror tile: rows n0 + wn*WT .. +WT, columns mrow0 .. +32, read
+        // mirror tile: rows n0 + wn*WN .. +WN, columns mrow0 .. +32, read
         // column-wise from the staged block (8 lanes per row, 4 columns each)
         const int cm = (lane & 7) * 4;
 #pragma unroll
-        for (int it = 0; it < WT / 8; ++it) {
+        for (int it = 0; it < WN / 8; ++it) {
           const int nn = it * 8 + (lane >> 3);
           const float a0 = ep[(cm + 0) * LDW + nn], a1 = ep[(cm + 1) * LDW + nn];
           const float a2 = ep[(cm + 2) * LDW + nn], a3 = ep[(cm + 3) * LDW + nn];
-          const int64_t om = (int64_t)u * g.out_ustride + (int64_t)(n0 + wn * WT + nn) * g.ldo + mrow0 + cm;
+          const int64_t om = (int64_t)u * g.out_ustride + (int64_t)(n0 + wn * WN + nn) * g.ldo + mrow0 + cm;
           if constexpr (kBF)
             store_bf16x4(g.out16, om, a0, a1, a2, a3);
           else
@@ -826,15 +863,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
     }
     if constexpr (PHASE == APPLY) {
       if (g.final_mode == FINAL_NONE) {
-        // X'^T rows n0 + wn*WT .. +WT, columns mrow0 .. +32: 8 lanes per
+        // X'^T rows n0 + wn*WN .. +WN, columns mrow0 .. +32: 8 lanes per
         // row, 4 consecutive columns (staged rows) per lane.
         const int cm = (lane & 7) * 4;
 #pragma unroll
-        for (int it = 0; it < WT / 8; ++it) {
+        for (int it = 0; it < WN / 8; ++it) {
           const int nn = it * 8 + (lane >> 3);
           const float a0 = ep[(cm + 0) * LDW + nn], a1 = ep[(cm + 1) * LDW + nn];
           const float a2 = ep[(cm + 2) * LDW + nn], a3 = ep[(cm + 3) * LDW + nn];
-          const int64_t ot = (int64_t)u * g.out_ustride + (int64_t)(n0 + wn * WT + nn) * g.ldt + mrow0 + cm;
+          const int64_t ot = (int64_t)u * g.out_ustride + (int64_t)(n0 + wn * WN + nn) * g.ldt + mrow0 + cm;
           if constexpr (kBF)
             store_bf16x4(g.outt, ot, a0, a1, a2, a3);
           else
@@ -859,7 +896,7 @@ __device__ __forceinline__ void sym_tile(int t, int T, int& tm, int& tn) {
 
 // One launch per product: workgroup -> (unit, tile), XCD-aware.
 template <int PHASE, typename T, int TILE>
-__global__ __launch_bounds__(kThreads) void ns_gemm(GemmArgs g, ChunkArgs ca) {
+__global__ __launch_bounds__(gemm_threads<TILE>()) void ns_gemm(GemmArgs g, ChunkArgs ca) {
   const int tiles_per_unit = g.sym ? g.tiles_m * (g.tiles_m + 1) / 2 : g.tiles_m * g.tiles_n;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
   const int u = logical / tiles_per_unit;
@@ -1217,7 +1254,7 @@ __device__ __forceinline__ int xcc_id() {
 }
 
 template <typename T, int TILE>
-__global__ __launch_bounds__(kThreads) void ns_persistent(NsSched p, ChunkArgs ca) {
+__global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p, ChunkArgs ca) {
   // Every branch below is uniform across the workgroup or across a wave:
   // the scheduling work (claim, completion count, dependency wait) is done
   // by all of wave 0 with only lane 0 contributing to the atomics, never
@@ -1242,9 +1279,10 @@ __global__ __launch_bounds__(kThreads) void ns_persistent(NsSched p, ChunkArgs c
   int uq = units_of(q);
   int pending = -1;      // unit whose finished tile wave 0 has yet to count
   bool alone = false;    // running unclaimed queues after every other workgroup left
-  // Wave 0 claims the next item (and reads the error word) as soon as the
-  // current one may start, so the round trip overlaps the tile.  Holding
-  // one claimed item ahead cannot stall the schedule: the earliest
+  // Wave 0 claims the next item (and reads the error word) once the current
+  // tile's first copies are in flight, so that the round trip overlaps
+  // their latency.  Holding one claimed item ahead cannot stall the
+  // schedule: the earliest
   // unfinished item in claim order is always some workgroup's current one
   // (a held item comes after its holder's current, unfinished item).
   bool have_next = false;
@@ -1255,7 +1293,7 @@ __global__ __launch_bounds__(kThreads) void ns_persistent(NsSched p, ChunkArgs c
         next_raw = __hip_atomic_fetch_add(p.queue + q, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         err_raw = __hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
-      int item = __builtin_amdgcn_readfirstlane((int)next_raw);
+      int item = (int)__builtin_amdgcn_readfirstlane(next_raw);
       if (__builtin_amdgcn_readfirstlane(err_raw) != 0u) item = -1;
       s_item = item;  // every lane writes the same value
       // Count the finished tile after reading the claim, so that the wait
@@ -1349,11 +1387,15 @@ __global__ __launch_bounds__(kThreads) void ns_persistent(NsSched p, ChunkArgs c
     // (acquire at agent scope: the L1 must be dropped in any case, and a
     // workgroup-scope invalidate does not reach it).
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    if (wave == 0) {
-      next_raw = __hip_atomic_fetch_add(p.queue + q, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      err_raw = __hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      have_next = true;
-    }
+    // Wave 0 claims the next item once the tile's first copies are in
+    // flight (a zero unit's item runs no tile; the next head claims).
+    auto claim_next = [&]() {
+      if (wave == 0) {
+        next_raw = __hip_atomic_fetch_add(p.queue + q, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        err_raw = __hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        have_next = true;
+      }
+    };
     const int cur = it & 1;
     if (phase == GRAM) {
       if (live) {
@@ -1361,7 +1403,7 @@ __global__ __launch_bounds__(kThreads) void ns_persistent(NsSched p, ChunkArgs c
         g.a = g.b = cur ? p.gram_op[1] : p.gram_op[0];
         int tm, tn;
         sym_tile(t, g.tiles_m, tm, tn);
-        gemm_tile<GRAM, T, TILE>(g, ca, u, tm, tn);
+        gemm_tile<GRAM, T, TILE>(g, ca, u, tm, tn, claim_next);
       }
     } else if (phase == POLY) {
       if (live) {
@@ -1377,7 +1419,7 @@ __global__ __launch_bounds__(kThreads) void ns_persistent(NsSched p, ChunkArgs c
         g.cc = cc;
         int tm, tn;
         sym_tile(t, g.tiles_m, tm, tn);
-        gemm_tile<POLY, T, TILE>(g, ca, u, tm, tn);
+        gemm_tile<POLY, T, TILE>(g, ca, u, tm, tn, claim_next);
       }
     } else {
       const int fm = it == p.n_iter - 1 ? p.final_mode : (int)FINAL_NONE;
@@ -1397,7 +1439,7 @@ __global__ __launch_bounds__(kThreads) void ns_persistent(NsSched p, ChunkArgs c
         g.outt = cur ? p.app_outt[1] : p.app_outt[0];
         g.aux = cur ? p.app_aux[1] : p.app_aux[0];
         g.aux16 = cur ? p.app_aux16[1] : p.app_aux16[0];
-        gemm_tile<APPLY, T, TILE>(g, ca, u, tm, tn);
+        gemm_tile<APPLY, T, TILE>(g, ca, u, tm, tn, claim_next);
       } else if (fm != FINAL_NONE) {
         zero_unit_tile<TILE>(ca, fm, u, tm * TILE, tn * TILE);
       }

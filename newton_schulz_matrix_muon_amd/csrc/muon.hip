@@ -320,7 +320,8 @@ DeviceInfo g_dev[kMaxDevices];
 template <typename T, int TILE>
 int resident_of(int cus) {
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ns_persistent<T, TILE>, kThreads, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ns_persistent<T, TILE>,
+                                                   gemm_threads<TILE>(), 0) !=
           hipSuccess ||
       per_cu < 1)
     per_cu = 1;
@@ -358,9 +359,9 @@ void launch_gemm(int tile, const GemmArgs& g, const ChunkArgs& ca, hipStream_t s
   const int per_unit = g.sym ? g.tiles_m * (g.tiles_m + 1) / 2 : g.tiles_m * g.tiles_n;
   const int grid = g.n_units * per_unit;
   if (tile == 256)
-    hipLaunchKernelGGL((ns_gemm<PHASE, T, 256>), dim3(grid), dim3(kThreads), 0, s, g, ca);
+    hipLaunchKernelGGL((ns_gemm<PHASE, T, 256>), dim3(grid), dim3(gemm_threads<256>()), 0, s, g, ca);
   else
-    hipLaunchKernelGGL((ns_gemm<PHASE, T, 128>), dim3(grid), dim3(kThreads), 0, s, g, ca);
+    hipLaunchKernelGGL((ns_gemm<PHASE, T, 128>), dim3(grid), dim3(gemm_threads<128>()), 0, s, g, ca);
 }
 
 template <int PHASE>
@@ -619,14 +620,14 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
     tr.before(MUON_KERNEL_NS);
     if (bf16) {
       if (T == 256)
-        hipLaunchKernelGGL((ns_persistent<__bf16, 256>), dim3(grid), dim3(kThreads), 0, s, p, ca);
+        hipLaunchKernelGGL((ns_persistent<__bf16, 256>), dim3(grid), dim3(gemm_threads<256>()), 0, s, p, ca);
       else
-        hipLaunchKernelGGL((ns_persistent<__bf16, 128>), dim3(grid), dim3(kThreads), 0, s, p, ca);
+        hipLaunchKernelGGL((ns_persistent<__bf16, 128>), dim3(grid), dim3(gemm_threads<128>()), 0, s, p, ca);
     } else {
       if (T == 256)
-        hipLaunchKernelGGL((ns_persistent<float, 256>), dim3(grid), dim3(kThreads), 0, s, p, ca);
+        hipLaunchKernelGGL((ns_persistent<float, 256>), dim3(grid), dim3(gemm_threads<256>()), 0, s, p, ca);
       else
-        hipLaunchKernelGGL((ns_persistent<float, 128>), dim3(grid), dim3(kThreads), 0, s, p, ca);
+        hipLaunchKernelGGL((ns_persistent<float, 128>), dim3(grid), dim3(gemm_threads<128>()), 0, s, p, ca);
     }
     tr.after(MUON_KERNEL_NS);
     return hipGetLastError() == hipSuccess ? MUON_OK : MUON_ERR_HIP;
