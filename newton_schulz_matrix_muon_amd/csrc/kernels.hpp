@@ -524,12 +524,14 @@ struct NoHook {
   __device__ __forceinline__ void operator()() const {}
 };
 
-// `issued` runs once the prologue's copies are in flight (the persistent
-// schedule claims its next item there, so that the claim's round trip
-// overlaps the copies' latency).
-template <int PHASE, typename T, int TILE, typename Hook = NoHook>
+// `issued` runs once the prologue's first copies are in flight (the
+// persistent schedule claims its next item there, so that the claim's round
+// trip overlaps the copies' latency); `ready` runs after the prologue's
+// barrier, when every wave's older memory accesses are complete.
+template <int PHASE, typename T, int TILE, typename Hook = NoHook, typename Hook2 = NoHook>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca, int u, int tm,
-                                          int tn, const Hook& issued = Hook()) {
+                                          int tn, const Hook& issued = Hook(),
+                                          const Hook2& ready = Hook2()) {
   constexpr int NW = gemm_waves<TILE>();
   constexpr int WM = TILE / (NW / 2);  // wave tile rows (waves in a (NW/2) x 2 grid)
   constexpr int WN = TILE / 2;         // wave tile columns
@@ -631,6 +633,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
   wait_vmcnt<2 * NI>();
   wait_lgkm0();
   __builtin_amdgcn_s_barrier();
+  ready();
 #pragma unroll
   for (int i = 0; i < FA; ++i) read_a(ring, 0, 0, i);
 #pragma unroll
@@ -1277,8 +1280,30 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
   auto units_of = [&](int qq) { return ca.n_units > qq ? (ca.n_units - qq + nq - 1) / nq : 0; };
   int q = local ? xcc_id() % nq : 0;
   int uq = units_of(q);
-  int pending = -1;      // unit whose finished tile wave 0 has yet to count
+  // A finished tile is counted (its unit's completion count raised) once
+  // every wave's stores of it are complete.  With XCC-local queues the
+  // count is deferred into the next tile's prologue, whose in-order copy
+  // wait covers the stores; it is made at once (a flush) before any wait
+  // that could block, before an item that runs no tile and on every exit,
+  // so no workgroup ever blocks while holding an uncounted tile.  With one
+  // queue the release also writes the L2 back, and tiles are flushed as
+  // they end.
+  int pending = -1;      // unit of the finished tile not yet counted
   bool alone = false;    // running unclaimed queues after every other workgroup left
+  auto count_pending = [&]() {  // wave 0; every wave's stores of the tile are complete
+    if (wave == 0 && pending >= 0) {
+      if (!local) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      __hip_atomic_fetch_add(p.done + pending, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    pending = -1;
+  };
+  auto flush = [&]() {  // every wave
+    if (pending >= 0) {
+      wait_vmcnt<0>();
+      __syncthreads();
+      count_pending();
+    }
+  };
   // Wave 0 claims the next item (and reads the error word) once the current
   // tile's first copies are in flight, so that the round trip overlaps
   // their latency.  Holding one claimed item ahead cannot stall the
@@ -1296,20 +1321,12 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
       int item = (int)__builtin_amdgcn_readfirstlane(next_raw);
       if (__builtin_amdgcn_readfirstlane(err_raw) != 0u) item = -1;
       s_item = item;  // every lane writes the same value
-      // Count the finished tile after reading the claim, so that the wait
-      // for the claim's value does not also wait for this atomic.
-      if (pending >= 0) {
-        // Every wave's stores are complete (the barrier that ended the
-        // tile); with one queue they are written back to memory first.
-        if (!local) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        __hip_atomic_fetch_add(p.done + pending, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
     }
     have_next = false;
-    pending = -1;
     lds_barrier();
     const int item = __builtin_amdgcn_readfirstlane(s_item);
     const int per_iter = uq * per_unit;
+    if (item < 0 || item >= p.n_iter * per_iter) flush();
     if (item < 0) break;  // stopped
     if (item >= p.n_iter * per_iter) {
       // This queue is drained.
@@ -1358,9 +1375,22 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
     // A zero unit computes nothing, so its items wait for nothing.
     const uint32_t need =
         (uint32_t)(it * per_unit + (phase == GRAM ? 0 : phase == POLY ? p.tg : 2 * p.tg));
+    // One look at the completion count; if the item must wait, the pending
+    // tile is counted first (it may be what the wait is for).
+    if (wave == 0) {
+      int ready = 1;
+      if (live && need > 0u)
+        ready = __builtin_amdgcn_readfirstlane(__hip_atomic_load(
+                    p.done + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) >= need;
+      s_go = ready;
+    }
+    lds_barrier();
+    const bool ready = __builtin_amdgcn_readfirstlane(s_go) != 0;
+    lds_barrier();  // every wave has read s_go
+    if (!ready || !live) flush();
     if (wave == 0) {
       int go = 1;
-      if (live && need > 0u) {
+      if (!ready) {
         const uint64_t t0 = wall_clock64();
         uint32_t d = __builtin_amdgcn_readfirstlane(
             __hip_atomic_load(p.done + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
@@ -1382,7 +1412,10 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
     lds_barrier();
     const int go = __builtin_amdgcn_readfirstlane(s_go);
     lds_barrier();  // every wave has read the broadcast words
-    if (!go) break;
+    if (!go) {
+      flush();
+      break;
+    }
     // Make the other workgroups' results visible to this wave's loads
     // (acquire at agent scope: the L1 must be dropped in any case, and a
     // workgroup-scope invalidate does not reach it).
@@ -1403,7 +1436,7 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
         g.a = g.b = cur ? p.gram_op[1] : p.gram_op[0];
         int tm, tn;
         sym_tile(t, g.tiles_m, tm, tn);
-        gemm_tile<GRAM, T, TILE>(g, ca, u, tm, tn, claim_next);
+        gemm_tile<GRAM, T, TILE>(g, ca, u, tm, tn, claim_next, count_pending);
       }
     } else if (phase == POLY) {
       if (live) {
@@ -1419,7 +1452,7 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
         g.cc = cc;
         int tm, tn;
         sym_tile(t, g.tiles_m, tm, tn);
-        gemm_tile<POLY, T, TILE>(g, ca, u, tm, tn, claim_next);
+        gemm_tile<POLY, T, TILE>(g, ca, u, tm, tn, claim_next, count_pending);
       }
     } else {
       const int fm = it == p.n_iter - 1 ? p.final_mode : (int)FINAL_NONE;
@@ -1439,18 +1472,17 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
         g.outt = cur ? p.app_outt[1] : p.app_outt[0];
         g.aux = cur ? p.app_aux[1] : p.app_aux[0];
         g.aux16 = cur ? p.app_aux16[1] : p.app_aux16[0];
-        gemm_tile<APPLY, T, TILE>(g, ca, u, tm, tn, claim_next);
+        gemm_tile<APPLY, T, TILE>(g, ca, u, tm, tn, claim_next, count_pending);
       } else if (fm != FINAL_NONE) {
         zero_unit_tile<TILE>(ca, fm, u, tm * TILE, tn * TILE);
       }
     }
-    // Every wave's stores of the tile complete before the barrier; wave 0
-    // counts the tile at the top of the next iteration.
-    wait_vmcnt<0>();
-    __syncthreads();
     if (live) pending = u;
+    if (!local) flush();
+    // The next tile's first copies overwrite the LDS that this tile's
+    // epilogue staged through; the barrier after the next claim orders them.
   }
-  // Every exit passes the claim first, which counts the pending tile.
+  // Every exit flushes the pending tile first.
 }
 
 }  // namespace muon_dev
