@@ -1310,17 +1310,20 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
   // schedule: the earliest
   // unfinished item in claim order is always some workgroup's current one
   // (a held item comes after its holder's current, unfinished item).
+  // The claimed item is kept as a scalar (-1 after an error), so that the
+  // next head reads it without waiting on memory accesses issued since.
   bool have_next = false;
-  uint32_t next_raw = 0u, err_raw = 0u;
+  int next_item = 0;
+  auto claim = [&]() {  // wave 0
+    const uint32_t raw =
+        __hip_atomic_fetch_add(p.queue + q, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t err = __hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    next_item = __builtin_amdgcn_readfirstlane(err) != 0u ? -1 : (int)__builtin_amdgcn_readfirstlane(raw);
+  };
   for (;;) {
     if (wave == 0) {
-      if (!have_next) {
-        next_raw = __hip_atomic_fetch_add(p.queue + q, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        err_raw = __hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      int item = (int)__builtin_amdgcn_readfirstlane(next_raw);
-      if (__builtin_amdgcn_readfirstlane(err_raw) != 0u) item = -1;
-      s_item = item;  // every lane writes the same value
+      if (!have_next) claim();
+      s_item = next_item;  // every lane writes the same value
     }
     have_next = false;
     lds_barrier();
@@ -1424,8 +1427,7 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
     // flight (a zero unit's item runs no tile; the next head claims).
     auto claim_next = [&]() {
       if (wave == 0) {
-        next_raw = __hip_atomic_fetch_add(p.queue + q, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        err_raw = __hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        claim();
         have_next = true;
       }
     };
