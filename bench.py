@@ -370,6 +370,10 @@ def main():
             "frac": achieved / peak,
             "traffic": traffic["bytes_per_launch"] if traffic else None,
             "flops_per_launch": flops_per_launch,
+            # the symmetric products run only their upper-triangle tiles:
+            # the FLOPs the matrix cores execute, and their share of the peak
+            "achieved_executed": exe[dominant] * iters / launches / (avg_launch_ms * 1e-3) / 1e12,
+            "frac_executed": exe[dominant] * iters / launches / (avg_launch_ms * 1e-3) / 1e12 / peak,
             "avg_launch_ms": avg_launch_ms,
             "launches_timed": len(launch_ms),
         },
