@@ -274,9 +274,10 @@ __global__ __launch_bounds__(64) void k_norm_finish(const double* __restrict__ p
 }
 
 // X0 = N * (1/nu) over the whole padded iterate (zeros in the padding):
-// in bf16 (BF16) or in place in the fp32 buffer, and X0^T in the same type.
-// One 64x64 tile per workgroup; the transpose goes through LDS so that both
-// the row-major and the transposed writes are coalesced.
+// in bf16 (BF16; the products read X itself, K-major where needed), or in
+// place in the fp32 buffer plus X0^T.  One 64x64 tile per workgroup; the
+// transpose goes through LDS so that both the row-major and the transposed
+// writes are coalesced.
 template <bool BF16>
 __global__ __launch_bounds__(kThreads) void k_normalize(ChunkArgs ca, float* __restrict__ x32,
                                                          uint16_t* __restrict__ xb,
@@ -304,19 +305,20 @@ __global__ __launch_bounds__(kThreads) void k_normalize(ChunkArgs ca, float* __r
       val.z = (c + 2 < ca.cols) ? nv.z * s : 0.f;
       val.w = (c + 3 < ca.cols) ? nv.w * s : 0.f;
     }
-    if (BF16) {
+    if constexpr (BF16) {
       uint2 packed;
       packed.x = (uint32_t)to_bf16_bits(val.x) | ((uint32_t)to_bf16_bits(val.y) << 16);
       packed.y = (uint32_t)to_bf16_bits(val.z) | ((uint32_t)to_bf16_bits(val.w) << 16);
       *reinterpret_cast<uint2*>(xb + (int64_t)u * ca.x_stride + e) = packed;
     } else {
       *reinterpret_cast<float4*>(xu + e) = val;
+      tile[rr][cc] = val.x;
+      tile[rr][cc + 1] = val.y;
+      tile[rr][cc + 2] = val.z;
+      tile[rr][cc + 3] = val.w;
     }
-    tile[rr][cc] = val.x;
-    tile[rr][cc + 1] = val.y;
-    tile[rr][cc + 2] = val.z;
-    tile[rr][cc + 3] = val.w;
   }
+  if constexpr (BF16) return;
   __syncthreads();
   // X^T (cols_pad x rows_pad): row c takes tile column c - c0.
 #pragma unroll
@@ -324,14 +326,7 @@ __global__ __launch_bounds__(kThreads) void k_normalize(ChunkArgs ca, float* __r
     const int cc = t / 16 + 16 * i, rr = (t % 16) * 4;
     const int64_t e = (int64_t)u * ca.x_stride + (int64_t)(c0 + cc) * rp + r0 + rr;
     const float a = tile[rr][cc], b = tile[rr + 1][cc], c = tile[rr + 2][cc], d = tile[rr + 3][cc];
-    if (BF16) {
-      uint2 packed;
-      packed.x = (uint32_t)to_bf16_bits(a) | ((uint32_t)to_bf16_bits(b) << 16);
-      packed.y = (uint32_t)to_bf16_bits(c) | ((uint32_t)to_bf16_bits(d) << 16);
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(xt) + e) = packed;
-    } else {
-      *reinterpret_cast<float4*>(static_cast<float*>(xt) + e) = make_float4(a, b, c, d);
-    }
+    *reinterpret_cast<float4*>(static_cast<float*>(xt) + e) = make_float4(a, b, c, d);
   }
 }
 
@@ -415,7 +410,15 @@ constexpr int dma_per_wave() { return TILE * kRowChunks / (64 * gemm_waves<TILE>
 // every copy in flight before each LDS read.  Completion is tracked with
 // explicit vmcnt waits (vmcnt counts every vector-memory instruction in
 // issue order) before the barrier that publishes a stage.
-template <typename T, int TILE>
+//
+// K-major operands (KM, bf16 only) are stored with K along the rows (the
+// iterate X read as the right operand of B*X, or both sides of X^T X): a
+// half-stage holds BK rows of K x TILE columns, a row being TILE * 2 bytes
+// in 16-byte chunks, chunk c of row k stored at c ^ (4 * (k & 3)).  Each
+// row is copied as whole 128-byte lines (the XOR keeps every aligned group
+// of eight chunks together), and the MFMA fragments are read with the
+// transposing LDS read (see read_km).
+template <typename T, int TILE, bool KM = false>
 struct DmaPlan {
   static constexpr int kN = dma_per_wave<TILE>();
   int voff[kN];
@@ -424,9 +427,17 @@ struct DmaPlan {
 #pragma unroll
     for (int i = 0; i < kN; ++i) {
       const int sl = (w * kN + i) * 64 + lane;
-      const int row = sl >> 3, pc = sl & 7;
-      const int c = pc ^ ((row >> 1) & 7);  // logical chunk stored at (row, pc)
-      voff[i] = (row * ld + c * OpT<T>::kElems) * (int)sizeof(T);
+      if constexpr (KM) {
+        static_assert(sizeof(T) == 2, "K-major operands are bf16");
+        constexpr int CPR = TILE / 8;      // 16-byte chunks per K row
+        const int kr = sl / CPR, pc = sl % CPR;
+        const int c = pc ^ (4 * (kr & 3));  // logical chunk stored at (kr, pc)
+        voff[i] = (kr * ld + c * 8) * 2;
+      } else {
+        const int row = sl >> 3, pc = sl & 7;
+        const int c = pc ^ ((row >> 1) & 7);  // logical chunk stored at (row, pc)
+        voff[i] = (row * ld + c * OpT<T>::kElems) * (int)sizeof(T);
+      }
     }
   }
   // Instruction i of this wave's share.
@@ -528,7 +539,9 @@ struct NoHook {
 // persistent schedule claims its next item there, so that the claim's round
 // trip overlaps the copies' latency); `ready` runs after the prologue's
 // barrier, when every wave's older memory accesses are complete.
-template <int PHASE, typename T, int TILE, typename Hook = NoHook, typename Hook2 = NoHook>
+//
+// KM: bit 0 = the A operand is K-major, bit 1 = the B operand is.
+template <int PHASE, typename T, int TILE, int KM = 0, typename Hook = NoHook, typename Hook2 = NoHook>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca, int u, int tm,
                                           int tn, const Hook& issued = Hook(),
                                           const Hook2& ready = Hook2()) {
@@ -552,10 +565,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wid >> 1, wn = wid & 1;
 
+  constexpr bool AKM = (KM & 1) != 0, BKM = (KM & 2) != 0;
+  static_assert(KM == 0 || sizeof(T) == 2, "K-major operands are bf16");
   const T* A = static_cast<const T*>(g.a) + (int64_t)u * g.a_ustride;
   const T* B = static_cast<const T*>(g.b) + (int64_t)u * g.b_ustride;
-  const u32x4 rsa = tile_rsrc(A + (int64_t)m0 * g.lda);
-  const u32x4 rsb = tile_rsrc(B + (int64_t)n0 * g.ldb);
+  // a K-major operand's tile starts at its first column, a row-major one at its first row
+  const u32x4 rsa = tile_rsrc(AKM ? A + m0 : A + (int64_t)m0 * g.lda);
+  const u32x4 rsb = tile_rsrc(BKM ? B + n0 : B + (int64_t)n0 * g.ldb);
 
   f32x16 acc[FA][FB];
 #pragma unroll
@@ -574,16 +590,19 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
   // a persistent tile loop, where they would stay live for every phase.
   int lda = g.lda, ldb = g.ldb;
   asm volatile("" : "+s"(lda), "+s"(ldb));
-  DmaPlan<T, TILE> pa, pb;
+  DmaPlan<T, TILE, AKM> pa;
+  DmaPlan<T, TILE, BKM> pb;
   pa.init(lda);
   pb.init(ldb);
   auto issue_half = [&](int h, int i) {  // copy instruction i of half-stage h
-    const uint32_t koff = (uint32_t)((h >> 1) * BK * (int)sizeof(T));
+    // K offset of the stage: along a row-major operand's rows, or whole rows
+    // of a K-major one
+    const uint32_t kst = (uint32_t)((h >> 1) * BK * (int)sizeof(T));
     const uint32_t so = ring_off + (uint32_t)((h % kSlots) * kSlot) * 16u;
     if (h & 1)
-      pb.issue_one(rsb, koff, so, i);
+      pb.issue_one(rsb, BKM ? kst * (uint32_t)ldb : kst, so, i);
     else
-      pa.issue_one(rsa, koff, so, i);
+      pa.issue_one(rsa, AKM ? kst * (uint32_t)lda : kst, so, i);
   };
 
   // Schedule of stage k (four K sub-steps kk0..kk3 of 16 bf16 / 8 fp32):
@@ -609,13 +628,57 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
   // at the same time.
   const bool second = NW == 8 && wid >= 4;
   u32x4 af[2][FA], bf[2][FB];
+  // Fragment of a K-major operand: lane (x, half) needs K rows 16kk + 8half
+  // + 0..7 of column x.  Two transposing reads (ds_read_b64_tr_b16): in
+  // each group of 16 lanes, lane 4r + q points at 4 elements of K row
+  // k0 + r, columns 4q..4q+3 of the group's 16, and lane i receives column
+  // i of those four rows.
+  // The swizzle term depends on the lane only (16kk and +4 rows keep
+  // k & 3), so each lane's byte offset within a slot is fixed per 32-column
+  // block; the sub-step and the second read are immediate offsets.
+  int kmoa[AKM ? FA : 1], kmob[BKM ? FB : 1];
+  {
+    const int gq = lane >> 4, gi = lane & 15;
+    const int kr = 8 * (gq >> 1) + (gi >> 2);  // K row of the first read in sub-step 0
+    const int x4 = 4 * (kr & 3);
+    auto km_off = [&](int colbase) {
+      const int col = colbase + 16 * (gq & 1) + 4 * (gi & 3);
+      return (kr * TILE + ((((col >> 3) ^ x4) << 3) | (col & 7))) * 2;
+    };
+    if constexpr (AKM) {
+#pragma unroll
+      for (int i = 0; i < FA; ++i) kmoa[i] = km_off(wm * WM + i * 32);
+    }
+    if constexpr (BKM) {
+#pragma unroll
+      for (int j = 0; j < FB; ++j) kmob[j] = km_off(wn * WN + j * 32);
+    }
+  }
+  auto read_km = [&](const u32x4* S, int kk, int off) -> u32x4 {
+    typedef short v4s __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4s* lds_v4s;
+    __attribute__((address_space(3))) char* base =
+        (__attribute__((address_space(3))) char*)(lds_vptr)S + off + kk * 16 * TILE * 2;
+    const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)base);
+    const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(base + 4 * TILE * 2));
+    const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+    return u32x4{l2.x, l2.y, h2.x, h2.y};
+  };
   auto read_a = [&](const u32x4* S, int kk, int slot, int i) {
-    const int r = arow0 + i * 32;
-    af[slot][i] = S[r * kRowChunks + swz(r, 2 * kk + half)];
+    if constexpr (AKM) {
+      af[slot][i] = read_km(S, kk, kmoa[i]);
+    } else {
+      const int r = arow0 + i * 32;
+      af[slot][i] = S[r * kRowChunks + swz(r, 2 * kk + half)];
+    }
   };
   auto read_b = [&](const u32x4* S, int kk, int slot, int i) {
-    const int r = brow0 + i * 32;
-    bf[slot][i] = S[r * kRowChunks + swz(r, 2 * kk + half)];
+    if constexpr (BKM) {
+      bf[slot][i] = read_km(S, kk, kmob[i]);
+    } else {
+      const int r = brow0 + i * 32;
+      bf[slot][i] = S[r * kRowChunks + swz(r, 2 * kk + half)];
+    }
   };
 
   // Prologue: half-stages 0..3 (nh >= 4).  The scalar (kernel-argument)
@@ -865,7 +928,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
       }
     }
     if constexpr (PHASE == APPLY) {
-      if (g.final_mode == FINAL_NONE) {
+      if (g.final_mode == FINAL_NONE && g.outt != nullptr) {
         // X'^T rows n0 + wn*WN .. +WN, columns mrow0 .. +32: 8 lanes per
         // row, 4 consecutive columns (staged rows) per lane.
         const int cm = (lane & 7) * 4;
@@ -898,7 +961,7 @@ __device__ __forceinline__ void sym_tile(int t, int T, int& tm, int& tn) {
 }
 
 // One launch per product: workgroup -> (unit, tile), XCD-aware.
-template <int PHASE, typename T, int TILE>
+template <int PHASE, typename T, int TILE, int KM>
 __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_gemm(GemmArgs g, ChunkArgs ca) {
   const int tiles_per_unit = g.sym ? g.tiles_m * (g.tiles_m + 1) / 2 : g.tiles_m * g.tiles_n;
   const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -916,7 +979,7 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_gemm(GemmArgs g, Chun
       zero_unit_tile<TILE>(ca, g.final_mode, u, tm * TILE, tn * TILE);
     return;
   }
-  gemm_tile<PHASE, T, TILE>(g, ca, u, tm, tn);
+  gemm_tile<PHASE, T, TILE, KM>(g, ca, u, tm, tn);
 }
 
 // -------------------------------------------------------- small-s NS -------
@@ -1256,7 +1319,10 @@ __device__ __forceinline__ int xcc_id() {
   return __builtin_amdgcn_readfirstlane(__builtin_amdgcn_s_getreg((3 << 11) | 20)) & 15;
 }
 
-template <typename T, int TILE>
+// KMODE: 0 = every operand row-major (fp32 path: X^T is kept); 1 = wide
+// bf16 units, B*X reads X K-major; 2 = tall bf16 units, X^T X reads X
+// K-major on both sides.
+template <typename T, int TILE, int KMODE>
 __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p, ChunkArgs ca) {
   // Every branch below is uniform across the workgroup or across a wave:
   // the scheduling work (claim, completion count, dependency wait) is done
@@ -1438,7 +1504,7 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
         g.a = g.b = cur ? p.gram_op[1] : p.gram_op[0];
         int tm, tn;
         sym_tile(t, g.tiles_m, tm, tn);
-        gemm_tile<GRAM, T, TILE>(g, ca, u, tm, tn, claim_next, count_pending);
+        gemm_tile<GRAM, T, TILE, KMODE == 2 ? 3 : 0>(g, ca, u, tm, tn, claim_next, count_pending);
       }
     } else if (phase == POLY) {
       if (live) {
@@ -1454,7 +1520,7 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
         g.cc = cc;
         int tm, tn;
         sym_tile(t, g.tiles_m, tm, tn);
-        gemm_tile<POLY, T, TILE>(g, ca, u, tm, tn, claim_next, count_pending);
+        gemm_tile<POLY, T, TILE, 0>(g, ca, u, tm, tn, claim_next, count_pending);
       }
     } else {
       const int fm = it == p.n_iter - 1 ? p.final_mode : (int)FINAL_NONE;
@@ -1474,7 +1540,7 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
         g.outt = cur ? p.app_outt[1] : p.app_outt[0];
         g.aux = cur ? p.app_aux[1] : p.app_aux[0];
         g.aux16 = cur ? p.app_aux16[1] : p.app_aux16[0];
-        gemm_tile<APPLY, T, TILE>(g, ca, u, tm, tn, claim_next, count_pending);
+        gemm_tile<APPLY, T, TILE, KMODE == 1 ? 2 : 0>(g, ca, u, tm, tn, claim_next, count_pending);
       } else if (fm != FINAL_NONE) {
         zero_unit_tile<TILE>(ca, fm, u, tm * TILE, tn * TILE);
       }

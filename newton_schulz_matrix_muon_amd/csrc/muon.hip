@@ -86,9 +86,12 @@ Layout layout_of(const Chunk& c, bool bf16) {
     L.xb[0] = take(U * xs * 2);
     L.xb[1] = take(U * xs * 2);
   }
-  // Transposed operand copies of the iterate (bf16, or fp32 on the fp32 path).
-  L.xt[0] = take(U * xs * (bf16 ? 2 : 4));
-  L.xt[1] = take(U * xs * (bf16 ? 2 : 4));
+  // Transposed operand copies of the iterate, fp32 path only (the bf16
+  // products read X itself, K-major where they need columns of X).
+  if (!bf16) {
+    L.xt[0] = take(U * xs * 4);
+    L.xt[1] = take(U * xs * 4);
+  }
   // The Gram is stored once: fp32 on the fp32 path, bf16 on the bf16 path.
   if (bf16)
     L.ab = take(U * ss * 2);
@@ -232,6 +235,8 @@ int plan(const muon_matrix_desc* mats, int64_t n, const muon_hyper* h, bool step
     if (c.n_units * tiles > INT32_MAX / 2) return MUON_ERR_SHAPE;
     if (c.n_units * (int64_t)c.blocks_per_unit > INT32_MAX / 2) return MUON_ERR_SHAPE;
     if (c.n_units * (int64_t)c.norm_blocks_per_unit > INT32_MAX / 2) return MUON_ERR_SHAPE;
+    // a K-major bf16 operand tile spans every row of the iterate
+    if (c.rows_pad * c.cols_pad * 2 >= ((int64_t)1 << 31)) return MUON_ERR_SHAPE;
   }
   return MUON_OK;
 }
@@ -320,7 +325,7 @@ DeviceInfo g_dev[kMaxDevices];
 template <typename T, int TILE>
 int resident_of(int cus) {
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ns_persistent<T, TILE>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ns_persistent<T, TILE, sizeof(T) == 2 ? 1 : 0>,
                                                    gemm_threads<TILE>(), 0) !=
           hipSuccess ||
       per_cu < 1)
@@ -354,22 +359,27 @@ int device_info(DeviceInfo* out) {
 
 constexpr double kWaitLimitSeconds = 5.0;  // bound of one dependency wait
 
-template <int PHASE, typename T>
+template <int PHASE, typename T, int KM>
 void launch_gemm(int tile, const GemmArgs& g, const ChunkArgs& ca, hipStream_t s) {
   const int per_unit = g.sym ? g.tiles_m * (g.tiles_m + 1) / 2 : g.tiles_m * g.tiles_n;
   const int grid = g.n_units * per_unit;
   if (tile == 256)
-    hipLaunchKernelGGL((ns_gemm<PHASE, T, 256>), dim3(grid), dim3(gemm_threads<256>()), 0, s, g, ca);
+    hipLaunchKernelGGL((ns_gemm<PHASE, T, 256, KM>), dim3(grid), dim3(gemm_threads<256>()), 0, s, g, ca);
   else
-    hipLaunchKernelGGL((ns_gemm<PHASE, T, 128>), dim3(grid), dim3(gemm_threads<128>()), 0, s, g, ca);
+    hipLaunchKernelGGL((ns_gemm<PHASE, T, 128, KM>), dim3(grid), dim3(gemm_threads<128>()), 0, s, g, ca);
 }
 
+// km: bit 0 = the A operand is K-major, bit 1 = the B operand is (bf16 only).
 template <int PHASE>
-void launch_phase(bool bf16, int tile, const GemmArgs& g, const ChunkArgs& ca, hipStream_t s) {
-  if (bf16)
-    launch_gemm<PHASE, __bf16>(tile, g, ca, s);
+void launch_phase(bool bf16, int tile, int km, const GemmArgs& g, const ChunkArgs& ca, hipStream_t s) {
+  if (!bf16)
+    launch_gemm<PHASE, float, 0>(tile, g, ca, s);
+  else if (km == 3)
+    launch_gemm<PHASE, __bf16, 3>(tile, g, ca, s);
+  else if (km == 2)
+    launch_gemm<PHASE, __bf16, 2>(tile, g, ca, s);
   else
-    launch_gemm<PHASE, float>(tile, g, ca, s);
+    launch_gemm<PHASE, __bf16, 0>(tile, g, ca, s);
 }
 
 // Runs one chunk: momentum (or NS-input copy), norms, normalisation and the
@@ -409,7 +419,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
                    bf16 ? nullptr : reinterpret_cast<float*>(ws + L.x32[1])};
   uint16_t* xb[2] = {bf16 ? reinterpret_cast<uint16_t*>(ws + L.xb[0]) : nullptr,
                      bf16 ? reinterpret_cast<uint16_t*>(ws + L.xb[1]) : nullptr};
-  void* xt[2] = {ws + L.xt[0], ws + L.xt[1]};
+  void* xt[2] = {bf16 ? nullptr : ws + L.xt[0], bf16 ? nullptr : ws + L.xt[1]};
   float* a32 = bf16 ? nullptr : reinterpret_cast<float*>(ws + L.a32);
   uint16_t* ab = bf16 ? reinterpret_cast<uint16_t*>(ws + L.ab) : nullptr;
   void* bop = ws + L.bop;
@@ -519,11 +529,12 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
     NsSched p;
     std::memset(&p, 0, sizeof(p));
     // Gram: A = X X^T (wide, rows of X) or X^T X (tall, rows of X^T).
+    // bf16: a tall unit's X^T X reads X K-major; fp32: rows of X^T.
     GemmArgs& gg = p.gram;
     gg.n_units = U;
     gg.flag = flag;
     gg.a_ustride = gg.b_ustride = xs;
-    gg.lda = gg.ldb = (int32_t)(c.tall ? c.rows_pad : c.cols_pad);
+    gg.lda = gg.ldb = (int32_t)(c.tall && !bf16 ? c.rows_pad : c.cols_pad);
     gg.M = gg.N = (int32_t)sp;
     gg.K = (int32_t)(c.tall ? c.rows_pad : c.cols_pad);
     gg.tiles_m = gg.tiles_n = (int32_t)(sp / T);
@@ -532,7 +543,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
     gg.out16 = ab;
     gg.out_ustride = ss;
     gg.ldo = (int32_t)sp;
-    for (int k = 0; k < 2; ++k) p.gram_op[k] = c.tall ? (const void*)xt[k] : xop[k];
+    for (int k = 0; k < 2; ++k) p.gram_op[k] = c.tall && !bf16 ? (const void*)xt[k] : xop[k];
     // Polynomial: B = b*A + c*A*A.
     GemmArgs& gp = p.poly;
     gp.n_units = U;
@@ -564,7 +575,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
       ga.a_ustride = ss;
       ga.lda = (int32_t)sp;
       ga.b_ustride = xs;
-      ga.ldb = (int32_t)c.rows_pad;
+      ga.ldb = (int32_t)(bf16 ? c.cols_pad : c.rows_pad);  // X K-major, or rows of X^T
     } else {
       ga.a_ustride = xs;
       ga.lda = (int32_t)c.cols_pad;
@@ -579,10 +590,10 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
     for (int k = 0; k < 2; ++k) {
       const int nx = k ^ 1;
       p.app_a[k] = c.tall ? xop[k] : (const void*)bop;
-      p.app_b[k] = c.tall ? (const void*)bop : (const void*)xt[k];
+      p.app_b[k] = c.tall ? (const void*)bop : (bf16 ? xop[k] : (const void*)xt[k]);
       p.app_out32[k] = bf16 ? nullptr : x32[nx];
       p.app_out16[k] = bf16 ? (void*)xb[nx] : nullptr;
-      p.app_outt[k] = xt[nx];
+      p.app_outt[k] = xt[nx];  // nullptr on the bf16 path
       p.app_aux[k] = bf16 ? nullptr : x32[k];
       p.app_aux16[k] = bf16 ? (const void*)xb[k] : nullptr;
     }
@@ -618,16 +629,21 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
       if (c > 0) grid = std::min(grid, c);
     }
     tr.before(MUON_KERNEL_NS);
-    if (bf16) {
+    if (bf16 && !c.tall) {
       if (T == 256)
-        hipLaunchKernelGGL((ns_persistent<__bf16, 256>), dim3(grid), dim3(gemm_threads<256>()), 0, s, p, ca);
+        hipLaunchKernelGGL((ns_persistent<__bf16, 256, 1>), dim3(grid), dim3(gemm_threads<256>()), 0, s, p, ca);
       else
-        hipLaunchKernelGGL((ns_persistent<__bf16, 128>), dim3(grid), dim3(gemm_threads<128>()), 0, s, p, ca);
+        hipLaunchKernelGGL((ns_persistent<__bf16, 128, 1>), dim3(grid), dim3(gemm_threads<128>()), 0, s, p, ca);
+    } else if (bf16) {
+      if (T == 256)
+        hipLaunchKernelGGL((ns_persistent<__bf16, 256, 2>), dim3(grid), dim3(gemm_threads<256>()), 0, s, p, ca);
+      else
+        hipLaunchKernelGGL((ns_persistent<__bf16, 128, 2>), dim3(grid), dim3(gemm_threads<128>()), 0, s, p, ca);
     } else {
       if (T == 256)
-        hipLaunchKernelGGL((ns_persistent<float, 256>), dim3(grid), dim3(gemm_threads<256>()), 0, s, p, ca);
+        hipLaunchKernelGGL((ns_persistent<float, 256, 0>), dim3(grid), dim3(gemm_threads<256>()), 0, s, p, ca);
       else
-        hipLaunchKernelGGL((ns_persistent<float, 128>), dim3(grid), dim3(gemm_threads<128>()), 0, s, p, ca);
+        hipLaunchKernelGGL((ns_persistent<float, 128, 0>), dim3(grid), dim3(gemm_threads<128>()), 0, s, p, ca);
     }
     tr.after(MUON_KERNEL_NS);
     return hipGetLastError() == hipSuccess ? MUON_OK : MUON_ERR_HIP;
@@ -643,11 +659,12 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
       std::memset(&g, 0, sizeof(g));
       g.n_units = U;
       g.flag = flag;
-      // wide: rows of X (K = cols); tall: rows of X^T (K = rows)
-      g.a = c.tall ? (const void*)xt[cur] : xop[cur];
+      // wide: rows of X (K = cols); tall: X K-major (bf16) or rows of X^T
+      // (fp32), K = rows
+      g.a = c.tall && !bf16 ? (const void*)xt[cur] : xop[cur];
       g.b = g.a;
       g.a_ustride = g.b_ustride = xs;
-      g.lda = g.ldb = (int32_t)(c.tall ? c.rows_pad : c.cols_pad);
+      g.lda = g.ldb = (int32_t)(c.tall && !bf16 ? c.rows_pad : c.cols_pad);
       g.M = g.N = (int32_t)sp;
       g.K = (int32_t)(c.tall ? c.rows_pad : c.cols_pad);
       g.tiles_m = g.tiles_n = (int32_t)(sp / T);
@@ -657,7 +674,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
       g.out_ustride = ss;
       g.ldo = (int32_t)sp;
       tr.before(MUON_KERNEL_GRAM);
-      launch_phase<GRAM>(bf16, T, g, ca, s);
+      launch_phase<GRAM>(bf16, T, c.tall ? 3 : 0, g, ca, s);
       tr.after(MUON_KERNEL_GRAM);
       // Polynomial: B = b*A + c*A*A (A symmetric: both operands K-contiguous).
       std::memset(&g, 0, sizeof(g));
@@ -681,7 +698,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
       g.cb = sg.b;
       g.cc = sg.c;
       tr.before(MUON_KERNEL_POLY);
-      launch_phase<POLY>(bf16, T, g, ca, s);
+      launch_phase<POLY>(bf16, T, 0, g, ca, s);
       tr.after(MUON_KERNEL_POLY);
       // Apply: X' = a*X + B*X (wide) or a*X + X*B (tall).
       std::memset(&g, 0, sizeof(g));
@@ -696,9 +713,9 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
         g.a = bop;           // B[m][k]
         g.a_ustride = ss;
         g.lda = (int32_t)sp;
-        g.b = xt[cur];       // X[k][n] read as X^T[n][k]
+        g.b = bf16 ? xop[cur] : xt[cur];  // X[k][n]: K-major (bf16) or rows of X^T
         g.b_ustride = xs;
-        g.ldb = (int32_t)c.rows_pad;
+        g.ldb = (int32_t)(bf16 ? c.cols_pad : c.rows_pad);
       } else {
         g.a = xop[cur];      // X[m][k]
         g.a_ustride = xs;
@@ -720,7 +737,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
       g.ca = sg.a;
       g.final_mode = last ? (step ? FINAL_STEP : FINAL_NSOUT) : FINAL_NONE;
       tr.before(MUON_KERNEL_APPLY);
-      launch_phase<APPLY>(bf16, T, g, ca, s);
+      launch_phase<APPLY>(bf16, T, c.tall ? 0 : 2, g, ca, s);
       tr.after(MUON_KERNEL_APPLY);
     }
   }
