@@ -2,18 +2,20 @@
 //
 // Kernels, in launch order for one stacked pass ("chunk") of equal-shape NS
 // units:
-//   k_momentum      M <- mu*M + G, N = mu*M + G into the fp32 iterate buffer
-//                   (or the EMA style with bias corrections: two coefficient
-//                   pairs from the host, exact for the SGD style's 1s),
-//                   per-block fp64 partial sums of N^2 (DeepSeek tech notes
-//                   "Muon 优化器" section 1 Algorithm 1; RFC-0023 方案 1).
+//   k_momentum      M <- mu*M + G, N = mu*M + G (or the EMA style with bias
+//                   corrections: two coefficient pairs from the host, exact
+//                   for the SGD style's 1s), per-block fp64 partial sums of
+//                   N^2 (DeepSeek tech notes "Muon 优化器" section 1
+//                   Algorithm 1; RFC-0023 方案 1).  N goes to the fp32
+//                   buffer, or on the tiled bf16 path straight into the bf16
+//                   iterate with its padding zeroed.
 //   k_norm_finish   per unit: fixed-order fp64 sum of the partials, 1/||N||_F
 //                   and the non-zero flag (notes section 2: Frobenius
 //                   normalisation, a zero matrix stays zero).
-//   k_normalize     X0 = N/||N||_F over the padded iterate (zeros in the
-//                   padding) as the operand copies the products read: X0
-//                   and X0^T, in bf16 on the bf16 path (X0 is then held
-//                   only in bf16) or fp32, transposed through LDS.
+//   k_normalize     fp32 path: X0 = N/||N||_F over the padded iterate (zeros
+//                   in the padding) and X0^T, transposed through LDS.  The
+//                   tiled bf16 path has no such pass: its first iteration
+//                   reads N and scales the Gram by 1/nu^2, the apply by 1/nu.
 //   ns_gemm<GRAM>   A = X X^T (or X^T X for a tall unit: the smaller side).
 //   ns_gemm<POLY>   B = b*A + c*A*A (on the bf16 path A is kept only as its
 //                   bf16 operand copy, which the b*A term also reads).
@@ -34,10 +36,11 @@
 //                   completion counts, so tiles of different units and
 //                   phases overlap (no launch boundary between products).
 // The three products are the quintic step a*X + b*(X X^T)X + c*(X X^T)^2 X of
-// the notes' section 2, grouped as (b*A + c*A^2)*X.  Keeping X both as is and
-// transposed makes every product "A times B-transposed" with both operands
-// K-contiguous: Gram X X^T reads X twice (X^T X reads X^T twice), B*X reads B
-// and X^T, X*B reads X and B (B is symmetric).
+// the notes' section 2, grouped as (b*A + c*A^2)*X.  Every product reads
+// its operands K-contiguous or, on the bf16 path, K-major through the LDS
+// transposing read: Gram X X^T reads X twice (X^T X reads X K-major twice),
+// B*X reads B and X K-major, X*B reads X and B (B is symmetric).  The fp32
+// path keeps X^T beside X instead.
 //
 // Padding: every iterate is stored as rows_pad x cols_pad with exact zeros
 // outside rows x cols, and every Gram / polynomial matrix as s_pad x s_pad.
@@ -109,6 +112,8 @@ struct GemmArgs {
   int32_t ldaux;
   float ca, cb, cc;     // quintic coefficients
   const int32_t* flag;  // per unit: nonzero = the unit has a nonzero norm
+  const float* fold;    // per unit 1/nu when X holds N itself (first
+                        // iteration of the folded bf16 path), or nullptr
 };
 
 // The segment holding chunk-local unit u.  Every table entry is read at a
@@ -163,6 +168,14 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
   return __builtin_bit_cast(float, h << 16);
 }
 
+__device__ __forceinline__ void store_bf16x4(void* base, int64_t idx, float a, float b, float c,
+                                             float d) {
+  uint2 p;
+  p.x = (uint32_t)to_bf16_bits(a) | ((uint32_t)to_bf16_bits(b) << 16);
+  p.y = (uint32_t)to_bf16_bits(c) | ((uint32_t)to_bf16_bits(d) << 16);
+  *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + idx) = p;
+}
+
 // f rounded to bf16 (round to nearest even), as fp32.
 __device__ __forceinline__ float bf16_round(float f) {
   return bf16_bits_to_f32(to_bf16_bits(f));
@@ -170,8 +183,13 @@ __device__ __forceinline__ float bf16_round(float f) {
 
 // ------------------------------------------------------------- momentum ----
 // GK: 0 = bf16 gradient, 1 = fp32 gradient, 2 = NS-only (copy fp32 input).
+// N goes to the fp32 buffer x32, or, when nb is given, to the bf16 iterate
+// nb itself (the tiled bf16 path, which folds 1/nu into its first
+// iteration), padding included: each block clears its rows' padded columns
+// and a unit's last block its padded rows.
 template <int GK>
 __global__ __launch_bounds__(kThreads) void k_momentum(ChunkArgs ca, float* __restrict__ x32,
+                                                        uint16_t* __restrict__ nb,
                                                         double* __restrict__ partials,
                                                         int rows_per_block, int blocks_per_unit) {
   __shared__ double sh[kThreads / 64];
@@ -184,11 +202,13 @@ __global__ __launch_bounds__(kThreads) void k_momentum(ChunkArgs ca, float* __re
   const int r1 = min(r0 + rows_per_block, ca.rows);
   const float ma = ca.ma, mb = ca.mb, la = ca.la, lb = ca.lb;
   float* xu = x32 + (int64_t)u * ca.x_stride;
+  uint16_t* const nbu = nb ? nb + (int64_t)u * ca.x_stride : nullptr;
   double ss = 0.0;
   const bool vec = (cols & 3) == 0;
   for (int r = r0; r < r1; ++r) {
     const int64_t base = uoff + (int64_t)r * cols;
     float* xr = xu + (int64_t)r * ca.cols_pad;
+    uint16_t* const nr = nbu ? nbu + (int64_t)r * ca.cols_pad : nullptr;
     if (vec) {
       for (int c = threadIdx.x * 4; c < cols; c += kThreads * 4) {
         float g[4];
@@ -218,7 +238,10 @@ __global__ __launch_bounds__(kThreads) void k_momentum(ChunkArgs ca, float* __re
           }
           *mp = make_float4(m[0], m[1], m[2], m[3]);
         }
-        *reinterpret_cast<float4*>(xr + c) = make_float4(n[0], n[1], n[2], n[3]);
+        if (nr)
+          store_bf16x4(nr, c, n[0], n[1], n[2], n[3]);
+        else
+          *reinterpret_cast<float4*>(xr + c) = make_float4(n[0], n[1], n[2], n[3]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) ss = __builtin_fma((double)n[i], (double)n[i], ss);
       }
@@ -237,51 +260,90 @@ __global__ __launch_bounds__(kThreads) void k_momentum(ChunkArgs ca, float* __re
           sg.m[base + c] = m;
           n = __builtin_fmaf(la, m, lb * g);
         }
-        xr[c] = n;
+        if (nr)
+          nr[c] = to_bf16_bits(n);
+        else
+          xr[c] = n;
         ss = __builtin_fma((double)n, (double)n, ss);
       }
     }
+    if (nr)
+      for (int c = cols + threadIdx.x; c < ca.cols_pad; c += kThreads) nr[c] = 0;
   }
+  if (nbu && bb == blocks_per_unit - 1)
+    for (int64_t e = (int64_t)ca.rows * ca.cols_pad + threadIdx.x; e < ca.x_stride; e += kThreads)
+      nbu[e] = 0;
   const double t = block_sum(ss, sh);
   if (threadIdx.x == 0) partials[(int64_t)u * blocks_per_unit + bb] = t;
 }
 
-// One wave per unit: fixed-order sum of the partials.
+// Folded normalisation: the bf16 iterate holds N itself and the first NS
+// iteration applies 1/nu (Gram by 1/nu^2, apply by 1/nu).  Its fp32 Gram
+// accumulators hold sums of products of N's entries, so the fold is taken
+// for norms in [2^-40, 2^40] (entries' products stay normal, sums finite,
+// for units of up to 2^31 elements); other units are scaled in place first.
+constexpr double kFoldMin = 0x1p-80, kFoldMax = 0x1p80;  // bounds on nu^2
+
+// One workgroup per unit: fixed-order sum of the partials (first wave).
 // It also clears the persistent schedule's per-unit counts and claim
-// counter (when given), and the error word (when given).
-__global__ __launch_bounds__(64) void k_norm_finish(const double* __restrict__ partials,
-                                                    int blocks_per_unit, float* __restrict__ inv_nu,
-                                                    int32_t* __restrict__ flag,
-                                                    uint32_t* __restrict__ sched_done,
-                                                    uint32_t* __restrict__ sched_queue,
-                                                    int n_queue_words,
-                                                    uint32_t* __restrict__ err) {
+// counter (when given), and the error word (when given).  With nb (the
+// folded path: unit iterates of x_stride bf16 elements holding N), inv_nu
+// receives the first iteration's scale instead: 1/nu inside the fold's
+// range, else 1 after the unit has been scaled by 1/nu here.
+__global__ __launch_bounds__(kThreads) void k_norm_finish(const double* __restrict__ partials,
+                                                          int blocks_per_unit,
+                                                          float* __restrict__ inv_nu,
+                                                          int32_t* __restrict__ flag,
+                                                          uint32_t* __restrict__ sched_done,
+                                                          uint32_t* __restrict__ sched_queue,
+                                                          int n_queue_words,
+                                                          uint32_t* __restrict__ err,
+                                                          uint16_t* __restrict__ nb,
+                                                          int64_t x_stride) {
+  __shared__ double total;
   const int u = blockIdx.x;
-  double s = 0.0;
-  for (int i = threadIdx.x; i < blocks_per_unit; i += 64)
-    s += partials[(int64_t)u * blocks_per_unit + i];
-  s = wave_sum(s);
+  if (threadIdx.x < 64) {
+    double s = 0.0;
+    for (int i = threadIdx.x; i < blocks_per_unit; i += 64)
+      s += partials[(int64_t)u * blocks_per_unit + i];
+    s = wave_sum(s);
+    if (threadIdx.x == 0) total = s;
+  }
+  __syncthreads();
+  const double s = total;
+  // A NaN/Inf sum keeps the unit active so that it propagates.
+  const bool zero = (s == 0.0);
+  const float inv = zero ? 0.0f : (float)(1.0 / sqrt(s));
+  const bool rescale = nb && !zero && !(s >= kFoldMin && s <= kFoldMax);
   if (threadIdx.x == 0) {
-    // A NaN/Inf sum keeps the unit active so that it propagates.
-    const bool zero = (s == 0.0);
     flag[u] = zero ? 0 : 1;
-    inv_nu[u] = zero ? 0.0f : (float)(1.0 / sqrt(s));
+    inv_nu[u] = rescale ? 1.0f : inv;
     if (sched_done) sched_done[u] = 0u;
     if (u == 0 && sched_queue)
       for (int i = 0; i < n_queue_words; ++i) sched_queue[i] = 0u;
     if (u == 0 && err) *err = 0u;
   }
+  if (rescale) {
+    uint4* xu = reinterpret_cast<uint4*>(nb + (int64_t)u * x_stride);
+    for (int64_t e = threadIdx.x; e < x_stride / 8; e += kThreads) {
+      uint4 v = xu[e];
+      uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        w[i] = (uint32_t)to_bf16_bits(bf16_bits_to_f32(w[i] & 0xffffu) * inv) |
+               ((uint32_t)to_bf16_bits(bf16_bits_to_f32(w[i] >> 16) * inv) << 16);
+      xu[e] = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
 }
 
-// X0 = N * (1/nu) over the whole padded iterate (zeros in the padding):
-// in bf16 (BF16; the products read X itself, K-major where needed), or in
-// place in the fp32 buffer plus X0^T.  One 64x64 tile per workgroup; the
-// transpose goes through LDS so that both the row-major and the transposed
-// writes are coalesced.
-template <bool BF16>
+// fp32 path: X0 = N * (1/nu) in place over the whole padded iterate (zeros
+// in the padding), plus X0^T.  One 64x64 tile per workgroup; the transpose
+// goes through LDS so that both the row-major and the transposed writes are
+// coalesced.  (The bf16 products need no such pass: their first iteration
+// reads N and applies 1/nu itself.)
 __global__ __launch_bounds__(kThreads) void k_normalize(ChunkArgs ca, float* __restrict__ x32,
-                                                         uint16_t* __restrict__ xb,
-                                                         void* __restrict__ xt,
+                                                         float* __restrict__ xt,
                                                          const float* __restrict__ inv_nu,
                                                          int tiles_c, int tiles_per_unit) {
   __shared__ float tile[64][65];
@@ -305,20 +367,12 @@ __global__ __launch_bounds__(kThreads) void k_normalize(ChunkArgs ca, float* __r
       val.z = (c + 2 < ca.cols) ? nv.z * s : 0.f;
       val.w = (c + 3 < ca.cols) ? nv.w * s : 0.f;
     }
-    if constexpr (BF16) {
-      uint2 packed;
-      packed.x = (uint32_t)to_bf16_bits(val.x) | ((uint32_t)to_bf16_bits(val.y) << 16);
-      packed.y = (uint32_t)to_bf16_bits(val.z) | ((uint32_t)to_bf16_bits(val.w) << 16);
-      *reinterpret_cast<uint2*>(xb + (int64_t)u * ca.x_stride + e) = packed;
-    } else {
-      *reinterpret_cast<float4*>(xu + e) = val;
-      tile[rr][cc] = val.x;
-      tile[rr][cc + 1] = val.y;
-      tile[rr][cc + 2] = val.z;
-      tile[rr][cc + 3] = val.w;
-    }
+    *reinterpret_cast<float4*>(xu + e) = val;
+    tile[rr][cc] = val.x;
+    tile[rr][cc + 1] = val.y;
+    tile[rr][cc + 2] = val.z;
+    tile[rr][cc + 3] = val.w;
   }
-  if constexpr (BF16) return;
   __syncthreads();
   // X^T (cols_pad x rows_pad): row c takes tile column c - c0.
 #pragma unroll
@@ -326,7 +380,7 @@ __global__ __launch_bounds__(kThreads) void k_normalize(ChunkArgs ca, float* __r
     const int cc = t / 16 + 16 * i, rr = (t % 16) * 4;
     const int64_t e = (int64_t)u * ca.x_stride + (int64_t)(c0 + cc) * rp + r0 + rr;
     const float a = tile[rr][cc], b = tile[rr + 1][cc], c = tile[rr + 2][cc], d = tile[rr + 3][cc];
-    *reinterpret_cast<float4*>(static_cast<float*>(xt) + e) = make_float4(a, b, c, d);
+    *reinterpret_cast<float4*>(xt + e) = make_float4(a, b, c, d);
   }
 }
 
@@ -477,14 +531,6 @@ __device__ __forceinline__ void mfma_one(const u32x4& af, const u32x4& bf, f32x1
   }
 }
 
-__device__ __forceinline__ void store_bf16x4(void* base, int64_t idx, float a, float b, float c,
-                                             float d) {
-  uint2 p;
-  p.x = (uint32_t)to_bf16_bits(a) | ((uint32_t)to_bf16_bits(b) << 16);
-  p.y = (uint32_t)to_bf16_bits(c) | ((uint32_t)to_bf16_bits(d) << 16);
-  *reinterpret_cast<uint2*>(static_cast<uint16_t*>(base) + idx) = p;
-}
-
 // s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -541,7 +587,8 @@ struct NoHook {
 // barrier, when every wave's older memory accesses are complete.
 //
 // KM: bit 0 = the A operand is K-major, bit 1 = the B operand is.
-template <int PHASE, typename T, int TILE, int KM = 0, typename Hook = NoHook, typename Hook2 = NoHook>
+template <int PHASE, typename T, int TILE, int KM = 0, bool FOLD = false, typename Hook = NoHook,
+          typename Hook2 = NoHook>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca, int u, int tm,
                                           int tn, const Hook& issued = Hook(),
                                           const Hook2& ready = Hook2()) {
@@ -798,6 +845,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
     wout = sg.w + (int64_t)(u - sg.first) * ca.unit_elems;
   }
   const bool vec_w = (ca.cols & 3) == 0;
+  // FOLD (first iteration of the folded path): X = N, so A = (N N^T)/nu^2
+  // and X' = (a*N + B*N)/nu; the accumulators take the scale as they are
+  // staged, a takes 1/nu.  A separate instantiation, so that the other
+  // tiles' epilogues carry neither the branch nor its registers.
+  const float fs = FOLD ? g.fold[u] : 1.0f;
+  const float acc_scale = PHASE == GRAM ? fs * fs : fs;
+  const float coef_a = FOLD ? g.ca * fs : g.ca;
   // bf16 auxiliary input (A for POLY, X for APPLY), row-wise, two blocks
   // ahead: blocks 0 and 1 are issued here and block i + 2 once block i has
   // taken its values, so the load latency is paid about once per tile.
@@ -836,6 +890,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
       for (int it = 0; it < NIT; ++it)
         aux[it] = *reinterpret_cast<const float4*>(ap + (int64_t)(mrow0 + it * RPI + rl) * g.ldaux);
     }
+    if constexpr (FOLD && PHASE != POLY) {
+#pragma unroll
+      for (int j = 0; j < FB; ++j) acc[i][j] *= acc_scale;
+    }
     // stage the block
 #pragma unroll
     for (int j = 0; j < FB; ++j)
@@ -869,10 +927,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
           *reinterpret_cast<float4*>(g.out32 + o) = make_float4(v0, v1, v2, v3);
       } else {
         const float4 a = aux_at(it);
-        v0 = __builtin_fmaf(g.ca, a.x, v0);
-        v1 = __builtin_fmaf(g.ca, a.y, v1);
-        v2 = __builtin_fmaf(g.ca, a.z, v2);
-        v3 = __builtin_fmaf(g.ca, a.w, v3);
+        v0 = __builtin_fmaf(coef_a, a.x, v0);
+        v1 = __builtin_fmaf(coef_a, a.y, v1);
+        v2 = __builtin_fmaf(coef_a, a.z, v2);
+        v3 = __builtin_fmaf(coef_a, a.w, v3);
         if (g.final_mode == FINAL_NONE) {
           if constexpr (kBF)
             store_bf16x4(g.out16, o, v0, v1, v2, v3);
@@ -979,7 +1037,10 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_gemm(GemmArgs g, Chun
       zero_unit_tile<TILE>(ca, g.final_mode, u, tm * TILE, tn * TILE);
     return;
   }
-  gemm_tile<PHASE, T, TILE, KM>(g, ca, u, tm, tn);
+  if (PHASE != POLY && g.fold)
+    gemm_tile<PHASE, T, TILE, KM, PHASE != POLY>(g, ca, u, tm, tn);
+  else
+    gemm_tile<PHASE, T, TILE, KM>(g, ca, u, tm, tn);
 }
 
 // -------------------------------------------------------- small-s NS -------
@@ -1504,7 +1565,11 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
         g.a = g.b = cur ? p.gram_op[1] : p.gram_op[0];
         int tm, tn;
         sym_tile(t, g.tiles_m, tm, tn);
-        gemm_tile<GRAM, T, TILE, KMODE == 2 ? 3 : 0>(g, ca, u, tm, tn, claim_next, count_pending);
+        if (it == 0 && g.fold)
+          gemm_tile<GRAM, T, TILE, KMODE == 2 ? 3 : 0, true>(g, ca, u, tm, tn, claim_next,
+                                                            count_pending);
+        else
+          gemm_tile<GRAM, T, TILE, KMODE == 2 ? 3 : 0>(g, ca, u, tm, tn, claim_next, count_pending);
       }
     } else if (phase == POLY) {
       if (live) {
@@ -1540,7 +1605,12 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
         g.outt = cur ? p.app_outt[1] : p.app_outt[0];
         g.aux = cur ? p.app_aux[1] : p.app_aux[0];
         g.aux16 = cur ? p.app_aux16[1] : p.app_aux16[0];
-        gemm_tile<APPLY, T, TILE, KMODE == 1 ? 2 : 0>(g, ca, u, tm, tn, claim_next, count_pending);
+        if (it == 0 && g.fold)
+          gemm_tile<APPLY, T, TILE, KMODE == 1 ? 2 : 0, true>(g, ca, u, tm, tn, claim_next,
+                                                             count_pending);
+        else
+          gemm_tile<APPLY, T, TILE, KMODE == 1 ? 2 : 0>(g, ca, u, tm, tn, claim_next,
+                                                       count_pending);
       } else if (fm != FINAL_NONE) {
         zero_unit_tile<TILE>(ca, fm, u, tm * TILE, tn * TILE);
       }

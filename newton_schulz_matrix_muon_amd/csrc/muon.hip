@@ -428,28 +428,6 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
   int32_t* flag = reinterpret_cast<int32_t*>(ws + L.flag);
 
   const int U = (int)c.n_units;
-  // 1. momentum + Nesterov + partial sums of squares.
-  tr.before(MUON_KERNEL_MOMENTUM);
-  {
-    const dim3 grid(U * c.blocks_per_unit);
-    if (!step)
-      hipLaunchKernelGGL(k_momentum<2>, grid, dim3(kThreads), 0, s, ca, x32[0], partials,
-                         c.rows_per_block, c.blocks_per_unit);
-    else if (c.gdtype == MUON_DTYPE_BF16)
-      hipLaunchKernelGGL(k_momentum<0>, grid, dim3(kThreads), 0, s, ca, x32[0], partials,
-                         c.rows_per_block, c.blocks_per_unit);
-    else
-      hipLaunchKernelGGL(k_momentum<1>, grid, dim3(kThreads), 0, s, ca, x32[0], partials,
-                         c.rows_per_block, c.blocks_per_unit);
-  }
-  tr.after(MUON_KERNEL_MOMENTUM);
-  // 2. norms and X0 = N / ||N||_F.
-  tr.before(MUON_KERNEL_NORMALIZE);
-  uint32_t* done = reinterpret_cast<uint32_t*>(ws + L.done);
-  uint32_t* queue = reinterpret_cast<uint32_t*>(ws + L.queue);
-  uint32_t* err = reinterpret_cast<uint32_t*>(ws);
-  hipLaunchKernelGGL(k_norm_finish, dim3(U), dim3(64), 0, s, partials, c.blocks_per_unit, inv_nu,
-                     flag, done, queue, kMaxQueues + 1, first_chunk ? err : nullptr);
   // Small wide units (at most 128 rows, bf16 products, AUTO schedule): the
   // whole NS in one workgroup per unit, reading N itself (no normalisation
   // pass).  A unit's workgroup walks its column blocks in sequence, so the
@@ -464,6 +442,34 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
     if (dst != MUON_OK) return dst;
     small = 2 * U >= di.cus;
   }
+  // The tiled bf16 path folds 1/nu into the first iteration: momentum
+  // writes N straight into the bf16 iterate (padding zeroed) and no
+  // normalisation pass runs.
+  const bool fold = bf16 && !small;
+  uint16_t* const nb = fold ? xb[0] : nullptr;
+  // 1. momentum + Nesterov + partial sums of squares.
+  tr.before(MUON_KERNEL_MOMENTUM);
+  {
+    const dim3 grid(U * c.blocks_per_unit);
+    if (!step)
+      hipLaunchKernelGGL(k_momentum<2>, grid, dim3(kThreads), 0, s, ca, x32[0], nb, partials,
+                         c.rows_per_block, c.blocks_per_unit);
+    else if (c.gdtype == MUON_DTYPE_BF16)
+      hipLaunchKernelGGL(k_momentum<0>, grid, dim3(kThreads), 0, s, ca, x32[0], nb, partials,
+                         c.rows_per_block, c.blocks_per_unit);
+    else
+      hipLaunchKernelGGL(k_momentum<1>, grid, dim3(kThreads), 0, s, ca, x32[0], nb, partials,
+                         c.rows_per_block, c.blocks_per_unit);
+  }
+  tr.after(MUON_KERNEL_MOMENTUM);
+  // 2. norms (and, off the folded path, X0 = N / ||N||_F).
+  tr.before(MUON_KERNEL_NORMALIZE);
+  uint32_t* done = reinterpret_cast<uint32_t*>(ws + L.done);
+  uint32_t* queue = reinterpret_cast<uint32_t*>(ws + L.queue);
+  uint32_t* err = reinterpret_cast<uint32_t*>(ws);
+  hipLaunchKernelGGL(k_norm_finish, dim3(U), dim3(kThreads), 0, s, partials, c.blocks_per_unit,
+                     inv_nu, flag, done, queue, kMaxQueues + 1, first_chunk ? err : nullptr, nb,
+                     (int64_t)(c.rows_pad * c.cols_pad));
   if (small) {
     int total_it = 0;
     for (int i = 0; i < h->n_stages; ++i) total_it += h->stages[i].steps;
@@ -494,13 +500,13 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
     return hipGetLastError() == hipSuccess ? MUON_OK : MUON_ERR_HIP;
   }
   const int tiles_c = (int)(c.cols_pad / 64);
-  if (bf16)
-    hipLaunchKernelGGL(k_normalize<true>, dim3(U * c.norm_blocks_per_unit), dim3(kThreads), 0, s,
-                       ca, x32[0], xb[0], xt[0], inv_nu, tiles_c, c.norm_blocks_per_unit);
-  else
-    hipLaunchKernelGGL(k_normalize<false>, dim3(U * c.norm_blocks_per_unit), dim3(kThreads), 0, s,
-                       ca, x32[0], nullptr, xt[0], inv_nu, tiles_c, c.norm_blocks_per_unit);
+  if (!fold)
+    hipLaunchKernelGGL(k_normalize, dim3(U * c.norm_blocks_per_unit), dim3(kThreads), 0, s, ca,
+                       x32[0], static_cast<float*>(xt[0]), inv_nu, tiles_c, c.norm_blocks_per_unit);
   tr.after(MUON_KERNEL_NORMALIZE);
+  // First iteration's scale on the folded path (inv_nu as k_norm_finish
+  // left it): Gram by its square, apply by itself.
+  const float* const fold_scale = fold ? inv_nu : nullptr;
 
   // 3. Newton-Schulz iterations.
   const int T = c.tile;
@@ -533,6 +539,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
     GemmArgs& gg = p.gram;
     gg.n_units = U;
     gg.flag = flag;
+    gg.fold = fold_scale;  // the kernel keeps it for the first iteration only
     gg.a_ustride = gg.b_ustride = xs;
     gg.lda = gg.ldb = (int32_t)(c.tall && !bf16 ? c.rows_pad : c.cols_pad);
     gg.M = gg.N = (int32_t)sp;
@@ -566,6 +573,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
     GemmArgs& ga = p.apply;
     ga.n_units = U;
     ga.flag = flag;
+    ga.fold = fold_scale;
     ga.M = (int32_t)c.rows_pad;
     ga.N = (int32_t)c.cols_pad;
     ga.K = (int32_t)sp;
@@ -669,6 +677,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
       g.K = (int32_t)(c.tall ? c.rows_pad : c.cols_pad);
       g.tiles_m = g.tiles_n = (int32_t)(sp / T);
       g.sym = 1;       // A is symmetric: upper-triangle tiles, mirrored
+      g.fold = it == 0 ? fold_scale : nullptr;
       g.out32 = a32;   // fp32 path
       g.out16 = ab;    // bf16 path
       g.out_ustride = ss;
@@ -735,6 +744,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
       g.aux_ustride = xs;
       g.ldaux = (int32_t)c.cols_pad;
       g.ca = sg.a;
+      g.fold = it == 0 ? fold_scale : nullptr;
       g.final_mode = last ? (step ? FINAL_STEP : FINAL_NSOUT) : FINAL_NONE;
       tr.before(MUON_KERNEL_APPLY);
       launch_phase<APPLY>(bf16, T, c.tall ? 0 : 2, g, ca, s);

@@ -75,6 +75,27 @@ def test_ns_long_small_units_every_schedule(gpu_lib, sched, batch, rows, cols):
     assert worst <= TOL_NS["bf16"]
 
 
+# The tiled bf16 path folds 1/||N|| into the first iteration (its fp32 Gram
+# accumulates products of N's raw entries) inside a range of norms and
+# scales the iterate first outside it; NS is scale invariant, so every scale
+# must give the oracle's result.
+@pytest.mark.parametrize("sched", ["persistent", "launches"])
+@pytest.mark.parametrize("scale", [2.0**-70, 2.0**-30, 1.0, 2.0**30, 2.0**70],
+                         ids=["2^-70", "2^-30", "1", "2^30", "2^70"])
+def test_ns_bf16_folded_normalisation_any_scale(gpu_lib, scale, sched):
+    say(f"[ns fold] scale={scale:.3e} schedule={sched}")
+    worst = 0.0
+    for shape in [(2, 300, 200), (2, 200, 520)]:
+        x = _seeded(shape, 606 + shape[2], scale)
+        h = gpu_lib.Hyper(ns_precision="bf16", schedule=sched)
+        outs, _ = gpu_lib.newton_schulz([x], hyper=h)
+        torch.cuda.synchronize()
+        for i in range(shape[0]):
+            worst = max(worst, rel(f64(outs[0][i]), oracle.newton_schulz(f64(x[i]))))
+    say(f"   worst rel err {worst:.3e}")
+    assert worst <= TOL_NS["bf16"]
+
+
 @pytest.mark.parametrize("prec", ["fp32", "bf16"])
 def test_ns_split_heads_and_banks(gpu_lib, prec):
     # A (batch=3, 6*32, 96) bank split into 32-row heads: 18 units.
