@@ -1506,21 +1506,31 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
     const uint32_t need =
         (uint32_t)(it * per_unit + (phase == GRAM ? 0 : phase == POLY ? p.tg : 2 * p.tg));
     // One look at the completion count; if the item must wait, the pending
-    // tile is counted first (it may be what the wait is for).
+    // tile is counted first (it may be what the wait is for).  Wave 0 makes
+    // the producers' results visible to the whole workgroup before the
+    // barrier that releases the other waves to load them: an acquire at
+    // agent scope (it drops the CU's L1, which every wave shares, and this
+    // L2's copies of lines other XCCs wrote), waited for in full.  One
+    // invalidate per tile rather than one per wave.
+    auto acquire = [&]() {  // wave 0
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      wait_vmcnt<0>();
+    };
     if (wave == 0) {
       int ready = 1;
       if (live && need > 0u)
         ready = __builtin_amdgcn_readfirstlane(__hip_atomic_load(
                     p.done + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) >= need;
+      if (ready && live) acquire();
       s_go = ready;
     }
     lds_barrier();
     const bool ready = __builtin_amdgcn_readfirstlane(s_go) != 0;
     lds_barrier();  // every wave has read s_go
     if (!ready || !live) flush();
-    if (wave == 0) {
-      int go = 1;
-      if (!ready) {
+    if (!ready) {
+      if (wave == 0) {
+        int go = 1;
         const uint64_t t0 = wall_clock64();
         uint32_t d = __builtin_amdgcn_readfirstlane(
             __hip_atomic_load(p.done + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
@@ -1536,20 +1546,17 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
           d = __builtin_amdgcn_readfirstlane(
               __hip_atomic_load(p.done + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
         }
+        if (go) acquire();
+        s_go = go;
       }
-      s_go = go;
+      lds_barrier();
+      const int go = __builtin_amdgcn_readfirstlane(s_go);
+      lds_barrier();  // every wave has read the broadcast words
+      if (!go) {
+        flush();
+        break;
+      }
     }
-    lds_barrier();
-    const int go = __builtin_amdgcn_readfirstlane(s_go);
-    lds_barrier();  // every wave has read the broadcast words
-    if (!go) {
-      flush();
-      break;
-    }
-    // Make the other workgroups' results visible to this wave's loads
-    // (acquire at agent scope: the L1 must be dropped in any case, and a
-    // workgroup-scope invalidate does not reach it).
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     // Wave 0 claims the next item once the tile's first copies are in
     // flight (a zero unit's item runs no tile; the next head claims).
     auto claim_next = [&]() {
