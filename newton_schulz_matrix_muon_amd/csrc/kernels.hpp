@@ -17,16 +17,15 @@
 //                   tiled bf16 path has no such pass: its first iteration
 //                   reads N and scales the Gram by 1/nu^2, the apply by 1/nu.
 //   ns_gemm<GRAM>   A = X X^T (or X^T X for a tall unit: the smaller side).
-//   ns_gemm<POLY>   B = b*A + c*A*A (on the bf16 path A is kept only as its
-//                   bf16 operand copy, which the b*A term also reads).
-//                   Both outputs are symmetric: only the upper-triangle tiles
-//                   are computed, each also written mirrored.
-//   ns_gemm<APPLY>  X' = a*X + B*X (or X*B), written as its operand copies
-//                   X' and X'^T.  On the bf16 path the iterate exists only
-//                   as these bf16 copies: the a*X term reads the same
-//                   rounded X that the products read.  In the last
-//                   iteration the epilogue
-//                   writes W <- W*(1 - lr*wd) - lr*scale*X' instead
+//   ns_gemm<POLY>   B' = a*I + b*A + c*A*A (on the bf16 path A is kept only
+//                   as its bf16 operand copy, which the b*A term also
+//                   reads; a*I carries the apply's a*X term).  Both outputs
+//                   are symmetric: only the upper-triangle tiles are
+//                   computed, each also written mirrored.
+//   ns_gemm<APPLY>  X' = B'*X (or X*B'), written as its operand copy X' (and
+//                   X'^T on the fp32 path).  On the bf16 path the iterate
+//                   exists only in bf16.  In the last iteration the
+//                   epilogue writes W <- W*(1 - lr*wd) - lr*scale*X' instead
 //                   (Algorithm 1's decoupled update) or the NS output.
 //   k_ns_small      the whole NS of a wide unit with at most 128 rows in one
 //                   workgroup, A and B on chip, one pass over X per
@@ -36,11 +35,13 @@
 //                   completion counts, so tiles of different units and
 //                   phases overlap (no launch boundary between products).
 // The three products are the quintic step a*X + b*(X X^T)X + c*(X X^T)^2 X of
-// the notes' section 2, grouped as (b*A + c*A^2)*X.  Every product reads
-// its operands K-contiguous or, on the bf16 path, K-major through the LDS
-// transposing read: Gram X X^T reads X twice (X^T X reads X K-major twice),
-// B*X reads B and X K-major, X*B reads X and B (B is symmetric).  The fp32
-// path keeps X^T beside X instead.
+// the notes' section 2, grouped as (a*I + b*A + c*A^2)*X: the polynomial's
+// epilogue adds a on the diagonal, so the apply is one plain product and
+// reads nothing beside its operands.  Every product reads its operands
+// K-contiguous or, on the bf16 path, K-major through the LDS transposing
+// read: Gram X X^T reads X twice (X^T X reads X K-major twice), B'*X reads
+// B' and X K-major, X*B' reads X and B' (B' is symmetric).  The fp32 path
+// keeps X^T beside X instead.
 //
 // Padding: every iterate is stored as rows_pad x cols_pad with exact zeros
 // outside rows x cols, and every Gram / polynomial matrix as s_pad x s_pad.
@@ -846,16 +847,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
   }
   const bool vec_w = (ca.cols & 3) == 0;
   // FOLD (first iteration of the folded path): X = N, so A = (N N^T)/nu^2
-  // and X' = (a*N + B*N)/nu; the accumulators take the scale as they are
-  // staged, a takes 1/nu.  A separate instantiation, so that the other
-  // tiles' epilogues carry neither the branch nor its registers.
+  // and X' = (B' N)/nu; the accumulators take the scale as they are staged.
+  // A separate instantiation, so that the other tiles' epilogues carry
+  // neither the branch nor its registers.
   const float fs = FOLD ? g.fold[u] : 1.0f;
   const float acc_scale = PHASE == GRAM ? fs * fs : fs;
-  const float coef_a = FOLD ? g.ca * fs : g.ca;
-  // bf16 auxiliary input (A for POLY, X for APPLY), row-wise, two blocks
+  // bf16 auxiliary input (A, for POLY's b*A term), row-wise, two blocks
   // ahead: blocks 0 and 1 are issued here and block i + 2 once block i has
   // taken its values, so the load latency is paid about once per tile.
-  constexpr bool kAuxB = PHASE != GRAM && kBF;
+  constexpr bool kAuxB = PHASE == POLY && kBF;
   uint2 auxr[kAuxB ? 2 : 1][NIT];
   const uint16_t* const aux_p =
       kAuxB ? static_cast<const uint16_t*>(g.aux16) + (int64_t)u * g.aux_ustride + ncol : nullptr;
@@ -874,17 +874,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
     const int mrow0 = m0 + wm * WM + i * 32;  // first global row of the block
     // auxiliary input of the block, row-wise (fp32: issued before the
     // staging; bf16: converted as the row pass uses it)
-    float4 aux[(PHASE != GRAM && !kBF) ? NIT : 1];
+    float4 aux[(PHASE == POLY && !kBF) ? NIT : 1];
     auto aux_at = [&](int it) -> float4 {
       if constexpr (kAuxB) {
         const uint2 h = auxr[i & 1][it];
         return make_float4(bf16_bits_to_f32(h.x & 0xffffu), bf16_bits_to_f32(h.x >> 16),
                            bf16_bits_to_f32(h.y & 0xffffu), bf16_bits_to_f32(h.y >> 16));
       } else {
-        return aux[(PHASE != GRAM && !kBF) ? it : 0];
+        return aux[(PHASE == POLY && !kBF) ? it : 0];
       }
     };
-    if constexpr (PHASE != GRAM && !kBF) {
+    if constexpr (PHASE == POLY && !kBF) {
       const float* ap = g.aux + (int64_t)u * g.aux_ustride + ncol;
 #pragma unroll
       for (int it = 0; it < NIT; ++it)
@@ -918,6 +918,15 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
           v1 = g.cb * a.y + g.cc * v1;
           v2 = g.cb * a.z + g.cc * v2;
           v3 = g.cb * a.w + g.cc * v3;
+          if (tm == tn) {
+            // B' = a*I + b*A + c*A^2: the apply's a*X term rides on the
+            // diagonal (the padded diagonal too; X is zero there)
+            const int d = m - ncol;
+            v0 += d == 0 ? g.ca : 0.0f;
+            v1 += d == 1 ? g.ca : 0.0f;
+            v2 += d == 2 ? g.ca : 0.0f;
+            v3 += d == 3 ? g.ca : 0.0f;
+          }
           // the mirror pass below reads the final values
           *reinterpret_cast<float4*>(ep + r * LDW + cl) = make_float4(v0, v1, v2, v3);
         }
@@ -926,18 +935,12 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
         else
           *reinterpret_cast<float4*>(g.out32 + o) = make_float4(v0, v1, v2, v3);
       } else {
-        const float4 a = aux_at(it);
-        v0 = __builtin_fmaf(coef_a, a.x, v0);
-        v1 = __builtin_fmaf(coef_a, a.y, v1);
-        v2 = __builtin_fmaf(coef_a, a.z, v2);
-        v3 = __builtin_fmaf(coef_a, a.w, v3);
+        // X' = B' X (or X B'): the staged block is the result
         if (g.final_mode == FINAL_NONE) {
           if constexpr (kBF)
             store_bf16x4(g.out16, o, v0, v1, v2, v3);
           else
             *reinterpret_cast<float4*>(g.out32 + o) = make_float4(v0, v1, v2, v3);
-          // keep a*X + C for the transposed pass
-          *reinterpret_cast<float4*>(ep + r * LDW + cl) = make_float4(v0, v1, v2, v3);
         } else if (m < ca.rows && ncol < ca.cols) {
           const int n = ncol;
           float* p = wout + (int64_t)m * ca.cols + n;
@@ -1358,8 +1361,6 @@ struct NsSched {
   float* app_out32[2];            // apply outputs (buffer cur ^ 1)
   void* app_out16[2];
   void* app_outt[2];
-  const float* app_aux[2];        // the iterate X (buffer cur): fp32 path
-  const void* app_aux16[2];       // the same, bf16 path
   int32_t final_mode;             // of the last iteration's apply
   int32_t n_iter;
   int32_t n_stages;
@@ -1581,13 +1582,15 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
     } else if (phase == POLY) {
       if (live) {
         GemmArgs g = p.poly;
-        float cb = p.sb[0], cc = p.sc[0];
+        float a = p.sa[0], cb = p.sb[0], cc = p.sc[0];
 #pragma unroll
         for (int s = 1; s < 4; ++s)
           if (s < p.n_stages && it >= p.stage_begin[s]) {
+            a = p.sa[s];
             cb = p.sb[s];
             cc = p.sc[s];
           }
+        g.ca = a;
         g.cb = cb;
         g.cc = cc;
         int tm, tn;
@@ -1599,19 +1602,12 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
       const int tm = t / p.apply.tiles_n, tn = t - (t / p.apply.tiles_n) * p.apply.tiles_n;
       if (live) {
         GemmArgs g = p.apply;
-        float a = p.sa[0];
-#pragma unroll
-        for (int s = 1; s < 4; ++s)
-          if (s < p.n_stages && it >= p.stage_begin[s]) a = p.sa[s];
-        g.ca = a;
         g.final_mode = fm;
         g.a = cur ? p.app_a[1] : p.app_a[0];
         g.b = cur ? p.app_b[1] : p.app_b[0];
         g.out32 = cur ? p.app_out32[1] : p.app_out32[0];
         g.out16 = cur ? p.app_out16[1] : p.app_out16[0];
         g.outt = cur ? p.app_outt[1] : p.app_outt[0];
-        g.aux = cur ? p.app_aux[1] : p.app_aux[0];
-        g.aux16 = cur ? p.app_aux16[1] : p.app_aux16[0];
         if (it == 0 && g.fold)
           gemm_tile<APPLY, T, TILE, KMODE == 1 ? 2 : 0, true>(g, ca, u, tm, tn, claim_next,
                                                              count_pending);

@@ -551,7 +551,8 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
     gg.out_ustride = ss;
     gg.ldo = (int32_t)sp;
     for (int k = 0; k < 2; ++k) p.gram_op[k] = c.tall && !bf16 ? (const void*)xt[k] : xop[k];
-    // Polynomial: B = b*A + c*A*A.
+    // Polynomial: B' = a*I + b*A + c*A*A (the apply's a*X term on its
+    // diagonal; a comes per iteration).
     GemmArgs& gp = p.poly;
     gp.n_units = U;
     gp.flag = flag;
@@ -569,7 +570,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
     gp.aux16 = ab;
     gp.aux_ustride = ss;
     gp.ldaux = (int32_t)sp;
-    // Apply: X' = a*X + B*X (wide) or a*X + X*B (tall).
+    // Apply: X' = B'*X (wide) or X*B' (tall).
     GemmArgs& ga = p.apply;
     ga.n_units = U;
     ga.flag = flag;
@@ -593,8 +594,6 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
     ga.out_ustride = xs;
     ga.ldo = (int32_t)c.cols_pad;
     ga.ldt = (int32_t)c.rows_pad;
-    ga.aux_ustride = xs;
-    ga.ldaux = (int32_t)c.cols_pad;
     for (int k = 0; k < 2; ++k) {
       const int nx = k ^ 1;
       p.app_a[k] = c.tall ? xop[k] : (const void*)bop;
@@ -602,8 +601,6 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
       p.app_out32[k] = bf16 ? nullptr : x32[nx];
       p.app_out16[k] = bf16 ? (void*)xb[nx] : nullptr;
       p.app_outt[k] = xt[nx];  // nullptr on the bf16 path
-      p.app_aux[k] = bf16 ? nullptr : x32[k];
-      p.app_aux16[k] = bf16 ? (const void*)xb[k] : nullptr;
     }
     p.final_mode = step ? FINAL_STEP : FINAL_NSOUT;
     p.n_iter = total;
@@ -685,7 +682,8 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
       tr.before(MUON_KERNEL_GRAM);
       launch_phase<GRAM>(bf16, T, c.tall ? 3 : 0, g, ca, s);
       tr.after(MUON_KERNEL_GRAM);
-      // Polynomial: B = b*A + c*A*A (A symmetric: both operands K-contiguous).
+      // Polynomial: B' = a*I + b*A + c*A*A (A symmetric: both operands
+      // K-contiguous; a*I carries the apply's a*X term).
       std::memset(&g, 0, sizeof(g));
       g.n_units = U;
       g.flag = flag;
@@ -695,7 +693,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
       g.lda = g.ldb = (int32_t)sp;
       g.M = g.N = g.K = (int32_t)sp;
       g.tiles_m = g.tiles_n = (int32_t)(sp / T);
-      g.sym = 1;       // B = b*A + c*A*A is symmetric as well
+      g.sym = 1;       // B' is symmetric as well
       g.out32 = bf16 ? nullptr : static_cast<float*>(bop);
       g.out16 = bf16 ? bop : nullptr;
       g.out_ustride = ss;
@@ -704,12 +702,13 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
       g.aux16 = ab;
       g.aux_ustride = ss;
       g.ldaux = (int32_t)sp;
+      g.ca = sg.a;
       g.cb = sg.b;
       g.cc = sg.c;
       tr.before(MUON_KERNEL_POLY);
       launch_phase<POLY>(bf16, T, 0, g, ca, s);
       tr.after(MUON_KERNEL_POLY);
-      // Apply: X' = a*X + B*X (wide) or a*X + X*B (tall).
+      // Apply: X' = B'*X (wide) or X*B' (tall).
       std::memset(&g, 0, sizeof(g));
       g.n_units = U;
       g.flag = flag;
@@ -739,11 +738,6 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
       g.ldo = (int32_t)c.cols_pad;
       g.outt = xt[nxt];
       g.ldt = (int32_t)c.rows_pad;
-      g.aux = bf16 ? nullptr : x32[cur];
-      g.aux16 = bf16 ? (const void*)xb[cur] : nullptr;
-      g.aux_ustride = xs;
-      g.ldaux = (int32_t)c.cols_pad;
-      g.ca = sg.a;
       g.fold = it == 0 ? fold_scale : nullptr;
       g.final_mode = last ? (step ? FINAL_STEP : FINAL_NSOUT) : FINAL_NONE;
       tr.before(MUON_KERNEL_APPLY);
