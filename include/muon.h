@@ -72,11 +72,13 @@ typedef enum { MUON_DTYPE_F32 = 0, MUON_DTYPE_BF16 = 1 } muon_dtype;
 typedef enum { MUON_SCALE_SPECTRAL = 0, MUON_SCALE_UNIT_RMS_NORM = 1 } muon_scale_mode;
 
 /* Precision of the Newton-Schulz matrix products.  FP32: fp32 operands on
- * the fp32 matrix cores.  BF16: bf16 operands with fp32 accumulation; the
- * iterate X and every epilogue (b*A + c*A^2, a*X + B*X, the update) are
- * fp32, and what is rounded (nearest-even) to bf16 is what the products
- * read: X, the Gram A (whose bf16 copy also feeds the b*A term) and the
- * polynomial B. */
+ * the fp32 matrix cores.  BF16: bf16 operands with fp32 accumulation.  What
+ * is rounded (nearest-even) to bf16 is what the products read: the iterate
+ * X (kept only in bf16), the Gram A (whose bf16 copy also feeds the b*A
+ * term) and B' = a*I + b*A + c*A^2 (the quintic step regrouped as B'*X, so
+ * a*X rides on B's diagonal).  The epilogues form their results in fp32
+ * before rounding; the last iteration's output and the weight update stay
+ * fp32. */
 typedef enum { MUON_NS_FP32 = 0, MUON_NS_BF16 = 1 } muon_ns_precision;
 
 /* How the Newton-Schulz of a stacked pass is run.  PERSISTENT and LAUNCHES
@@ -193,10 +195,12 @@ int muon_newton_schulz_batched(const float* const* x_in, float* const* o_out,
 /* Kernel classes that a trace can bracket. */
 typedef enum {
   MUON_KERNEL_MOMENTUM = 1, /* momentum + Nesterov + Frobenius partial sums */
-  MUON_KERNEL_NORMALIZE = 2,/* norm finish + scaling of the NS input */
+  MUON_KERNEL_NORMALIZE = 2,/* norm finish (+ X0 = N/||N|| on the fp32 path;
+                               the tiled bf16 path folds 1/||N|| into its
+                               first iteration) */
   MUON_KERNEL_GRAM = 3,     /* A = X X^T on the smaller side */
-  MUON_KERNEL_POLY = 4,     /* B = b*A + c*A*A */
-  MUON_KERNEL_APPLY = 5,    /* X <- a*X + B*X (last one: the weight update) */
+  MUON_KERNEL_POLY = 4,     /* B' = a*I + b*A + c*A*A */
+  MUON_KERNEL_APPLY = 5,    /* X <- B'*X (last one: the weight update) */
   MUON_KERNEL_NS = 6        /* every NS product of a pass in one launch
                                (the persistent or the on-chip small-unit
                                kernel) */

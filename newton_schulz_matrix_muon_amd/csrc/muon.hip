@@ -382,8 +382,9 @@ void launch_phase(bool bf16, int tile, int km, const GemmArgs& g, const ChunkArg
     launch_gemm<PHASE, __bf16, 0>(tile, g, ca, s);
 }
 
-// Runs one chunk: momentum (or NS-input copy), norms, normalisation and the
-// NS iterations with the fused final epilogue.
+// Runs one chunk: momentum (or NS-input copy), norms, normalisation (folded
+// into the first iteration on the tiled bf16 path) and the NS iterations
+// with the fused final epilogue.
 int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs,
               const void* const* ins, float* const* moms, const muon_matrix_desc* mats,
               unsigned char* ws, hipStream_t s, Tracer& tr, bool first_chunk) {
@@ -514,7 +515,8 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
   const int64_t ss = c.s_pad * c.s_pad;
   const int64_t sp = c.s_pad;
   // Operand copies of the iterate: X as is (bf16, or the fp32 iterate
-  // itself) and X^T (cols_pad x rows_pad).
+  // itself) and, on the fp32 path only, X^T (cols_pad x rows_pad); the bf16
+  // products read X K-major instead.
   const void* xop[2] = {bf16 ? (const void*)xb[0] : (const void*)x32[0],
                         bf16 ? (const void*)xb[1] : (const void*)x32[1]};
   const void* aop = bf16 ? (const void*)ab : (const void*)a32;
