@@ -107,11 +107,11 @@ struct GemmArgs {
   int32_t sym;          // GRAM/POLY: symmetric output; only tiles tm <= tn run
                         // and each off-diagonal tile also writes its mirror
   int32_t final_mode;
-  const float* aux;     // fp32 A (POLY) or X (APPLY) on the fp32 path, laid out like the output
-  const void* aux16;    // bf16 A (POLY) or X (APPLY) on the bf16 path
+  const float* aux;     // POLY: fp32 A on the fp32 path, laid out like the output
+  const void* aux16;    // POLY: bf16 A on the bf16 path
   int64_t aux_ustride;
   int32_t ldaux;
-  float ca, cb, cc;     // quintic coefficients
+  float ca, cb, cc;     // quintic coefficients (POLY forms a*I + b*A + c*A^2)
   const int32_t* flag;  // per unit: nonzero = the unit has a nonzero norm
   const float* fold;    // per unit 1/nu when X holds N itself (first
                         // iteration of the folded bf16 path), or nullptr
