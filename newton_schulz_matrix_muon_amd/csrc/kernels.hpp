@@ -202,13 +202,13 @@ __global__ __launch_bounds__(kThreads) void k_momentum(ChunkArgs ca, float* __re
   const int r0 = bb * rows_per_block;
   const int r1 = min(r0 + rows_per_block, ca.rows);
   const float ma = ca.ma, mb = ca.mb, la = ca.la, lb = ca.lb;
-  float* xu = x32 + (int64_t)u * ca.x_stride;
+  float* xu = nb ? nullptr : x32 + (int64_t)u * ca.x_stride;  // x32 is null with nb
   uint16_t* const nbu = nb ? nb + (int64_t)u * ca.x_stride : nullptr;
   double ss = 0.0;
   const bool vec = (cols & 3) == 0;
   for (int r = r0; r < r1; ++r) {
     const int64_t base = uoff + (int64_t)r * cols;
-    float* xr = xu + (int64_t)r * ca.cols_pad;
+    float* const xr = xu ? xu + (int64_t)r * ca.cols_pad : nullptr;
     uint16_t* const nr = nbu ? nbu + (int64_t)r * ca.cols_pad : nullptr;
     if (vec) {
       for (int c = threadIdx.x * 4; c < cols; c += kThreads * 4) {

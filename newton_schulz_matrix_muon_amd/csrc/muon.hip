@@ -71,16 +71,28 @@ struct Layout {
 constexpr size_t kHeader = 256;  // status header at the start of the workspace
 constexpr int kMaxQueues = 16;   // persistent schedule: at most one queue per XCC
 
-Layout layout_of(const Chunk& c, bool bf16) {
+// Whether the AUTO schedule may run the pass on the on-chip small-unit
+// kernel (bf16 products, wide units with at most 128 rows; the final choice
+// also looks at the unit count and the CUs).  Only that kernel reads N in
+// fp32 on the bf16 path.
+bool small_possible(const Chunk& c, const muon_hyper* h) {
+  return h->schedule == MUON_SCHEDULE_AUTO && h->ns_precision == MUON_NS_BF16 && !c.tall &&
+         c.rows_u <= kSmall && c.rows_pad == kSmall;
+}
+
+Layout layout_of(const Chunk& c, const muon_hyper* h) {
+  const bool bf16 = h->ns_precision == MUON_NS_BF16;
   Layout L{};
   const size_t U = (size_t)c.n_units;
   const size_t xs = (size_t)(c.rows_pad * c.cols_pad);
   const size_t ss = (size_t)(c.s_pad * c.s_pad);
   size_t off = kHeader;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, kAlign); return o; };
-  // fp32 iterates: N (and X0) in the first; the second only on the fp32
-  // path (the bf16 path keeps the iterate as its bf16 operand copies).
-  L.x32[0] = take(U * xs * 4);
+  // fp32 iterates: N (and X0) in the first, on the fp32 path and for the
+  // small-unit kernel; the second only on the fp32 path (the bf16 path keeps
+  // the iterate in bf16, and its tiled products start from N written
+  // straight into it).
+  if (!bf16 || small_possible(c, h)) L.x32[0] = take(U * xs * 4);
   if (!bf16) L.x32[1] = take(U * xs * 4);
   if (bf16) {
     L.xb[0] = take(U * xs * 2);
@@ -241,9 +253,9 @@ int plan(const muon_matrix_desc* mats, int64_t n, const muon_hyper* h, bool step
   return MUON_OK;
 }
 
-size_t workspace_of(const std::vector<Chunk>& chunks, bool bf16) {
+size_t workspace_of(const std::vector<Chunk>& chunks, const muon_hyper* h) {
   size_t need = kHeader;
-  for (const Chunk& c : chunks) need = std::max(need, layout_of(c, bf16).total);
+  for (const Chunk& c : chunks) need = std::max(need, layout_of(c, h).total);
   return need;
 }
 
@@ -389,7 +401,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
               const void* const* ins, float* const* moms, const muon_matrix_desc* mats,
               unsigned char* ws, hipStream_t s, Tracer& tr, bool first_chunk) {
   const bool bf16 = h->ns_precision == MUON_NS_BF16;
-  const Layout L = layout_of(c, bf16);
+  const Layout L = layout_of(c, h);
   ChunkArgs ca;
   std::memset(&ca, 0, sizeof(ca));
   ca.n_seg = (int32_t)c.segs.size();
@@ -416,7 +428,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
     first += (int32_t)r.count;
   }
 
-  float* x32[2] = {reinterpret_cast<float*>(ws + L.x32[0]),
+  float* x32[2] = {L.x32[0] ? reinterpret_cast<float*>(ws + L.x32[0]) : nullptr,
                    bf16 ? nullptr : reinterpret_cast<float*>(ws + L.x32[1])};
   uint16_t* xb[2] = {bf16 ? reinterpret_cast<uint16_t*>(ws + L.xb[0]) : nullptr,
                      bf16 ? reinterpret_cast<uint16_t*>(ws + L.xb[1]) : nullptr};
@@ -435,8 +447,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
   // path is taken for short units (up to eight 128-column blocks) or when
   // the units number at least half the CUs; a few long units go to the
   // tiled products, which spread each unit over many CUs.
-  bool small = h->schedule == MUON_SCHEDULE_AUTO && bf16 && !c.tall && c.rows_u <= kSmall &&
-               c.rows_pad == kSmall;
+  bool small = small_possible(c, h);
   if (small && c.cols_pad / kSmall > 8) {
     DeviceInfo di;
     const int dst = device_info(&di);
@@ -783,8 +794,7 @@ int run(bool step, float* const* outs, const void* const* ins, float* const* mom
     std::vector<Chunk> chunks;
     st = plan(mats, n, h, step, &chunks);
     if (st != MUON_OK) return st;
-    const bool bf16 = h->ns_precision == MUON_NS_BF16;
-    const size_t need = workspace_of(chunks, bf16);
+    const size_t need = workspace_of(chunks, h);
     if (need > 0 && (!ws || ws_bytes < need)) return MUON_ERR_WORKSPACE;
     if (((uintptr_t)ws & (kAlign - 1)) != 0) return MUON_ERR_ALIGN;
     Tracer tr{trace, stream};
@@ -840,8 +850,7 @@ int muon_workspace_size(const muon_matrix_desc* mats, int64_t n, const muon_hype
     std::vector<Chunk> chunks_ns;
     st = plan(mats, n, h, false, &chunks_ns);
     if (st != MUON_OK) return st;
-    const bool bf16 = h->ns_precision == MUON_NS_BF16;
-    *bytes = std::max(workspace_of(chunks, bf16), workspace_of(chunks_ns, bf16));
+    *bytes = std::max(workspace_of(chunks, h), workspace_of(chunks_ns, h));
     return MUON_OK;
   } catch (...) {
     return MUON_ERR_SHAPE;

@@ -60,21 +60,39 @@ def test_workspace_sizes():
     mib = 1024 * 1024
     st, n = ws_size([(32, 1024, 1024, 0)])
     assert st == 0
-    # bf16 path: the fp32 look-ahead, two bf16 iterates (no transposed
-    # copies: the products read X K-major), bf16 Gram, bf16 polynomial = 12
-    # bytes per element, plus the status header, per-unit norms and schedule
-    # counters
-    assert 32 * mib * 12 <= n < 32 * mib * 12 + mib
+    # bf16 path, tiled products: two bf16 iterates (momentum writes N into
+    # the first; no transposed copies: the products read X K-major), bf16
+    # Gram, bf16 polynomial = 8 bytes per element, plus the status header,
+    # per-unit norms and schedule counters
+    assert 32 * mib * 8 <= n < 32 * mib * 8 + mib
     h = muon.default_hyper_c()
     h.batch_update_size = 8
     st, n8 = ws_size([(32, 1024, 1024, 0)], h)
-    assert st == 0 and 8 * mib * 12 <= n8 < 8 * mib * 12 + mib
+    assert st == 0 and 8 * mib * 8 <= n8 < 8 * mib * 8 + mib
     h.ns_precision = muon.NS_FP32
     st, nf = ws_size([(32, 1024, 1024, 0)], h)
     # fp32 path: two fp32 iterates and their two transposes, fp32 Gram and
     # polynomial = 24 bytes
     assert st == 0 and 8 * mib * 24 <= nf < 8 * mib * 24 + mib
     assert ws_size([])[0] == 0
+
+
+def test_workspace_keeps_fp32_n_only_where_the_small_kernel_may_run():
+    # 128-row wide heads under AUTO may run on chip, which reads N in fp32:
+    # 4 (fp32 N) + 2 x 2 (bf16 iterates) bytes per element of the 128 x 4096
+    # iterate, plus two 128 x 128 bf16 matrices per unit
+    per_unit_auto = 128 * 4096 * 8 + 2 * 128 * 128 * 2
+    st, n = ws_size([(48, 128, 4096, 0)])
+    assert st == 0 and 48 * per_unit_auto <= n < 48 * per_unit_auto + (1 << 20)
+    # a forced schedule never runs the small kernel: no fp32 N
+    h = muon.default_hyper_c()
+    h.schedule = muon.SCHEDULE_PERSISTENT
+    per_unit_tiled = 128 * 4096 * 4 + 2 * 128 * 128 * 2
+    st, nt = ws_size([(48, 128, 4096, 0)], h)
+    assert st == 0 and 48 * per_unit_tiled <= nt < 48 * per_unit_tiled + (1 << 20)
+    # tall 4096 x 128 units have a 128-wide Gram but are never small: no fp32 N
+    st, ntall = ws_size([(48, 4096, 128, 0)])
+    assert st == 0 and ntall < n
 
 
 @pytest.mark.parametrize(
