@@ -56,7 +56,10 @@ extern "C" {
 typedef enum {
   MUON_OK = 0,
   MUON_ERR_NULL = -1,      /* a required pointer is NULL */
-  MUON_ERR_SHAPE = -2,     /* rows/cols/batch < 1, split_rows not dividing rows, sizes too large */
+  MUON_ERR_SHAPE = -2,     /* rows/cols/batch < 1, split_rows not dividing rows, sizes too
+                              large: one NS unit padded to the tile (256, or 128 when
+                              min(rows, cols) < 256) must hold under 2^30 elements, and the
+                              launch grids stay under 2^30 workgroups */
   MUON_ERR_DTYPE = -3,     /* unknown dtype / precision / scale enum */
   MUON_ERR_ALIGN = -4,     /* a data pointer is not 16-byte aligned */
   MUON_ERR_WORKSPACE = -5, /* workspace NULL or smaller than muon_workspace_size() */

@@ -109,6 +109,17 @@ def test_bad_shapes_rejected(shape, code):
     assert ws_size([shape])[0] == code
 
 
+def test_unit_size_limit():
+    # A unit's bf16 iterate, padded to the tile (256), must stay under 2^31
+    # bytes (its K-major copies address it with 32-bit offsets):
+    # 32768 x 32512 pads to itself and fits; one more column pads to
+    # 32768 x 32768 = 2^31 bytes and is rejected.
+    assert ws_size([(1, 32768, 32512, 0)])[0] == 0
+    assert ws_size([(1, 32768, 32513, 0)])[0] == -2
+    # the limit is per unit: a batch of large units is fine
+    assert ws_size([(2, 16384, 16384, 0)])[0] == 0
+
+
 def test_bad_hyper_rejected():
     h = muon.default_hyper_c()
     h.n_stages = 0
