@@ -131,10 +131,30 @@ def ns_route(rows, cols, n_units, ns, schedule, cus):
         return "ns"
     if schedule == "launches":
         return "launches"
-    if ns == "bf16" and rows <= cols and rows <= 128:
-        if -(-cols // 128) <= 8 or 2 * n_units >= cus:
-            return "ns"
+    if on_chip(rows, cols, n_units, ns, schedule, cus):
+        return "ns"
     return "ns" if min(rows, cols) >= 256 else "launches"
+
+
+def on_chip(rows, cols, n_units, ns, schedule, cus):
+    """Whether the library runs a stacked pass on the on-chip small-unit
+    kernel (AUTO schedule, bf16 products, wide units with at most 128 rows,
+    short units or at least half as many units as CUs)."""
+    return (schedule == "auto" and ns == "bf16" and rows <= cols and rows <= 128
+            and (-(-cols // 128) <= 8 or 2 * n_units >= cus))
+
+
+def momentum_bytes(matrix_specs, ns, schedule, cus, units_of_shape):
+    """Algorithmic bytes of the momentum kernel per step: G read (2 or 4 B
+    per element), M read and written (8 B), N written: into the bf16
+    iterate (2 B) on the tiled bf16 path, else in fp32 (4 B)."""
+    total = 0
+    for m in matrix_specs:
+        r, c = m.unit_shape
+        small = on_chip(r, c, units_of_shape[(r, c)], ns, schedule, cus)
+        n_bytes = 2 if ns == "bf16" and not small else 4
+        total += m.numel * ((2 if m.grad_dtype == "bf16" else 4) + 8 + n_bytes)
+    return total
 
 
 def kernel_flops(units):
@@ -292,6 +312,10 @@ def main():
     launch_ms = []
     for ev, cnt in zip(evs, counts):
         launch_ms += [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(min(cnt, len(ev) // 2))]
+    # The dominant class's time per step from the timed steps (the one
+    # traced step after warm-up can run at a different clock); the other
+    # classes keep their traced step.
+    per_kind[dominant] = sum(launch_ms) / max(1, args.steps)
 
     flops, exe = class_flops(groups, args.ns, args.schedule, cus)
     ns_flops_step = sum(flops.values()) * iters
@@ -303,9 +327,8 @@ def main():
     ns_ms = sum(per_kind.values())
     ns_tflops = ns_flops_step / (ns_ms * 1e-3) / 1e12
     peak = PEAK_TFLOPS[args.ns]
-    # momentum kernel: G read (2 or 4 B), M read and written (8 B), the fp32
-    # look-ahead written (4 B)
-    elem_bytes = sum(m.numel * (14 if m.grad_dtype == "bf16" else 16) for m in wl.matrices)
+    elem_bytes = momentum_bytes(wl.matrices, args.ns, args.schedule, cus,
+                                {(r, c): n for r, c, n, _ in groups})
     if dominant != "ns":
         kernel_name = f"ns_gemm {dominant}"
     elif any(ns_route(r, c, n, args.ns, args.schedule, cus) == "ns" and min(r, c) < 256

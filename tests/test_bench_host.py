@@ -42,6 +42,27 @@ def test_ns_route_follows_the_auto_rule():
     assert r(64, 128, 1, "bf16", "persistent", 256) == "ns"
 
 
+def test_momentum_bytes_follow_the_route():
+    # 32 x 1024^2, bf16 grads: G 2 + M 8 + N 2 (written into the bf16
+    # iterate of the tiled path) = 12 B per element; with fp32 products N is
+    # written in fp32 (14 B)
+    wl = W.workload(2)
+    shapes = {(r, c): n for r, c, n, _ in bench.unit_groups(wl)}
+    numel = sum(m.numel for m in wl.matrices)
+    assert bench.momentum_bytes(wl.matrices, "bf16", "auto", 256, shapes) == 12 * numel
+    assert bench.momentum_bytes(wl.matrices, "fp32", "auto", 256, shapes) == 14 * numel
+    # the layer's 48 heads run tiled (few long heads): 12 B everywhere; with
+    # many heads they run on chip, which reads N in fp32 (14 B for the heads)
+    wl3 = W.workload(3)
+    g3 = {(r, c): n for r, c, n, _ in bench.unit_groups(wl3)}
+    n3 = sum(m.numel for m in wl3.matrices)
+    assert bench.momentum_bytes(wl3.matrices, "bf16", "auto", 256, g3) == 12 * n3
+    many = dict(g3)
+    many[(128, 4096)] = 1536
+    heads = sum(m.numel for m in wl3.matrices if m.unit_shape == (128, 4096))
+    assert bench.momentum_bytes(wl3.matrices, "bf16", "auto", 256, many) == 12 * n3 + 2 * heads
+
+
 def test_class_flops_split_by_route():
     groups = [(1024, 1024, 4, 4), (128, 4096, 48, 40)]
     alg, exe = bench.class_flops(groups, "bf16", "auto", 256)
