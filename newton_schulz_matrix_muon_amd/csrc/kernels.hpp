@@ -1350,9 +1350,10 @@ __global__ __launch_bounds__(kThreads) void k_ns_small(NsSmallArgs p, ChunkArgs 
 // count).  With one queue per XCC, unit u belongs to queue u % n_queues and
 // only workgroups running on that XCC claim from it: every tile of a unit
 // is then produced and consumed through the same L2, so publishing only
-// needs the stores to have completed.  Readers acquire at agent scope in
-// both cases.  The last workgroup to leave runs, on its own, any queue that
-// no workgroup ever claimed from (an XCC that received none).
+// needs the stores to have completed.  Before a tile's first load, wave 0
+// of the reading workgroup acquires at agent scope once for all its waves
+// (in both cases).  The last workgroup to leave runs, on its own, any queue
+// that no workgroup ever claimed from (an XCC that received none).
 struct NsSched {
   GemmArgs gram, poly, apply;     // cur-independent fields of each product
   const void* gram_op[2];         // Gram operand (both sides) for X in buffer cur
@@ -1382,7 +1383,7 @@ __device__ __forceinline__ int xcc_id() {
 }
 
 // KMODE: 0 = every operand row-major (fp32 path: X^T is kept); 1 = wide
-// bf16 units, B*X reads X K-major; 2 = tall bf16 units, X^T X reads X
+// bf16 units, B'*X reads X K-major; 2 = tall bf16 units, X^T X reads X
 // K-major on both sides.
 template <typename T, int TILE, int KMODE>
 __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p, ChunkArgs ca) {
@@ -1432,10 +1433,12 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
       count_pending();
     }
   };
-  // Wave 0 claims the next item (and reads the error word) once the current
-  // tile's first copies are in flight, so that the round trip overlaps
-  // their latency.  Holding one claimed item ahead cannot stall the
-  // schedule: the earliest
+  // Wave 0 claims the next item (and reads the error word) right after the
+  // current tile's first copies are issued.  The claim's result is read at
+  // once, and as the vector-memory counter completes in order that read
+  // also waits for those copies, which the prologue waits for in any case
+  // (claiming after the tile's last copies had landed measured no faster).
+  // Holding one claimed item ahead cannot stall the schedule: the earliest
   // unfinished item in claim order is always some workgroup's current one
   // (a held item comes after its holder's current, unfinished item).
   // The claimed item is kept as a scalar (-1 after an error), so that the
