@@ -102,7 +102,7 @@ struct GemmArgs {
   void* out16;          // bf16 output (unit 0) or nullptr
   int64_t out_ustride;
   int32_t ldo;
-  void* outt;           // APPLY: transposed operand copy of X' (T), or nullptr
+  void* outt;           // APPLY, fp32 path: transposed operand copy of X' (T); else nullptr
   int32_t ldt;          // its leading dimension (rows of X')
   int32_t sym;          // GRAM/POLY: symmetric output; only tiles tm <= tn run
                         // and each off-diagonal tile also writes its mirror
@@ -467,7 +467,7 @@ constexpr int dma_per_wave() { return TILE * kRowChunks / (64 * gemm_waves<TILE>
 // issue order) before the barrier that publishes a stage.
 //
 // K-major operands (KM, bf16 only) are stored with K along the rows (the
-// iterate X read as the right operand of B*X, or both sides of X^T X): a
+// iterate X read as the right operand of B'*X, or both sides of X^T X): a
 // half-stage holds BK rows of K x TILE columns, a row being TILE * 2 bytes
 // in 16-byte chunks, chunk c of row k stored at c ^ (4 * (k & 3)).  Each
 // row is copied as whole 128-byte lines (the XOR keeps every aligned group
