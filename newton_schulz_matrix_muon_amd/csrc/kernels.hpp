@@ -655,8 +655,10 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
 
   // Schedule of stage k (four K sub-steps kk0..kk3 of 16 bf16 / 8 fp32):
   //   sub-steps 0-2: read the fragments of kk(s+1) | MFMAs of kk(s), with
-  //   the copies of half-stage 2k+4 (A of stage k+2) spread over them, into
-  //   the slot of half 2k-1, which the previous stage's barrier released
+  //   the copies of half-stage 2k+4 (A of stage k+2) spread over sub-steps
+  //   0 and 1 (as early as the slot allows, which gives them the most time
+  //   to land; spread over all three they ran ~1% slower), into the slot of
+  //   half 2k-1, which the previous stage's barrier released
   //   wait for this wave's copies of stage k+1 (half-stage 2k+4 may stay in
   //   flight); s_barrier: stage k+1 is complete and every wave is done
   //   reading stage k
@@ -766,10 +768,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
 #pragma unroll
       for (int j = 0; j < FB; ++j) read_b(SB, ss + 1, (ss + 1) & 1, j);
       __builtin_amdgcn_sched_barrier(0);
-      // this sub-step's share of the copies of half-stage ha, spread over
-      // its MFMA blocks
+      // this sub-step's share of the copies of half-stage ha (half of them
+      // in sub-steps 0 and 1 each, none in 2), spread over its MFMA blocks
       constexpr int M = FA * FB;
-      const int c0 = ss * NI / 3, c1 = (ss + 1) * NI / 3;
+      const int c0 = ss * NI / 2 < NI ? ss * NI / 2 : NI;
+      const int c1 = (ss + 1) * NI / 2 < NI ? (ss + 1) * NI / 2 : NI;
 #pragma unroll
       for (int m = 0; m < M; ++m) {
 #pragma unroll
