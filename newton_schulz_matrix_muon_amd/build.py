@@ -36,9 +36,6 @@ FLAGS = [
     "-Wno-unused-result",
     # the LDS copy names M0 as clobbered on purpose (it sets M0 itself)
     "-Wno-inline-asm",
-    # a wave's atomic on one address becomes one atomic of the lanes' sum,
-    # formed with DPP rather than a scalar loop over the lanes
-    "-mllvm", "-amdgpu-atomic-optimizer-strategy=DPP",
     "-I", os.path.join(ROOT, "include"),
 ]
 

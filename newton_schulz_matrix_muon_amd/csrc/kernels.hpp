@@ -1385,6 +1385,45 @@ __device__ __forceinline__ int xcc_id() {
   return __builtin_amdgcn_readfirstlane(__builtin_amdgcn_s_getreg((3 << 11) | 20)) & 15;
 }
 
+// Atomic add of v at the wave-uniform address p, made by lane 0 alone: the
+// execution mask is narrowed to lane 0 for that one instruction, so the
+// wave makes exactly one request to the L2.  Left to the compiler, a
+// wave's atomic is either rewritten into one atomic of the lanes' sum or
+// issued by all 64 lanes (63 of them adding 0), and which of the two it
+// does changed with unrelated edits elsewhere in the kernel; 64-lane
+// atomics on the one queue line made the whole schedule about five times
+// slower.  The leading s_nop covers an address the compiler has just
+// moved into scalar registers from a vector one.  The returning form waits
+// for its result (and so for every older vector-memory access of the
+// wave) and gives every lane the old value; the other form does not wait.
+__device__ __forceinline__ uint32_t lane0_atomic_add(uint32_t* p, uint32_t v) {
+  uint32_t old;
+  uint64_t saved;
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b64 %[sv], exec\n\t"
+      "s_mov_b64 exec, 1\n\t"
+      "global_atomic_add %[old], %[zero], %[v], %[base] sc0\n\t"
+      "s_waitcnt vmcnt(0)\n\t"
+      "s_mov_b64 exec, %[sv]"
+      : [old] "=&v"(old), [sv] "=&s"(saved)
+      : [zero] "v"(0u), [v] "v"(v), [base] "s"(p)
+      : "memory");
+  return __builtin_amdgcn_readfirstlane(old);
+}
+__device__ __forceinline__ void lane0_atomic_add_noret(uint32_t* p, uint32_t v) {
+  uint64_t saved;
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b64 %[sv], exec\n\t"
+      "s_mov_b64 exec, 1\n\t"
+      "global_atomic_add %[zero], %[v], %[base]\n\t"
+      "s_mov_b64 exec, %[sv]"
+      : [sv] "=&s"(saved)
+      : [zero] "v"(0u), [v] "v"(v), [base] "s"(p)
+      : "memory");
+}
+
 // KMODE: 0 = every operand row-major (fp32 path: X^T is kept); 1 = wide
 // bf16 units, B'*X reads X K-major; 2 = tall bf16 units, X^T X reads X
 // K-major on both sides.
@@ -1392,8 +1431,8 @@ template <typename T, int TILE, int KMODE>
 __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p, ChunkArgs ca) {
   // Every branch below is uniform across the workgroup or across a wave:
   // the scheduling work (claim, completion count, dependency wait) is done
-  // by all of wave 0 with only lane 0 contributing to the atomics, never
-  // under a per-lane condition.  A per-lane branch around it lets the
+  // by all of wave 0, whose atomics lane 0 makes alone (lane0_atomic_add),
+  // never under a per-lane condition.  A per-lane branch around it lets the
   // compiler thread the tail of one iteration into the head of the next for
   // that lane alone, and the other lanes would then reach the barriers on
   // stale state.
@@ -1406,7 +1445,6 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
   const int nq = p.n_queues;
   const bool local = nq > 1;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const uint32_t one = (threadIdx.x & 63) == 0 ? 1u : 0u;  // lane 0's share
   uint32_t* const left = p.queue + nq;                    // workgroups that have left
   // units of queue qq: qq, qq + nq, ...
   auto units_of = [&](int qq) { return ca.n_units > qq ? (ca.n_units - qq + nq - 1) / nq : 0; };
@@ -1425,7 +1463,7 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
   auto count_pending = [&]() {  // wave 0; every wave's stores of the tile are complete
     if (wave == 0 && pending >= 0) {
       if (!local) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-      __hip_atomic_fetch_add(p.done + pending, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      lane0_atomic_add_noret(p.done + pending, 1u);
     }
     pending = -1;
   };
@@ -1449,10 +1487,9 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
   bool have_next = false;
   int next_item = 0;
   auto claim = [&]() {  // wave 0
-    const uint32_t raw =
-        __hip_atomic_fetch_add(p.queue + q, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t raw = lane0_atomic_add(p.queue + q, 1u);
     const uint32_t err = __hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    next_item = __builtin_amdgcn_readfirstlane(err) != 0u ? -1 : (int)__builtin_amdgcn_readfirstlane(raw);
+    next_item = __builtin_amdgcn_readfirstlane(err) != 0u ? -1 : (int)raw;
   };
   for (;;) {
     if (wave == 0) {
@@ -1472,8 +1509,7 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
         // Count this workgroup out; the last one continues alone.
         __syncthreads();
         if (wave == 0)
-          s_go = __builtin_amdgcn_readfirstlane((int)__hip_atomic_fetch_add(
-                     left, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) == (int)gridDim.x - 1;
+          s_go = (int)lane0_atomic_add(left, 1u) == (int)gridDim.x - 1;
         __syncthreads();
         if (!__builtin_amdgcn_readfirstlane(s_go)) break;
         alone = true;
