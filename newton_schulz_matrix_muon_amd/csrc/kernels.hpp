@@ -1393,9 +1393,12 @@ __device__ __forceinline__ int xcc_id() {
 // does changed with unrelated edits elsewhere in the kernel; 64-lane
 // atomics on the one queue line made the whole schedule about five times
 // slower.  The leading s_nop covers an address the compiler has just
-// moved into scalar registers from a vector one.  The returning form waits
-// for its result (and so for every older vector-memory access of the
-// wave) and gives every lane the old value; the other form does not wait.
+// moved into scalar registers from a vector one, the trailing one the
+// execution-mask write the compiler does not see (an instruction that
+// reads the mask through DPP must not follow it at once).  The returning
+// form waits for its result (and so for every older vector-memory access
+// of the wave) and gives every lane the old value; the other form does not
+// wait.
 __device__ __forceinline__ uint32_t lane0_atomic_add(uint32_t* p, uint32_t v) {
   uint32_t old;
   uint64_t saved;
@@ -1405,7 +1408,8 @@ __device__ __forceinline__ uint32_t lane0_atomic_add(uint32_t* p, uint32_t v) {
       "s_mov_b64 exec, 1\n\t"
       "global_atomic_add %[old], %[zero], %[v], %[base] sc0\n\t"
       "s_waitcnt vmcnt(0)\n\t"
-      "s_mov_b64 exec, %[sv]"
+      "s_mov_b64 exec, %[sv]\n\t"
+      "s_nop 4"
       : [old] "=&v"(old), [sv] "=&s"(saved)
       : [zero] "v"(0u), [v] "v"(v), [base] "s"(p)
       : "memory");
@@ -1418,7 +1422,8 @@ __device__ __forceinline__ void lane0_atomic_add_noret(uint32_t* p, uint32_t v) 
       "s_mov_b64 %[sv], exec\n\t"
       "s_mov_b64 exec, 1\n\t"
       "global_atomic_add %[zero], %[v], %[base]\n\t"
-      "s_mov_b64 exec, %[sv]"
+      "s_mov_b64 exec, %[sv]\n\t"
+      "s_nop 4"
       : [sv] "=&s"(saved)
       : [zero] "v"(0u), [v] "v"(v), [base] "s"(p)
       : "memory");
@@ -1462,7 +1467,14 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
   bool alone = false;    // running unclaimed queues after every other workgroup left
   auto count_pending = [&]() {  // wave 0; every wave's stores of the tile are complete
     if (wave == 0 && pending >= 0) {
-      if (!local) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      if (!local) {
+        // Other XCCs read the tile from memory: write this L2 back and wait
+        // for the write-back before the count can be seen.  The compiler
+        // drops its own wait after the write-back when the tile's stores
+        // are already complete, as they are here.
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        wait_vmcnt<0>();
+      }
       lane0_atomic_add_noret(p.done + pending, 1u);
     }
     pending = -1;
