@@ -11,7 +11,9 @@ spectral scale, bf16 NS products (fp32 accumulation).
 Prints one JSON line with matrices/s (the metric), NS TFLOP/s and its
 fraction of the bf16 MFMA peak, the roofline of the dominant kernel class
 (timed live with HIP events around each of its launches on the step's
-stream), and a float64 CPU-oracle baseline on a bounded sample.
+stream), a float64 CPU-oracle baseline on a bounded sample, and the same NS
+iterations written with torch's bf16 batched products on the workload's
+largest group of equal-shape units (a vendor-library reference on this GPU).
 """
 
 from __future__ import annotations
@@ -43,6 +45,9 @@ def parse():
                          "launch per pass, or one launch per product")
     ap.add_argument("--grad-sets", type=int, default=4, help="distinct resident gradient batches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-library-baseline", action="store_true",
+                    help="skip timing the same NS iterations written with torch's bf16 batched "
+                         "products on the largest unit group")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after the timed region, run one plain copy kernel over this many MiB "
@@ -232,6 +237,62 @@ def cpu_baseline(wl, hyper_o, seconds):
     }
 
 
+def library_group(groups):
+    """The unit shape with the most nominal NS FLOPs, and its unit count."""
+    def work(g):
+        r, c, n, _ = g
+        sm, lg = min(r, c), max(r, c)
+        return n * (4 * sm * sm * lg + 2 * sm ** 3)
+    r, c, n, _ = max(groups, key=work)
+    return r, c, n
+
+
+def gpu_library_baseline(groups, dev, stages, reps=3):
+    """The same Newton-Schulz iterations on the workload's largest group of
+    equal-shape units, written with torch's bf16 batched products (the ROCm
+    GEMM libraries): per iteration A = X X^T, B = b*A + c*A*A, X = a*X + B X
+    (baddbmm for the last two, X^T made contiguous first).  Units start as
+    normalised N(0, 1) matrices on the smaller side.  Timed with HIP events
+    on the current stream, median over `reps` runs after one warm-up."""
+    import torch
+
+    r, c, n = library_group(groups)
+    sm, lg = min(r, c), max(r, c)
+    gen = torch.Generator(device=dev).manual_seed(0)
+    x0 = torch.randn((n, sm, lg), device=dev, generator=gen)
+    x0 = (x0 / torch.linalg.vector_norm(x0, dim=(1, 2), keepdim=True)).to(torch.bfloat16)
+
+    def run():
+        x = x0.clone()
+        for steps, (a, b, cc) in stages:
+            for _ in range(steps):
+                xt = x.transpose(1, 2).contiguous()
+                am = torch.bmm(x, xt)
+                bm = torch.baddbmm(am, am, am, beta=b, alpha=cc)
+                x = torch.baddbmm(x, bm, x, beta=a, alpha=1.0)
+        return x
+
+    run()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = sorted(times)[len(times) // 2]
+    iters = sum(k for k, _ in stages)
+    flops = n * iters * (4 * sm * sm * lg + 2 * sm ** 3)
+    return {
+        "ns_ms": ms,
+        "ns_tflops": flops / (ms * 1e-3) / 1e12,
+        "kind": "torch.bmm/baddbmm, bf16",
+        "sample": f"{n} units of {sm}x{lg}, {iters} NS iterations, median of {reps} runs",
+    }
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -401,6 +462,12 @@ def main():
             "launches_timed": len(launch_ms),
         },
     }
+    if not args.no_library_baseline and args.ns == "bf16":
+        lib = gpu_library_baseline(groups, dev, hyper.stages)
+        if len(groups) == 1:
+            # one unit shape: the same units as this step's NS time
+            lib["this_library_speedup"] = lib["ns_ms"] / ns_ms
+        line["gpu_library_baseline"] = lib
     if not args.no_cpu_baseline:
         import oracle
 

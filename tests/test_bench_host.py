@@ -30,6 +30,15 @@ def test_unit_groups_merge_heads_of_one_shape():
     assert sum(n for n, _ in g.values()) == wl.units
 
 
+def test_library_baseline_takes_the_group_with_the_most_work():
+    # the transformer layer: 48 heads of 128 x 4096 carry far less NS work
+    # than the three 4096 x 14336 MLP matrices (two of one unit shape)
+    r, c, n = bench.library_group(bench.unit_groups(W.workload(3)))
+    assert (min(r, c), max(r, c)) == (4096, 14336) and n == 2
+    assert bench.library_group([(1024, 1024, 32, 32)]) == (1024, 1024, 32)
+    assert bench.library_group([(128, 4096, 1536, 1536), (4096, 4096, 32, 32)]) == (4096, 4096, 32)
+
+
 def test_ns_route_follows_the_auto_rule():
     r = bench.ns_route
     assert r(1024, 1024, 32, "bf16", "auto", 256) == "ns"            # 256 tiles: persistent
