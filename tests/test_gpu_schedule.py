@@ -104,3 +104,41 @@ def test_persistent_with_xccs_left_without_workgroups(gpu_lib, workgroups, monke
         out[sched] = params[0]
     monkeypatch.delenv("MUON_PERSISTENT_WORKGROUPS")
     assert torch.equal(out["launches"], out["persistent"])
+
+
+_FRESH = r"""
+import sys
+import torch
+sys.path.insert(0, sys.argv[1])
+from newton_schulz_matrix_muon_amd import muon
+g = torch.Generator().manual_seed(int(sys.argv[2]))
+shapes = [(4, 100, 200), (3, 300, 200), (6, 256, 384)]  # one queue each; 128- and 256-row tiles
+xs = [torch.randn(s, generator=g).cuda() for s in shapes]
+res = {}
+for sched in ("persistent", "launches"):  # the persistent launch is the process's first
+    outs, _ = muon.newton_schulz(xs, hyper=muon.Hyper(schedule=sched))
+    torch.cuda.synchronize()
+    res[sched] = [o.cpu() for o in outs]
+same = all(torch.equal(a, b) for a, b in zip(res["persistent"], res["launches"]))
+print("agree" if same else "differ", flush=True)
+sys.exit(0 if same else 3)
+"""
+
+
+@pytest.mark.parametrize("seed", [1, 2, 3])
+def test_single_queue_first_launch_of_a_fresh_process(seed):
+    # Units on one queue run their tiles on several XCCs, so a tile is
+    # published through an L2 write-back; the first persistent launch of a
+    # fresh process, on small single-queue units, is checked bit for bit
+    # against the per-product launches.  One child process at a time.
+    import os
+    import subprocess
+    import sys
+
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    print(f"[schedule fresh process] seed {seed}", flush=True)
+    r = subprocess.run([sys.executable, "-c", _FRESH, root, str(seed)], capture_output=True, text=True,
+                       timeout=180)
+    assert r.returncode == 0 and "agree" in r.stdout, (r.returncode, r.stdout[-500:], r.stderr[-2000:])
