@@ -1398,7 +1398,8 @@ __device__ __forceinline__ int xcc_id() {
 // reads the mask through DPP must not follow it at once).  The returning
 // form waits for its result (and so for every older vector-memory access
 // of the wave) and gives every lane the old value; the other form does not
-// wait.
+// wait.  Both are called in wave-uniform code with every lane active: lane
+// 0 must hold v and the zero offset when the mask is narrowed.
 __device__ __forceinline__ uint32_t lane0_atomic_add(uint32_t* p, uint32_t v) {
   uint32_t old;
   uint64_t saved;
