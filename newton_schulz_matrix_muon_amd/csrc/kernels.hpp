@@ -31,7 +31,7 @@
 //                   workgroup, A and B on chip, one pass over X per
 //                   iteration (bf16 products).
 //   ns_persistent   the three products of every iteration in one launch:
-//                   workgroups claim tiles in order and wait on per-unit
+//                   workgroups claim tiles in order and wait on per-panel
 //                   completion counts, so tiles of different units and
 //                   phases overlap (no launch boundary between products).
 // The three products are the quintic step a*X + b*(X X^T)X + c*(X X^T)^2 X of
@@ -286,7 +286,7 @@ __global__ __launch_bounds__(kThreads) void k_momentum(ChunkArgs ca, float* __re
 constexpr double kFoldMin = 0x1p-80, kFoldMax = 0x1p80;  // bounds on nu^2
 
 // One workgroup per unit: fixed-order sum of the partials (first wave).
-// It also clears the persistent schedule's per-unit counts and claim
+// It also clears the persistent schedule's counts of the unit and claim
 // counter (when given), and the error word (when given).  With nb (the
 // folded path: unit iterates of x_stride bf16 elements holding N), inv_nu
 // receives the first iteration's scale instead: 1/nu inside the fold's
@@ -296,6 +296,7 @@ __global__ __launch_bounds__(kThreads) void k_norm_finish(const double* __restri
                                                           float* __restrict__ inv_nu,
                                                           int32_t* __restrict__ flag,
                                                           uint32_t* __restrict__ sched_done,
+                                                          int done_per_unit,
                                                           uint32_t* __restrict__ sched_queue,
                                                           int n_queue_words,
                                                           uint32_t* __restrict__ err,
@@ -319,11 +320,13 @@ __global__ __launch_bounds__(kThreads) void k_norm_finish(const double* __restri
   if (threadIdx.x == 0) {
     flag[u] = zero ? 0 : 1;
     inv_nu[u] = rescale ? 1.0f : inv;
-    if (sched_done) sched_done[u] = 0u;
     if (u == 0 && sched_queue)
       for (int i = 0; i < n_queue_words; ++i) sched_queue[i] = 0u;
     if (u == 0 && err) *err = 0u;
   }
+  if (sched_done)
+    for (int i = threadIdx.x; i < done_per_unit; i += kThreads)
+      sched_done[(int64_t)u * done_per_unit + i] = 0u;
   if (rescale) {
     uint4* xu = reinterpret_cast<uint4*>(nb + (int64_t)u * x_stride);
     for (int64_t e = threadIdx.x; e < x_stride / 8; e += kThreads) {
@@ -1341,8 +1344,8 @@ __global__ __launch_bounds__(kThreads) void k_ns_small(NsSmallArgs p, ChunkArgs 
 // claim order: for each iteration, the Gram tiles of every unit, then the
 // polynomial tiles, then the apply tiles (unit-major within a phase).  A
 // workgroup claims the next item from an atomic counter, waits until the
-// item's unit has finished every item of the phases before it (a per-unit
-// count of finished items), runs the tile and adds one to the count.  An
+// tile panels it reads are final (counts of finished tiles per panel, see
+// below), runs the tile and adds one to the counts of its panels.  An
 // item only waits for items that precede it in claim order, and those were
 // claimed by running workgroups, so the schedule always makes progress; the
 // wait is still bounded by a wall-clock limit, after which the launch stops
@@ -1372,10 +1375,13 @@ struct NsSched {
   float sa[4], sb[4], sc[4];      // coefficients of each stage
   int32_t tg;                     // tiles per unit of a symmetric product
   int32_t ta;                     // tiles per unit of the apply product
+  int32_t apply_s_m;              // 1: an apply tile's small-side panel is its
+                                  // row (wide units), 0: its column (tall)
   int32_t n_queues;               // 1, or one queue per XCC (see below)
   uint32_t* queue;                // per queue: next item to claim; then the
                                   // count of workgroups that have left
-  uint32_t* done;                 // per unit: finished items
+  uint32_t* done;                 // per unit: finished tiles per small-side
+                                  // panel, for each of the three products
   uint32_t* err;                  // set when a wait timed out
   uint64_t timeout_ticks;         // wall-clock ticks
 };
@@ -1456,18 +1462,33 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
   auto units_of = [&](int qq) { return ca.n_units > qq ? (ca.n_units - qq + nq - 1) / nq : 0; };
   int q = local ? xcc_id() % nq : 0;
   int uq = units_of(q);
-  // A finished tile is counted (its unit's completion count raised) once
-  // every wave's stores of it are complete.  With XCC-local queues the
-  // count is deferred into the next tile's prologue, whose in-order copy
-  // wait covers the stores; it is made at once (a flush) before any wait
-  // that could block, before an item that runs no tile and on every exit,
-  // so no workgroup ever blocks while holding an uncounted tile.  With one
-  // queue the release also writes the L2 back, and tiles are flushed as
-  // they end.
-  int pending = -1;      // unit of the finished tile not yet counted
-  bool alone = false;    // running unclaimed queues after every other workgroup left
+  // Completion counts, per unit three arrays of ts words (Gram, polynomial,
+  // apply), indexed by tile panel on the small side: a Gram or polynomial
+  // tile (r, c) counts in panels r and c (once when r == c), an apply tile
+  // in its small-side panel.  Each iteration adds ts to every Gram and
+  // polynomial panel and tl to every apply panel.  A tile waits only for
+  // the panels it reads:
+  //   Gram (r, c) of iteration it > 0: apply panels r and c at it * tl;
+  //   polynomial (r, c): Gram panels r and c at (it + 1) * ts;
+  //   apply with small-side panel i: polynomial panel i at (it + 1) * ts.
+  // Each of these points to items earlier in claim order.  The buffers that
+  // are rewritten every iteration (A, B', the two iterates) cannot be
+  // overwritten while still read: every such write depends, through those
+  // chains, on the whole earlier phase that reads them.
+  // A finished tile is counted once every wave's stores of it are
+  // complete.  With XCC-local queues the count is deferred into the next
+  // tile's prologue, whose in-order copy wait covers the stores; it is
+  // made at once (a flush) before any wait that could block, before an
+  // item that runs no tile and on every exit, so no workgroup ever blocks
+  // while holding an uncounted tile.  With one queue the release also
+  // writes the L2 back, and tiles are flushed as they end.
+  const int ts = p.gram.tiles_m;
+  const int tl = p.ta / ts;
+  uint32_t* pend_a = nullptr;  // counts of the finished tile not yet made
+  uint32_t* pend_b = nullptr;
+  bool alone = false;  // running unclaimed queues after every other workgroup left
   auto count_pending = [&]() {  // wave 0; every wave's stores of the tile are complete
-    if (wave == 0 && pending >= 0) {
+    if (wave == 0 && pend_a) {
       if (!local) {
         // Other XCCs read the tile from memory: write this L2 back and wait
         // for the write-back before the count can be seen.  The compiler
@@ -1476,12 +1497,13 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         wait_vmcnt<0>();
       }
-      lane0_atomic_add_noret(p.done + pending, 1u);
+      lane0_atomic_add_noret(pend_a, 1u);
+      if (pend_b) lane0_atomic_add_noret(pend_b, 1u);
     }
-    pending = -1;
+    pend_a = pend_b = nullptr;
   };
   auto flush = [&]() {  // every wave
-    if (pending >= 0) {
+    if (pend_a) {
       wait_vmcnt<0>();
       __syncthreads();
       count_pending();
@@ -1558,10 +1580,42 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
     t = r - u * tpu;
     u = q + nq * u;
     const bool live = __builtin_amdgcn_readfirstlane(p.gram.flag[u]) != 0;
-    // A zero unit computes nothing, so its items wait for nothing.
-    const uint32_t need =
-        (uint32_t)(it * per_unit + (phase == GRAM ? 0 : phase == POLY ? p.tg : 2 * p.tg));
-    // One look at the completion count; if the item must wait, the pending
+    int tm, tn;
+    if (phase == APPLY) {
+      tm = t / p.apply.tiles_n;
+      tn = t - tm * p.apply.tiles_n;
+    } else {
+      sym_tile(t, ts, tm, tn);
+    }
+    // Small-side panels the tile reads and completes, and the counts it
+    // waits for (a zero unit computes nothing, so its items wait for
+    // nothing).
+    const int pa = phase == APPLY ? (p.apply_s_m ? tm : tn) : tm;
+    const int pb = phase == APPLY ? pa : tn;
+    uint32_t* const cnt = p.done + (int64_t)u * 3 * ts;  // Gram | polynomial | apply
+    uint32_t* dep = nullptr;  // the counts waited for: dep[pa] and dep[pb]
+    uint32_t need = 0;
+    if (phase == GRAM) {
+      if (it > 0) {
+        dep = cnt + 2 * ts;
+        need = (uint32_t)(it * tl);
+      }
+    } else if (phase == POLY) {
+      dep = cnt;
+      need = (uint32_t)((it + 1) * ts);
+    } else {
+      dep = cnt + ts;
+      need = (uint32_t)((it + 1) * ts);
+    }
+    auto deps_met = [&]() -> bool {  // wave 0
+      if (!dep) return true;
+      if (__builtin_amdgcn_readfirstlane(
+              __hip_atomic_load(dep + pa, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < need)
+        return false;
+      return pb == pa || __builtin_amdgcn_readfirstlane(__hip_atomic_load(
+                             dep + pb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) >= need;
+    };
+    // One look at the completion counts; if the item must wait, the pending
     // tile is counted first (it may be what the wait is for).  Wave 0 makes
     // the producers' results visible to the whole workgroup before the
     // barrier that releases the other waves to load them: an acquire at
@@ -1574,9 +1628,7 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
     };
     if (wave == 0) {
       int ready = 1;
-      if (live && need > 0u)
-        ready = __builtin_amdgcn_readfirstlane(__hip_atomic_load(
-                    p.done + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) >= need;
+      if (live) ready = deps_met();
       if (ready && live) acquire();
       s_go = ready;
     }
@@ -1588,9 +1640,7 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
       if (wave == 0) {
         int go = 1;
         const uint64_t t0 = wall_clock64();
-        uint32_t d = __builtin_amdgcn_readfirstlane(
-            __hip_atomic_load(p.done + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        while (d < need) {
+        while (!deps_met()) {
           const uint32_t e = __builtin_amdgcn_readfirstlane(
               __hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
           if (e != 0u || wall_clock64() - t0 > p.timeout_ticks) {
@@ -1599,8 +1649,6 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
             break;
           }
           __builtin_amdgcn_s_sleep(2);
-          d = __builtin_amdgcn_readfirstlane(
-              __hip_atomic_load(p.done + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
         }
         if (go) acquire();
         s_go = go;
@@ -1626,8 +1674,6 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
       if (live) {
         GemmArgs g = p.gram;
         g.a = g.b = cur ? p.gram_op[1] : p.gram_op[0];
-        int tm, tn;
-        sym_tile(t, g.tiles_m, tm, tn);
         if (it == 0 && g.fold)
           gemm_tile<GRAM, T, TILE, KMODE == 2 ? 3 : 0, true>(g, ca, u, tm, tn, claim_next,
                                                             count_pending);
@@ -1648,13 +1694,10 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
         g.ca = a;
         g.cb = cb;
         g.cc = cc;
-        int tm, tn;
-        sym_tile(t, g.tiles_m, tm, tn);
         gemm_tile<POLY, T, TILE, 0>(g, ca, u, tm, tn, claim_next, count_pending);
       }
     } else {
       const int fm = it == p.n_iter - 1 ? p.final_mode : (int)FINAL_NONE;
-      const int tm = t / p.apply.tiles_n, tn = t - (t / p.apply.tiles_n) * p.apply.tiles_n;
       if (live) {
         GemmArgs g = p.apply;
         g.final_mode = fm;
@@ -1673,7 +1716,10 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
         zero_unit_tile<TILE>(ca, fm, u, tm * TILE, tn * TILE);
       }
     }
-    if (live) pending = u;
+    if (live) {
+      pend_a = cnt + (phase == GRAM ? 0 : phase == POLY ? ts : 2 * ts) + pa;
+      pend_b = pb != pa ? pend_a + (pb - pa) : nullptr;
+    }
     if (!local) flush();
     // The next tile's first copies overwrite the LDS that this tile's
     // epilogue staged through; the barrier after the next claim orders them.

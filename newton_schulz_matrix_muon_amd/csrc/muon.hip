@@ -80,6 +80,10 @@ bool small_possible(const Chunk& c, const muon_hyper* h) {
          c.rows_u <= kSmall && c.rows_pad == kSmall;
 }
 
+// Words of persistent-schedule completion counts per unit: three per tile
+// panel on the small side.
+int64_t done_words(const Chunk& c) { return 3 * (c.s_pad / c.tile); }
+
 Layout layout_of(const Chunk& c, const muon_hyper* h) {
   const bool bf16 = h->ns_precision == MUON_NS_BF16;
   Layout L{};
@@ -113,7 +117,9 @@ Layout layout_of(const Chunk& c, const muon_hyper* h) {
   L.partials = take(U * (size_t)c.blocks_per_unit * 8);
   L.inv_nu = take(U * 4);
   L.flag = take(U * 4);
-  L.done = take(U * 4);   // persistent schedule: finished items per unit
+  // persistent schedule: finished tiles per small-side tile panel, for each
+  // of the three products
+  L.done = take(U * done_words(c) * 4);
   L.queue = take(4 * (kMaxQueues + 1));  // persistent schedule: claim counters, leavers
   L.total = off;
   return L;
@@ -480,7 +486,8 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
   uint32_t* queue = reinterpret_cast<uint32_t*>(ws + L.queue);
   uint32_t* err = reinterpret_cast<uint32_t*>(ws);
   hipLaunchKernelGGL(k_norm_finish, dim3(U), dim3(kThreads), 0, s, partials, c.blocks_per_unit,
-                     inv_nu, flag, done, queue, kMaxQueues + 1, first_chunk ? err : nullptr, nb,
+                     inv_nu, flag, done, (int)done_words(c), queue, kMaxQueues + 1,
+                     first_chunk ? err : nullptr, nb,
                      (int64_t)(c.rows_pad * c.cols_pad));
   if (small) {
     int total_it = 0;
@@ -630,6 +637,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
     // takes the last stage whose beginning it has reached.
     p.tg = tg;
     p.ta = ta;
+    p.apply_s_m = c.tall ? 0 : 1;
     // One queue per XCC when the units spread over the XCCs with at most
     // an eighth of the slots idle; one queue otherwise.
     const int nx = di.xccs;

@@ -1,5 +1,5 @@
 """The persistent NS launch (one launch per stacked pass, workgroups
-claiming tiles and waiting on per-unit completion counts) against one launch
+claiming tiles and waiting on per-panel completion counts) against one launch
 per product: both run the same tile code on the same inputs, so their
 results must agree bit for bit, and the persistent launch must report a
 clean status."""
