@@ -1609,11 +1609,11 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
     }
     auto deps_met = [&]() -> bool {  // wave 0
       if (!dep) return true;
-      if (__builtin_amdgcn_readfirstlane(
-              __hip_atomic_load(dep + pa, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) < need)
-        return false;
-      return pb == pa || __builtin_amdgcn_readfirstlane(__hip_atomic_load(
-                             dep + pb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) >= need;
+      // both loads in flight at once (the same word twice when pb == pa)
+      const uint32_t da = __hip_atomic_load(dep + pa, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t db = __hip_atomic_load(dep + pb, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      const uint32_t d = __builtin_amdgcn_readfirstlane(da < db ? da : db);
+      return d >= need;
     };
     // One look at the completion counts; if the item must wait, the pending
     // tile is counted first (it may be what the wait is for).  Wave 0 makes
