@@ -111,6 +111,28 @@ def test_dependencies_point_back_and_order_every_access(ts, tl):
             assert ordered(last, y), ("read after write", last, y, reg)
 
 
+@pytest.mark.parametrize("ts,tl", [(1, 2), (2, 3), (3, 2), (4, 4)])
+def test_counts_cannot_run_ahead(ts, tl):
+    # The kernel keeps one cumulative count per product and panel and waits
+    # for count >= (iterations so far) * (tiles per panel per iteration).
+    # That equals waiting for the exact tiles above only if no tile can
+    # finish before every tile of the same product and panel of the
+    # previous iteration: each such tile is among its dependencies.
+    order = items(ts, tl, 4)
+    before = closure(order, ts, tl)
+
+    def panels(x):
+        return set(x[2]) if x[1] != "A" else {x[2][0]}
+
+    for x in order:
+        it, ph, _ = x
+        if it == 0:
+            continue
+        for y in order:
+            if y[0] == it - 1 and y[1] == ph and panels(x) & panels(y):
+                assert y in before[x], (x, y)
+
+
 def test_iteration_zero_reads_no_earlier_item():
     # the first Gram reads N / nu, written before the launch
     assert deps((0, "G", (0, 1)), 2, 3) == []
