@@ -114,6 +114,30 @@ def test_ns_split_heads_and_banks(gpu_lib, prec):
     assert worst <= TOL_NS[prec]
 
 
+# A caller's own schedule of up to four stages: a zero-step stage (skipped),
+# a cubic stage (c = 0: X <- 1.5 X - 0.5 (X X^T) X) and the two of the pages.
+CUSTOM_STAGES = [(3, (3.4445, -4.7750, 2.0315)), (0, (1.0, 1.0, 1.0)), (2, (1.5, -0.5, 0.0)),
+                 (1, (2.0, -1.5, 0.5))]
+
+
+@pytest.mark.parametrize("prec", ["fp32", "bf16"])
+@pytest.mark.parametrize("shape", [(2, 256, 512), (2, 200, 300), (2, 128, 300)],
+                         ids=["tiles-256", "tiles-128", "128-rows"])  # 128 rows: on chip in bf16
+def test_ns_custom_stages_match_oracle(gpu_lib, shape, prec):
+    say(f"[ns custom stages] shape={shape} prec={prec}")
+    x = _seeded(shape, 777 + shape[1])
+    h = gpu_lib.Hyper(ns_precision=prec, stages=CUSTOM_STAGES)
+    outs, _ = gpu_lib.newton_schulz([x], hyper=h)
+    torch.cuda.synchronize()
+    sched = tuple((k, tuple(c)) for k, c in CUSTOM_STAGES)
+    worst = 0.0
+    for i in range(shape[0]):
+        ref = oracle.newton_schulz(f64(x[i]), schedule=sched)
+        worst = max(worst, rel(f64(outs[0][i]), ref))
+    say(f"   worst rel err {worst:.3e}")
+    assert worst <= TOL_NS[prec]
+
+
 def test_ns_zero_unit_gives_zero(gpu_lib):
     x = _seeded((2, 64, 128), 5)
     x[1].zero_()
