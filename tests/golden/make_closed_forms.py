@@ -12,7 +12,9 @@ weight decay W(1 - eta*lambda) - eta*O), section 2 (Frobenius normalisation,
 quintic step, hybrid schedule 8 x (3.4445, -4.7750, 2.0315) + 2 x (2, -1.5,
 0.5)), section-2 sketch defaults lr 2.7e-4, mu 0.95, wd 0.1, gamma 0.18.
 Megatron-LM PR "Scaling for MuP over Muon optimizer": unit_rms_norm scale
-sqrt(fan_out / fan_in).
+sqrt(fan_out / fan_in).  RFC-0023 方案 1: the EMA-style buffer
+mu = beta*mu + (1 - beta)*g and its bias-corrected look-ahead
+beta*bc(mu, t+1) + (1 - beta)*bc(g, t), with t the 1-based step.
 
 Run:  python tests/golden/make_closed_forms.py
 """
@@ -51,11 +53,24 @@ def ns_diag(d: list[D]) -> list[D]:
     return [phi(v / nu) for v in d]
 
 
-def step_diag(w, g, m, n_rows, n_cols, scale_mode):
+def bc(x: D, count: int) -> D:
+    """Bias correction x / (1 - mu^count)."""
+    return x / (D(1) - MU**count)
+
+
+def step_diag(w, g, m, n_rows, n_cols, scale_mode, style="sgd", t=1):
     """One Muon step on a diagonal n_rows x n_cols matrix given by its
-    diagonal entries (w is the full matrix as nested lists)."""
-    m_new = [MU * mi + gi for mi, gi in zip(m, g)]
-    look = [MU * mi + gi for mi, gi in zip(m_new, g)]
+    diagonal entries (w is the full matrix as nested lists).  style "sgd":
+    classic momentum with the look-ahead on the updated buffer; "ema": the
+    buffer is an exponential moving average and the look-ahead combines the
+    buffer corrected with count t+1 and the gradient corrected with count t
+    (RFC-0023 方案 1), t being the 1-based step."""
+    if style == "sgd":
+        m_new = [MU * mi + gi for mi, gi in zip(m, g)]
+        look = [MU * mi + gi for mi, gi in zip(m_new, g)]
+    else:
+        m_new = [MU * mi + (D(1) - MU) * gi for mi, gi in zip(m, g)]
+        look = [MU * bc(mi, t + 1) + (D(1) - MU) * bc(gi, t) for mi, gi in zip(m_new, g)]
     o = ns_diag(look)
     if scale_mode == "spectral":
         scale = D(max(n_rows, n_cols)).sqrt() * GAMMA
@@ -108,6 +123,20 @@ def main():
                   "steps": [{"g": [f(v) for v in g], "w": [[f(v) for v in r] for r in w],
                              "m": [f(v) for v in m], "nesterov": [f(v) for v in look],
                              "o_diag": [f(v) for v in o], "scale": f(scale)}]})
+    # (4) 3x5 diagonal, EMA-style look-ahead with bias correction, two steps
+    # with different gradients (t = 1, 2), spectral scale.
+    rows, cols = 3, 5
+    w0 = [[D(i * cols + j + 1) / D(64) for j in range(cols)] for i in range(rows)]
+    w, m = [r[:] for r in w0], [D(0)] * rows
+    steps = []
+    for t, g in enumerate(([D(2), D("-0.5"), D(1)], [D("-1.25"), D(3), D("0.75")]), start=1):
+        w, m, look, o, scale = step_diag(w, g, m, rows, cols, "spectral", style="ema", t=t)
+        steps.append({"g": [f(v) for v in g], "w": [[f(v) for v in r] for r in w],
+                      "m": [f(v) for v in m], "nesterov": [f(v) for v in look],
+                      "o_diag": [f(v) for v in o], "scale": f(scale)})
+    cases.append({"name": "3x5_diag_ema_two_steps", "rows": rows, "cols": cols,
+                  "scale": "spectral", "nesterov_style": "ema",
+                  "w0": [[f(v) for v in r] for r in w0], "steps": steps})
     # Scalar map values.
     table = {
         "phi(1)": f(phi(D(1))),

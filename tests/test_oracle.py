@@ -240,15 +240,18 @@ def test_closed_form_worked_examples():
     gold = json.load(open(GOLDEN))
     for case in gold["cases"]:
         rows, cols = case["rows"], case["cols"]
-        h = Hyper(scale=case["scale"])
+        h = Hyper(scale=case["scale"], nesterov_style=case.get("nesterov_style", "sgd"))
         w = np.array([[float(v) for v in r] for r in case["w0"]])
         m = np.zeros((rows, cols))
         k = min(rows, cols)
-        for st in case["steps"]:
+        for t, st in enumerate(case["steps"], start=1):
             g = np.zeros((rows, cols))
             g[np.arange(k), np.arange(k)] = [float(v) for v in st["g"]]
-            w, m, rec = oracle.muon_step(w, g, m, h)
+            w, m, rec = oracle.muon_step(w, g, m, h, step=t)
             np.testing.assert_allclose(np.diag(m), [float(v) for v in st["m"]], rtol=1e-15)
+            np.testing.assert_allclose(
+                np.diag(rec.nesterov), [float(v) for v in st["nesterov"]], rtol=1e-14
+            )
             np.testing.assert_allclose(
                 np.diag(rec.ortho[0]), [float(v) for v in st["o_diag"]], rtol=1e-13, atol=1e-300
             )
@@ -291,3 +294,35 @@ def test_ema_bias_correction_recovers_a_constant_gradient():
     m_late = oracle.ema_momentum(np.full_like(g, 0.3), g, beta)
     look = oracle.ema_lookahead(m_late, g, beta, 4000)
     np.testing.assert_allclose(look, beta * m_late + (1 - beta) * g, rtol=1e-12)
+
+
+def test_ema_lookahead_closed_forms_for_a_constant_gradient():
+    # A constant gradient g from a zero buffer gives the EMA buffer
+    # (1 - beta^t) g after t steps.  With the look-ahead of RFC-0023 方案 1
+    # (the buffer corrected with count t+1, the gradient with count t) the
+    # first steps reduce to rational functions of beta alone:
+    #   t = 1: (1 + 2 beta) / (1 + beta) * g
+    #   t = 2: (beta (1 + beta) / (1 + beta + beta^2) + 1 / (1 + beta)) * g
+    #   t = 3: (beta (1 + beta + beta^2) / (1 + beta + beta^2 + beta^3)
+    #           + 1 / (1 + beta + beta^2)) * g
+    # Swapping the two counts, or shifting them, changes every one of these.
+    beta = 0.95
+    g = np.array([[2.0, -0.5, 1.25], [0.0, 3.0, -4.0]])
+    expect = {
+        1: (1 + 2 * beta) / (1 + beta),
+        2: beta * (1 + beta) / (1 + beta + beta**2) + 1 / (1 + beta),
+        3: beta * (1 + beta + beta**2) / (1 + beta + beta**2 + beta**3) + 1 / (1 + beta + beta**2),
+    }
+    m = np.zeros_like(g)
+    for t in (1, 2, 3):
+        m = oracle.ema_momentum(m, g, beta)
+        look = oracle.ema_lookahead(m, g, beta, t)
+        np.testing.assert_allclose(look, expect[t] * g, rtol=1e-14, atol=0)
+    # The whole step: NS is scale invariant, so O is NS(g) at every step,
+    # and the step index reaches the look-ahead through muon_step.
+    h = Hyper(nesterov_style="ema", mu=beta)
+    w0 = np.ones_like(g) * 0.01
+    w, m = w0.copy(), np.zeros_like(g)
+    for t in (1, 2):
+        w, m, rec = oracle.muon_step(w, g, m, h, step=t)
+        np.testing.assert_allclose(rec.nesterov, expect[t] * g, rtol=1e-14, atol=0)
