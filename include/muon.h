@@ -58,16 +58,18 @@ typedef enum {
   MUON_ERR_NULL = -1,      /* a required pointer is NULL */
   MUON_ERR_SHAPE = -2,     /* rows/cols/batch < 1, split_rows not dividing rows, sizes too
                               large: one NS unit padded to the tile (256, or 128 when
-                              min(rows, cols) < 256) must hold under 2^30 elements, and the
-                              launch grids stay under 2^30 workgroups */
+                              min(rows, cols) < 256) must hold under 2^30 elements, the
+                              launch grids stay under 2^30 workgroups, and one call makes
+                              at most 2^20 stacked passes */
   MUON_ERR_DTYPE = -3,     /* unknown dtype / precision / scale enum */
   MUON_ERR_ALIGN = -4,     /* a data pointer is not 16-byte aligned */
   MUON_ERR_WORKSPACE = -5, /* workspace NULL or smaller than muon_workspace_size() */
   MUON_ERR_HYPER = -6,     /* invalid hyper-parameters (non-finite, bad stage table) */
   MUON_ERR_HIP = -7,       /* a HIP call failed; outputs are undefined */
   MUON_ERR_ALIAS = -8,     /* overlapping input/output buffers where not allowed */
-  MUON_ERR_SCHEDULE = -9   /* the persistent NS schedule stopped (reported by
-                              muon_workspace_status); outputs are undefined */
+  MUON_ERR_SCHEDULE = -9   /* a persistent NS launch stopped: a dependency wait ran
+                              out of time (reported only by muon_workspace_status,
+                              never by the step calls); outputs are undefined */
 } muon_status;
 
 typedef enum { MUON_DTYPE_F32 = 0, MUON_DTYPE_BF16 = 1 } muon_dtype;
@@ -204,19 +206,27 @@ typedef enum {
   MUON_KERNEL_GRAM = 3,     /* A = X X^T on the smaller side */
   MUON_KERNEL_POLY = 4,     /* B' = a*I + b*A + c*A*A */
   MUON_KERNEL_APPLY = 5,    /* X <- B'*X (last one: the weight update) */
-  MUON_KERNEL_NS = 6        /* every NS product of a pass in one launch
-                               (the persistent or the on-chip small-unit
-                               kernel) */
+  MUON_KERNEL_NS = 6,       /* every NS product of a pass in one launch
+                               (the persistent kernel) */
+  MUON_KERNEL_NS_SMALL = 7  /* the whole NS of a pass of small units in one
+                               launch (the on-chip kernel) */
 } muon_kernel_kind;
 
 /* Timing hook: when passed to the *_traced entry points, every launch of
  * kernel class `kind` is bracketed by hipEventRecord(events[2k]) and
  * hipEventRecord(events[2k+1]) on the step's stream, for k = 0 .. capacity-1;
  * `count` returns how many launches were bracketed (it may exceed capacity;
- * only the first `capacity` are recorded).  Events are created and owned by
- * the caller. */
+ * only the first `capacity` are recorded).  When `info` is not NULL, the
+ * four values info[4k .. 4k+3] describe what launch k covered:
+ *   NS classes (GRAM, POLY, APPLY, NS, NS_SMALL): the smaller and the larger
+ *     side of the units (unpadded), the number of units, the tile size;
+ *   MOMENTUM: elements, algorithmic bytes (gradient or NS input read,
+ *     momentum read and written, look-ahead written), units, 0;
+ *   NORMALIZE: units, 0, 0, 0.
+ * Events and the info array are owned by the caller. */
 typedef struct {
   hipEvent_t* events;
+  int64_t* info;     /* NULL, or 4 * capacity values */
   int32_t capacity;
   int32_t kind;
   int32_t count;
@@ -235,16 +245,22 @@ int muon_newton_schulz_batched_traced(const float* const* x_in, float* const* o_
                                       size_t workspace_bytes, hipStream_t stream,
                                       muon_trace* trace);
 
-/* Waits for `stream`, then reads the status word that the last call on this
- * workspace left: MUON_OK, or MUON_ERR_SCHEDULE if a persistent NS launch
- * stopped early.  Errors: MUON_ERR_NULL, MUON_ERR_WORKSPACE (fewer than 256
- * bytes), MUON_ERR_ALIGN, MUON_ERR_HIP. */
-int muon_workspace_status(const void* workspace, size_t workspace_bytes, hipStream_t stream);
+/* Waits for `stream`, then reports whether any call on this workspace since
+ * the previous muon_workspace_status (or since the workspace's first call)
+ * had a persistent NS launch stop early: MUON_OK, or MUON_ERR_SCHEDULE, after
+ * which the outputs of the calls in question are undefined.  The report is
+ * sticky across calls and cleared by this function, so one check after a
+ * series of steps covers all of them.  The step entry points return before
+ * their kernels run and cannot see a stop: callers that need to know call
+ * this function (the Python binding does with check=True).  Uses the first
+ * 256 bytes of the workspace.  Errors: MUON_ERR_NULL, MUON_ERR_WORKSPACE
+ * (fewer than 256 bytes), MUON_ERR_ALIGN, MUON_ERR_HIP. */
+int muon_workspace_status(void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static description of a status code (never NULL). */
 const char* muon_status_string(int status);
 
-/* ABI version of this header: 4. */
+/* ABI version of this header: 5. */
 int muon_abi_version(void);
 
 #ifdef __cplusplus

@@ -60,6 +60,54 @@ def build(verbose: bool = True, extra: list[str] | None = None) -> str:
     return LIB
 
 
+# Host code built with AddressSanitizer and UndefinedBehaviorSanitizer (the
+# device code is compiled as usual): the CPU tests run the ABI suite, which
+# drives the host planner, against this build.  It loads only with the ASan
+# runtime preloaded (see tests/test_sanitizers.py).
+SAN_LIB = os.path.join(ROOT, "_build", "libmuon_san.so")
+SAN_FLAGS = [
+    "--offload-arch=gfx950",
+    "-O1",
+    "-g",
+    "-std=c++17",
+    "-shared",
+    "-fPIC",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-disable-promote-alloca-to-lds",
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined",
+    "-Xarch_host", "-fno-omit-frame-pointer",
+    "-Wno-unused-result",
+    "-Wno-inline-asm",
+    "-I", os.path.join(ROOT, "include"),
+]
+
+
+def build_sanitized(verbose: bool = False) -> str:
+    """Compile the host-sanitized library into _build/ unless it is newer
+    than every source."""
+    if os.path.exists(SAN_LIB) and all(os.path.getmtime(p) <= os.path.getmtime(SAN_LIB) for p in DEPS):
+        return SAN_LIB
+    os.makedirs(os.path.dirname(SAN_LIB), exist_ok=True)
+    tmp = SAN_LIB + ".tmp"
+    cmd = [HIPCC, *SAN_FLAGS, *SOURCES, "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc (sanitizer build) failed:\n" + (res.stdout + res.stderr)[-4000:])
+    os.replace(tmp, SAN_LIB)
+    return SAN_LIB
+
+
+def asan_runtime() -> str:
+    """Path of the compiler's shared ASan runtime."""
+    out = subprocess.run([HIPCC, "-print-file-name=libclang_rt.asan-x86_64.so"], capture_output=True,
+                         text=True)
+    return out.stdout.strip()
+
+
 def is_stale() -> bool:
     if not os.path.exists(LIB):
         return True

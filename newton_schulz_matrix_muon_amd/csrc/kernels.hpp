@@ -285,9 +285,18 @@ __global__ __launch_bounds__(kThreads) void k_momentum(ChunkArgs ca, float* __re
 // for units of up to 2^31 elements); other units are scaled in place first.
 constexpr double kFoldMin = 0x1p-80, kFoldMax = 0x1p80;  // bounds on nu^2
 
+// Status header at the start of the workspace (32-bit words): word 0 is the
+// current call's stop flag, which a persistent launch sets when a wait runs
+// out and reads to stop early; word 1 is sticky, the OR of the stop flags of
+// every call since the header was last read (muon_workspace_status clears
+// both); words 2-3 hold kStatusMagic once the header has been initialised
+// (a fresh workspace holds arbitrary bytes).
+constexpr uint64_t kStatusMagic = 0x4e4f554d53544154ull;
+
 // One workgroup per unit: fixed-order sum of the partials (first wave).
 // It also clears the persistent schedule's counts of the unit and claim
-// counter (when given), and the error word (when given).  With nb (the
+// counter (when given), and, on the first pass of a call (err given), moves
+// the previous call's stop flag into the sticky word and clears it.  With nb (the
 // folded path: unit iterates of x_stride bf16 elements holding N), inv_nu
 // receives the first iteration's scale instead: 1/nu inside the fold's
 // range, else 1 after the unit has been scaled by 1/nu here.
@@ -322,7 +331,16 @@ __global__ __launch_bounds__(kThreads) void k_norm_finish(const double* __restri
     inv_nu[u] = rescale ? 1.0f : inv;
     if (u == 0 && sched_queue)
       for (int i = 0; i < n_queue_words; ++i) sched_queue[i] = 0u;
-    if (u == 0 && err) *err = 0u;
+    if (u == 0 && err) {
+      uint64_t* const magic = reinterpret_cast<uint64_t*>(err + 2);
+      if (*magic != kStatusMagic) {
+        err[1] = 0u;
+        *magic = kStatusMagic;
+      } else {
+        err[1] |= err[0];
+      }
+      err[0] = 0u;
+    }
   }
   if (sched_done)
     for (int i = threadIdx.x; i < done_per_unit; i += kThreads)

@@ -69,6 +69,7 @@ struct Layout {
 };
 
 constexpr size_t kHeader = 256;  // status header at the start of the workspace
+constexpr int64_t kMaxChunks = (int64_t)1 << 20;  // stacked passes per call
 constexpr int kMaxQueues = 16;   // persistent schedule: at most one queue per XCC
 
 // Whether the AUTO schedule may run the pass on the on-chip small-unit
@@ -209,6 +210,20 @@ int plan(const muon_matrix_desc* mats, int64_t n, const muon_hyper* h, bool step
   }
   const int64_t cap = h->batch_update_size > 0 ? h->batch_update_size : INT64_MAX;
   const int64_t kMaxUnitsPerChunk = (int64_t)1 << 24;  // grid-size guard
+  // Every stacked pass is a host-side record and a series of launches: a
+  // plan of more than kMaxChunks passes is refused before it is built (a
+  // bank of 2^30 matrices under batch_update_size 1 would otherwise ask
+  // for 2^30 records).
+  int64_t n_chunks = 0;
+  for (const auto& grp : groups) {
+    int64_t units = 0;
+    for (int ui : grp) {
+      units += us[ui].n_units;  // each at most 9e15 (validate_descs)
+      if (units > ((int64_t)1 << 60)) return MUON_ERR_SHAPE;
+    }
+    n_chunks += (units + std::min(cap, kMaxUnitsPerChunk) - 1) / std::min(cap, kMaxUnitsPerChunk);
+    if (n_chunks > kMaxChunks) return MUON_ERR_SHAPE;
+  }
   for (const auto& grp : groups) {
     const Unitized& u0 = us[grp[0]];
     Chunk proto;
@@ -232,6 +247,7 @@ int plan(const muon_matrix_desc* mats, int64_t n, const muon_hyper* h, bool step
       while (begin < u.n_units) {
         const int64_t room = std::min(cap, kMaxUnitsPerChunk) - cur.n_units;
         if (room == 0 || (int)cur.segs.size() == kMaxSeg) {
+          if ((int64_t)chunks->size() >= kMaxChunks) return MUON_ERR_SHAPE;
           chunks->push_back(cur);
           cur = proto;
           continue;
@@ -318,11 +334,25 @@ struct Tracer {
     if (t && t->kind == kind && t->count < t->capacity)
       (void)hipEventRecord(t->events[2 * t->count], s);
   }
-  void after(int kind) {
+  // info: what the launch covered (muon.h, muon_trace)
+  void after(int kind, int64_t i0 = 0, int64_t i1 = 0, int64_t i2 = 0, int64_t i3 = 0) {
     if (t && t->kind == kind) {
-      if (t->count < t->capacity) (void)hipEventRecord(t->events[2 * t->count + 1], s);
+      if (t->count < t->capacity) {
+        (void)hipEventRecord(t->events[2 * t->count + 1], s);
+        if (t->info) {
+          int64_t* q = t->info + 4 * (int64_t)t->count;
+          q[0] = i0;
+          q[1] = i1;
+          q[2] = i2;
+          q[3] = i3;
+        }
+      }
       t->count++;
     }
+  }
+  // an NS launch over a chunk: smaller and larger unit side, units, tile
+  void after_ns(int kind, const Chunk& c) {
+    after(kind, std::min(c.rows_u, c.cols), std::max(c.rows_u, c.cols), c.n_units, c.tile);
   }
 };
 
@@ -376,6 +406,20 @@ int device_info(DeviceInfo* out) {
 }
 
 constexpr double kWaitLimitSeconds = 5.0;  // bound of one dependency wait
+
+// Bound of one dependency wait in wall-clock ticks.  Test hook:
+// MUON_WAIT_LIMIT_US replaces the 5 s bound (0 = give up as soon as a wait
+// does not succeed at once), so that tests can drive the schedule's stop
+// path from the host while every kernel still exits normally.
+uint64_t wait_limit_ticks(int wall_khz) {
+  double seconds = kWaitLimitSeconds;
+  if (const char* us = std::getenv("MUON_WAIT_LIMIT_US")) {
+    char* end = nullptr;
+    const double v = std::strtod(us, &end);
+    if (end != us && v >= 0.0 && v < 1e9) seconds = v * 1e-6;
+  }
+  return (uint64_t)(seconds * 1e3 * (double)wall_khz);
+}
 
 template <int PHASE, typename T, int KM>
 void launch_gemm(int tile, const GemmArgs& g, const ChunkArgs& ca, hipStream_t s) {
@@ -479,7 +523,14 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
       hipLaunchKernelGGL(k_momentum<1>, grid, dim3(kThreads), 0, s, ca, x32[0], nb, partials,
                          c.rows_per_block, c.blocks_per_unit);
   }
-  tr.after(MUON_KERNEL_MOMENTUM);
+  {
+    // algorithmic bytes: G (or the NS input) read, M read and written
+    // (step), N written into the bf16 iterate (2 B) or in fp32 (4 B)
+    const int64_t elems = c.n_units * c.rows_u * c.cols;
+    const int64_t gsz = (step && c.gdtype == MUON_DTYPE_BF16) ? 2 : 4;
+    const int64_t per = gsz + (step ? 8 : 0) + (nb ? 2 : 4);
+    tr.after(MUON_KERNEL_MOMENTUM, elems, elems * per, c.n_units, 0);
+  }
   // 2. norms (and, off the folded path, X0 = N / ||N||_F).
   tr.before(MUON_KERNEL_NORMALIZE);
   uint32_t* done = reinterpret_cast<uint32_t*>(ws + L.done);
@@ -512,17 +563,17 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
     p.final_mode = step ? FINAL_STEP : FINAL_NSOUT;
     p.inv_nu = inv_nu;
     p.flag = flag;
-    tr.after(MUON_KERNEL_NORMALIZE);
-    tr.before(MUON_KERNEL_NS);
+    tr.after(MUON_KERNEL_NORMALIZE, c.n_units);
+    tr.before(MUON_KERNEL_NS_SMALL);
     hipLaunchKernelGGL(k_ns_small, dim3(U), dim3(kThreads), 0, s, p, ca);
-    tr.after(MUON_KERNEL_NS);
+    tr.after_ns(MUON_KERNEL_NS_SMALL, c);
     return hipGetLastError() == hipSuccess ? MUON_OK : MUON_ERR_HIP;
   }
   const int tiles_c = (int)(c.cols_pad / 64);
   if (!fold)
     hipLaunchKernelGGL(k_normalize, dim3(U * c.norm_blocks_per_unit), dim3(kThreads), 0, s, ca,
                        x32[0], static_cast<float*>(xt[0]), inv_nu, tiles_c, c.norm_blocks_per_unit);
-  tr.after(MUON_KERNEL_NORMALIZE);
+  tr.after(MUON_KERNEL_NORMALIZE, c.n_units);
   // First iteration's scale on the folded path (inv_nu as k_norm_finish
   // left it): Gram by its square, apply by itself.
   const float* const fold_scale = fold ? inv_nu : nullptr;
@@ -646,7 +697,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
     p.queue = queue;
     p.done = done;
     p.err = err;
-    p.timeout_ticks = (uint64_t)(kWaitLimitSeconds * 1e3 * (double)di.wall_khz);
+    p.timeout_ticks = wait_limit_ticks(di.wall_khz);
     int grid = (int)std::min<int64_t>(n_items, di.resident[bf16 ? 1 : 0][T == 256 ? 1 : 0]);
     // Test hook: MUON_PERSISTENT_WORKGROUPS caps the grid, so that tests can
     // run the schedule with XCCs that receive no workgroup.
@@ -671,7 +722,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
       else
         hipLaunchKernelGGL((ns_persistent<float, 128, 0>), dim3(grid), dim3(gemm_threads<128>()), 0, s, p, ca);
     }
-    tr.after(MUON_KERNEL_NS);
+    tr.after_ns(MUON_KERNEL_NS, c);
     return hipGetLastError() == hipSuccess ? MUON_OK : MUON_ERR_HIP;
   }
   int it = 0;
@@ -702,7 +753,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
       g.ldo = (int32_t)sp;
       tr.before(MUON_KERNEL_GRAM);
       launch_phase<GRAM>(bf16, T, c.tall ? 3 : 0, g, ca, s);
-      tr.after(MUON_KERNEL_GRAM);
+      tr.after_ns(MUON_KERNEL_GRAM, c);
       // Polynomial: B' = a*I + b*A + c*A*A (A symmetric: both operands
       // K-contiguous; a*I carries the apply's a*X term).
       std::memset(&g, 0, sizeof(g));
@@ -728,7 +779,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
       g.cc = sg.c;
       tr.before(MUON_KERNEL_POLY);
       launch_phase<POLY>(bf16, T, 0, g, ca, s);
-      tr.after(MUON_KERNEL_POLY);
+      tr.after_ns(MUON_KERNEL_POLY, c);
       // Apply: X' = B'*X (wide) or X*B' (tall).
       std::memset(&g, 0, sizeof(g));
       g.n_units = U;
@@ -763,7 +814,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
       g.final_mode = last ? (step ? FINAL_STEP : FINAL_NSOUT) : FINAL_NONE;
       tr.before(MUON_KERNEL_APPLY);
       launch_phase<APPLY>(bf16, T, c.tall ? 0 : 2, g, ca, s);
-      tr.after(MUON_KERNEL_APPLY);
+      tr.after_ns(MUON_KERNEL_APPLY, c);
     }
   }
   if (hipGetLastError() != hipSuccess) return MUON_ERR_HIP;
@@ -909,17 +960,27 @@ const char* muon_status_string(int status) {
   }
 }
 
-int muon_workspace_status(const void* workspace, size_t workspace_bytes, hipStream_t stream) {
+int muon_workspace_status(void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!workspace) return MUON_ERR_NULL;
   if (workspace_bytes < kHeader) return MUON_ERR_WORKSPACE;
   if (((uintptr_t)workspace & (kAlign - 1)) != 0) return MUON_ERR_ALIGN;
-  if (hipStreamSynchronize(stream) != hipSuccess) return MUON_ERR_HIP;
-  uint32_t word = 0;
-  if (hipMemcpy(&word, workspace, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess)
+  // The header: stop flag of the last call, sticky flag of the calls
+  // before it, and the marker of an initialised header (kernels.hpp).
+  uint32_t words[4] = {0u, 0u, 0u, 0u};
+  if (hipMemcpyAsync(words, workspace, sizeof(words), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
     return MUON_ERR_HIP;
-  return word == 0u ? MUON_OK : MUON_ERR_SCHEDULE;
+  uint64_t magic = 0;
+  std::memcpy(&magic, words + 2, sizeof(magic));
+  if (magic != kStatusMagic) return MUON_OK;  // no call has used this workspace yet
+  if ((words[0] | words[1]) == 0u) return MUON_OK;
+  // Reported once: clear both flags before returning.
+  if (hipMemsetAsync(workspace, 0, 2 * sizeof(uint32_t), stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return MUON_ERR_HIP;
+  return MUON_ERR_SCHEDULE;
 }
 
-int muon_abi_version(void) { return 4; }
+int muon_abi_version(void) { return 5; }
 
 }  // extern "C"

@@ -9,7 +9,6 @@ library; if it is missing this module raises on import.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from dataclasses import dataclass, field
 from typing import Sequence
@@ -17,7 +16,9 @@ from typing import Sequence
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmuon.so")
+# MUON_LIBRARY selects another build of the same library (the sanitizer
+# build of the CPU tests); by default the in-tree libmuon.so.
+LIB_PATH = os.environ.get("MUON_LIBRARY") or os.path.join(_HERE, "libmuon.so")
 
 MUON_OK = 0
 STATUS_NAMES = {
@@ -36,7 +37,7 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 SCALE_SPECTRAL, SCALE_UNIT_RMS_NORM = 0, 1
 NS_FP32, NS_BF16 = 0, 1
 KERNEL_MOMENTUM, KERNEL_NORMALIZE, KERNEL_GRAM, KERNEL_POLY, KERNEL_APPLY = 1, 2, 3, 4, 5
-KERNEL_NS = 6
+KERNEL_NS, KERNEL_NS_SMALL = 6, 7
 SCHEDULE_AUTO, SCHEDULE_PERSISTENT, SCHEDULE_LAUNCHES = 0, 1, 2
 NESTEROV_SGD, NESTEROV_EMA = 0, 1
 MAX_STAGES = 4
@@ -95,6 +96,7 @@ class HyperC(ctypes.Structure):
 class TraceC(ctypes.Structure):
     _fields_ = [
         ("events", ctypes.POINTER(ctypes.c_void_p)),
+        ("info", ctypes.POINTER(ctypes.c_int64)),
         ("capacity", ctypes.c_int32),
         ("kind", ctypes.c_int32),
         ("count", ctypes.c_int32),
@@ -139,7 +141,7 @@ def _load() -> ctypes.CDLL:
     lib.muon_newton_schulz_batched.restype = ctypes.c_int
     lib.muon_newton_schulz_batched_traced.argtypes = ns_args + [ctypes.POINTER(TraceC)]
     lib.muon_newton_schulz_batched_traced.restype = ctypes.c_int
-    lib.muon_workspace_status.argtypes = [P, ctypes.c_size_t, P]
+    lib.muon_workspace_status.argtypes = [P, ctypes.c_size_t, P]  # workspace, bytes, stream
     lib.muon_workspace_status.restype = ctypes.c_int
     lib.muon_status_string.argtypes = [ctypes.c_int]
     lib.muon_status_string.restype = ctypes.c_char_p
@@ -227,23 +229,39 @@ def _ptrs(tensors) -> ctypes.Array:
     return arr
 
 
-_WS: dict[int, torch.Tensor] = {}
+# Cached workspaces, one per (device, stream): calls on one stream run in
+# order and may share a workspace; calls on different streams may overlap
+# and must not.
+_WS: dict[tuple[int, int], torch.Tensor] = {}
+
+# Whether step() and newton_schulz() check the schedule status after each
+# call when their `check` argument is None (the check waits for the stream).
+check_default = False
 
 
-def workspace(nbytes: int, device: torch.device) -> torch.Tensor:
-    """A cached byte workspace of at least `nbytes` on `device`."""
-    key = device.index if device.index is not None else torch.cuda.current_device()
+def workspace(nbytes: int, device: torch.device, stream=None) -> torch.Tensor:
+    """A cached byte workspace of at least `nbytes` on `device` for calls on
+    `stream` (torch's current stream when None)."""
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    dev = device.index if device.index is not None else torch.cuda.current_device()
+    key = (dev, s.cuda_stream)
     ws = _WS.get(key)
     if ws is None or ws.numel() < nbytes:
+        # The old buffer may still be in use by work queued on `s`; it was
+        # recorded on `s` when handed out, so the allocator keeps it until
+        # that work is done.
         _WS.pop(key, None)
         ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
         _WS[key] = ws
+    if s != torch.cuda.current_stream(device):
+        ws.record_stream(s)
     return ws
 
 
 def workspace_status(ws: torch.Tensor, stream=None) -> None:
-    """Waits for the stream and raises MuonError if the last call on `ws`
-    stopped early (muon_workspace_status)."""
+    """Waits for the stream and raises MuonError(MUON_ERR_SCHEDULE) if any
+    call on `ws` since the previous check had a persistent NS launch stop
+    early (muon_workspace_status; the report is sticky until read)."""
     st = LIB.muon_workspace_status(ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()),
                                    ctypes.c_void_p(_stream_ptr(stream)))
     if st != MUON_OK:
@@ -276,16 +294,53 @@ def _stream_ptr(stream) -> int:
     return s.cuda_stream
 
 
-def _trace(kind: int, events) -> tuple[TraceC, ctypes.Array]:
-    arr = (ctypes.c_void_p * len(events))()
-    for i, e in enumerate(events):
-        arr[i] = e.cuda_event
-    tr = TraceC()
-    tr.events = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
-    tr.capacity = len(events) // 2
-    tr.kind = kind
-    tr.count = 0
-    return tr, arr
+class Trace:
+    """Brackets every launch of one kernel class (muon_trace): `capacity`
+    pairs of timing events, recorded on the call's stream, and what each
+    launch covered (`info`, four values per launch as muon.h describes)."""
+
+    def __init__(self, kind: int, capacity: int, stream=None):
+        self.kind = kind
+        self.capacity = capacity
+        self.events = [torch.cuda.Event(enable_timing=True) for _ in range(2 * capacity)]
+        s = stream if stream is not None else torch.cuda.current_stream()
+        for e in self.events:  # create the underlying HIP events
+            e.record(s)
+        self._ev = (ctypes.c_void_p * max(1, 2 * capacity))()
+        for i, e in enumerate(self.events):
+            self._ev[i] = e.cuda_event
+        self._info = (ctypes.c_int64 * max(1, 4 * capacity))()
+        self.count = 0
+
+    def c(self) -> TraceC:
+        tr = TraceC()
+        tr.events = ctypes.cast(self._ev, ctypes.POINTER(ctypes.c_void_p))
+        tr.info = ctypes.cast(self._info, ctypes.POINTER(ctypes.c_int64))
+        tr.capacity = self.capacity
+        tr.kind = self.kind
+        tr.count = 0
+        tr.reserved = 0
+        return tr
+
+    @property
+    def recorded(self) -> int:
+        return min(self.count, self.capacity)
+
+    def ms(self) -> list[float]:
+        """Duration of each recorded launch (the stream must have passed them)."""
+        return [self.events[2 * i].elapsed_time(self.events[2 * i + 1]) for i in range(self.recorded)]
+
+    def info(self) -> list[tuple[int, int, int, int]]:
+        return [tuple(self._info[4 * i: 4 * i + 4]) for i in range(self.recorded)]
+
+
+def _run_traced(fn, args, trace: Trace | None):
+    if trace is None:
+        return fn(*args)
+    tr = trace.c()
+    st = fn(*args, ctypes.byref(tr))
+    trace.count = tr.count
+    return st
 
 
 def step(
@@ -296,15 +351,19 @@ def step(
     split_rows: Sequence[int] | None = None,
     stream=None,
     ws: torch.Tensor | None = None,
-    trace: tuple[int, list] | None = None,
+    trace: Trace | None = None,
+    check: bool | None = None,
 ) -> int:
     """One Muon step, in place on `params` and `momenta` (muon_step_batched).
 
     params/momenta: fp32 (rows, cols) or (batch, rows, cols) banks;
     grads: bf16 or fp32 of the same shapes; split_rows: per bank, 0 or the
-    head size.  `trace = (kernel_kind, [events])` brackets every launch of
-    that kernel class with the given events (pairs).  Returns the number of
-    launches of the traced class (0 without a trace)."""
+    head size.  `trace` (a Trace) brackets every launch of one kernel
+    class.  `check` (default:
+    `check_default`) waits for the stream afterwards and raises MuonError if
+    a persistent NS launch stopped, in which case params and momenta are
+    undefined.  Returns the number of launches of the traced class (0
+    without a trace)."""
     hyper = hyper or Hyper()
     n = len(params)
     if not (len(grads) == len(momenta) == n):
@@ -333,21 +392,18 @@ def step(
     if st != MUON_OK:
         raise MuonError(st, "muon_workspace_size")
     if ws is None:
-        ws = workspace(need.value, dev)
+        ws = workspace(need.value, dev, stream)
     args = (
         _ptrs(params), _ptrs(grads), _ptrs(momenta), descs, n, ctypes.byref(hc),
         ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()),
         ctypes.c_void_p(_stream_ptr(stream)),
     )
-    if trace is None:
-        st = LIB.muon_step_batched(*args)
-        count = 0
-    else:
-        tr, keep = _trace(trace[0], trace[1])
-        st = LIB.muon_step_batched_traced(*args, ctypes.byref(tr))
-        count = tr.count
+    st = _run_traced(LIB.muon_step_batched_traced if trace else LIB.muon_step_batched, args, trace)
+    count = trace.count if trace else 0
     if st != MUON_OK:
         raise MuonError(st, "muon_step_batched")
+    if check_default if check is None else check:
+        workspace_status(ws, stream)
     return count
 
 
@@ -358,11 +414,13 @@ def newton_schulz(
     split_rows: Sequence[int] | None = None,
     stream=None,
     ws: torch.Tensor | None = None,
-    trace: tuple[int, list] | None = None,
+    trace: Trace | None = None,
+    check: bool | None = None,
 ):
     """Hybrid Newton-Schulz only (muon_newton_schulz_batched): the unscaled
     NS output of every unit of every fp32 bank in `xs`, written to `outs`
-    (new tensors when None).  Returns (outs, traced launch count)."""
+    (new tensors when None).  `check` as for step().  Returns (outs, traced
+    launch count)."""
     hyper = hyper or Hyper()
     n = len(xs)
     if outs is None:
@@ -380,25 +438,17 @@ def newton_schulz(
     if st != MUON_OK:
         raise MuonError(st, "muon_workspace_size")
     if ws is None:
-        ws = workspace(need.value, dev)
+        ws = workspace(need.value, dev, stream)
     args = (
         _ptrs(xs), _ptrs(outs), descs, n, ctypes.byref(hc), ctypes.c_void_p(ws.data_ptr()),
         ctypes.c_size_t(ws.numel()), ctypes.c_void_p(_stream_ptr(stream)),
     )
-    if trace is None:
-        st = LIB.muon_newton_schulz_batched(*args)
-        count = 0
-    else:
-        tr, keep = _trace(trace[0], trace[1])
-        st = LIB.muon_newton_schulz_batched_traced(*args, ctypes.byref(tr))
-        count = tr.count
+    st = _run_traced(
+        LIB.muon_newton_schulz_batched_traced if trace else LIB.muon_newton_schulz_batched, args, trace
+    )
+    count = trace.count if trace else 0
     if st != MUON_OK:
         raise MuonError(st, "muon_newton_schulz_batched")
+    if check_default if check is None else check:
+        workspace_status(ws, stream)
     return outs, count
-
-
-def unit_scale(rows_u: int, cols: int, hyper: Hyper) -> float:
-    """The update scale the library applies to a unit (for reporting)."""
-    if hyper.scale == "spectral":
-        return math.sqrt(max(rows_u, cols)) * hyper.gamma
-    return math.sqrt(rows_u / cols)

@@ -22,4 +22,7 @@ def gpu_lib():
         pytest.skip("no GPU")
     from newton_schulz_matrix_muon_amd import muon
 
+    # every step and NS call of the GPU tests waits for its stream and
+    # raises if a persistent launch stopped early
+    muon.check_default = True
     return muon

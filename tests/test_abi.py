@@ -120,6 +120,18 @@ def test_unit_size_limit():
     assert ws_size([(2, 16384, 16384, 0)])[0] == 0
 
 
+def test_pass_count_limit():
+    # At most 2^20 stacked passes per call, refused before any is planned
+    # (2^30 one-unit passes would otherwise be built on the host).
+    h = muon.default_hyper_c()
+    h.batch_update_size = 1
+    assert ws_size([(1 << 20, 4, 4, 0)], h)[0] == 0
+    assert ws_size([(1 << 20, 4, 4, 0), (1, 4, 4, 0)], h)[0] == -2
+    assert ws_size([(1 << 30, 4, 4, 1)], h)[0] == -2
+    h.batch_update_size = 0
+    assert ws_size([(1 << 30, 4, 4, 1)], h)[0] == 0
+
+
 def test_bad_hyper_rejected():
     h = muon.default_hyper_c()
     h.n_stages = 0
@@ -187,6 +199,47 @@ def test_step_error_paths_touch_nothing():
     assert _step([], [], [], []) == 0                              # no-op
 
 
+def test_planner_fuzz():
+    # Random bank lists and hyper-parameters through the host planner
+    # (validation, grouping, chunking, workspace carve-up): every call
+    # returns a defined status; accepted ones give a 256-byte-aligned size
+    # of at least the status header; adding a bank never shrinks the
+    # workspace and a batch_update_size cap never grows it.  Under the
+    # sanitizer build (tests/test_sanitizers.py) this also checks the
+    # planner's arithmetic for overflow and its memory accesses.
+    import numpy as np
+
+    rng = np.random.default_rng(2024)
+    valid = {0, -2, -3, -6}
+    for _ in range(400):
+        n = int(rng.integers(0, 6))
+        shapes = []
+        for _ in range(n):
+            rows = int(rng.choice([1, 2, 63, 64, 127, 128, 129, 255, 256, 1000, 4096, 14336, 1 << 20]))
+            cols = int(rng.choice([1, 3, 64, 128, 300, 1024, 4096, 7168, 1 << 16]))
+            split = int(rng.choice([0, 0, 0, 1, 7, 128, rows]))
+            batch = int(rng.choice([1, 2, 13, 128, 1 << 20]))
+            shapes.append((batch, rows, cols, split))
+        h = muon.default_hyper_c()
+        h.ns_precision = int(rng.integers(0, 2))
+        h.schedule = int(rng.integers(0, 3))
+        h.batch_update_size = int(rng.choice([0, 1, 3, 16]))
+        h.stages[0].steps = int(rng.choice([0, 1, 8, 1000]))
+        st, size = ws_size(shapes, h)
+        assert st in valid, (shapes, st)
+        if st != 0:
+            continue
+        assert size >= 256 and size % 256 == 0
+        if n > 0:
+            st2, size2 = ws_size(shapes[:-1], h)
+            assert st2 == 0 and size2 <= size
+        if h.batch_update_size == 0:
+            h.batch_update_size = 2
+            st3, size3 = ws_size(shapes, h)
+            # more passes: refused only for exceeding the 2^20 pass limit
+            assert (st3 == 0 and size3 <= size) or st3 == -2
+
+
 def test_workspace_status_argument_errors():
     st = muon.LIB.muon_workspace_status
     assert st(None, 1 << 20, None) == -1
@@ -198,4 +251,4 @@ def test_status_strings():
     for code in range(-9, 1):
         assert muon.status_string(code) != "unknown status"
     assert muon.status_string(12345) == "unknown status"
-    assert muon.LIB.muon_abi_version() == 4
+    assert muon.LIB.muon_abi_version() == 5

@@ -19,6 +19,10 @@ CASES = [
     ([(3, 640, 256, 0)], "bf16", "fp32"),             # tall, fp32 products
     ([(5, 256, 256, 0)], "fp32", "fp32"),             # fp32 path, 256 tiles
     ([(1, 1024, 2048, 0)], "bf16", "bf16"),           # one unit, many tiles
+    # full-size units: 16 panels of 256 on the small side
+    ([(2, 14336, 4096, 0)], "bf16", "bf16"),          # the layer's gate/up, one queue
+    ([(1, 4096, 14336, 0)], "bf16", "bf16"),          # its down projection
+    ([(16, 2048, 7168, 0)], "bf16", "bf16"),          # MoE experts, one queue per XCC
 ]
 
 
@@ -70,19 +74,24 @@ def test_ns_only_schedules_agree_bitwise(gpu_lib, prec):
 
 def test_persistent_trace_brackets_one_launch_per_pass(gpu_lib):
     print("[schedule trace]", flush=True)
-    x = torch.randn((4, 256, 256), device=DEV)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(8)]
-    for e in ev:
-        e.record()
+    x = torch.randn((4, 256, 300), device=DEV)
     h = gpu_lib.Hyper(schedule="persistent")
-    _, n = gpu_lib.newton_schulz([x], hyper=h, trace=(gpu_lib.KERNEL_NS, ev))
+    tr = gpu_lib.Trace(gpu_lib.KERNEL_NS, 4)
+    _, n = gpu_lib.newton_schulz([x], hyper=h, trace=tr)
     torch.cuda.synchronize()
     assert n == 1
-    assert ev[0].elapsed_time(ev[1]) > 0
+    assert tr.ms()[0] > 0
+    assert tr.info() == [(256, 300, 4, 256)]  # s, l, units, tile
     h = gpu_lib.Hyper(schedule="launches")
-    _, n = gpu_lib.newton_schulz([x], hyper=h, trace=(gpu_lib.KERNEL_APPLY, ev))
+    tr = gpu_lib.Trace(gpu_lib.KERNEL_APPLY, 4)
+    _, n = gpu_lib.newton_schulz([x], hyper=h, trace=tr)
     torch.cuda.synchronize()
-    assert n == 10
+    assert n == 10 and tr.recorded == 4
+    tr = gpu_lib.Trace(gpu_lib.KERNEL_MOMENTUM, 2)
+    _, n = gpu_lib.newton_schulz([x], hyper=h, trace=tr)
+    torch.cuda.synchronize()
+    # NS only: the fp32 input read (4 B) and N written into the bf16 iterate (2 B)
+    assert n == 1 and tr.info() == [(4 * 256 * 300, 6 * 4 * 256 * 300, 4, 0)]
 
 
 @pytest.mark.parametrize("workgroups", [1, 3])
