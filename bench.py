@@ -1,19 +1,30 @@
 """Benchmark of the MI355X Muon step.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 2] [--ns bf16|fp32]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 5] [--ns bf16|fp32]
+                    [--no-sub-configs] [--no-cpu-baseline]
 
-A step is one Muon update (momentum, Nesterov, Frobenius normalisation, ten
-hybrid Newton-Schulz iterations, scale and decoupled weight decay) of every
-matrix of the workload, with inputs resident in HBM.  The default workload
-is 32 stacked 1024x1024 fp32 weights with bf16 gradients N(0, 1e-3),
-spectral scale, bf16 NS products (fp32 accumulation).
+A step is one Muon update (momentum, Nesterov look-ahead, Frobenius
+normalisation, ten hybrid Newton-Schulz iterations, scale and decoupled
+weight decay) of every matrix of a workload, with its inputs resident in
+HBM.  The headline workload is the largest one that fits one GPU: 32
+transformer layers of hidden 4096 (~7B parameters, 1664 NS units: 1536
+split heads of 128 x 4096, 32 projections of 4096 x 4096, 96 MLP matrices
+of 4096 x 14336 / 14336 x 4096), unit_rms_norm scale, bf16 NS products
+with fp32 accumulation.  Its W warm-up steps are followed by exactly K
+timed steps.
 
-Prints one JSON line with matrices/s (the metric), NS TFLOP/s and its
-fraction of the bf16 MFMA peak, the roofline of the dominant kernel class
-(timed live with HIP events around each of its launches on the step's
-stream), a float64 CPU-oracle baseline on a bounded sample, and the same NS
-iterations written with torch's bf16 batched products on the workload's
-largest group of equal-shape units (a vendor-library reference on this GPU).
+The one JSON line also carries, measured in the same run:
+  * `configs`: every other workload (the single 64 x 128 fp32 matrix on both
+    NS paths, 32 stacked 1024^2, one transformer layer, the MoE bank) and a
+    sampled step of the headline workload on the fp32 NS path;
+  * `roofline`: the dominant NS kernel of the headline step, its nominal
+    FLOPs per launch over its average launch duration (HIP events around
+    each launch, on the step's stream, over the timed steps);
+  * `cpu_baseline`: the float64 oracle on one sampled unit per unit shape,
+    extrapolated to a whole step.
+A line is printed only if no persistent launch stopped early (the
+workspace status is read after the warm-up, the traced and the timed
+steps).
 """
 
 from __future__ import annotations
@@ -30,31 +41,51 @@ if ROOT not in sys.path:
 
 PEAK_TFLOPS = {"bf16": 2516.6, "fp32": 157.3}  # MI355X dense MFMA
 HBM_GBS = 8000.0
+HEADLINE = 5
+# Other workloads of the same run: (config, NS path, timed steps, warm-up
+# steps, per-class traced steps)
+SUB_CONFIGS = [
+    (1, "fp32", 200, 20, True),
+    (1, "bf16", 200, 20, True),
+    (2, "bf16", 50, 5, True),
+    (3, "bf16", 10, 2, True),
+    (4, "bf16", 3, 1, True),
+]
+FP32_SAMPLE_STEPS = 1  # the headline workload on the fp32 NS path
+
+KERNEL_NAMES = {
+    "ns": "ns_persistent",
+    "ns_small": "k_ns_small",
+    "gram": "ns_gemm gram",
+    "poly": "ns_gemm poly",
+    "apply": "ns_gemm apply",
+}
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=2)
+    ap.add_argument("--config", type=int, default=HEADLINE, help="headline workload (1-5)")
     ap.add_argument("--ns", default="bf16", choices=["bf16", "fp32"])
-    ap.add_argument("--batch-update-size", type=int, default=0)
     ap.add_argument("--schedule", default="auto", choices=["auto", "persistent", "launches"],
                     help="NS schedule: the library's choice per pass, or force one persistent "
                          "launch per pass, or one launch per product")
-    ap.add_argument("--grad-sets", type=int, default=4, help="distinct resident gradient batches")
+    ap.add_argument("--grad-sets", type=int, default=2, help="distinct resident gradient batches")
+    ap.add_argument("--no-sub-configs", action="store_true",
+                    help="measure the headline workload only (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-library-baseline", action="store_true",
-                    help="skip timing the same NS iterations written with torch's bf16 batched "
-                         "products on the largest unit group")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=40.0,
+                    help="budget of the CPU-oracle sample; shape groups beyond it are scaled "
+                         "by FLOPs from the measured rate")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="after the timed region, run one plain copy kernel over this many MiB "
                          "(int32 bitwise-not, read once and written once) for counter calibration")
-    return ap.parse_args()
+    return ap.parse_args(argv)
 
 
+# ------------------------------------------------------------ accounting ---
 def kernel_sources_sha256():
     """Digest of the HIP sources, tying a stored counter record to the
     kernels it was taken on."""
@@ -94,6 +125,66 @@ def stored_traffic(kernel, workload, ns, pdir=None, digest=None):
     return None
 
 
+def shape_groups(wl):
+    """{(s, l): (units, units with a non-zero gradient)} over the workload's
+    NS units, s and l the smaller and the larger side (tall and wide units of
+    one (s, l) together); all-zero experts count only in the first figure."""
+    import workloads as W
+
+    out = {}
+    for spec in wl.matrices:
+        r, c = spec.unit_shape
+        n = spec.batch * spec.units_per_matrix
+        nz = n
+        if wl.zero_fraction:
+            nz -= len(W.zero_experts(wl, spec.batch)) * spec.units_per_matrix
+        key = (min(r, c), max(r, c))
+        a, b = out.get(key, (0, 0))
+        out[key] = (a + n, b + nz)
+    return out
+
+
+def unit_flops(s, l):
+    """Nominal NS FLOPs of one unit per iteration: X X^T (2 s^2 l), A A
+    (2 s^3) and B X (2 s^2 l)."""
+    return 4.0 * s * s * l + 2.0 * s**3
+
+
+def ns_flops_per_step(wl, iters):
+    """Nominal NS FLOPs of one step over the units with a non-zero gradient."""
+    return sum(live * iters * unit_flops(s, l) for (s, l), (_, live) in shape_groups(wl).items())
+
+
+def executed_fraction(s, tile):
+    """Share of a symmetric s x s product's tiles that run (upper triangle of
+    the tile grid)."""
+    t = -(-s // tile)
+    return (t * (t + 1) / 2) / (t * t)
+
+
+def launch_flops(cls, info, groups, iters):
+    """Nominal and executed FLOPs of one NS launch from what the library
+    reports it covered (s, l, units, tile), counting only the share of
+    units with a non-zero gradient in that unit shape.  One launch of class
+    "ns" or "ns_small" runs every iteration; one of "gram", "poly" or
+    "apply" runs one."""
+    s, l, units, tile = info
+    total, live = groups.get((s, l), (units, units))
+    n = units * (live / total if total else 1.0)
+    gram, poly, apply = 2.0 * s * s * l, 2.0 * s**3, 2.0 * s * s * l
+    if cls == "ns_small":
+        # whole products on rows padded to 128 and columns to 128-multiples
+        lp = -(-l // 128) * 128
+        exe = 2.0 * 128 * 128 * lp * 2 + 2.0 * 128**3
+        return n * iters * (gram + poly + apply), n * iters * exe
+    f = executed_fraction(s, tile)
+    if cls == "ns":
+        return n * iters * (gram + poly + apply), n * iters * (f * gram + f * poly + apply)
+    nom = {"gram": gram, "poly": poly, "apply": apply}[cls]
+    return n * nom, n * nom * (f if cls in ("gram", "poly") else 1.0)
+
+
+# -------------------------------------------------------------- the runs ---
 def build_inputs(wl, dev, grad_sets):
     import torch
 
@@ -109,101 +200,145 @@ def build_inputs(wl, dev, grad_sets):
     return params, moms, grads, splits
 
 
-def unit_groups(wl):
-    """(rows, cols, units, non-zero units) of every NS unit shape, banks of
-    one unit shape merged as the library stacks them; all-zero experts are
-    excluded from the second count."""
-    import workloads as W
+def measure(wl, ns, steps, warmup, dev, inputs, schedule="auto", trace_classes=True):
+    """Times `steps` steps of workload `wl` after `warmup` untimed ones.
 
-    out = {}
-    for spec in wl.matrices:
-        r, c = spec.unit_shape
-        n = spec.batch * spec.units_per_matrix
-        nz = n
-        if wl.zero_fraction:
-            nz -= len(W.zero_experts(wl, spec.batch)) * spec.units_per_matrix
-        a, b = out.get((r, c), (0, 0))
-        out[(r, c)] = (a + n, b + nz)
-    return [(r, c, n, nz) for (r, c), (n, nz) in out.items()]
+    With trace_classes, one traced step per kernel class (after the warm-up)
+    gives each class's kernel time and what its launches covered; the
+    timed steps then bracket every launch of the dominant NS class with HIP
+    events on the step's stream.  Raises if a persistent launch stopped."""
+    import torch
+
+    from newton_schulz_matrix_muon_amd import muon
+
+    params, moms, grads, splits = inputs
+    hyper = muon.Hyper(scale=wl.scale, ns_precision=ns, schedule=schedule)
+    ws = muon.workspace(muon.workspace_size(params, hyper, splits), dev)
+    iters = sum(k for k, _ in hyper.stages)
+    groups = shape_groups(wl)
+
+    def one_step(k, trace=None):
+        return muon.step(params, grads[k % len(grads)], moms, hyper=hyper, split_rows=splits,
+                         ws=ws, trace=trace, check=False)
+
+    for k in range(warmup):
+        one_step(k)
+    muon.workspace_status(ws)
+
+    classes = {"momentum": muon.KERNEL_MOMENTUM, "normalize": muon.KERNEL_NORMALIZE,
+               "ns": muon.KERNEL_NS, "ns_small": muon.KERNEL_NS_SMALL, "gram": muon.KERNEL_GRAM,
+               "poly": muon.KERNEL_POLY, "apply": muon.KERNEL_APPLY}
+    per_class = {}  # name -> (ms per launch, info per launch) of one step
+    if trace_classes:
+        for name, kind in classes.items():
+            tr = muon.Trace(kind, 1024)
+            one_step(warmup, tr)
+            torch.cuda.synchronize()
+            if tr.count:
+                assert tr.count <= tr.capacity, (name, tr.count)
+                per_class[name] = (tr.ms(), tr.info())
+        muon.workspace_status(ws)
+    ns_classes = [n for n in ("ns", "ns_small", "gram", "poly", "apply") if n in per_class]
+    dominant = max(ns_classes, key=lambda n: sum(per_class[n][0])) if ns_classes else None
+
+    traces = []
+    if dominant:
+        count = len(per_class[dominant][0])
+        traces = [muon.Trace(classes[dominant], count) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(steps):
+        one_step(k, traces[k] if traces else None)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    muon.workspace_status(ws)
+    sec = (t1 - t0) / steps
+
+    nsf = ns_flops_per_step(wl, iters)
+    out = {
+        "workload": wl.title,
+        "config_index": wl.cfg,
+        "ns_path": ns,
+        "units": wl.units,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": sec * 1e3,
+        "matrices_per_s": wl.units / sec,
+        "ns_tflop_per_step": nsf / 1e12,
+        # NS FLOPs over the whole step's wall time (elementwise kernels included)
+        "ns_tflops_step": nsf / sec / 1e12,
+    }
+    if not dominant:
+        return out, None
+    # The dominant class's time per step from the timed steps (the single
+    # traced step can run at a different clock); other classes from theirs.
+    launch_ms, launch_info = [], []
+    for tr in traces:
+        launch_ms += tr.ms()
+        launch_info += tr.info()
+    kernel_ms = {n: sum(per_class[n][0]) for n in per_class}
+    kernel_ms[dominant] = sum(launch_ms) / steps
+    ns_ms = sum(kernel_ms[n] for n in ns_classes)
+    peak = PEAK_TFLOPS[ns]
+    out.update({
+        "ns_ms_per_step": ns_ms,
+        "ns_tflops": nsf / (ns_ms * 1e-3) / 1e12,
+        "ns_frac_of_peak": nsf / (ns_ms * 1e-3) / 1e12 / peak,
+        "kernel_ms_per_step": {n: round(v, 4) for n, v in kernel_ms.items()},
+    })
+    mom = per_class.get("momentum")
+    if mom:
+        mom_bytes = sum(i[1] for i in mom[1])
+        out["elementwise_gbs"] = mom_bytes / (sum(mom[0]) * 1e-3) / 1e9
+        out["elementwise_frac_of_hbm"] = out["elementwise_gbs"] / HBM_GBS
+    nom = exe = 0.0
+    for info in launch_info:
+        a, b = launch_flops(dominant, info, groups, iters)
+        nom += a
+        exe += b
+    t = sum(launch_ms) * 1e-3
+    roof = {
+        "bound": "mfma",
+        "kernel": KERNEL_NAMES[dominant],
+        "achieved": nom / t / 1e12,
+        "peak": peak,
+        "unit": "TFLOP/s",
+        "frac": nom / t / 1e12 / peak,
+        "flops_per_launch": nom / len(launch_ms),
+        # the symmetric products run only their upper-triangle tiles: the
+        # FLOPs the matrix cores execute, and their share of the peak
+        "achieved_executed": exe / t / 1e12,
+        "frac_executed": exe / t / 1e12 / peak,
+        "avg_launch_ms": sum(launch_ms) / len(launch_ms),
+        "launches_timed": len(launch_ms),
+    }
+    out["dominant_kernel"] = roof["kernel"]
+    out["dominant_frac"] = roof["frac"]
+    return out, roof
 
 
-def ns_route(rows, cols, n_units, ns, schedule, cus):
-    """Kernel class that runs the NS of a stacked pass: "ns" (one launch per
-    pass: the on-chip small-unit kernel or the persistent kernel) or
-    "launches" (one launch per product).  Mirrors the library's AUTO rule
-    for attributing FLOPs to the traced kernel classes."""
-    if schedule == "persistent":
-        return "ns"
-    if schedule == "launches":
-        return "launches"
-    if on_chip(rows, cols, n_units, ns, schedule, cus):
-        return "ns"
-    return "ns" if min(rows, cols) >= 256 else "launches"
+def blas_rate():
+    """float64 FLOP/s of the host BLAS on a 1024^3 product (the best of
+    three), used only to predict whether a shape fits the sample budget."""
+    import numpy as np
+
+    a = np.random.default_rng(1).standard_normal((1024, 1024))
+    a @ a
+    best = float("inf")
+    for _ in range(3):
+        t0 = time.perf_counter()
+        a @ a
+        best = min(best, time.perf_counter() - t0)
+    return 2.0 * 1024**3 / best
 
 
-def on_chip(rows, cols, n_units, ns, schedule, cus):
-    """Whether the library runs a stacked pass on the on-chip small-unit
-    kernel (AUTO schedule, bf16 products, wide units with at most 128 rows,
-    short units or at least half as many units as CUs)."""
-    return (schedule == "auto" and ns == "bf16" and rows <= cols and rows <= 128
-            and (-(-cols // 128) <= 8 or 2 * n_units >= cus))
-
-
-def momentum_bytes(matrix_specs, ns, schedule, cus, units_of_shape):
-    """Algorithmic bytes of the momentum kernel per step: G read (2 or 4 B
-    per element), M read and written (8 B), N written: into the bf16
-    iterate (2 B) on the tiled bf16 path, else in fp32 (4 B)."""
-    total = 0
-    for m in matrix_specs:
-        r, c = m.unit_shape
-        small = on_chip(r, c, units_of_shape[(r, c)], ns, schedule, cus)
-        n_bytes = 2 if ns == "bf16" and not small else 4
-        total += m.numel * ((2 if m.grad_dtype == "bf16" else 4) + 8 + n_bytes)
-    return total
-
-
-def kernel_flops(units):
-    """Algorithmic FLOPs of each NS kernel class per iteration, summed over
-    (s, l, count) shape groups: X X^T and A*A as full products (2 s^2 l and
-    2 s^3), B*X as 2 s^2 l."""
-    gram = sum(n * 2.0 * s * s * l for s, l, n in units)
-    poly = sum(n * 2.0 * s**3 for s, l, n in units)
-    apply = sum(n * 2.0 * s * s * l for s, l, n in units)
-    return {"gram": gram, "poly": poly, "apply": apply}
-
-
-def executed_fraction(s):
-    """Share of a symmetric s x s product's tiles that run (upper triangle
-    of the tile grid; tiles are 256, or 128 when s < 256)."""
-    tile = 256 if s >= 256 else 128
-    t = -(-s // tile)
-    return (t * (t + 1) / 2) / (t * t)
-
-
-def class_flops(groups, ns, schedule, cus):
-    """Per NS kernel class ("ns", "gram", "poly", "apply"): algorithmic FLOPs
-    per iteration, and the FLOPs the kernels execute (symmetric products run
-    their upper-triangle tiles only; the on-chip small-unit kernel runs
-    whole 128 x 128 products)."""
-    alg = dict.fromkeys(("ns", "gram", "poly", "apply"), 0.0)
-    exe = dict(alg)
-    for r, c, n, nz in groups:
-        s, l = min(r, c), max(r, c)
-        f = kernel_flops([(s, l, nz)])
-        frac = executed_fraction(s)
-        e = {"gram": f["gram"] * frac, "poly": f["poly"] * frac, "apply": f["apply"]}
-        if ns_route(r, c, n, ns, schedule, cus) == "ns":
-            alg["ns"] += sum(f.values())
-            exe["ns"] += sum(e.values())
-        else:
-            for k in ("gram", "poly", "apply"):
-                alg[k] += f[k]
-                exe[k] += e[k]
-    return alg, exe
-
-
-def cpu_baseline(wl, hyper_o, seconds):
-    """The float64 oracle on a bounded sample of the workload's units."""
+def cpu_baseline(wl, budget_s):
+    """The float64 oracle (as it stands) on one seeded unit per unit shape
+    (s, l), one Muon step each, cheapest shape first; the step's oracle time
+    is extrapolated as the sum over shapes of the per-unit time times the
+    units with a non-zero gradient.  A shape whose predicted time (its FLOPs
+    at the host BLAS rate) would take the sample past the budget is not run
+    but scaled by FLOPs from the largest shape measured."""
     import numpy as np
 
     import oracle
@@ -216,85 +351,40 @@ def cpu_baseline(wl, hyper_o, seconds):
         blas_name = blas[0].get("internal_api", "?") if blas else "?"
     except Exception:  # pragma: no cover
         threads, blas_name = os.cpu_count(), "?"
-    spec = max(wl.matrices, key=lambda m: m.batch)
-    r, c = spec.unit_shape
+    ho = oracle.Hyper(scale=wl.scale)
+    groups = sorted(shape_groups(wl).items(), key=lambda kv: unit_flops(*kv[0]))
     rng = np.random.default_rng(0)
-    done, t0 = 0, time.perf_counter()
-    while True:
-        w = rng.standard_normal((r, c)) * 0.02
-        g = rng.standard_normal((r, c)) * 1e-3
-        oracle.muon_step(w, g, np.zeros((r, c)), hyper_o)
-        done += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
+    probe = blas_rate()
+    per_unit, spent, rate, notes = {}, 0.0, None, []
+    for (s, l), (n, live) in groups:
+        fl = 10 * unit_flops(s, l)
+        if rate is not None and spent + fl / probe > budget_s:
+            per_unit[(s, l)] = fl / rate
+            notes.append(f"{s}x{l}: scaled by FLOPs")
+            continue
+        w = rng.standard_normal((s, l)) * 0.02
+        g = rng.standard_normal((s, l)) * 1e-3
+        t0 = time.perf_counter()
+        oracle.muon_step(w, g, np.zeros((s, l)), ho)
+        dt = time.perf_counter() - t0
+        spent += dt
+        per_unit[(s, l)] = dt
+        rate = fl / dt
+        notes.append(f"{s}x{l}: {dt:.2f} s per unit")
+    step_s = sum(per_unit[k] * live for k, (_, live) in groups)
     return {
-        "value": done / el,
+        "value": wl.units / step_s,
         "unit": "matrices/s",
         "cores": threads,
         "kind": "oracle",
-        "sample": f"{done} units of {r}x{c}, one float64 NumPy Muon step each ({el:.1f} s, {blas_name})",
+        "sample": (f"one seeded unit per unit shape, one float64 NumPy Muon step each ({spent:.1f} s, "
+                   f"{blas_name}); step time extrapolated as the sum over shapes of per-unit time x "
+                   f"units ({step_s:.0f} s per step): " + "; ".join(notes)),
     }
 
 
-def library_group(groups):
-    """The unit shape with the most nominal NS FLOPs, and its unit count."""
-    def work(g):
-        r, c, n, _ = g
-        sm, lg = min(r, c), max(r, c)
-        return n * (4 * sm * sm * lg + 2 * sm ** 3)
-    r, c, n, _ = max(groups, key=work)
-    return r, c, n
-
-
-def gpu_library_baseline(groups, dev, stages, reps=3):
-    """The same Newton-Schulz iterations on the workload's largest group of
-    equal-shape units, written with torch's bf16 batched products (the ROCm
-    GEMM libraries): per iteration A = X X^T, B = b*A + c*A*A, X = a*X + B X
-    (baddbmm for the last two, X^T made contiguous first).  Units start as
-    normalised N(0, 1) matrices on the smaller side.  Timed with HIP events
-    on the current stream, median over `reps` runs after one warm-up."""
-    import torch
-
-    r, c, n = library_group(groups)
-    sm, lg = min(r, c), max(r, c)
-    gen = torch.Generator(device=dev).manual_seed(0)
-    x0 = torch.randn((n, sm, lg), device=dev, generator=gen)
-    x0 = (x0 / torch.linalg.vector_norm(x0, dim=(1, 2), keepdim=True)).to(torch.bfloat16)
-
-    def run():
-        x = x0.clone()
-        for steps, (a, b, cc) in stages:
-            for _ in range(steps):
-                xt = x.transpose(1, 2).contiguous()
-                am = torch.bmm(x, xt)
-                bm = torch.baddbmm(am, am, am, beta=b, alpha=cc)
-                x = torch.baddbmm(x, bm, x, beta=a, alpha=1.0)
-        return x
-
-    run()
-    torch.cuda.synchronize()
-    times = []
-    for _ in range(reps):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        run()
-        e1.record()
-        torch.cuda.synchronize()
-        times.append(e0.elapsed_time(e1))
-    ms = sorted(times)[len(times) // 2]
-    iters = sum(k for k, _ in stages)
-    flops = n * iters * (4 * sm * sm * lg + 2 * sm ** 3)
-    return {
-        "ns_ms": ms,
-        "ns_tflops": flops / (ms * 1e-3) / 1e12,
-        "kind": "torch.bmm/baddbmm, bf16",
-        "sample": f"{n} units of {sm}x{lg}, {iters} NS iterations, median of {reps} runs",
-    }
-
-
-def main():
-    args = parse()
+def main(argv=None):
+    args = parse(argv)
     if args.gpus != 1:
         print(
             f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -306,98 +396,31 @@ def main():
     import torch
 
     import workloads as W
-    from newton_schulz_matrix_muon_amd import muon
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+
+    def free():
+        import gc
+
+        from newton_schulz_matrix_muon_amd import muon
+
+        muon._WS.clear()
+        gc.collect()
+        torch.cuda.empty_cache()
+
     wl = W.workload(args.config)
-    hyper = muon.Hyper(scale=wl.scale, ns_precision=args.ns, batch_update_size=args.batch_update_size,
-                       schedule=args.schedule)
-    params, moms, grads, splits = build_inputs(wl, dev, args.grad_sets)
-    ws_bytes = muon.workspace_size(params, hyper, splits)
-    ws = muon.workspace(ws_bytes, dev)
-    torch.cuda.synchronize()
-
-    groups = unit_groups(wl)
-    n_units = wl.units
-    cus = torch.cuda.get_device_properties(dev).multi_processor_count
-
-    def one_step(k, trace=None):
-        return muon.step(params, grads[k % len(grads)], moms, hyper=hyper, split_rows=splits,
-                         ws=ws, trace=trace)
-
-    iters = sum(s for s, _ in hyper.stages)
-    n_groups = len({(m.unit_shape, m.grad_dtype) for m in wl.matrices})
-    per_step = iters * n_groups * 64  # upper bound on launches of one class per step
-    s0 = torch.cuda.current_stream()
-
-    def make_events(n):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n)]
-        for e in ev:  # create the underlying HIP events
-            e.record(s0)
-        return ev
-
-    def traced_ms(kind, k, ev):
-        cnt = one_step(k, trace=(kind, ev))
-        torch.cuda.synchronize()
-        n = min(cnt, len(ev) // 2)
-        return [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n)]
-
-    # Warm-up (untimed), then one traced step per kernel class to find the
-    # dominant NS class.
-    for k in range(args.warmup):
-        one_step(k)
-    ev1 = make_events(per_step)
-    torch.cuda.synchronize()
-    kinds = {"ns": muon.KERNEL_NS, "gram": muon.KERNEL_GRAM, "poly": muon.KERNEL_POLY,
-             "apply": muon.KERNEL_APPLY}
-    per_kind = {}
-    for name, kind in kinds.items():
-        ms = traced_ms(kind, 0, ev1)
-        if ms:
-            per_kind[name] = sum(ms)
-    mom_ms = traced_ms(muon.KERNEL_MOMENTUM, 0, ev1)
-    norm_ms = traced_ms(muon.KERNEL_NORMALIZE, 0, ev1)
-    dominant = max(per_kind, key=per_kind.get)
-
-    # Timed region: exactly `steps` steps; every launch of the dominant class
-    # is bracketed by HIP events on the step's stream, read back afterwards.
-    launches = one_step(0, trace=(kinds[dominant], ev1[:2]))  # launches per step
-    evs = [make_events(launches) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    counts = [one_step(k, trace=(kinds[dominant], evs[k])) for k in range(args.steps)]
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    sec_per_step = (t1 - t0) / args.steps
-    launch_ms = []
-    for ev, cnt in zip(evs, counts):
-        launch_ms += [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(min(cnt, len(ev) // 2))]
-    # The dominant class's time per step from the timed steps (the one
-    # traced step after warm-up can run at a different clock); the other
-    # classes keep their traced step.
-    per_kind[dominant] = sum(launch_ms) / max(1, args.steps)
-
-    flops, exe = class_flops(groups, args.ns, args.schedule, cus)
-    ns_flops_step = sum(flops.values()) * iters
-    avg_launch_ms = sum(launch_ms) / max(1, len(launch_ms))
-    # algorithmic FLOPs of one launch: the class's FLOPs per step (every
-    # iteration, every non-zero unit) over its launches per step
-    flops_per_launch = flops[dominant] * iters / launches
-    achieved = flops_per_launch / (avg_launch_ms * 1e-3) / 1e12
-    ns_ms = sum(per_kind.values())
-    ns_tflops = ns_flops_step / (ns_ms * 1e-3) / 1e12
-    peak = PEAK_TFLOPS[args.ns]
-    elem_bytes = momentum_bytes(wl.matrices, args.ns, args.schedule, cus,
-                                {(r, c): n for r, c, n, _ in groups})
-    if dominant != "ns":
-        kernel_name = f"ns_gemm {dominant}"
-    elif any(ns_route(r, c, n, args.ns, args.schedule, cus) == "ns" and min(r, c) < 256
-             for r, c, n, _ in groups):
-        kernel_name = "k_ns_small" if all(min(r, c) < 256 for r, c, _, _ in groups) else "ns"
-    else:
-        kernel_name = "ns_persistent"
-    traffic = stored_traffic(kernel_name, wl.title, args.ns)
+    inputs = build_inputs(wl, dev, args.grad_sets)
+    head, roof = measure(wl, args.ns, args.steps, args.warmup, dev, inputs, args.schedule)
+    subs = {}
+    if not args.no_sub_configs and args.config == HEADLINE and args.ns == "bf16":
+        free()
+        r, _ = measure(wl, "fp32", FP32_SAMPLE_STEPS, 1, dev, inputs, args.schedule,
+                       trace_classes=False)
+        r["sample"] = f"{FP32_SAMPLE_STEPS} step after 1 warm-up step"
+        subs[f"{args.config}_fp32"] = r
+    del inputs
+    free()
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib * (1 << 20) // 4
         src = torch.zeros(n, dtype=torch.int32, device=dev)
@@ -406,15 +429,30 @@ def main():
         torch.bitwise_not(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
+    if not args.no_sub_configs:
+        for cfg, ns, steps, warmup, tc in SUB_CONFIGS:
+            if cfg == args.config and ns == args.ns:
+                continue
+            w = W.workload(cfg)
+            inp = build_inputs(w, dev, 2)
+            r, _ = measure(w, ns, steps, warmup, dev, inp, "auto", trace_classes=tc)
+            if cfg == 1:
+                r["us_per_step"] = r["ms_per_step"] * 1e3
+            subs[f"{cfg}_{ns}"] = r
+            del inp
+            free()
 
+    traffic = stored_traffic(roof["kernel"], wl.title, args.ns) if roof else None
+    if roof:
+        roof["traffic"] = traffic["bytes_per_launch"] if traffic else None
     line = {
         "metric": "Muon matrices/sec + NS TFLOP/s (% of MI355X bf16 MFMA peak) per config",
-        "value": n_units / sec_per_step,
+        "value": head["matrices_per_s"],
         "unit": "matrices/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": sec_per_step * 1e3,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -423,7 +461,7 @@ def main():
         "config": {
             "workload": wl.title,
             "config_index": args.config,
-            "units": n_units,
+            "units": wl.units,
             "unit_shapes": sorted({f"{m.unit_shape[0]}x{m.unit_shape[1]}" for m in wl.matrices}),
             "grad_dtype": wl.matrices[0].grad_dtype,
             "scale": wl.scale,
@@ -431,48 +469,14 @@ def main():
             "schedule": args.schedule,
             "parallelism": "single GPU",
         },
-        "ns_tflops": ns_tflops,
-        "ns_frac_of_peak": ns_tflops / peak,
-        "ns_ms_per_step": ns_ms,
-        "kernel_ms_per_step": {
-            **{k: round(v, 4) for k, v in per_kind.items()},
-            "momentum": round(sum(mom_ms), 4),
-            "normalize": round(sum(norm_ms), 4),
-        },
-        # FLOPs the kernels execute: the symmetric products run only their
-        # upper-triangle tiles
-        "kernel_tflops_executed": {
-            k: round(exe[k] * iters / (per_kind[k] * 1e-3) / 1e12, 2) for k in per_kind
-        },
-        "elementwise_gbs": elem_bytes / (sum(mom_ms) * 1e-3) / 1e9 if mom_ms else None,
-        "roofline": {
-            "bound": "mfma",
-            "kernel": kernel_name,
-            "achieved": achieved,
-            "peak": peak,
-            "unit": "TFLOP/s",
-            "frac": achieved / peak,
-            "traffic": traffic["bytes_per_launch"] if traffic else None,
-            "flops_per_launch": flops_per_launch,
-            # the symmetric products run only their upper-triangle tiles:
-            # the FLOPs the matrix cores execute, and their share of the peak
-            "achieved_executed": exe[dominant] * iters / launches / (avg_launch_ms * 1e-3) / 1e12,
-            "frac_executed": exe[dominant] * iters / launches / (avg_launch_ms * 1e-3) / 1e12 / peak,
-            "avg_launch_ms": avg_launch_ms,
-            "launches_timed": len(launch_ms),
-        },
+        **{k: head[k] for k in ("ns_tflops", "ns_frac_of_peak", "ns_ms_per_step", "ns_tflops_step",
+                                "kernel_ms_per_step", "elementwise_gbs", "elementwise_frac_of_hbm")
+           if k in head},
+        "roofline": roof,
+        "configs": subs,
     }
-    if not args.no_library_baseline and args.ns == "bf16":
-        lib = gpu_library_baseline(groups, dev, hyper.stages)
-        if len(groups) == 1:
-            # one unit shape: the same units as this step's NS time
-            lib["this_library_speedup"] = lib["ns_ms"] / ns_ms
-        line["gpu_library_baseline"] = lib
     if not args.no_cpu_baseline:
-        import oracle
-
-        ho = oracle.Hyper(scale=wl.scale)
-        line["cpu_baseline"] = cpu_baseline(wl, ho, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 

@@ -1,87 +1,85 @@
 """Host-side pieces of bench.py (no GPU): the workload FLOP counts, the
-executed share of the symmetric products and the stored-traffic lookup."""
+FLOPs of a launch from what the library reports it covered, the executed
+share of the symmetric products, the CPU-baseline extrapolation and the
+stored-traffic lookup."""
 
 import json
+
+import pytest
 
 import bench
 import workloads as W
 
 
-def test_kernel_flops_match_the_workload_total():
-    wl = W.workload(2)
-    units = [(min(r, c), max(r, c), nz) for r, c, _, nz in bench.unit_groups(wl)]
-    f = bench.kernel_flops(units)
-    iters = 10
-    # one NS iteration: X X^T (2 s^2 l) + A A (2 s^3) + B X (2 s^2 l)
-    assert (f["gram"] + f["poly"] + f["apply"]) * iters == wl.ns_flops()
+def test_step_flops_match_the_workload_total():
+    for cfg in (1, 2, 3, 5):
+        wl = W.workload(cfg)
+        assert bench.ns_flops_per_step(wl, 10) == pytest.approx(wl.ns_flops(), rel=1e-12)
+    # the MoE bank: 13 of 128 experts per bank have zero gradients and no NS work
+    wl = W.workload(4)
+    assert bench.ns_flops_per_step(wl, 10) == pytest.approx(wl.ns_flops() * 115 / 128, rel=1e-12)
+
+
+def test_shape_groups_merge_tall_and_wide_units():
+    g = bench.shape_groups(W.workload(3))
+    assert g[(128, 4096)] == (48, 48)        # Q, K and V heads
+    assert g[(4096, 14336)] == (3, 3)        # gate, up (tall) and down (wide)
+    assert g[(4096, 4096)] == (1, 1)
+    g4 = bench.shape_groups(W.workload(4))
+    assert g4 == {(2048, 7168): (384, 345)}
+    assert sum(n for n, _ in bench.shape_groups(W.workload(5)).values()) == W.workload(5).units
 
 
 def test_executed_fraction_of_symmetric_tiles():
-    assert bench.executed_fraction(1024) == 10 / 16   # 4 x 4 tiles of 256
-    assert bench.executed_fraction(256) == 1.0
-    assert bench.executed_fraction(128) == 1.0        # one 128 tile
-    assert bench.executed_fraction(4096) == (16 * 17 / 2) / 256
+    assert bench.executed_fraction(1024, 256) == 10 / 16   # 4 x 4 tiles of 256
+    assert bench.executed_fraction(256, 256) == 1.0
+    assert bench.executed_fraction(128, 128) == 1.0
+    assert bench.executed_fraction(4096, 256) == (16 * 17 / 2) / 256
+    assert bench.executed_fraction(1024, 128) == 36 / 64
 
 
-def test_unit_groups_merge_heads_of_one_shape():
-    wl = W.workload(3)  # Q, K and V heads are all 128 x 4096
-    g = {(r, c): (n, nz) for r, c, n, nz in bench.unit_groups(wl)}
-    assert g[(128, 4096)] == (48, 48)
-    assert sum(n for n, _ in g.values()) == wl.units
+def test_launch_flops():
+    groups = {(1024, 1024): (32, 32), (2048, 7168): (384, 345)}
+    s, l = 1024, 1024
+    nom, exe = bench.launch_flops("ns", (s, l, 32, 256), groups, 10)
+    assert nom == 32 * 10 * (4 * s * s * l + 2 * s**3)
+    assert exe == pytest.approx(32 * 10 * (2 * s * s * l * (10 / 16) + 2 * s**3 * (10 / 16) + 2 * s * s * l))
+    # one product per launch under the per-product schedule
+    assert bench.launch_flops("apply", (s, l, 32, 256), groups, 10) == (32 * 2 * s * s * l,) * 2
+    g, ge = bench.launch_flops("gram", (s, l, 32, 256), groups, 10)
+    assert (g, ge) == (32 * 2 * s * s * l, 32 * 2 * s * s * l * 10 / 16)
+    # only units with a non-zero gradient count
+    nom, _ = bench.launch_flops("ns", (2048, 7168, 384, 256), groups, 10)
+    assert nom == pytest.approx(345 * 10 * (4 * 2048**2 * 7168 + 2 * 2048**3))
+    # the on-chip kernel: whole 128-row products
+    nom, exe = bench.launch_flops("ns_small", (64, 128, 1, 128), {}, 10)
+    assert nom == 10 * (4 * 64 * 64 * 128 + 2 * 64**3)
+    assert exe == 10 * (4 * 128**3 + 2 * 128**3)
 
 
-def test_library_baseline_takes_the_group_with_the_most_work():
-    # the transformer layer: 48 heads of 128 x 4096 carry far less NS work
-    # than the three 4096 x 14336 MLP matrices (two of one unit shape)
-    r, c, n = bench.library_group(bench.unit_groups(W.workload(3)))
-    assert (min(r, c), max(r, c)) == (4096, 14336) and n == 2
-    assert bench.library_group([(1024, 1024, 32, 32)]) == (1024, 1024, 32)
-    assert bench.library_group([(128, 4096, 1536, 1536), (4096, 4096, 32, 32)]) == (4096, 4096, 32)
+def test_cpu_baseline_extrapolates_over_shapes(monkeypatch):
+    import oracle
 
+    calls = []
 
-def test_ns_route_follows_the_auto_rule():
-    r = bench.ns_route
-    assert r(1024, 1024, 32, "bf16", "auto", 256) == "ns"            # 256 tiles: persistent
-    assert r(128, 4096, 48, "bf16", "auto", 256) == "launches"       # few long heads
-    assert r(128, 4096, 128, "bf16", "auto", 256) == "ns"            # many heads: on chip
-    assert r(64, 128, 1, "bf16", "auto", 256) == "ns"                # short: on chip
-    assert r(64, 128, 1, "fp32", "auto", 256) == "launches"          # fp32 products: tiled
-    assert r(300, 128, 4, "bf16", "auto", 256) == "launches"         # tall
-    assert r(128, 4096, 512, "bf16", "launches", 256) == "launches"
-    assert r(64, 128, 1, "bf16", "persistent", 256) == "ns"
+    def fake_step(w, g, m, h):
+        calls.append(w.shape)
 
-
-def test_momentum_bytes_follow_the_route():
-    # 32 x 1024^2, bf16 grads: G 2 + M 8 + N 2 (written into the bf16
-    # iterate of the tiled path) = 12 B per element; with fp32 products N is
-    # written in fp32 (14 B)
-    wl = W.workload(2)
-    shapes = {(r, c): n for r, c, n, _ in bench.unit_groups(wl)}
-    numel = sum(m.numel for m in wl.matrices)
-    assert bench.momentum_bytes(wl.matrices, "bf16", "auto", 256, shapes) == 12 * numel
-    assert bench.momentum_bytes(wl.matrices, "fp32", "auto", 256, shapes) == 14 * numel
-    # the layer's 48 heads run tiled (few long heads): 12 B everywhere; with
-    # many heads they run on chip, which reads N in fp32 (14 B for the heads)
-    wl3 = W.workload(3)
-    g3 = {(r, c): n for r, c, n, _ in bench.unit_groups(wl3)}
-    n3 = sum(m.numel for m in wl3.matrices)
-    assert bench.momentum_bytes(wl3.matrices, "bf16", "auto", 256, g3) == 12 * n3
-    many = dict(g3)
-    many[(128, 4096)] = 1536
-    heads = sum(m.numel for m in wl3.matrices if m.unit_shape == (128, 4096))
-    assert bench.momentum_bytes(wl3.matrices, "bf16", "auto", 256, many) == 12 * n3 + 2 * heads
-
-
-def test_class_flops_split_by_route():
-    groups = [(1024, 1024, 4, 4), (128, 4096, 48, 40)]
-    alg, exe = bench.class_flops(groups, "bf16", "auto", 256)
-    big = bench.kernel_flops([(1024, 1024, 4)])
-    heads = bench.kernel_flops([(128, 4096, 40)])
-    assert alg["ns"] == sum(big.values())
-    for k in ("gram", "poly", "apply"):
-        assert alg[k] == heads[k]
-    assert exe["ns"] < alg["ns"]                     # symmetric tiles of 1024 squares
-    assert exe["gram"] == alg["gram"]                # one 128 tile
+    monkeypatch.setattr(oracle, "muon_step", fake_step)
+    t = iter([0.0, 1.0, 1.0, 3.0])  # two measured shapes: 1 s and 2 s per unit
+    monkeypatch.setattr(bench.time, "perf_counter", lambda: next(t))
+    # a host BLAS rate at which O (4.1e12 FLOPs) is predicted at 2 s and the
+    # MLP shape at 5.3 s
+    monkeypatch.setattr(bench, "blas_rate", lambda: 10 * bench.unit_flops(4096, 4096) / 2.0)
+    wl = W.workload(3)
+    # heads first (cheapest), then O; the MLP shape is predicted past the
+    # budget and scaled by FLOPs from O's measured rate
+    r = bench.cpu_baseline(wl, budget_s=5.0)
+    assert calls == [(128, 4096), (4096, 4096)]
+    mlp = 2.0 * bench.unit_flops(4096, 14336) / bench.unit_flops(4096, 4096)
+    step = 48 * 1.0 + 1 * 2.0 + 3 * mlp
+    assert r["value"] == pytest.approx(wl.units / step)
+    assert "scaled by FLOPs" in r["sample"] and r["kind"] == "oracle"
 
 
 def test_stored_traffic_lookup(tmp_path):
@@ -108,7 +106,7 @@ def test_committed_traffic_records_are_well_formed():
                 assert len(rec["sources_sha256"]) == 64
 
 
-def test_multi_gpu_request_exits_with_a_message(capsys):
+def test_multi_gpu_request_exits_with_a_message():
     import subprocess
     import sys
 

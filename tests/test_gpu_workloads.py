@@ -2,17 +2,25 @@
 
 The GPU runs every unit of each workload at its real shape and in the launch
 configuration the benchmark uses (one call over all banks, whole shape
-groups stacked).  The oracle then checks:
-  * every unit it can afford in seconds: all 48 split heads of the layer, the
-    all-zero experts of the MoE bank (exactly), one sampled expert per shape,
-    the 4096x4096 projection for one step;
-  * the 4096-wide MLP units through properties that hold at any size: the
-    momentum recurrence (element-wise, exact up to fp32 storage), the fused
-    update against the NS-only entry point on the same look-ahead, and the
-    singular values of the NS output (eigenvalues of O O^T in float64), which
-    for these i.i.d. inputs lie in phi's band [1, 1.0021] up to the bf16
-    rounding of the products.
+groups stacked).  The oracle then checks, on the exact bytes the GPU
+consumed (the weights before the first step and every step's gradients,
+read back):
+  * all 48 split heads of the layer over three steps, and its large units:
+    the 4096 x 4096 projection, gate and up (14336 x 4096) and down
+    (4096 x 14336) at step 1, down also at step 2;
+  * in the MoE bank, one expert of each bank (gate, up, down) over three
+    steps, and the all-zero experts exactly;
+  * in the ~7B set, on both NS paths over all three steps: the heads of two
+    layers and one projection, one gate and one down matrix (the oracle runs
+    once per unit; both paths consume the same seeded bytes);
+  * as extras beside the oracle: the momentum recurrence of the layer's MLP
+    units element by element, the fused update against the NS-only entry
+    point on the same look-ahead, and the singular values of the NS output
+    (eigenvalues of O O^T in float64), which for these i.i.d. inputs lie in
+    phi's band [1, 1.0021] up to the rounding of the products.
 """
+
+import hashlib
 
 import numpy as np
 import pytest
@@ -49,6 +57,65 @@ def _alloc(wl):
     moms = [torch.zeros_like(p) for p in params]
     splits = [m.split_rows for m in wl.matrices]
     return params, moms, splits
+
+
+def _digest(a: np.ndarray) -> str:
+    return hashlib.sha256(np.ascontiguousarray(a).tobytes()).hexdigest()
+
+
+# Oracle trajectories of single units, kept across tests: the bf16 and the
+# fp32 test of the ~7B set consume the same bytes (checked by digest) and
+# share one oracle run per unit.
+_ORACLE = {}
+
+
+def _oracle_trajectory(key, w0, grads, hw, split_rows=0):
+    """(W_t, M_t) of the oracle for t = 1..len(grads), from W0 and M0 = 0."""
+    ident = (key, _digest(w0), tuple(_digest(g) for g in grads))
+    if ident not in _ORACLE:
+        w, m, out = w0.copy(), np.zeros_like(w0), []
+        for t, g in enumerate(grads, start=1):
+            w, m, _ = oracle.muon_step(w, g, m, hw, split_rows, t)
+            out.append((w, m))
+        _ORACLE[ident] = out
+    return _ORACLE[ident]
+
+
+def _run_and_collect(gpu_lib, wl, h, steps, watch):
+    """Runs `steps` steps of the whole workload on the GPU (one call over
+    all banks per step) and returns, per watched (bank, matrix): W0, the
+    gradients of every step and the GPU's W_t and M_t after every step, as
+    float64 host copies."""
+    params, moms, splits = _alloc(wl)
+    rec = {k: {"w0": f64(params[k[0]][k[1]]), "g": [], "w": [], "m": []} for k in watch}
+    for t in range(1, steps + 1):
+        say(f"   GPU step {t}")
+        grads = [W.bank_grads(wl, t - 1, i, DEV) for i in range(len(wl.matrices))]
+        gpu_lib.step(params, grads, moms, hyper=h, split_rows=splits)
+        torch.cuda.synchronize()
+        for (b, e), r in rec.items():
+            r["g"].append(f64(grads[b][e]))
+            r["w"].append(f64(params[b][e]))
+            r["m"].append(f64(moms[b][e]))
+        del grads
+    del params, moms
+    torch.cuda.empty_cache()
+    return rec
+
+
+def _check_trajectory(r, ref, h, tol, what, split_rows=0):
+    """Momentum and weight of every step against the oracle's."""
+    for t, ((wr, mr), wg, mg) in enumerate(zip(ref, r["w"], r["m"]), start=1):
+        em = rel(mg, mr)
+        assert em <= TOL_M, f"{what} step {t}: momentum rel err {em:.3e}"
+        if split_rows:
+            for hd in range(wr.shape[0] // split_rows):
+                blk = slice(hd * split_rows, (hd + 1) * split_rows)
+                check_weight(wg[blk], wr[blk], r["w0"][blk], t, h, tol, f"{what} head {hd} step {t}")
+            say(f"   {what} step {t}: every head within tolerance")
+        else:
+            e = check_weight(wg, wr, r["w0"], t, h, tol, f"{what} step {t}")
+            say(f"   {what} step {t}: relative update error {e:.3e}")
 
 
 def _spectrum_band(o64, lo, hi, what):
@@ -116,6 +183,24 @@ def test_transformer_layer_workload(gpu_lib):
     torch.cuda.empty_cache()
 
 
+LAYER_UNITS = {"o_proj": (1, 1), "gate": (2, 1), "up": (3, 1), "down": (4, 2)}  # bank, steps
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", list(LAYER_UNITS))
+def test_layer_large_units_against_oracle(gpu_lib, name):
+    # The layer's 4096-wide units (O 4096^2, gate and up 14336 x 4096, down
+    # 4096 x 14336) against the oracle: step 1 for each, step 2 for down.
+    wl = W.workload(3)
+    bank, steps = LAYER_UNITS[name]
+    say(f"[layer {name}] {wl.matrices[bank].rows}x{wl.matrices[bank].cols}, {steps} step(s)")
+    h = gpu_lib.Hyper(scale=wl.scale, ns_precision="bf16")
+    hw = oracle_hyper(h)
+    r = _run_and_collect(gpu_lib, wl, h, steps, [(bank, 0)])[(bank, 0)]
+    ref = _oracle_trajectory(("layer", name), r["w0"], r["g"], hw)
+    _check_trajectory(r, ref, h, TOL_NS["bf16"], name)
+
+
 def test_moe_bank_workload(gpu_lib):
     # 128 experts x {gate, up 2048x7168, down 7168x2048}, bf16 N(0, 1e-3)
     # grads, 13 experts all-zero on every step, three steps.
@@ -124,11 +209,11 @@ def test_moe_bank_workload(gpu_lib):
     hw = oracle_hyper(h)
     params, moms, splits = _alloc(wl)
     zero = W.zero_experts(wl, 128)
-    live_gate = int(next(e for e in range(128) if e not in set(zero.tolist())))
-    samples = {0: live_gate, 2: int(next(e for e in range(127, -1, -1) if e not in set(zero.tolist())))}
-    w0 = {b: f64(params[b][e]) for b, e in samples.items()}
+    live = [e for e in range(128) if e not in set(zero.tolist())]
+    # one live expert per bank: gate, up (2048 x 7168) and down (7168 x 2048)
+    samples = {0: live[0], 1: live[len(live) // 2], 2: live[-1]}
+    rec = {b: {"w0": f64(params[b][e]), "g": [], "w": [], "m": []} for b, e in samples.items()}
     z0 = [f64(params[b][zero]) for b in range(3)]
-    refs = {b: (w0[b].copy(), np.zeros_like(w0[b])) for b in samples}
     for t in range(1, wl.steps + 1):
         say(f"[moe] step {t}")
         grads = [W.bank_grads(wl, t - 1, i, DEV) for i in range(3)]
@@ -142,56 +227,45 @@ def test_moe_bank_workload(gpu_lib):
             for _ in range(t):
                 expect = expect * d
             np.testing.assert_array_max_ulp(f64(params[b][zero]).astype(np.float32), expect, maxulp=2 * t)
-        if t == 1:
-            for b, e in samples.items():
-                wr, mr = refs[b]
-                wr, mr, _ = oracle.muon_step(wr, f64(grads[b][e]), mr, hw, 0, 1)
-                assert rel(f64(moms[b][e]), mr) <= TOL_M
-                err = check_weight(f64(params[b][e]), wr, w0[b], 1, h, TOL_NS["bf16"], f"bank {b} expert {e}")
-                say(f"   bank {b} expert {e}: relative update error {err:.3e}")
+        for b, e in samples.items():
+            rec[b]["g"].append(f64(grads[b][e]))
+            rec[b]["w"].append(f64(params[b][e]))
+            rec[b]["m"].append(f64(moms[b][e]))
         del grads
+    del params, moms
     torch.cuda.empty_cache()
+    for b, e in samples.items():
+        ref = _oracle_trajectory(("moe", b, e), rec[b]["w0"], rec[b]["g"], hw)
+        _check_trajectory(rec[b], ref, h, TOL_NS["bf16"], f"bank {b} expert {e}")
 
 
+# The ~7B set's watched matrices: (bank, layer, split_rows): the fused QKV of
+# layers 0 and 31 (48 heads each), one projection, one gate, one down.
+SEVEN_B_WATCH = [(0, 0, 128), (0, 31, 128), (1, 3, 0), (2, 11, 0), (4, 29, 0)]
+
+
+@pytest.mark.timeout(1200)
 @pytest.mark.parametrize("prec", ["bf16", "fp32"])
 def test_seven_billion_matrix_set(gpu_lib, prec):
-    # 32 transformer layers of the hidden-4096 shapes (6.98e9 parameters),
-    # unit_rms_norm scale, N(0, 1e-3) grads times a per-matrix scale drawn
-    # log-uniform in [1e-5, 1e-1].  The fp32 path runs one step, bf16 three.
+    # 32 transformer layers of the hidden-4096 shapes (6.98e9 parameters,
+    # 1664 units), unit_rms_norm scale, N(0, 1e-3) grads times a per-matrix
+    # scale drawn log-uniform in [1e-5, 1e-1]; three steps on each NS path.
     wl = W.workload(5)
+    say(f"[7B {prec}] {wl.units} units, {wl.steps} steps")
     h = gpu_lib.Hyper(scale=wl.scale, ns_precision=prec)
     hw = oracle_hyper(h)
-    params, moms, splits = _alloc(wl)
-    layers = [0, 31]
-    heads0 = {L: f64(params[0][L]) for L in layers}
-    refs = {L: (heads0[L].copy(), np.zeros_like(heads0[L])) for L in layers}
-    steps = wl.steps if prec == "bf16" else 1
-    for t in range(1, steps + 1):
-        say(f"[7B {prec}] step {t}")
-        grads = [W.bank_grads(wl, t - 1, i, DEV) for i in range(len(wl.matrices))]
-        gpu_lib.step(params, grads, moms, hyper=h, split_rows=splits)
-        torch.cuda.synchronize()
-        for L in layers:
-            wr, mr = refs[L]
-            wr, mr, _ = oracle.muon_step(wr, f64(grads[0][L]), mr, hw, 128, t)
-            refs[L] = (wr, mr)
-            assert rel(f64(moms[0][L]), mr) <= TOL_M
-            wg = f64(params[0][L])
-            for hd in (0, 17, 47):
-                blk = slice(hd * 128, (hd + 1) * 128)
-                check_weight(wg[blk], wr[blk], heads0[L][blk], t, h, TOL_NS[prec], f"layer {L} head {hd}")
-        if t == 1:
-            # unit_rms_norm: the update of the 4096x14336 down projection is
-            # -lr * sqrt(fan_out / fan_in) * O, and O's singular values sit
-            # in phi's band
-            L = 7
-            spec = wl.matrices[4]
-            g32 = grads[4][L].float().cpu().numpy()
-            _, look32 = _lookahead32(np.zeros_like(g32), g32, h.mu)
-            look = torch.from_numpy(look32).to(DEV)
-            o, _ = gpu_lib.newton_schulz([look], hyper=h)
-            torch.cuda.synchronize()
-            tol = 0.05 if prec == "bf16" else 1e-3
-            _spectrum_band(f64(o[0]), 1.0 - tol, 1.0021 + tol, f"down layer {L}")
-        del grads
-    torch.cuda.empty_cache()
+    rec = _run_and_collect(gpu_lib, wl, h, wl.steps, [(b, L) for b, L, _ in SEVEN_B_WATCH])
+    for b, L, split in SEVEN_B_WATCH:
+        name = f"{wl.matrices[b].name} layer {L}"
+        say(f"   oracle: {name}")
+        r = rec[(b, L)]
+        ref = _oracle_trajectory(("7b", b, L), r["w0"], r["g"], hw, split)
+        _check_trajectory(r, ref, h, TOL_NS[prec], name, split)
+    # extra: the NS-only entry point on the step-1 look-ahead of the down
+    # projection; O's singular values sit in phi's band
+    g32 = rec[(4, 29)]["g"][0].astype(np.float32)
+    _, look32 = _lookahead32(np.zeros_like(g32), g32, h.mu)
+    o, _ = gpu_lib.newton_schulz([torch.from_numpy(look32).to(DEV)], hyper=h)
+    torch.cuda.synchronize()
+    tol = 0.05 if prec == "bf16" else 1e-3
+    _spectrum_band(f64(o[0]), 1.0 - tol, 1.0021 + tol, "down layer 29, step 1")
