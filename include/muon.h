@@ -197,6 +197,25 @@ int muon_newton_schulz_batched(const float* const* x_in, float* const* o_out,
                                const muon_matrix_desc* mats, int64_t n_mats, const muon_hyper* h,
                                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* muon_step_batched without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops,
+ * harnesses that forbid hipMalloc).  The library's own fixed device scratch
+ * of 128 MiB per GPU (held until the process ends) takes the workspace's
+ * place; nothing is allocated on any call.  Arguments, results and the
+ * other errors are those of muon_step_batched.  Differences:
+ *  - MUON_ERR_WORKSPACE when the step needs more scratch than 128 MiB (the
+ *    size muon_workspace_size reports), before anything runs;
+ *  - every tiled pass runs as one launch per product (the schedule's
+ *    PERSISTENT and AUTO choice of it do not apply), whose kernels never
+ *    wait, so there is no stopped launch to report; results are bit-identical
+ *    to muon_step_batched's;
+ *  - all calls on one GPU share its scratch: calls that overlap on one GPU
+ *    (on different streams, or from several threads) race and give
+ *    undefined results; the caller orders them. */
+int muon_step_batched_noalloc(float* const* params, const void* const* grads,
+                              float* const* momenta, const muon_matrix_desc* mats, int64_t n_mats,
+                              const muon_hyper* h, hipStream_t stream);
+
 /* Kernel classes that a trace can bracket. */
 typedef enum {
   MUON_KERNEL_MOMENTUM = 1, /* momentum + Nesterov + Frobenius partial sums */

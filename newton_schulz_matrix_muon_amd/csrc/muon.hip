@@ -70,6 +70,15 @@ struct Layout {
 
 constexpr size_t kHeader = 256;  // status header at the start of the workspace
 constexpr int64_t kMaxChunks = (int64_t)1 << 20;  // stacked passes per call
+
+// Device scratch of muon_step_batched_noalloc, for callers that cannot
+// allocate: a fixed array in the library's code object, one copy per GPU
+// the library runs on, held until the process ends.  Host code never uses
+// the array's name as an address (on the host it is only a stand-in): the
+// device address comes from hipGetSymbolAddress, once per device, and is
+// kept in g_scratch.
+constexpr size_t kScratchBytes = (size_t)128 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 constexpr int kMaxQueues = 16;   // persistent schedule: at most one queue per XCC
 
 // Whether the AUTO schedule may run the pass on the on-chip small-unit
@@ -405,6 +414,25 @@ int device_info(DeviceInfo* out) {
   return MUON_OK;
 }
 
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (its address looked up on the
+// first call on the device).
+int scratch_workspace(void** ws, size_t* bytes) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MUON_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MUON_ERR_HIP;
+    g_scratch[dev] = p;
+  }
+  *ws = g_scratch[dev];
+  *bytes = kScratchBytes;
+  return MUON_OK;
+}
+
 constexpr double kWaitLimitSeconds = 5.0;  // bound of one dependency wait
 
 // Bound of one dependency wait in wall-clock ticks.  Test hook:
@@ -449,7 +477,8 @@ void launch_phase(bool bf16, int tile, int km, const GemmArgs& g, const ChunkArg
 // with the fused final epilogue.
 int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs,
               const void* const* ins, float* const* moms, const muon_matrix_desc* mats,
-              unsigned char* ws, hipStream_t s, Tracer& tr, bool first_chunk) {
+              unsigned char* ws, hipStream_t s, Tracer& tr, bool first_chunk,
+              bool allow_persistent) {
   const bool bf16 = h->ns_precision == MUON_NS_BF16;
   const Layout L = layout_of(c, h);
   ChunkArgs ca;
@@ -597,8 +626,8 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
   const int64_t n_items = (int64_t)total * U * (2 * tg + ta);
   // AUTO: persistent for 256-tile passes; 128-tile passes (short K) run
   // faster as separate launches than as claimed tiles.
-  const bool persistent = h->schedule == MUON_SCHEDULE_PERSISTENT ||
-                          (h->schedule == MUON_SCHEDULE_AUTO && T == 256);
+  const bool persistent = allow_persistent && (h->schedule == MUON_SCHEDULE_PERSISTENT ||
+                                               (h->schedule == MUON_SCHEDULE_AUTO && T == 256));
   if (persistent && n_items < INT32_MAX / 2) {
     DeviceInfo di;
     const int dst = device_info(&di);
@@ -821,9 +850,13 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
   return MUON_OK;
 }
 
+// scratch_ws: instead of a caller workspace, the library's fixed device
+// scratch (muon_step_batched_noalloc); ws and ws_bytes are then ignored.
+int scratch_workspace(void** ws, size_t* bytes);
+
 int run(bool step, float* const* outs, const void* const* ins, float* const* moms,
         const muon_matrix_desc* mats, int64_t n, const muon_hyper* h, void* ws, size_t ws_bytes,
-        hipStream_t stream, muon_trace* trace) {
+        hipStream_t stream, muon_trace* trace, bool scratch_ws = false) {
   try {
     int st = validate_hyper(h);
     if (st != MUON_OK) return st;
@@ -854,13 +887,22 @@ int run(bool step, float* const* outs, const void* const* ins, float* const* mom
     st = plan(mats, n, h, step, &chunks);
     if (st != MUON_OK) return st;
     const size_t need = workspace_of(chunks, h);
+    if (scratch_ws) {
+      // the fixed scratch: refuse a step that needs more, before anything runs
+      if (need > kScratchBytes) return MUON_ERR_WORKSPACE;
+      st = scratch_workspace(&ws, &ws_bytes);
+      if (st != MUON_OK) return st;
+    }
     if (need > 0 && (!ws || ws_bytes < need)) return MUON_ERR_WORKSPACE;
     if (((uintptr_t)ws & (kAlign - 1)) != 0) return MUON_ERR_ALIGN;
     Tracer tr{trace, stream};
     if (trace) trace->count = 0;
     for (const Chunk& c : chunks) {
+      // The scratch's status header cannot be read by the callers of the
+      // scratch entry point, so their passes run as one launch per product,
+      // whose kernels never wait (bit-identical to the persistent launch).
       st = run_chunk(c, h, step, outs, ins, moms, mats, static_cast<unsigned char*>(ws), stream, tr,
-                     &c == &chunks.front());
+                     &c == &chunks.front(), !scratch_ws);
       if (st != MUON_OK) return st;
     }
     return MUON_OK;
@@ -927,6 +969,12 @@ int muon_step_batched(float* const* params, const void* const* grads, float* con
                       const muon_matrix_desc* mats, int64_t n, const muon_hyper* h,
                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return run(true, params, grads, momenta, mats, n, h, workspace, workspace_bytes, stream, nullptr);
+}
+
+int muon_step_batched_noalloc(float* const* params, const void* const* grads,
+                              float* const* momenta, const muon_matrix_desc* mats, int64_t n,
+                              const muon_hyper* h, hipStream_t stream) {
+  return run(true, params, grads, momenta, mats, n, h, nullptr, 0, stream, nullptr, true);
 }
 
 int muon_newton_schulz_batched_traced(const float* const* x_in, float* const* o_out,

@@ -49,6 +49,7 @@ EXPORTED = (
     "muon_newton_schulz_batched",
     "muon_step_batched_traced",
     "muon_newton_schulz_batched_traced",
+    "muon_step_batched_noalloc",
     "muon_workspace_status",
     "muon_status_string",
     "muon_abi_version",
@@ -141,6 +142,8 @@ def _load() -> ctypes.CDLL:
     lib.muon_newton_schulz_batched.restype = ctypes.c_int
     lib.muon_newton_schulz_batched_traced.argtypes = ns_args + [ctypes.POINTER(TraceC)]
     lib.muon_newton_schulz_batched_traced.restype = ctypes.c_int
+    lib.muon_step_batched_noalloc.argtypes = step_args[:6] + [P]
+    lib.muon_step_batched_noalloc.restype = ctypes.c_int
     lib.muon_workspace_status.argtypes = [P, ctypes.c_size_t, P]  # workspace, bytes, stream
     lib.muon_workspace_status.restype = ctypes.c_int
     lib.muon_status_string.argtypes = [ctypes.c_int]
@@ -405,6 +408,46 @@ def step(
     if check_default if check is None else check:
         workspace_status(ws, stream)
     return count
+
+
+def step_noalloc(
+    params: Sequence[torch.Tensor],
+    grads: Sequence[torch.Tensor],
+    momenta: Sequence[torch.Tensor],
+    hyper: Hyper | None = None,
+    split_rows: Sequence[int] | None = None,
+    stream=None,
+) -> None:
+    """One Muon step on the library's fixed device scratch
+    (muon_step_batched_noalloc): no workspace, nothing allocated; the step
+    may need at most 128 MiB of scratch.  Calls that overlap on one GPU
+    race."""
+    hyper = hyper or Hyper()
+    n = len(params)
+    if not (len(grads) == len(momenta) == n):
+        raise ValueError("params, grads and momenta must have the same length")
+    if n == 0:
+        return
+    dev = params[0].device
+    _check(params, torch.float32, "params", dev)
+    _check(momenta, torch.float32, "momenta", dev)
+    _check(grads, None, "grads", dev)
+    gd = []
+    for p, g, m in zip(params, grads, momenta):
+        if p.shape != g.shape or p.shape != m.shape:
+            raise ValueError("params, grads and momenta shapes differ")
+        if g.dtype not in (torch.bfloat16, torch.float32):
+            raise TypeError(f"grads must be bf16 or fp32, got {g.dtype}")
+        gd.append(DTYPE_BF16 if g.dtype == torch.bfloat16 else DTYPE_F32)
+    split_rows = list(split_rows) if split_rows is not None else [0] * n
+    descs = _descs(params, split_rows, gd)
+    hc = hyper.to_c()
+    st = LIB.muon_step_batched_noalloc(
+        _ptrs(params), _ptrs(grads), _ptrs(momenta), descs, n, ctypes.byref(hc),
+        ctypes.c_void_p(_stream_ptr(stream)),
+    )
+    if st != MUON_OK:
+        raise MuonError(st, "muon_step_batched_noalloc")
 
 
 def newton_schulz(

@@ -240,6 +240,27 @@ def test_planner_fuzz():
             assert (st3 == 0 and size3 <= size) or st3 == -2
 
 
+def test_noalloc_error_paths_touch_nothing():
+    # the scratch entry point validates like muon_step_batched and refuses a
+    # step that needs more than its 128 MiB before looking up the scratch
+    f = muon.LIB.muon_step_batched_noalloc
+    P = ctypes.c_void_p * 1
+
+    def call(w, g, m, shapes, h=None):
+        h = h or muon.default_hyper_c()
+        return f(P(w), P(g), P(m), _desc(shapes), len(shapes), ctypes.byref(h), None)
+
+    s = [(1, 64, 128, 0)]
+    sz = 64 * 128 * 4
+    assert call(0, BASE + 2 * sz, BASE + 4 * sz, s) == -1
+    assert call(BASE + 4, BASE + 2 * sz, BASE + 4 * sz, s) == -4
+    assert call(BASE, BASE + 2 * sz, BASE + 4 * sz, [(1, 64, 128, 5)]) == -2
+    big = [(40, 1024, 1024, 0)]  # 320 MiB of workspace
+    n = 40 * 1024 * 1024 * 4
+    assert call(BASE, BASE + 2 * n, BASE + 4 * n, big) == -5
+    assert f(P(), P(), P(), _desc([]), 0, ctypes.byref(muon.default_hyper_c()), None) == 0
+
+
 def test_workspace_status_argument_errors():
     st = muon.LIB.muon_workspace_status
     assert st(None, 1 << 20, None) == -1
