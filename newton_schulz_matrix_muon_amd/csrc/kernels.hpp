@@ -70,19 +70,30 @@ struct Seg {
   float* m;        // momentum of the first unit (step only)
   int32_t first;   // chunk-local index of the first unit
   int32_t count;   // number of units
+  int32_t trans;   // 1: the units are stored transposed relative to the
+                   // chunk's shape (wide units in a tall chunk, see below)
+  float lr_scale;  // lr * the units' update scale (their own fan_out, fan_in)
 };
 
+// A chunk's units share one shape rows x cols.  Units whose caller
+// matrices are that shape transposed (a wide unit, fan_out < fan_in, in a
+// tall chunk: the tiled products always take the tall form, so that a unit's
+// result does not depend on the other units of its batch) have `trans`
+// set: their gradient, momentum and weight are caller matrices of cols x
+// rows, the iterate holds N^T, and the update is written back transposed.
 struct ChunkArgs {
   int32_t n_seg;
   int32_t n_units;
-  int32_t rows, cols;          // unit shape (fan_out x fan_in)
+  int32_t rows, cols;          // unit shape in the chunk (fan_out x fan_in
+                               // unless transposed)
   int32_t rows_pad, cols_pad;  // padded iterate shape
   int64_t unit_elems;          // rows * cols
   int64_t x_stride;            // rows_pad * cols_pad
   float ma, mb;                // M <- ma*M + mb*G
   float la, lb;                // N  = la*M + lb*G (on the updated M)
   float decay;                 // 1 - lr * weight_decay
-  float lr_scale;              // lr * scale
+  float lr_scale;              // lr * scale of units in the chunk's shape
+                               // (each segment carries its own, Seg::lr_scale)
   int32_t pad0;
   Seg seg[kMaxSeg];
 };
@@ -125,10 +136,13 @@ struct SegView {
   const void* g;
   float* m;
   int32_t first;
+  int32_t trans;
+  float lr_scale;
 };
 
 __device__ __forceinline__ SegView find_seg(const ChunkArgs& ca, int u) {
-  SegView v{ca.seg[0].w, ca.seg[0].g, ca.seg[0].m, ca.seg[0].first};
+  SegView v{ca.seg[0].w, ca.seg[0].g, ca.seg[0].m, ca.seg[0].first, ca.seg[0].trans,
+            ca.seg[0].lr_scale};
 #pragma unroll
   for (int s = 1; s < kMaxSeg; ++s) {
     if (s < ca.n_seg && ca.seg[s].first <= u) {
@@ -136,6 +150,8 @@ __device__ __forceinline__ SegView find_seg(const ChunkArgs& ca, int u) {
       v.g = ca.seg[s].g;
       v.m = ca.seg[s].m;
       v.first = ca.seg[s].first;
+      v.trans = ca.seg[s].trans;
+      v.lr_scale = ca.seg[s].lr_scale;
     }
   }
   return v;
@@ -188,14 +204,18 @@ __device__ __forceinline__ float bf16_round(float f) {
 // nb itself (the tiled bf16 path, which folds 1/nu into its first
 // iteration), padding included: each block clears its rows' padded columns
 // and a unit's last block its padded rows.
+// Units u0, u0 + 1, ... (not transposed) take blocks_per_unit blocks each;
+// a unit's partial sums fill slots 0 .. blocks_per_unit - 1 of its pp
+// slots, and its last block zeroes the rest.
 template <int GK>
 __global__ __launch_bounds__(kThreads) void k_momentum(ChunkArgs ca, float* __restrict__ x32,
                                                         uint16_t* __restrict__ nb,
                                                         double* __restrict__ partials,
-                                                        int rows_per_block, int blocks_per_unit) {
+                                                        int rows_per_block, int blocks_per_unit,
+                                                        int u0, int pp) {
   __shared__ double sh[kThreads / 64];
-  const int u = blockIdx.x / blocks_per_unit;
-  const int bb = blockIdx.x - u * blocks_per_unit;
+  const int u = u0 + (int)(blockIdx.x / blocks_per_unit);
+  const int bb = (int)blockIdx.x - (u - u0) * blocks_per_unit;
   const SegView sg = find_seg(ca, u);
   const int64_t uoff = (int64_t)(u - sg.first) * ca.unit_elems;
   const int cols = ca.cols;
@@ -275,7 +295,116 @@ __global__ __launch_bounds__(kThreads) void k_momentum(ChunkArgs ca, float* __re
     for (int64_t e = (int64_t)ca.rows * ca.cols_pad + threadIdx.x; e < ca.x_stride; e += kThreads)
       nbu[e] = 0;
   const double t = block_sum(ss, sh);
-  if (threadIdx.x == 0) partials[(int64_t)u * blocks_per_unit + bb] = t;
+  if (threadIdx.x == 0) partials[(int64_t)u * pp + bb] = t;
+  if (bb == blocks_per_unit - 1)
+    for (int i = blocks_per_unit + threadIdx.x; i < pp; i += kThreads) partials[(int64_t)u * pp + i] = 0.0;
+}
+
+// The same for transposed units (a tall chunk's wide units): the caller's
+// matrices are cols x rows (chunk shape rows x cols), and N^T goes to the
+// iterate.  One 64 x 64 tile of the caller matrix per workgroup, over its
+// padded extent (cols_pad x rows_pad); the tile passes through LDS so that
+// both the caller-side accesses and the iterate's rows are contiguous, and
+// elements outside the matrix give the iterate's zero padding.  Partial
+// sums: one per tile, the unit's remaining slots zeroed by its last tile.
+template <int GK>
+__global__ __launch_bounds__(kThreads) void k_momentum_t(ChunkArgs ca, float* __restrict__ x32,
+                                                          uint16_t* __restrict__ nb,
+                                                          double* __restrict__ partials, int u0,
+                                                          int pp) {
+  __shared__ float tile[64][65];
+  __shared__ double sh[kThreads / 64];
+  const int tr = ca.cols_pad / 64, tc = ca.rows_pad / 64;  // tiles of the caller matrix
+  const int per_unit = tr * tc;
+  const int u = u0 + (int)(blockIdx.x / per_unit);
+  const int bb = (int)blockIdx.x - (u - u0) * per_unit;
+  const int ti = bb / tc, tj = bb - ti * tc;
+  const SegView sg = find_seg(ca, u);
+  const int64_t uoff = (int64_t)(u - sg.first) * ca.unit_elems;
+  const int crow = ca.cols, ccol = ca.rows;  // caller matrix: crow x ccol
+  const int i0 = ti * 64, j0 = tj * 64;
+  const float ma = ca.ma, mb = ca.mb, la = ca.la, lb = ca.lb;
+  const int t = threadIdx.x;
+  double ss = 0.0;
+  const bool vec = (ccol & 3) == 0;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int rr = t / 16 + 16 * k, cc = (t % 16) * 4;
+    const int i = i0 + rr, j = j0 + cc;
+    float n[4] = {0.f, 0.f, 0.f, 0.f};
+    if (i < crow && j < ccol) {
+      const int64_t e = uoff + (int64_t)i * ccol + j;
+      float g[4] = {0.f, 0.f, 0.f, 0.f};
+      float m[4] = {0.f, 0.f, 0.f, 0.f};
+      const int w = vec ? 4 : min(4, ccol - j);
+      if (vec) {
+        if (GK == 0) {
+          const uint2 raw = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(sg.g) + e);
+          g[0] = bf16_bits_to_f32(raw.x & 0xffffu);
+          g[1] = bf16_bits_to_f32(raw.x >> 16);
+          g[2] = bf16_bits_to_f32(raw.y & 0xffffu);
+          g[3] = bf16_bits_to_f32(raw.y >> 16);
+        } else {
+          const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(sg.g) + e);
+          g[0] = v.x;
+          g[1] = v.y;
+          g[2] = v.z;
+          g[3] = v.w;
+        }
+        if (GK != 2) {
+          const float4 v = *reinterpret_cast<const float4*>(sg.m + e);
+          m[0] = v.x;
+          m[1] = v.y;
+          m[2] = v.z;
+          m[3] = v.w;
+        }
+      } else {
+        for (int q = 0; q < w; ++q) {
+          g[q] = GK == 0 ? bf16_bits_to_f32(static_cast<const uint16_t*>(sg.g)[e + q])
+                         : static_cast<const float*>(sg.g)[e + q];
+          if (GK != 2) m[q] = sg.m[e + q];
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (GK == 2) {
+          n[q] = g[q];
+        } else {
+          m[q] = __builtin_fmaf(ma, m[q], mb * g[q]);
+          n[q] = __builtin_fmaf(la, m[q], lb * g[q]);
+        }
+        if (q >= w) n[q] = 0.f;
+      }
+      if (GK != 2) {
+        if (vec)
+          *reinterpret_cast<float4*>(sg.m + e) = make_float4(m[0], m[1], m[2], m[3]);
+        else
+          for (int q = 0; q < w; ++q) sg.m[e + q] = m[q];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) ss = __builtin_fma((double)n[q], (double)n[q], ss);
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) tile[rr][cc + q] = n[q];
+  }
+  __syncthreads();
+  // iterate row j0 + jj (caller column), columns i0 .. i0 + 63 (caller rows)
+  float* const xu = nb ? nullptr : x32 + (int64_t)u * ca.x_stride;
+  uint16_t* const nbu = nb ? nb + (int64_t)u * ca.x_stride : nullptr;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int jj = t / 16 + 16 * k, ii = (t % 16) * 4;
+    const int64_t o = (int64_t)(j0 + jj) * ca.cols_pad + i0 + ii;
+    const float a = tile[ii][jj], b = tile[ii + 1][jj], c = tile[ii + 2][jj], d = tile[ii + 3][jj];
+    if (nbu)
+      store_bf16x4(nbu, o, a, b, c, d);
+    else
+      *reinterpret_cast<float4*>(xu + o) = make_float4(a, b, c, d);
+  }
+  const double tot = block_sum(ss, sh);
+  if (threadIdx.x == 0) partials[(int64_t)u * pp + bb] = tot;
+  if (bb == per_unit - 1)
+    for (int i = per_unit + threadIdx.x; i < pp; i += kThreads) partials[(int64_t)u * pp + i] = 0.0;
 }
 
 // Folded normalisation: the bf16 iterate holds N itself and the first NS
@@ -587,9 +716,12 @@ __device__ __forceinline__ void zero_unit_tile(const ChunkArgs& ca, int final_mo
   const SegView sg = find_seg(ca, u);
   float* wout = sg.w + (int64_t)(u - sg.first) * ca.unit_elems;
   for (int idx = threadIdx.x; idx < TILE * TILE; idx += gemm_threads<TILE>()) {
-    const int mm = m0 + idx / TILE, nn = n0 + idx % TILE;
+    // a transposed unit's caller element (nn, mm) is the chunk's (mm, nn);
+    // walk the tile so that consecutive threads touch consecutive elements
+    const int a = idx / TILE, b = idx % TILE;
+    const int mm = m0 + (sg.trans ? b : a), nn = n0 + (sg.trans ? a : b);
     if (mm < ca.rows && nn < ca.cols) {
-      float* p = wout + (int64_t)mm * ca.cols + nn;
+      float* p = wout + (sg.trans ? (int64_t)nn * ca.rows + mm : (int64_t)mm * ca.cols + nn);
       *p = (final_mode == FINAL_STEP) ? (*p) * ca.decay : 0.0f;
     }
   }
@@ -865,9 +997,13 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
   __builtin_amdgcn_s_barrier();  // every wave is done with the stage buffers
   float* ep = reinterpret_cast<float*>(ring) + wid * (32 * LDW);
   float* wout = nullptr;
+  bool wtrans = false;  // the unit's weight is the chunk shape transposed
+  float lrs = 0.0f;     // lr * the unit's update scale
   if (PHASE == APPLY && g.final_mode != FINAL_NONE) {
     const SegView sg = find_seg(ca, u);
     wout = sg.w + (int64_t)(u - sg.first) * ca.unit_elems;
+    wtrans = sg.trans != 0;
+    lrs = sg.lr_scale;
   }
   const bool vec_w = (ca.cols & 3) == 0;
   // FOLD (first iteration of the folded path): X = N, so A = (N N^T)/nu^2
@@ -965,17 +1101,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
             store_bf16x4(g.out16, o, v0, v1, v2, v3);
           else
             *reinterpret_cast<float4*>(g.out32 + o) = make_float4(v0, v1, v2, v3);
-        } else if (m < ca.rows && ncol < ca.cols) {
+        } else if (!wtrans && m < ca.rows && ncol < ca.cols) {
           const int n = ncol;
           float* p = wout + (int64_t)m * ca.cols + n;
           const bool step = g.final_mode == FINAL_STEP;
           if (vec_w && n + 3 < ca.cols) {
             float4 wv = step ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
             if (step) {
-              wv.x = __builtin_fmaf(-ca.lr_scale, v0, wv.x * ca.decay);
-              wv.y = __builtin_fmaf(-ca.lr_scale, v1, wv.y * ca.decay);
-              wv.z = __builtin_fmaf(-ca.lr_scale, v2, wv.z * ca.decay);
-              wv.w = __builtin_fmaf(-ca.lr_scale, v3, wv.w * ca.decay);
+              wv.x = __builtin_fmaf(-lrs, v0, wv.x * ca.decay);
+              wv.y = __builtin_fmaf(-lrs, v1, wv.y * ca.decay);
+              wv.z = __builtin_fmaf(-lrs, v2, wv.z * ca.decay);
+              wv.w = __builtin_fmaf(-lrs, v3, wv.w * ca.decay);
             } else {
               wv = make_float4(v0, v1, v2, v3);
             }
@@ -985,7 +1121,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               if (n + e < ca.cols)
-                p[e] = step ? __builtin_fmaf(-ca.lr_scale, vv[e], p[e] * ca.decay) : vv[e];
+                p[e] = step ? __builtin_fmaf(-lrs, vv[e], p[e] * ca.decay) : vv[e];
             }
           }
         }
@@ -1013,6 +1149,41 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
       }
     }
     if constexpr (PHASE == APPLY) {
+      if (wtrans) {
+        // transposed unit: caller row n0 + wn*WN + nn holds the staged
+        // block's column nn, caller columns mrow0 .. +32 its rows (8 lanes
+        // per caller row, 4 consecutive elements each)
+        const int cm = (lane & 7) * 4;
+        const bool step = g.final_mode == FINAL_STEP;
+        const bool vec_t = (ca.rows & 3) == 0;
+#pragma unroll
+        for (int it = 0; it < WN / 8; ++it) {
+          const int nn = it * 8 + (lane >> 3);
+          const int crow = n0 + wn * WN + nn, ccol = mrow0 + cm;
+          if (crow < ca.cols && ccol < ca.rows) {
+            const float vv[4] = {ep[(cm + 0) * LDW + nn], ep[(cm + 1) * LDW + nn],
+                                 ep[(cm + 2) * LDW + nn], ep[(cm + 3) * LDW + nn]};
+            float* p = wout + (int64_t)crow * ca.rows + ccol;
+            if (vec_t && ccol + 3 < ca.rows) {
+              float4 wv = step ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
+              if (step) {
+                wv.x = __builtin_fmaf(-lrs, vv[0], wv.x * ca.decay);
+                wv.y = __builtin_fmaf(-lrs, vv[1], wv.y * ca.decay);
+                wv.z = __builtin_fmaf(-lrs, vv[2], wv.z * ca.decay);
+                wv.w = __builtin_fmaf(-lrs, vv[3], wv.w * ca.decay);
+              } else {
+                wv = make_float4(vv[0], vv[1], vv[2], vv[3]);
+              }
+              *reinterpret_cast<float4*>(p) = wv;
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (ccol + e < ca.rows)
+                  p[e] = step ? __builtin_fmaf(-lrs, vv[e], p[e] * ca.decay) : vv[e];
+            }
+          }
+        }
+      }
       if (g.final_mode == FINAL_NONE && g.outt != nullptr) {
         // X'^T rows n0 + wn*WN .. +WN, columns mrow0 .. +32: 8 lanes per
         // row, 4 consecutive columns (staged rows) per lane.

@@ -5,9 +5,15 @@
 //  1. Every bank expands into NS units: each matrix, or each split_rows
 //     block of it (RFC-0023 split_head, fan_out = head size).  Within a bank
 //     the units sit at a uniform stride of rows_u*cols elements.
-//  2. Units are grouped by their exact shape (rows_u, cols) and gradient
-//     dtype; every group is cut into chunks of at most batch_update_size
-//     units (0 = no limit) and at most kMaxSeg bank segments.
+//  2. Units are grouped by (s, l) = (smaller, larger side) and gradient
+//     dtype: a tall unit and the wide unit of the same two sides stack in
+//     one pass.  The tiled products always take the tall form (rows >= cols,
+//     the Gram X^T X), a unit's own choice that no batch changes, so a wide
+//     unit is stored transposed in the iterate and written back transposed.
+//     Wide units of at most 128 rows that the AUTO schedule may run on chip
+//     keep their own form and group apart.  Every group is cut into chunks
+//     of at most batch_update_size units (0 = no limit) and at most kMaxSeg
+//     bank segments, transposed units after the others.
 //  3. A chunk is one stacked pass: every kernel of the step runs once over
 //     all of its units (and the ten NS iterations run back to back), with the
 //     iterates laid out at a fixed stride in the caller's workspace.
@@ -43,23 +49,29 @@ struct Unitized {
   int64_t rows_u;      // unit rows
   int64_t cols;
   int32_t gdtype;
+  bool trans;          // stored transposed in its chunk (a wide unit, tiled)
 };
 
 struct SegRef {
   int desc;
   int64_t unit_begin;  // first unit inside the bank
   int64_t count;
+  bool trans;
 };
 
 struct Chunk {
-  int64_t rows_u, cols;
+  int64_t rows_u, cols;  // unit shape in the chunk (transposed units: caller cols x rows)
   int32_t gdtype;
   int tile;             // 128 or 256
   int64_t rows_pad, cols_pad, s_pad;
-  bool tall;            // rows_u > cols: the Gram is X^T X
+  bool tall;            // rows_u >= cols: the Gram is X^T X (every tiled chunk
+                        // but one whose wide units may run on chip)
   int64_t n_units;
+  int64_t n_plain;      // units 0 .. n_plain - 1 in their own form, the rest transposed
   std::vector<SegRef> segs;
-  int rows_per_block, blocks_per_unit;   // momentum kernel
+  int rows_per_block, blocks_per_unit;   // momentum kernel (units in their own form)
+  int tiles_t;                           // momentum kernel of transposed units: 64x64 tiles
+  int partials_per_unit;                 // max of the two
   int norm_blocks_per_unit;              // 64x64 tiles of the padded iterate
 };
 
@@ -88,6 +100,13 @@ constexpr int kMaxQueues = 16;   // persistent schedule: at most one queue per X
 bool small_possible(const Chunk& c, const muon_hyper* h) {
   return h->schedule == MUON_SCHEDULE_AUTO && h->ns_precision == MUON_NS_BF16 && !c.tall &&
          c.rows_u <= kSmall && c.rows_pad == kSmall;
+}
+
+// A unit that the on-chip kernel may run keeps its own (wide) form; every
+// other unit takes the tall form.
+bool unit_small_possible(int64_t rows_u, int64_t cols, const muon_hyper* h) {
+  return h->schedule == MUON_SCHEDULE_AUTO && h->ns_precision == MUON_NS_BF16 && rows_u < cols &&
+         rows_u <= kSmall;
 }
 
 // Words of persistent-schedule completion counts per unit: three per tile
@@ -124,7 +143,7 @@ Layout layout_of(const Chunk& c, const muon_hyper* h) {
   else
     L.a32 = take(U * ss * 4);
   L.bop = take(U * ss * (bf16 ? 2 : 4));
-  L.partials = take(U * (size_t)c.blocks_per_unit * 8);
+  L.partials = take(U * (size_t)c.partials_per_unit * 8);
   L.inv_nu = take(U * 4);
   L.flag = take(U * 4);
   // persistent schedule: finished tiles per small-side tile panel, for each
@@ -198,23 +217,30 @@ int plan(const muon_matrix_desc* mats, int64_t n, const muon_hyper* h, bool step
     const muon_matrix_desc& d = mats[i];
     Unitized u;
     u.desc = (int)i;
-    u.rows_u = d.split_rows > 0 ? d.split_rows : d.rows;
-    u.n_units = d.batch * (d.rows / u.rows_u);
-    u.cols = d.cols;
+    const int64_t ru = d.split_rows > 0 ? d.split_rows : d.rows;
+    u.n_units = d.batch * (d.rows / ru);
     u.gdtype = step ? d.grad_dtype : MUON_DTYPE_F32;
+    // the unit's shape in its chunk: its own, or transposed to the tall form
+    u.trans = ru < d.cols && !unit_small_possible(ru, d.cols, h);
+    u.rows_u = u.trans ? d.cols : ru;
+    u.cols = u.trans ? ru : d.cols;
     us.push_back(u);
   }
-  // Group in order of first appearance.
+  // Group in order of first appearance, the units in their own form first
+  // within each group (a chunk's transposed units follow the others).
   std::map<std::tuple<int64_t, int64_t, int32_t>, int> gid;
   std::vector<std::vector<int>> groups;
-  for (size_t i = 0; i < us.size(); ++i) {
-    auto key = std::make_tuple(us[i].rows_u, us[i].cols, us[i].gdtype);
-    auto it = gid.find(key);
-    if (it == gid.end()) {
-      gid.emplace(key, (int)groups.size());
-      groups.push_back({(int)i});
-    } else {
-      groups[it->second].push_back((int)i);
+  for (int pass = 0; pass < 2; ++pass) {
+    for (size_t i = 0; i < us.size(); ++i) {
+      if (us[i].trans != (pass == 1)) continue;
+      auto key = std::make_tuple(us[i].rows_u, us[i].cols, us[i].gdtype);
+      auto it = gid.find(key);
+      if (it == gid.end()) {
+        gid.emplace(key, (int)groups.size());
+        groups.push_back({(int)i});
+      } else {
+        groups[it->second].push_back((int)i);
+      }
     }
   }
   const int64_t cap = h->batch_update_size > 0 ? h->batch_update_size : INT64_MAX;
@@ -242,12 +268,16 @@ int plan(const muon_matrix_desc* mats, int64_t n, const muon_hyper* h, bool step
     proto.tile = pick_tile(u0.rows_u, u0.cols);
     proto.rows_pad = round_up(u0.rows_u, proto.tile);
     proto.cols_pad = round_up(u0.cols, proto.tile);
-    proto.tall = u0.rows_u > u0.cols;
+    proto.tall = u0.rows_u >= u0.cols;
     proto.s_pad = proto.tall ? proto.cols_pad : proto.rows_pad;
     proto.n_units = 0;
-    // Momentum kernel: about 16K elements per block.
+    proto.n_plain = 0;
+    // Momentum kernel: about 16K elements per block; transposed units one
+    // 64x64 tile of the padded caller matrix per block.
     proto.rows_per_block = (int)std::max<int64_t>(1, std::min<int64_t>(u0.rows_u, 16384 / u0.cols));
     proto.blocks_per_unit = (int)((u0.rows_u + proto.rows_per_block - 1) / proto.rows_per_block);
+    proto.tiles_t = (int)((proto.rows_pad / 64) * (proto.cols_pad / 64));
+    proto.partials_per_unit = proto.blocks_per_unit;
     proto.norm_blocks_per_unit = (int)((proto.rows_pad / 64) * (proto.cols_pad / 64));
     Chunk cur = proto;
     for (int ui : grp) {
@@ -262,8 +292,10 @@ int plan(const muon_matrix_desc* mats, int64_t n, const muon_hyper* h, bool step
           continue;
         }
         const int64_t take = std::min(room, u.n_units - begin);
-        cur.segs.push_back({u.desc, begin, take});
+        cur.segs.push_back({u.desc, begin, take, u.trans});
         cur.n_units += take;
+        if (!u.trans) cur.n_plain += take;
+        if (u.trans) cur.partials_per_unit = std::max(cur.partials_per_unit, cur.tiles_t);
         begin += take;
       }
     }
@@ -277,6 +309,7 @@ int plan(const muon_matrix_desc* mats, int64_t n, const muon_hyper* h, bool step
     const int64_t tiles = (c.s_pad / c.tile) * (std::max(c.rows_pad, c.cols_pad) / c.tile);
     if (c.n_units * tiles > INT32_MAX / 2) return MUON_ERR_SHAPE;
     if (c.n_units * (int64_t)c.blocks_per_unit > INT32_MAX / 2) return MUON_ERR_SHAPE;
+    if (c.n_units * (int64_t)c.tiles_t > INT32_MAX / 2) return MUON_ERR_SHAPE;
     if (c.n_units * (int64_t)c.norm_blocks_per_unit > INT32_MAX / 2) return MUON_ERR_SHAPE;
     // a K-major bf16 operand tile spans every row of the iterate
     if (c.rows_pad * c.cols_pad * 2 >= ((int64_t)1 << 31)) return MUON_ERR_SHAPE;
@@ -309,8 +342,10 @@ void momentum_coefficients(const muon_hyper* h, float* ma, float* mb, float* la,
   }
 }
 
-double unit_scale(const Chunk& c, const muon_hyper* h) {
-  const double fo = (double)c.rows_u, fi = (double)c.cols;
+// Update scale of a unit of fan_out x fan_in ([V4-notes]-style spectral, or
+// the Megatron PR's unit_rms_norm).
+double unit_scale(int64_t fan_out, int64_t fan_in, const muon_hyper* h) {
+  const double fo = (double)fan_out, fi = (double)fan_in;
   if (h->scale_mode == MUON_SCALE_SPECTRAL) return std::sqrt(std::max(fo, fi)) * (double)h->gamma;
   return std::sqrt(fo / fi);
 }
@@ -493,7 +528,8 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
   ca.x_stride = c.rows_pad * c.cols_pad;
   momentum_coefficients(h, &ca.ma, &ca.mb, &ca.la, &ca.lb);
   ca.decay = (float)(1.0 - (double)h->lr * (double)h->weight_decay);
-  ca.lr_scale = (float)((double)h->lr * unit_scale(c, h));
+  ca.lr_scale = (float)((double)h->lr * unit_scale(c.rows_u, c.cols, h));
+  const float lr_scale_t = (float)((double)h->lr * unit_scale(c.cols, c.rows_u, h));
   int32_t first = 0;
   for (size_t i = 0; i < c.segs.size(); ++i) {
     const SegRef& r = c.segs[i];
@@ -504,6 +540,9 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
     ca.seg[i].m = step ? moms[r.desc] + off : nullptr;
     ca.seg[i].first = first;
     ca.seg[i].count = (int32_t)r.count;
+    ca.seg[i].trans = r.trans ? 1 : 0;
+    // a transposed unit's fan_out is the chunk's cols
+    ca.seg[i].lr_scale = r.trans ? lr_scale_t : ca.lr_scale;
     first += (int32_t)r.count;
   }
 
@@ -539,33 +578,47 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
   const bool fold = bf16 && !small;
   uint16_t* const nb = fold ? xb[0] : nullptr;
   // 1. momentum + Nesterov + partial sums of squares.
-  tr.before(MUON_KERNEL_MOMENTUM);
-  {
-    const dim3 grid(U * c.blocks_per_unit);
-    if (!step)
-      hipLaunchKernelGGL(k_momentum<2>, grid, dim3(kThreads), 0, s, ca, x32[0], nb, partials,
-                         c.rows_per_block, c.blocks_per_unit);
-    else if (c.gdtype == MUON_DTYPE_BF16)
-      hipLaunchKernelGGL(k_momentum<0>, grid, dim3(kThreads), 0, s, ca, x32[0], nb, partials,
-                         c.rows_per_block, c.blocks_per_unit);
-    else
-      hipLaunchKernelGGL(k_momentum<1>, grid, dim3(kThreads), 0, s, ca, x32[0], nb, partials,
-                         c.rows_per_block, c.blocks_per_unit);
-  }
-  {
-    // algorithmic bytes: G (or the NS input) read, M read and written
-    // (step), N written into the bf16 iterate (2 B) or in fp32 (4 B)
-    const int64_t elems = c.n_units * c.rows_u * c.cols;
+  // Units in their own form (0 .. n_plain - 1), then transposed ones; each
+  // launch's algorithmic bytes: G (or the NS input) read, M read and
+  // written (step), N written into the bf16 iterate (2 B) or in fp32 (4 B).
+  const int64_t pp = c.partials_per_unit;
+  const int gk = !step ? 2 : (c.gdtype == MUON_DTYPE_BF16 ? 0 : 1);
+  auto mom_info = [&](int64_t units) {
+    const int64_t elems = units * c.rows_u * c.cols;
     const int64_t gsz = (step && c.gdtype == MUON_DTYPE_BF16) ? 2 : 4;
     const int64_t per = gsz + (step ? 8 : 0) + (nb ? 2 : 4);
-    tr.after(MUON_KERNEL_MOMENTUM, elems, elems * per, c.n_units, 0);
+    tr.after(MUON_KERNEL_MOMENTUM, elems, elems * per, units, 0);
+  };
+  if (c.n_plain > 0) {
+    tr.before(MUON_KERNEL_MOMENTUM);
+    const dim3 grid((unsigned)(c.n_plain * c.blocks_per_unit));
+    const int bpu = c.blocks_per_unit, rpb = c.rows_per_block;
+    if (gk == 2)
+      hipLaunchKernelGGL(k_momentum<2>, grid, dim3(kThreads), 0, s, ca, x32[0], nb, partials, rpb, bpu, 0, (int)pp);
+    else if (gk == 0)
+      hipLaunchKernelGGL(k_momentum<0>, grid, dim3(kThreads), 0, s, ca, x32[0], nb, partials, rpb, bpu, 0, (int)pp);
+    else
+      hipLaunchKernelGGL(k_momentum<1>, grid, dim3(kThreads), 0, s, ca, x32[0], nb, partials, rpb, bpu, 0, (int)pp);
+    mom_info(c.n_plain);
+  }
+  if (c.n_units > c.n_plain) {
+    tr.before(MUON_KERNEL_MOMENTUM);
+    const dim3 grid((unsigned)((c.n_units - c.n_plain) * c.tiles_t));
+    const int u0 = (int)c.n_plain;
+    if (gk == 2)
+      hipLaunchKernelGGL(k_momentum_t<2>, grid, dim3(kThreads), 0, s, ca, x32[0], nb, partials, u0, (int)pp);
+    else if (gk == 0)
+      hipLaunchKernelGGL(k_momentum_t<0>, grid, dim3(kThreads), 0, s, ca, x32[0], nb, partials, u0, (int)pp);
+    else
+      hipLaunchKernelGGL(k_momentum_t<1>, grid, dim3(kThreads), 0, s, ca, x32[0], nb, partials, u0, (int)pp);
+    mom_info(c.n_units - c.n_plain);
   }
   // 2. norms (and, off the folded path, X0 = N / ||N||_F).
   tr.before(MUON_KERNEL_NORMALIZE);
   uint32_t* done = reinterpret_cast<uint32_t*>(ws + L.done);
   uint32_t* queue = reinterpret_cast<uint32_t*>(ws + L.queue);
   uint32_t* err = reinterpret_cast<uint32_t*>(ws);
-  hipLaunchKernelGGL(k_norm_finish, dim3(U), dim3(kThreads), 0, s, partials, c.blocks_per_unit,
+  hipLaunchKernelGGL(k_norm_finish, dim3(U), dim3(kThreads), 0, s, partials, (int)pp,
                      inv_nu, flag, done, (int)done_words(c), queue, kMaxQueues + 1,
                      first_chunk ? err : nullptr, nb,
                      (int64_t)(c.rows_pad * c.cols_pad));

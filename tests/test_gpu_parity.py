@@ -296,3 +296,67 @@ def test_step_stacked_1024_workload_sampled(gpu_lib, prec):
             assert rel(f64(m[i]), m_ref[i]) <= TOL_M
             e = check_weight(f64(w[i]), w_ref[i], w0[i], t, h, TOL_NS[prec], f"step {t} mat {i}")
         say(f"   step {t}: last rel update err {e:.3e}")
+
+
+# ---------------------------------------- tall and wide units in one pass ---
+# A tall unit and a wide unit of the same two sides stack in one pass, in the
+# tall form: the wide unit's look-ahead is transposed into the iterate and its
+# update written back transposed.  unit_rms_norm gives them different scales
+# (sqrt(fan_out / fan_in)).  Odd caller widths take the scalar paths of the
+# transposing kernels; split heads of 128 x 600 are transposed head by head.
+MIXED = [
+    [(2, 600, 260, 0), (3, 260, 600, 0)],            # 256 tiles, both forms
+    [(1, 1001, 300, 0), (2, 300, 1001, 0)],          # odd caller widths
+    [(1, 512, 600, 128), (2, 600, 128, 0)],          # transposed heads with tall units
+]
+
+
+@pytest.mark.parametrize("sched", ["auto", "persistent", "launches"])
+@pytest.mark.parametrize("prec", ["fp32", "bf16"])
+@pytest.mark.parametrize("case", range(len(MIXED)))
+def test_step_tall_and_wide_units_in_one_pass(gpu_lib, case, prec, sched):
+    banks = MIXED[case]
+    say(f"[mixed] {banks} prec={prec} sched={sched}")
+    h = gpu_lib.Hyper(ns_precision=prec, schedule=sched, scale="unit_rms_norm")
+    hw = oracle_hyper(h)
+    g = torch.Generator(device="cpu").manual_seed(77 + case)
+    w0 = [torch.randn((b, r, c), generator=g) * 0.02 for b, r, c, _ in banks]
+    grads = [[(torch.randn((b, r, c), generator=g) * 1e-3).to(torch.bfloat16)
+              for b, r, c, _ in banks] for _ in range(2)]
+    splits = [s for *_, s in banks]
+    params = [w.to(DEV) for w in w0]
+    moms = [torch.zeros_like(p) for p in params]
+    refs = [[(f64(w[i]), np.zeros(w[i].shape)) for i in range(w.shape[0])] for w in w0]
+    for t in (1, 2):
+        gpu_lib.step(params, [gr.to(DEV) for gr in grads[t - 1]], moms, hyper=h, split_rows=splits)
+        torch.cuda.synchronize()
+        for k, (b, r, c, sp) in enumerate(banks):
+            for i in range(b):
+                wr, mr = refs[k][i]
+                wr, mr, _ = oracle.muon_step(wr, f64(grads[t - 1][k][i]), mr, hw, sp, t)
+                refs[k][i] = (wr, mr)
+                assert rel(f64(moms[k][i]), mr) <= TOL_M
+                blocks = [slice(0, r)] if not sp else [slice(j, j + sp) for j in range(0, r, sp)]
+                for blk in blocks:
+                    check_weight(f64(params[k][i])[blk], wr[blk], f64(w0[k][i])[blk], t, h,
+                                 TOL_NS[prec], f"bank {k} unit {i} rows {blk}")
+
+
+@pytest.mark.parametrize("sched", ["persistent", "launches"])
+def test_wide_unit_alone_or_stacked_with_tall_units_bitwise(gpu_lib, sched):
+    # a unit's form depends on its own shape only: a wide unit gives the same
+    # bits alone and stacked with tall units of the same sides
+    say(f"[mixed bitwise] sched={sched}")
+    g = torch.Generator(device="cpu").manual_seed(5)
+    wide = (torch.randn((2, 300, 700), generator=g) * 0.02).to(DEV)
+    tall = (torch.randn((3, 700, 300), generator=g) * 0.02).to(DEV)
+    gw = (torch.randn((2, 300, 700), generator=g) * 1e-3).to(torch.bfloat16).to(DEV)
+    gt = (torch.randn((3, 700, 300), generator=g) * 1e-3).to(torch.bfloat16).to(DEV)
+    h = gpu_lib.Hyper(schedule=sched)
+    a_w, a_m = wide.clone(), torch.zeros_like(wide)
+    gpu_lib.step([a_w], [gw], [a_m], hyper=h)
+    b_w, b_m = wide.clone(), torch.zeros_like(wide)
+    t_w, t_m = tall.clone(), torch.zeros_like(tall)
+    gpu_lib.step([t_w, b_w], [gt, gw], [t_m, b_m], hyper=h)
+    torch.cuda.synchronize()
+    assert torch.equal(a_w, b_w) and torch.equal(a_m, b_m)
