@@ -690,6 +690,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
+// Lanes of one wave exchanging data through LDS: the hardware runs a wave's
+// LDS accesses in order, but the compiler reasons per lane and may reorder a
+// lane's accesses to different addresses, or reuse a value the lane loaded
+// before another lane overwrote it (a version of the epilogue whose staging
+// writes were made by half of the lanes had its reads of the other lanes'
+// rows replaced by the values loaded for the previous rows).  A compiler
+// fence between the phases of such an exchange keeps them in program order.
+__device__ __forceinline__ void wave_lds_fence() { __atomic_signal_fence(__ATOMIC_SEQ_CST); }
+
 // Workgroup barrier for LDS broadcasts: waits for this wave's LDS (and
 // scalar) accesses only, not for its global stores and atomics in flight,
 // which a __syncthreads() fence would drain first.  The signal fences keep
@@ -1054,7 +1063,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
 #pragma unroll
       for (int j = 0; j < FB; ++j) acc[i][j] *= acc_scale;
     }
-    // stage the block
+    // stage the block (after the previous block's reads)
+    wave_lds_fence();
 #pragma unroll
     for (int j = 0; j < FB; ++j)
 #pragma unroll
@@ -1063,6 +1073,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
         *reinterpret_cast<float4*>(ep + (lane & 31) * LDW + j * 32 + 8 * q + 4 * half) =
             make_float4(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
       }
+    wave_lds_fence();
     // row-wise pass (a wave's LDS accesses complete in order)
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
@@ -1130,6 +1141,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
     if constexpr (kAuxB) {
       if (i + 2 < FA) load_aux(i + 2);  // the row pass has taken block i's values
     }
+    wave_lds_fence();  // the column-wise passes read what other lanes wrote
     if constexpr (PHASE == GRAM || PHASE == POLY) {
       if (g.sym && tm != tn) {
         // mirror tile: rows n0 + wn*WN .. +WN, columns mrow0 .. +32, read
