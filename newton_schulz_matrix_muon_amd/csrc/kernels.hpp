@@ -422,6 +422,19 @@ constexpr double kFoldMin = 0x1p-80, kFoldMax = 0x1p80;  // bounds on nu^2
 // (a fresh workspace holds arbitrary bytes).
 constexpr uint64_t kStatusMagic = 0x4e4f554d53544154ull;
 
+// Start of a call (one thread of its first launch): the previous call's stop
+// flag joins the sticky word and is cleared.
+__device__ __forceinline__ void status_fold(uint32_t* err) {
+  uint64_t* const magic = reinterpret_cast<uint64_t*>(err + 2);
+  if (*magic != kStatusMagic) {
+    err[1] = 0u;
+    *magic = kStatusMagic;
+  } else {
+    err[1] |= err[0];
+  }
+  err[0] = 0u;
+}
+
 // One workgroup per unit: fixed-order sum of the partials (first wave).
 // It also clears the persistent schedule's counts of the unit and claim
 // counter (when given), and, on the first pass of a call (err given), moves
@@ -460,16 +473,7 @@ __global__ __launch_bounds__(kThreads) void k_norm_finish(const double* __restri
     inv_nu[u] = rescale ? 1.0f : inv;
     if (u == 0 && sched_queue)
       for (int i = 0; i < n_queue_words; ++i) sched_queue[i] = 0u;
-    if (u == 0 && err) {
-      uint64_t* const magic = reinterpret_cast<uint64_t*>(err + 2);
-      if (*magic != kStatusMagic) {
-        err[1] = 0u;
-        *magic = kStatusMagic;
-      } else {
-        err[1] |= err[0];
-      }
-      err[0] = 0u;
-    }
+    if (u == 0 && err) status_fold(err);
   }
   if (sched_done)
     for (int i = threadIdx.x; i < done_per_unit; i += kThreads)
@@ -1351,6 +1355,24 @@ __device__ __forceinline__ void sm_put_cols(uint16_t* L, const float (&v)[2][2][
       }
 }
 
+__device__ __forceinline__ void sm_zero(f32x16 (&a)[2][2]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) a[i][j][r] = 0.0f;
+}
+
+__device__ __forceinline__ void sm_vals(const f32x16 (&a)[2][2], float (&v)[2][2][16]) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) v[i][j][r] = a[i][j][r];
+}
+
 __global__ __launch_bounds__(kThreads) void k_ns_small(NsSmallArgs p, ChunkArgs ca) {
   __shared__ __attribute__((aligned(16))) uint16_t LA[kSmall * kSmall];  // A, then B
   __shared__ __attribute__((aligned(16))) uint16_t LX[kSmall * kSmall];  // X_j^T
@@ -1413,26 +1435,9 @@ __global__ __launch_bounds__(kThreads) void k_ns_small(NsSmallArgs p, ChunkArgs 
           xv[i][jj][4 * q + 3] = bf16_bits_to_f32(h.y >> 16);
         }
   };
-  auto zero = [](f32x16 (&a)[2][2]) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) a[i][j][r] = 0.0f;
-  };
-  auto as_vals = [](const f32x16 (&a)[2][2], float (&v)[2][2][16]) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) v[i][j][r] = a[i][j][r];
-  };
-
   // Gram of iteration 0.
   f32x16 accA[2][2], accC[2][2];
-  zero(accA);
+  sm_zero(accA);
   auto gram_block = [&](Blk& xv, Blk& xnext, int j) {
     if (j + 1 < nb) load_x0(xnext, j + 1);
     __syncthreads();  // LR is free
@@ -1461,11 +1466,11 @@ __global__ __launch_bounds__(kThreads) void k_ns_small(NsSmallArgs p, ChunkArgs 
 
     // B = b*A + c*A*A (A symmetric), into LA as the apply's operand.
     float av[2][2][16];
-    as_vals(accA, av);
+    sm_vals(accA, av);
     __syncthreads();  // every wave is done with LA and LR
     sm_put_rows(LA, av, wm, wn, lane);
     __syncthreads();
-    zero(accC);
+    sm_zero(accC);
     sm_mma(LA, LA, accC, wm, wn, lane);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -1477,7 +1482,7 @@ __global__ __launch_bounds__(kThreads) void k_ns_small(NsSmallArgs p, ChunkArgs 
     sm_put_rows(LA, av, wm, wn, lane);
 
     // Apply pass, with the next Gram accumulated on the way.
-    zero(accA);
+    sm_zero(accA);
     auto apply_block = [&](Blk& xv, Blk& xnext, int j) {
       if (j + 1 < nb) {
         if (it == 0)
@@ -1488,7 +1493,7 @@ __global__ __launch_bounds__(kThreads) void k_ns_small(NsSmallArgs p, ChunkArgs 
       __syncthreads();  // LA complete; LX and LR free
       sm_put_cols(LX, xv, wm, wn, lane);
       __syncthreads();
-      zero(accC);
+      sm_zero(accC);
       sm_mma(LA, LX, accC, wm, wn, lane);  // (B X_j)[m][n] = sum_k B[m][k] X_j[k][n]
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -1536,6 +1541,302 @@ __global__ __launch_bounds__(kThreads) void k_ns_small(NsSmallArgs p, ChunkArgs 
     for (int j = 0; j < nb; j += 2) {  // unrolled by two: the register sets alternate
       apply_block(xbuf[0], xbuf[1], j);
       if (j + 1 < nb) apply_block(xbuf[1], xbuf[0], j + 1);
+    }
+  }
+}
+
+// ------------------------------------------------ one-launch small step ----
+// The whole step of units whose wide form fits one 128 x 128 block (at most
+// 128 rows and 128 columns, rows <= columns), one workgroup per unit and one
+// launch per chunk: momentum and the look-ahead go straight into registers,
+// the Frobenius norm is a block reduction, and every product of every
+// iteration runs on chip over the unit's own extent rounded up to 32 (BS
+// row blocks, BL column blocks of 32) rather than over 128 x 128.  Products
+// are split into 32 x 32 output blocks, block b of a product going to wave
+// b % 4; a wave keeps the iterate's blocks it updates, and the Gram blocks
+// it later combines with A*A, in registers.  LDS holds bf16 operands: X
+// (two buffers: one read by this iteration's products, the other receiving
+// X'), A and B, so an iteration needs three barriers.  The roundings are
+// those of the other bf16 paths: bf16 operands, fp32 accumulation, the
+// iterate rounded to bf16 between iterations.  gk: 0 bf16 gradient, 1 fp32
+// gradient, 2 NS only.  err: the call's status words when this is its
+// first launch, else null.
+
+// Element (row, k) of a bf16 operand with 128-element rows in LDS: 16 chunks
+// of 8 per row, the chunk index XOR-ed with a permutation of the row's low
+// four bits.  16-byte reads of 16 consecutive rows at one k, and transposing
+// reads of 4 consecutive rows (from a multiple of 4) x 16 columns, each touch
+// distinct banks.
+__device__ __forceinline__ int sb_at(int row, int k) {
+  const int f = ((row & 7) << 1) | ((row >> 3) & 1);
+  return row * kSmall + ((((k >> 3) ^ f) << 3) | (k & 7));
+}
+
+// MFMA fragment of rows r0 .. r0 + 31 of a row-major operand (K along the
+// row): lane (x, half) gets k = 16kk + 8half .. +7 of row r0 + x.
+__device__ __forceinline__ u32x4 sb_rows(const uint16_t* L, int r0, int kk, int lane) {
+  const int r = r0 + (lane & 31);
+  return *reinterpret_cast<const u32x4*>(L + sb_at(r, 16 * kk + 8 * (lane >> 5)));
+}
+
+// MFMA fragment of columns c0 .. c0 + 31 of a row-major operand whose K runs
+// down the rows: lane (x, half) gets rows 16kk + 8half .. +7 of column
+// c0 + x, by two transposing reads (ds_read_b64_tr_b16).  In each group of
+// 16 lanes, lane 4r + q points at 4 elements of row k0 + r, columns
+// 4q .. 4q + 3 of the group's 16, and lane i receives column i of the four
+// rows.
+__device__ __forceinline__ u32x4 sb_cols(const uint16_t* L, int c0, int kk, int lane) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s* lds_v4s;
+  const int g = lane >> 4, gi = lane & 15;
+  const int k = 16 * kk + 8 * (g >> 1) + (gi >> 2);
+  const int col = c0 + 16 * (g & 1) + 4 * (gi & 3);
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(lds_vptr)(L + sb_at(k, col)));
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(lds_vptr)(L + sb_at(k + 4, col)));
+  const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+  return u32x4{l2.x, l2.y, h2.x, h2.y};
+}
+
+// Accumulator-layout block (lane (x, half) holds row r0 + x, columns
+// c0 + 8q + 4half + e for value 4q + e) into LDS as bf16, row-major.
+__device__ __forceinline__ void sb_put(uint16_t* L, const float (&v)[16], int r0, int c0, int lane) {
+  const int row = r0 + (lane & 31), half = lane >> 5;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint2 pk;
+    pk.x = (uint32_t)to_bf16_bits(v[4 * q]) | ((uint32_t)to_bf16_bits(v[4 * q + 1]) << 16);
+    pk.y = (uint32_t)to_bf16_bits(v[4 * q + 2]) | ((uint32_t)to_bf16_bits(v[4 * q + 3]) << 16);
+    *reinterpret_cast<uint2*>(L + sb_at(row, c0 + 8 * q + 4 * half)) = pk;
+  }
+}
+
+template <int BS, int BL>
+__global__ __launch_bounds__(kThreads) void k_ns_small_step(NsSmallArgs p, ChunkArgs ca, int gk,
+                                                             uint32_t* __restrict__ err) {
+  constexpr int R = 32 * BS;                // rows of every LDS operand
+  constexpr int NA = BS * BS, NX = BS * BL;  // 32 x 32 blocks of A (and B), of X
+  constexpr int TA = (NA + 3) / 4, TX = (NX + 3) / 4;  // blocks per wave, at most
+  __shared__ __attribute__((aligned(16))) uint16_t LX[2][R * kSmall];
+  __shared__ __attribute__((aligned(16))) uint16_t LA[R * kSmall];
+  __shared__ __attribute__((aligned(16))) uint16_t LB[R * kSmall];
+  __shared__ double wsum[kThreads / 64];
+  const int u = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int m = lane & 31, half = lane >> 5;
+  if (err && u == 0 && threadIdx.x == 0) status_fold(err);
+
+  const SegView sg = find_seg(ca, u);
+  const int64_t uoff = (int64_t)(u - sg.first) * ca.unit_elems;
+  const int rows = ca.rows, cols = ca.cols;
+  const bool vec = (cols & 3) == 0;
+
+  // 1. M = ma*M + mb*G and N = la*M + lb*G for this wave's blocks of X
+  // (block b: rows 32(b / BL) .., columns 32(b % BL) ..), zero outside the
+  // matrix; gk == 2 takes the input itself as N.
+  float xv[TX][16];
+  double ss = 0.0;
+#pragma unroll
+  for (int t = 0; t < TX; ++t) {
+    const int b = w + 4 * t;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float n[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      const int row = 32 * (b / BL) + m;
+      const int c0 = 32 * (b % BL) + 8 * q + 4 * half;
+      if (b < NX && row < rows && c0 < cols) {
+        const int64_t base = uoff + (int64_t)row * cols + c0;
+        const int ne = vec ? 4 : min(4, cols - c0);
+        float g[4] = {0.0f, 0.0f, 0.0f, 0.0f}, mo[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (vec) {
+          if (gk == 0) {
+            const uint2 raw = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(sg.g) + base);
+            g[0] = bf16_bits_to_f32(raw.x & 0xffffu);
+            g[1] = bf16_bits_to_f32(raw.x >> 16);
+            g[2] = bf16_bits_to_f32(raw.y & 0xffffu);
+            g[3] = bf16_bits_to_f32(raw.y >> 16);
+          } else {
+            const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(sg.g) + base);
+            g[0] = v.x; g[1] = v.y; g[2] = v.z; g[3] = v.w;
+          }
+          if (gk != 2) {
+            const float4 v = *reinterpret_cast<const float4*>(sg.m + base);
+            mo[0] = v.x; mo[1] = v.y; mo[2] = v.z; mo[3] = v.w;
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (e >= ne) continue;
+            g[e] = gk == 0 ? bf16_bits_to_f32(static_cast<const uint16_t*>(sg.g)[base + e])
+                           : static_cast<const float*>(sg.g)[base + e];
+            if (gk != 2) mo[e] = sg.m[base + e];
+          }
+        }
+        if (gk == 2) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) n[e] = g[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            mo[e] = __builtin_fmaf(ca.ma, mo[e], ca.mb * g[e]);
+            n[e] = __builtin_fmaf(ca.la, mo[e], ca.lb * g[e]);
+          }
+          if (vec) {
+            *reinterpret_cast<float4*>(sg.m + base) = make_float4(mo[0], mo[1], mo[2], mo[3]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (e < ne) sg.m[base + e] = mo[e];
+          }
+        }
+        // lanes past the last column read nothing: g = 0, M = 0, N = 0
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        xv[t][4 * q + e] = n[e];
+        ss = __builtin_fma((double)n[e], (double)n[e], ss);
+      }
+    }
+  }
+
+  // 2. ||N||_F^2: fixed shuffle tree per wave, then the waves in order (the
+  // same value in every thread).
+  ss = wave_sum(ss);
+  if (lane == 0) wsum[w] = ss;
+  __syncthreads();
+  double s2 = 0.0;
+#pragma unroll
+  for (int i = 0; i < kThreads / 64; ++i) s2 += wsum[i];
+
+  float* const wout = sg.w + uoff;
+  if (s2 == 0.0) {
+    // Zero look-ahead: O' = 0, so the weight only decays / the output is zero.
+    for (int64_t e = threadIdx.x; e < ca.unit_elems; e += kThreads)
+      wout[e] = (p.final_mode == FINAL_STEP) ? wout[e] * ca.decay : 0.0f;
+    return;
+  }
+  // A NaN/Inf sum keeps the unit active so that it propagates.
+  const float inv = (float)(1.0 / sqrt(s2));
+#pragma unroll
+  for (int t = 0; t < TX; ++t) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) xv[t][r] = bf16_round(xv[t][r] * inv);
+    const int b = w + 4 * t;
+    if (b < NX) sb_put(LX[0], xv[t], 32 * (b / BL), 32 * (b % BL), lane);
+  }
+  __syncthreads();
+
+  // 3. The iterations.
+  float av[TA][16];
+  f32x16 acc[TA > TX ? TA : TX];
+  for (int it = 0; it < p.n_iter; ++it) {
+    float ca_ = p.sa[0], cb = p.sb[0], cc = p.sc[0];
+#pragma unroll
+    for (int st = 1; st < 4; ++st)
+      if (st < p.n_stages && it >= p.stage_begin[st]) {
+        ca_ = p.sa[st];
+        cb = p.sb[st];
+        cc = p.sc[st];
+      }
+    const uint16_t* const X = LX[it & 1];
+    // A = X X^T over K = 32 BL; block b: rows 32(b / BS), columns 32(b % BS).
+#pragma unroll
+    for (int t = 0; t < TA; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < 2 * BL; ++kk)
+#pragma unroll
+      for (int t = 0; t < TA; ++t) {
+        const int b = w + 4 * t;
+        if (b < NA)
+          mfma_one<__bf16>(sb_rows(X, 32 * (b / BS), kk, lane), sb_rows(X, 32 * (b % BS), kk, lane), acc[t]);
+      }
+#pragma unroll
+    for (int t = 0; t < TA; ++t) {
+      const int b = w + 4 * t;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) av[t][r] = acc[t][r];
+      if (b < NA) sb_put(LA, av[t], 32 * (b / BS), 32 * (b % BS), lane);
+    }
+    __syncthreads();
+    // B = b*A + c*A*A (A symmetric: both operands read rows of A).
+#pragma unroll
+    for (int t = 0; t < TA; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < 2 * BS; ++kk)
+#pragma unroll
+      for (int t = 0; t < TA; ++t) {
+        const int b = w + 4 * t;
+        if (b < NA)
+          mfma_one<__bf16>(sb_rows(LA, 32 * (b / BS), kk, lane), sb_rows(LA, 32 * (b % BS), kk, lane), acc[t]);
+      }
+#pragma unroll
+    for (int t = 0; t < TA; ++t) {
+      const int b = w + 4 * t;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) av[t][r] = cb * av[t][r] + cc * acc[t][r];
+      if (b < NA) sb_put(LB, av[t], 32 * (b / BS), 32 * (b % BS), lane);
+    }
+    __syncthreads();
+    // X' = a*X + B*X over K = 32 BS.
+#pragma unroll
+    for (int t = 0; t < TX; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
+#pragma unroll
+    for (int kk = 0; kk < 2 * BS; ++kk)
+#pragma unroll
+      for (int t = 0; t < TX; ++t) {
+        const int b = w + 4 * t;
+        if (b < NX)
+          mfma_one<__bf16>(sb_rows(LB, 32 * (b / BL), kk, lane), sb_cols(X, 32 * (b % BL), kk, lane), acc[t]);
+      }
+#pragma unroll
+    for (int t = 0; t < TX; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xv[t][r] = __builtin_fmaf(ca_, xv[t][r], acc[t][r]);
+    if (it == p.n_iter - 1) break;
+#pragma unroll
+    for (int t = 0; t < TX; ++t) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xv[t][r] = bf16_round(xv[t][r]);
+      const int b = w + 4 * t;
+      if (b < NX) sb_put(LX[(it & 1) ^ 1], xv[t], 32 * (b / BL), 32 * (b % BL), lane);
+    }
+    __syncthreads();
+  }
+
+  // 4. The decoupled update (or the NS output) of this wave's blocks.
+  const float lrs = sg.lr_scale;
+#pragma unroll
+  for (int t = 0; t < TX; ++t) {
+    const int b = w + 4 * t;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = 32 * (b / BL) + m;
+      const int c0 = 32 * (b % BL) + 8 * q + 4 * half;
+      if (b >= NX || row >= rows || c0 >= cols) continue;
+      float* const wp = wout + (int64_t)row * cols + c0;
+      const float o[4] = {xv[t][4 * q], xv[t][4 * q + 1], xv[t][4 * q + 2], xv[t][4 * q + 3]};
+      if (vec) {
+        float4 wv = make_float4(o[0], o[1], o[2], o[3]);
+        if (p.final_mode == FINAL_STEP) {
+          const float4 w0 = *reinterpret_cast<const float4*>(wp);
+          wv.x = __builtin_fmaf(-lrs, o[0], w0.x * ca.decay);
+          wv.y = __builtin_fmaf(-lrs, o[1], w0.y * ca.decay);
+          wv.z = __builtin_fmaf(-lrs, o[2], w0.z * ca.decay);
+          wv.w = __builtin_fmaf(-lrs, o[3], w0.w * ca.decay);
+        }
+        *reinterpret_cast<float4*>(wp) = wv;
+      } else {
+        const int ne = min(4, cols - c0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (e < ne) wp[e] = (p.final_mode == FINAL_STEP) ? __builtin_fmaf(-lrs, o[e], wp[e] * ca.decay) : o[e];
+      }
     }
   }
 }

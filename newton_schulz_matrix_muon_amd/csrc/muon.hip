@@ -572,6 +572,54 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
     if (dst != MUON_OK) return dst;
     small = 2 * U >= di.cus;
   }
+  const int gk = !step ? 2 : (c.gdtype == MUON_DTYPE_BF16 ? 0 : 1);
+  auto small_args = [&]() {
+    NsSmallArgs p;
+    std::memset(&p, 0, sizeof(p));
+    p.n32 = x32[0];
+    p.xb[0] = xb[0];
+    p.xb[1] = xb[1];
+    p.x_stride = c.rows_pad * c.cols_pad;
+    p.ldx = (int32_t)c.cols_pad;
+    p.n_stages = h->n_stages;
+    int begin = 0;
+    for (int i = 0; i < h->n_stages; ++i) {
+      p.stage_begin[i] = begin;
+      begin += h->stages[i].steps;
+      p.sa[i] = h->stages[i].a;
+      p.sb[i] = h->stages[i].b;
+      p.sc[i] = h->stages[i].c;
+    }
+    p.n_iter = begin;
+    p.final_mode = step ? FINAL_STEP : FINAL_NSOUT;
+    p.inv_nu = reinterpret_cast<float*>(ws + L.inv_nu);
+    p.flag = reinterpret_cast<int32_t*>(ws + L.flag);
+    return p;
+  };
+  // Units of one 128 x 128 block: the whole step in one launch, over the
+  // unit's extent in 32-row and 32-column blocks.
+  if (small && c.cols_pad == kSmall) {
+    const NsSmallArgs p = small_args();
+    uint32_t* err = first_chunk ? reinterpret_cast<uint32_t*>(ws) : nullptr;
+    const int bs = (int)((c.rows_u + 31) / 32), bl = (int)((c.cols + 31) / 32);
+    tr.before(MUON_KERNEL_NS_SMALL);
+    const dim3 grid(U), block(kThreads);
+#define MUON_SMALL_STEP(BS, BL) \
+  case BS * 8 + BL:             \
+    hipLaunchKernelGGL((k_ns_small_step<BS, BL>), grid, block, 0, s, p, ca, gk, err); \
+    break;
+    switch (bs * 8 + bl) {
+      MUON_SMALL_STEP(1, 1) MUON_SMALL_STEP(1, 2) MUON_SMALL_STEP(1, 3) MUON_SMALL_STEP(1, 4)
+      MUON_SMALL_STEP(2, 2) MUON_SMALL_STEP(2, 3) MUON_SMALL_STEP(2, 4)
+      MUON_SMALL_STEP(3, 3) MUON_SMALL_STEP(3, 4)
+      MUON_SMALL_STEP(4, 4)
+      default:
+        return MUON_ERR_SHAPE;  // not reached: rows <= cols <= 128
+    }
+#undef MUON_SMALL_STEP
+    tr.after_ns(MUON_KERNEL_NS_SMALL, c);
+    return hipGetLastError() == hipSuccess ? MUON_OK : MUON_ERR_HIP;
+  }
   // The tiled bf16 path folds 1/nu into the first iteration: momentum
   // writes N straight into the bf16 iterate (padding zeroed) and no
   // normalisation pass runs.
@@ -582,7 +630,6 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
   // launch's algorithmic bytes: G (or the NS input) read, M read and
   // written (step), N written into the bf16 iterate (2 B) or in fp32 (4 B).
   const int64_t pp = c.partials_per_unit;
-  const int gk = !step ? 2 : (c.gdtype == MUON_DTYPE_BF16 ? 0 : 1);
   auto mom_info = [&](int64_t units) {
     const int64_t elems = units * c.rows_u * c.cols;
     const int64_t gsz = (step && c.gdtype == MUON_DTYPE_BF16) ? 2 : 4;
@@ -623,28 +670,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
                      first_chunk ? err : nullptr, nb,
                      (int64_t)(c.rows_pad * c.cols_pad));
   if (small) {
-    int total_it = 0;
-    for (int i = 0; i < h->n_stages; ++i) total_it += h->stages[i].steps;
-    NsSmallArgs p;
-    std::memset(&p, 0, sizeof(p));
-    p.n32 = x32[0];
-    p.xb[0] = xb[0];
-    p.xb[1] = xb[1];
-    p.x_stride = c.rows_pad * c.cols_pad;
-    p.ldx = (int32_t)c.cols_pad;
-    p.n_iter = total_it;
-    p.n_stages = h->n_stages;
-    int begin = 0;
-    for (int i = 0; i < h->n_stages; ++i) {
-      p.stage_begin[i] = begin;
-      begin += h->stages[i].steps;
-      p.sa[i] = h->stages[i].a;
-      p.sb[i] = h->stages[i].b;
-      p.sc[i] = h->stages[i].c;
-    }
-    p.final_mode = step ? FINAL_STEP : FINAL_NSOUT;
-    p.inv_nu = inv_nu;
-    p.flag = flag;
+    const NsSmallArgs p = small_args();
     tr.after(MUON_KERNEL_NORMALIZE, c.n_units);
     tr.before(MUON_KERNEL_NS_SMALL);
     hipLaunchKernelGGL(k_ns_small, dim3(U), dim3(kThreads), 0, s, p, ca);

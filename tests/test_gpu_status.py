@@ -51,3 +51,26 @@ def test_stop_is_reported_sticky_and_cleared(gpu_lib, monkeypatch):
     gpu_lib.newton_schulz([x], [ref], hyper=gpu_lib.Hyper(schedule="launches"), check=True)
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
+
+
+def test_stop_report_kept_through_a_one_launch_call(gpu_lib, monkeypatch):
+    # A call whose only launch is the one-workgroup small-unit step (a
+    # 64 x 128 unit, bf16 products) moves the previous call's stop flag into
+    # the sticky word like any first launch of a call.
+    print("[status] stop, then a one-launch 64x128 call on the same workspace", flush=True)
+    g = torch.Generator(device="cpu").manual_seed(6)
+    x = torch.randn((1, 4096, 4096), generator=g).to(DEV)
+    small = torch.randn((64, 128), generator=g).to(DEV)
+    h = gpu_lib.Hyper(schedule="persistent")
+    ws = gpu_lib.workspace(gpu_lib.workspace_size([x], h), torch.device(DEV))
+    hs = gpu_lib.Hyper()
+    assert gpu_lib.workspace_size([small], hs) <= ws.numel()
+    out, out_s = torch.empty_like(x), torch.empty_like(small)
+    monkeypatch.setenv("MUON_WAIT_LIMIT_US", "0")
+    gpu_lib.newton_schulz([x], [out], hyper=h, ws=ws, check=False)
+    monkeypatch.delenv("MUON_WAIT_LIMIT_US")
+    gpu_lib.newton_schulz([small], [out_s], hyper=hs, ws=ws, check=False)
+    with pytest.raises(gpu_lib.MuonError) as e:
+        gpu_lib.workspace_status(ws)
+    assert e.value.status == -9
+    gpu_lib.newton_schulz([small], [out_s], hyper=hs, ws=ws, check=True)
