@@ -1258,21 +1258,10 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_gemm(GemmArgs g, Chun
 }
 
 // -------------------------------------------------------- small-s NS -------
-// Whole Newton-Schulz of a wide unit with at most 128 rows (a split head, a
-// small matrix) in one workgroup, bf16 products.  A and B never leave the
-// chip: A lives in the accumulators, its bf16 copy and B's in LDS.  Per
-// iteration one pass streams X (fp32, rows padded to 128) in 128-column
-// blocks X_j and, for each block,
-//   X'_j = a*X_j + B*X_j          (B*X_j: B rows x X_j^T rows from LDS)
-//   A'  += X'_j X'_j^T            (the next iteration's Gram)
-// so X makes one round trip per iteration and the Gram, polynomial and apply
-// of the notes' section 2 quintic step need no separate passes.  The
-// roundings match the general path (bf16 operands of every product, fp32
-// accumulation, fp32 iterate); the b*A term uses A's fp32 accumulator.
-// Iteration 0 reads the look-ahead N straight from the momentum kernel and
-// scales it by 1/||N||_F, masking the padding.
+// Wide units of at most 128 rows (split heads, small matrices), bf16
+// products, on chip: the Gram A and B' = bA + cA^2 (128 x 128) never leave
+// the workgroup, and each iteration makes one pass over X.
 struct NsSmallArgs {
-  const float* n32;       // the look-ahead N (unit 0), rows 128 x ldx
   uint16_t* xb[2];        // ping-pong bf16 iterates (unit 0), rows 128 x ldx
   int64_t x_stride;       // elements per unit
   int32_t ldx;            // padded columns (multiple of 128)
@@ -1281,286 +1270,11 @@ struct NsSmallArgs {
   int32_t stage_begin[4];
   float sa[4], sb[4], sc[4];
   int32_t final_mode;     // FINAL_STEP or FINAL_NSOUT
-  const float* inv_nu;    // per unit: 1/||N||_F
+  const float* inv_nu;    // per unit: first-iteration scale (k_norm_finish)
   const int32_t* flag;    // per unit: nonzero norm
 };
 
 constexpr int kSmall = 128;  // padded rows (= Gram size) of the small path
-
-// bf16 element (row, k) of a 128 x 128 operand in LDS: 256-byte rows of 16
-// chunks, chunk index XOR-ed with the row so that 32-row fragment reads and
-// the transposed writes spread over the banks.
-__device__ __forceinline__ int sm_at(int row, int k) {
-  return row * kSmall + ((((k >> 3) ^ (row & 15)) << 3) | (k & 7));
-}
-
-// C[m][n] += sum_k L1[m][k] * L2[n][k] over K = 128 for this wave's 64 x 64
-// quadrant (2 x 2 blocks of 32 x 32).
-__device__ __forceinline__ void sm_mma(const uint16_t* L1, const uint16_t* L2, f32x16 (&acc)[2][2],
-                                       int wm, int wn, int lane) {
-  const u32x4* A = reinterpret_cast<const u32x4*>(L1);
-  const u32x4* B = reinterpret_cast<const u32x4*>(L2);
-  const int half = lane >> 5;
-#pragma unroll
-  for (int kk = 0; kk < kSmall / 16; ++kk) {
-    const int ch = 2 * kk + half;
-    u32x4 af[2], bf[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int ra = wm * 64 + i * 32 + (lane & 31);
-      const int rb = wn * 64 + i * 32 + (lane & 31);
-      af[i] = A[ra * 16 + (ch ^ (ra & 15))];
-      bf[i] = B[rb * 16 + (ch ^ (rb & 15))];
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) mfma_one<__bf16>(af[i], bf[j], acc[i][j]);
-  }
-}
-
-// Accumulator-layout values (lane (m, half) of block (i, j) holds row
-// wm*64 + i*32 + m, columns wn*64 + j*32 + 8q + 4*half + e) into LDS as bf16,
-// row-major (L[row][col]) or transposed (L[col][row]).
-__device__ __forceinline__ void sm_put_rows(uint16_t* L, const float (&v)[2][2][16], int wm, int wn,
-                                            int lane) {
-  const int m = lane & 31, half = lane >> 5;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int row = wm * 64 + i * 32 + m;
-        const int col = wn * 64 + j * 32 + 8 * q + 4 * half;
-        uint2 pk;
-        pk.x = (uint32_t)to_bf16_bits(v[i][j][4 * q]) | ((uint32_t)to_bf16_bits(v[i][j][4 * q + 1]) << 16);
-        pk.y = (uint32_t)to_bf16_bits(v[i][j][4 * q + 2]) | ((uint32_t)to_bf16_bits(v[i][j][4 * q + 3]) << 16);
-        *reinterpret_cast<uint2*>(L + sm_at(row, col)) = pk;
-      }
-}
-
-__device__ __forceinline__ void sm_put_cols(uint16_t* L, const float (&v)[2][2][16], int wm, int wn,
-                                            int lane) {
-  const int m = lane & 31, half = lane >> 5;
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = wm * 64 + i * 32 + m;
-        const int col = wn * 64 + j * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        L[sm_at(col, row)] = to_bf16_bits(v[i][j][r]);
-      }
-}
-
-__device__ __forceinline__ void sm_zero(f32x16 (&a)[2][2]) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) a[i][j][r] = 0.0f;
-}
-
-__device__ __forceinline__ void sm_vals(const f32x16 (&a)[2][2], float (&v)[2][2][16]) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) v[i][j][r] = a[i][j][r];
-}
-
-__global__ __launch_bounds__(kThreads) void k_ns_small(NsSmallArgs p, ChunkArgs ca) {
-  __shared__ __attribute__((aligned(16))) uint16_t LA[kSmall * kSmall];  // A, then B
-  __shared__ __attribute__((aligned(16))) uint16_t LX[kSmall * kSmall];  // X_j^T
-  __shared__ __attribute__((aligned(16))) uint16_t LR[kSmall * kSmall];  // X'_j (or X_0j), row-major
-  const int u = blockIdx.x;
-  const int lane = threadIdx.x & 63;
-  const int wid = threadIdx.x >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
-  const int m = lane & 31, half = lane >> 5;
-  const int nb = p.ldx / kSmall;
-
-  const SegView sg = find_seg(ca, u);
-  float* const wout = sg.w + (int64_t)(u - sg.first) * ca.unit_elems;
-  if (!p.flag[u]) {
-    // Zero unit: O' = 0, so the weight only decays / the output is zero.
-    for (int64_t e = threadIdx.x; e < ca.unit_elems; e += kThreads)
-      wout[e] = (p.final_mode == FINAL_STEP) ? wout[e] * ca.decay : 0.0f;
-    return;
-  }
-  const float inv0 = p.inv_nu[u];
-
-  // Block j of the iterate, in accumulator layout, with bf16-rounded
-  // values: iteration 0 rounds the masked, scaled look-ahead, later ones
-  // read the bf16 iterate (the iterate is held in bf16 as on the tiled
-  // path).  Two register sets: block j+1 is loaded while block j is
-  // processed.
-  typedef float Blk[2][2][16];
-  Blk xbuf[2];
-  auto load_x0 = [&](Blk& xv, int j) {
-    const float* N = p.n32 + (int64_t)u * p.x_stride;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int row = wm * 64 + i * 32 + m;
-          const int col = j * kSmall + wn * 64 + jj * 32 + 8 * q + 4 * half;
-          const float4 x = *reinterpret_cast<const float4*>(N + (int64_t)row * p.ldx + col);
-          const bool rin = row < ca.rows;
-          xv[i][jj][4 * q] = bf16_round((rin && col + 0 < ca.cols) ? x.x * inv0 : 0.0f);
-          xv[i][jj][4 * q + 1] = bf16_round((rin && col + 1 < ca.cols) ? x.y * inv0 : 0.0f);
-          xv[i][jj][4 * q + 2] = bf16_round((rin && col + 2 < ca.cols) ? x.z * inv0 : 0.0f);
-          xv[i][jj][4 * q + 3] = bf16_round((rin && col + 3 < ca.cols) ? x.w * inv0 : 0.0f);
-        }
-  };
-  auto load_x = [&](Blk& xv, const uint16_t* X, int j) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int row = wm * 64 + i * 32 + m;
-          const int col = j * kSmall + wn * 64 + jj * 32 + 8 * q + 4 * half;
-          const uint2 h = *reinterpret_cast<const uint2*>(X + (int64_t)row * p.ldx + col);
-          xv[i][jj][4 * q] = bf16_bits_to_f32(h.x & 0xffffu);
-          xv[i][jj][4 * q + 1] = bf16_bits_to_f32(h.x >> 16);
-          xv[i][jj][4 * q + 2] = bf16_bits_to_f32(h.y & 0xffffu);
-          xv[i][jj][4 * q + 3] = bf16_bits_to_f32(h.y >> 16);
-        }
-  };
-  // Gram of iteration 0.
-  f32x16 accA[2][2], accC[2][2];
-  sm_zero(accA);
-  auto gram_block = [&](Blk& xv, Blk& xnext, int j) {
-    if (j + 1 < nb) load_x0(xnext, j + 1);
-    __syncthreads();  // LR is free
-    sm_put_rows(LR, xv, wm, wn, lane);
-    __syncthreads();
-    sm_mma(LR, LR, accA, wm, wn, lane);
-  };
-  load_x0(xbuf[0], 0);
-  for (int j = 0; j < nb; j += 2) {  // unrolled by two: the register sets alternate
-    gram_block(xbuf[0], xbuf[1], j);
-    if (j + 1 < nb) gram_block(xbuf[1], xbuf[0], j + 1);
-  }
-
-  for (int it = 0; it < p.n_iter; ++it) {
-    float ca_ = p.sa[0], cb = p.sb[0], cc = p.sc[0];
-#pragma unroll
-    for (int s = 1; s < 4; ++s)
-      if (s < p.n_stages && it >= p.stage_begin[s]) {
-        ca_ = p.sa[s];
-        cb = p.sb[s];
-        cc = p.sc[s];
-      }
-    const bool last = it == p.n_iter - 1;
-    const uint16_t* X = p.xb[it & 1] + (int64_t)u * p.x_stride;
-    uint16_t* Xn = p.xb[(it & 1) ^ 1] + (int64_t)u * p.x_stride;
-
-    // B = b*A + c*A*A (A symmetric), into LA as the apply's operand.
-    float av[2][2][16];
-    sm_vals(accA, av);
-    __syncthreads();  // every wave is done with LA and LR
-    sm_put_rows(LA, av, wm, wn, lane);
-    __syncthreads();
-    sm_zero(accC);
-    sm_mma(LA, LA, accC, wm, wn, lane);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) av[i][j][r] = cb * av[i][j][r] + cc * accC[i][j][r];
-    __syncthreads();  // every wave has read A
-    sm_put_rows(LA, av, wm, wn, lane);
-
-    // Apply pass, with the next Gram accumulated on the way.
-    sm_zero(accA);
-    auto apply_block = [&](Blk& xv, Blk& xnext, int j) {
-      if (j + 1 < nb) {
-        if (it == 0)
-          load_x0(xnext, j + 1);
-        else
-          load_x(xnext, X, j + 1);
-      }
-      __syncthreads();  // LA complete; LX and LR free
-      sm_put_cols(LX, xv, wm, wn, lane);
-      __syncthreads();
-      sm_zero(accC);
-      sm_mma(LA, LX, accC, wm, wn, lane);  // (B X_j)[m][n] = sum_k B[m][k] X_j[k][n]
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) xv[i][jj][r] = __builtin_fmaf(ca_, xv[i][jj][r], accC[i][jj][r]);
-      if (last) {
-        // O' block: the decoupled update (or the NS output), masked.
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int row = wm * 64 + i * 32 + m;
-              const int col = j * kSmall + wn * 64 + jj * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-              if (row < ca.rows && col < ca.cols) {
-                float* q = wout + (int64_t)row * ca.cols + col;
-                *q = (p.final_mode == FINAL_STEP) ? __builtin_fmaf(-ca.lr_scale, xv[i][jj][r], *q * ca.decay)
-                                                   : xv[i][jj][r];
-              }
-            }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const int row = wm * 64 + i * 32 + m;
-              const int col = j * kSmall + wn * 64 + jj * 32 + 8 * q + 4 * half;
-              store_bf16x4(Xn, (int64_t)row * p.ldx + col, xv[i][jj][4 * q], xv[i][jj][4 * q + 1],
-                           xv[i][jj][4 * q + 2], xv[i][jj][4 * q + 3]);
-            }
-        sm_put_rows(LR, xv, wm, wn, lane);
-        __syncthreads();
-        sm_mma(LR, LR, accA, wm, wn, lane);
-      }
-    };
-    if (it == 0)
-      load_x0(xbuf[0], 0);
-    else
-      load_x(xbuf[0], X, 0);
-    for (int j = 0; j < nb; j += 2) {  // unrolled by two: the register sets alternate
-      apply_block(xbuf[0], xbuf[1], j);
-      if (j + 1 < nb) apply_block(xbuf[1], xbuf[0], j + 1);
-    }
-  }
-}
-
-// ------------------------------------------------ one-launch small step ----
-// The whole step of units whose wide form fits one 128 x 128 block (at most
-// 128 rows and 128 columns, rows <= columns), one workgroup per unit and one
-// launch per chunk: momentum and the look-ahead go straight into registers,
-// the Frobenius norm is a block reduction, and every product of every
-// iteration runs on chip over the unit's own extent rounded up to 32 (BS
-// row blocks, BL column blocks of 32) rather than over 128 x 128.  Products
-// are split into 32 x 32 output blocks, block b of a product going to wave
-// b % 4; a wave keeps the iterate's blocks it updates, and the Gram blocks
-// it later combines with A*A, in registers.  LDS holds bf16 operands: X
-// (two buffers: one read by this iteration's products, the other receiving
-// X'), A and B, so an iteration needs three barriers.  The roundings are
-// those of the other bf16 paths: bf16 operands, fp32 accumulation, the
-// iterate rounded to bf16 between iterations.  gk: 0 bf16 gradient, 1 fp32
-// gradient, 2 NS only.  err: the call's status words when this is its
-// first launch, else null.
 
 // Element (row, k) of a bf16 operand with 128-element rows in LDS: 16 chunks
 // of 8 per row, the chunk index XOR-ed with a permutation of the row's low
@@ -1609,6 +1323,256 @@ __device__ __forceinline__ void sb_put(uint16_t* L, const float (&v)[16], int r0
     *reinterpret_cast<uint2*>(L + sb_at(row, c0 + 8 * q + 4 * half)) = pk;
   }
 }
+
+// Multi-block units (more than 128 columns), one workgroup per unit.  Per
+// iteration the bf16 iterate streams through LDS in 128-column blocks X_j
+// (row-major, the next block's loads in flight while one is used), and for
+// each block
+//   X'_j = B'*X_j                  (B' = a*I + b*A + c*A^2, its rows in
+//                                   registers; X_j read K-major with the
+//                                   transposing read)
+//   A'  += X'_j X'_j^T             (the next iteration's Gram)
+// so X makes one round trip through memory per iteration and the Gram,
+// polynomial and apply of the notes' section 2 quintic step need no passes of
+// their own.  Each wave owns a 64 x 64 quadrant of every 128 x 128 product.
+// The iterate is the folded look-ahead on entry (k_momentum wrote bf16 N,
+// padding zeroed; k_norm_finish left the first iteration's scale s = 1/nu,
+// or 1 for a unit it rescaled): the first Gram is scaled by s^2 and the first
+// X' by s.  Roundings as on the tiled bf16 path: bf16 operands, fp32
+// accumulation, the iterate held in bf16.
+__global__ __launch_bounds__(kThreads) void k_ns_small(NsSmallArgs p, ChunkArgs ca) {
+  __shared__ __attribute__((aligned(16))) uint16_t LS[2][kSmall * kSmall];  // X_j, row-major
+  __shared__ __attribute__((aligned(16))) uint16_t LR[kSmall * kSmall];     // A, B', then X'_j
+  const int u = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int wm = w >> 1, wn = w & 1;
+  const int m = lane & 31, half = lane >> 5;
+  const int nb = p.ldx / kSmall;
+
+  const SegView sg = find_seg(ca, u);
+  float* const wout = sg.w + (int64_t)(u - sg.first) * ca.unit_elems;
+  if (!p.flag[u]) {
+    // Zero unit: O' = 0, so the weight only decays / the output is zero.
+    for (int64_t e = threadIdx.x; e < ca.unit_elems; e += kThreads)
+      wout[e] = (p.final_mode == FINAL_STEP) ? wout[e] * ca.decay : 0.0f;
+    return;
+  }
+  const float s0 = p.inv_nu[u];
+
+  // Block j of an iterate into registers: 128 rows x 16 chunks of 8, chunk
+  // t + 256 i of the block for thread t (16 threads per 256-byte row).
+  u32x4 pf[8];
+  auto fetch = [&](const uint16_t* X, int j) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = threadIdx.x + kThreads * i, row = c >> 4, ch = c & 15;
+      pf[i] = *reinterpret_cast<const u32x4*>(X + (int64_t)row * p.ldx + j * kSmall + ch * 8);
+    }
+  };
+  auto stage = [&](uint16_t* L) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = threadIdx.x + kThreads * i, row = c >> 4, ch = c & 15;
+      *reinterpret_cast<u32x4*>(L + sb_at(row, ch * 8)) = pf[i];
+    }
+  };
+  auto zero = [](f32x16 (&a)[2][2]) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) a[i][j][r] = 0.0f;
+  };
+  // acc += rows of L (this wave's 64-row half) x rows of L (its 64-column half)
+  auto gram = [&](const uint16_t* L, f32x16 (&acc)[2][2]) {
+#pragma unroll
+    for (int kk = 0; kk < kSmall / 16; ++kk) {
+      u32x4 af[2], bf[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        af[i] = sb_rows(L, wm * 64 + i * 32, kk, lane);
+        bf[i] = sb_rows(L, wn * 64 + i * 32, kk, lane);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) mfma_one<__bf16>(af[i], bf[j], acc[i][j]);
+    }
+  };
+
+  f32x16 accA[2][2], accC[2][2];
+  const uint16_t* const X0 = p.xb[0] + (int64_t)u * p.x_stride;
+  // Gram of the entry iterate, scaled by s^2.
+  zero(accA);
+  fetch(X0, 0);
+  for (int j = 0; j < nb; ++j) {
+    stage(LS[j & 1]);
+    if (j + 1 < nb) fetch(X0, j + 1);
+    lds_barrier();  // block j staged; every wave is done with block j - 1
+    gram(LS[j & 1], accA);
+  }
+  {
+    const float s2 = s0 * s0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) accA[i][jj][r] *= s2;
+  }
+
+  const float lrs = sg.lr_scale;
+  for (int it = 0; it < p.n_iter; ++it) {
+    float ca_ = p.sa[0], cb = p.sb[0], cc = p.sc[0];
+#pragma unroll
+    for (int st = 1; st < 4; ++st)
+      if (st < p.n_stages && it >= p.stage_begin[st]) {
+        ca_ = p.sa[st];
+        cb = p.sb[st];
+        cc = p.sc[st];
+      }
+    const bool last = it == p.n_iter - 1;
+    const float xs = it == 0 ? s0 : 1.0f;  // scale of this iteration's X'
+    const uint16_t* const X = p.xb[it & 1] + (int64_t)u * p.x_stride;
+    uint16_t* const Xn = p.xb[(it & 1) ^ 1] + (int64_t)u * p.x_stride;
+
+    // B' = b*A + c*A*A (A symmetric), via LR; then this wave's rows of B'
+    // into registers (the apply's first operand for every block).
+    float av[2][2][16];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) av[i][jj][r] = accA[i][jj][r];
+    // Every wave is done with LR and the last block, and the previous
+    // iteration's stores of X (the barrier's fence drains them) are visible
+    // to the whole workgroup before it reads X.
+    __syncthreads();
+    fetch(X, 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) sb_put(LR, av[i][jj], wm * 64 + i * 32, wn * 64 + jj * 32, lane);
+    lds_barrier();
+    zero(accC);
+    gram(LR, accC);
+    // B' = a*I + b*A + c*A*A: the apply's a*X term rides on the diagonal.
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          av[i][jj][r] = cb * av[i][jj][r] + cc * accC[i][jj][r];
+          if (wm == wn && i == jj && m == 8 * (r >> 2) + 4 * half + (r & 3)) av[i][jj][r] += ca_;
+        }
+    lds_barrier();  // every wave has read A
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) sb_put(LR, av[i][jj], wm * 64 + i * 32, wn * 64 + jj * 32, lane);
+    lds_barrier();
+    u32x4 bfr[2][kSmall / 16];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int kk = 0; kk < kSmall / 16; ++kk) bfr[i][kk] = sb_rows(LR, wm * 64 + i * 32, kk, lane);
+
+    zero(accA);
+    for (int j = 0; j < nb; ++j) {
+      stage(LS[j & 1]);
+      if (j + 1 < nb) fetch(X, j + 1);
+      lds_barrier();  // block j staged; every wave is done with LR and block j - 1
+      // X'_j = a*X_j + B'*X_j over this wave's quadrant.
+      zero(accC);
+#pragma unroll
+      for (int kk = 0; kk < kSmall / 16; ++kk) {
+        u32x4 xf[2];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) xf[jj] = sb_cols(LS[j & 1], wn * 64 + jj * 32, kk, lane);
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj) mfma_one<__bf16>(bfr[i][kk], xf[jj], accC[i][jj]);
+      }
+      float xv[2][2][16];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) xv[i][jj][r] = xs * accC[i][jj][r];
+      if (last) {
+        // O' block: the decoupled update (or the NS output), masked.
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int row = wm * 64 + i * 32 + m;
+              const int c0 = j * kSmall + wn * 64 + jj * 32 + 8 * q + 4 * half;
+              if (row >= ca.rows || c0 >= ca.cols) continue;
+              float* const wp = wout + (int64_t)row * ca.cols + c0;
+              const float o[4] = {xv[i][jj][4 * q], xv[i][jj][4 * q + 1], xv[i][jj][4 * q + 2],
+                                  xv[i][jj][4 * q + 3]};
+              if ((ca.cols & 3) == 0) {
+                float4 wv = make_float4(o[0], o[1], o[2], o[3]);
+                if (p.final_mode == FINAL_STEP) {
+                  const float4 w0 = *reinterpret_cast<const float4*>(wp);
+                  wv.x = __builtin_fmaf(-lrs, o[0], w0.x * ca.decay);
+                  wv.y = __builtin_fmaf(-lrs, o[1], w0.y * ca.decay);
+                  wv.z = __builtin_fmaf(-lrs, o[2], w0.z * ca.decay);
+                  wv.w = __builtin_fmaf(-lrs, o[3], w0.w * ca.decay);
+                }
+                *reinterpret_cast<float4*>(wp) = wv;
+              } else {
+                const int ne = min(4, ca.cols - c0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  if (e < ne)
+                    wp[e] = (p.final_mode == FINAL_STEP) ? __builtin_fmaf(-lrs, o[e], wp[e] * ca.decay) : o[e];
+              }
+            }
+        continue;
+      }
+      // X'_j in bf16 into LR, for the next Gram and, in whole rows, for
+      // memory (the next iteration's X).
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) sb_put(LR, xv[i][jj], wm * 64 + i * 32, wn * 64 + jj * 32, lane);
+      lds_barrier();  // X'_j complete in LR
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int c = threadIdx.x + kThreads * i, row = c >> 4, ch = c & 15;
+        *reinterpret_cast<u32x4*>(Xn + (int64_t)row * p.ldx + j * kSmall + ch * 8) =
+            *reinterpret_cast<const u32x4*>(LR + sb_at(row, ch * 8));
+      }
+      gram(LR, accA);
+    }
+  }
+}
+
+// ------------------------------------------------ one-launch small step ----
+// The whole step of units whose wide form fits one 128 x 128 block (at most
+// 128 rows and 128 columns, rows <= columns), one workgroup per unit and one
+// launch per chunk: momentum and the look-ahead go straight into registers,
+// the Frobenius norm is a block reduction, and every product of every
+// iteration runs on chip over the unit's own extent rounded up to 32 (BS
+// row blocks, BL column blocks of 32) rather than over 128 x 128.  Products
+// are split into 32 x 32 output blocks, block b of a product going to wave
+// b % 4; a wave keeps the iterate's blocks it updates, and the Gram blocks
+// it later combines with A*A, in registers.  LDS holds bf16 operands: X
+// (two buffers: one read by this iteration's products, the other receiving
+// X'), A and B, so an iteration needs three barriers.  The roundings are
+// those of the other bf16 paths: bf16 operands, fp32 accumulation, the
+// iterate rounded to bf16 between iterations.  gk: 0 bf16 gradient, 1 fp32
+// gradient, 2 NS only.  err: the call's status words when this is its
+// first launch, else null.
 
 template <int BS, int BL>
 __global__ __launch_bounds__(kThreads) void k_ns_small_step(NsSmallArgs p, ChunkArgs ca, int gk,

@@ -125,7 +125,7 @@ Layout layout_of(const Chunk& c, const muon_hyper* h) {
   // small-unit kernel; the second only on the fp32 path (the bf16 path keeps
   // the iterate in bf16, and its tiled products start from N written
   // straight into it).
-  if (!bf16 || small_possible(c, h)) L.x32[0] = take(U * xs * 4);
+  if (!bf16) L.x32[0] = take(U * xs * 4);
   if (!bf16) L.x32[1] = take(U * xs * 4);
   if (bf16) {
     L.xb[0] = take(U * xs * 2);
@@ -272,9 +272,11 @@ int plan(const muon_matrix_desc* mats, int64_t n, const muon_hyper* h, bool step
     proto.s_pad = proto.tall ? proto.cols_pad : proto.rows_pad;
     proto.n_units = 0;
     proto.n_plain = 0;
-    // Momentum kernel: about 16K elements per block; transposed units one
-    // 64x64 tile of the padded caller matrix per block.
-    proto.rows_per_block = (int)std::max<int64_t>(1, std::min<int64_t>(u0.rows_u, 16384 / u0.cols));
+    // Momentum kernel: about 8K elements per block (measured on 32 x 1024^2
+    // units: 2K per block ran at 0.65x the speed, 4K-8K fastest, 16K 6%
+    // slower, 64K 25% slower); transposed units one 64x64 tile of the
+    // padded caller matrix per block.
+    proto.rows_per_block = (int)std::max<int64_t>(1, std::min<int64_t>(u0.rows_u, 8192 / u0.cols));
     proto.blocks_per_unit = (int)((u0.rows_u + proto.rows_per_block - 1) / proto.rows_per_block);
     proto.tiles_t = (int)((proto.rows_pad / 64) * (proto.cols_pad / 64));
     proto.partials_per_unit = proto.blocks_per_unit;
@@ -560,8 +562,8 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
 
   const int U = (int)c.n_units;
   // Small wide units (at most 128 rows, bf16 products, AUTO schedule): the
-  // whole NS in one workgroup per unit, reading N itself (no normalisation
-  // pass).  A unit's workgroup walks its column blocks in sequence, so the
+  // whole NS in one workgroup per unit.  A unit's workgroup walks its
+  // column blocks in sequence, so the
   // path is taken for short units (up to eight 128-column blocks) or when
   // the units number at least half the CUs; a few long units go to the
   // tiled products, which spread each unit over many CUs.
@@ -576,7 +578,6 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
   auto small_args = [&]() {
     NsSmallArgs p;
     std::memset(&p, 0, sizeof(p));
-    p.n32 = x32[0];
     p.xb[0] = xb[0];
     p.xb[1] = xb[1];
     p.x_stride = c.rows_pad * c.cols_pad;
@@ -620,10 +621,10 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
     tr.after_ns(MUON_KERNEL_NS_SMALL, c);
     return hipGetLastError() == hipSuccess ? MUON_OK : MUON_ERR_HIP;
   }
-  // The tiled bf16 path folds 1/nu into the first iteration: momentum
-  // writes N straight into the bf16 iterate (padding zeroed) and no
-  // normalisation pass runs.
-  const bool fold = bf16 && !small;
+  // The bf16 paths fold 1/nu into the first iteration: momentum writes N
+  // straight into the bf16 iterate (padding zeroed) and no normalisation
+  // pass runs.
+  const bool fold = bf16;
   uint16_t* const nb = fold ? xb[0] : nullptr;
   // 1. momentum + Nesterov + partial sums of squares.
   // Units in their own form (0 .. n_plain - 1), then transposed ones; each

@@ -77,22 +77,23 @@ def test_workspace_sizes():
     assert ws_size([])[0] == 0
 
 
-def test_workspace_keeps_fp32_n_only_where_the_small_kernel_may_run():
-    # 128-row wide heads under AUTO may run on chip, which reads N in fp32:
-    # 4 (fp32 N) + 2 x 2 (bf16 iterates) bytes per element of the 128 x 4096
-    # iterate, plus two 128 x 128 bf16 matrices per unit
-    per_unit_auto = 128 * 4096 * 8 + 2 * 128 * 128 * 2
+def test_bf16_workspace_holds_only_bf16_iterates():
+    # The bf16 paths (tiled and on chip) fold 1/||N|| into the first
+    # iteration, so no fp32 copy of N exists: two bf16 iterates (2 x 2 bytes
+    # per element of the 128 x 4096 iterate) plus two 128 x 128 bf16
+    # matrices per unit, under any schedule.
+    per_unit = 128 * 4096 * 4 + 2 * 128 * 128 * 2
     st, n = ws_size([(48, 128, 4096, 0)])
-    assert st == 0 and 48 * per_unit_auto <= n < 48 * per_unit_auto + (1 << 20)
-    # a forced schedule never runs the small kernel: no fp32 N
+    assert st == 0 and 48 * per_unit <= n < 48 * per_unit + (1 << 20)
     h = muon.default_hyper_c()
     h.schedule = muon.SCHEDULE_PERSISTENT
-    per_unit_tiled = 128 * 4096 * 4 + 2 * 128 * 128 * 2
     st, nt = ws_size([(48, 128, 4096, 0)], h)
-    assert st == 0 and 48 * per_unit_tiled <= nt < 48 * per_unit_tiled + (1 << 20)
-    # tall 4096 x 128 units have a 128-wide Gram but are never small: no fp32 N
-    st, ntall = ws_size([(48, 4096, 128, 0)])
-    assert st == 0 and ntall < n
+    assert st == 0 and 48 * per_unit <= nt < 48 * per_unit + (1 << 20)
+    # the fp32 path keeps X and X^T in fp32, twice
+    h = muon.default_hyper_c()
+    h.ns_precision = muon.NS_FP32
+    st, nf = ws_size([(48, 128, 4096, 0)], h)
+    assert st == 0 and nf >= 48 * 128 * 4096 * 16
 
 
 @pytest.mark.parametrize(
