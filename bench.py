@@ -317,6 +317,30 @@ def measure(wl, ns, steps, warmup, dev, inputs, schedule="auto", trace_classes=T
     return out, roof
 
 
+def hbm_copy_rate(dev, mib=1024, reps=5):
+    """Best rate of a plain device copy (torch's copy kernel) over `mib` MiB,
+    read once and written once, in GB/s: the streaming rate the elementwise
+    kernels are read against (the nominal 8 TB/s is not reached by any
+    streaming kernel)."""
+    import torch
+
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    best = float("inf")
+    for r in range(reps + 1):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        if r > 0:
+            best = min(best, e0.elapsed_time(e1))
+    del src, dst
+    return 2 * n * 4 / (best * 1e-3) / 1e9
+
+
 def blas_rate():
     """float64 FLOP/s of the host BLAS on a 1024^3 product (the best of
     three), used only to predict whether a shape fits the sample budget."""
@@ -421,6 +445,7 @@ def main(argv=None):
         subs[f"{args.config}_fp32"] = r
     del inputs
     free()
+    copy_gbs = hbm_copy_rate(dev)
     if args.calibrate_copy_mib > 0:
         n = args.calibrate_copy_mib * (1 << 20) // 4
         src = torch.zeros(n, dtype=torch.int32, device=dev)
@@ -472,9 +497,12 @@ def main(argv=None):
         **{k: head[k] for k in ("ns_tflops", "ns_frac_of_peak", "ns_ms_per_step", "ns_tflops_step",
                                 "kernel_ms_per_step", "elementwise_gbs", "elementwise_frac_of_hbm")
            if k in head},
+        "hbm_copy_gbs": copy_gbs,
         "roofline": roof,
         "configs": subs,
     }
+    if "elementwise_gbs" in head:
+        line["elementwise_frac_of_copy"] = head["elementwise_gbs"] / copy_gbs
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, args.cpu_seconds)
     print(json.dumps(line), flush=True)

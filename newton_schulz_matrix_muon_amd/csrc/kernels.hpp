@@ -1559,30 +1559,83 @@ __global__ __launch_bounds__(kThreads) void k_ns_small(NsSmallArgs p, ChunkArgs 
 
 // ------------------------------------------------ one-launch small step ----
 // The whole step of units whose wide form fits one 128 x 128 block (at most
-// 128 rows and 128 columns, rows <= columns), one workgroup per unit and one
-// launch per chunk: momentum and the look-ahead go straight into registers,
-// the Frobenius norm is a block reduction, and every product of every
-// iteration runs on chip over the unit's own extent rounded up to 32 (BS
-// row blocks, BL column blocks of 32) rather than over 128 x 128.  Products
-// are split into 32 x 32 output blocks, block b of a product going to wave
-// b % 4; a wave keeps the iterate's blocks it updates, and the Gram blocks
-// it later combines with A*A, in registers.  LDS holds bf16 operands: X
-// (two buffers: one read by this iteration's products, the other receiving
-// X'), A and B, so an iteration needs three barriers.  The roundings are
-// those of the other bf16 paths: bf16 operands, fp32 accumulation, the
-// iterate rounded to bf16 between iterations.  gk: 0 bf16 gradient, 1 fp32
-// gradient, 2 NS only.  err: the call's status words when this is its
-// first launch, else null.
+// 128 rows and 128 columns, rows <= columns; fp32 products: at most 64
+// rows), one workgroup per unit and one launch per chunk: momentum and the
+// look-ahead go straight into registers, the Frobenius norm is a block
+// reduction, and every product of every iteration runs on chip over the
+// unit's own extent rounded up to 32 (BS row blocks, BL column blocks of 32)
+// rather than over 128 x 128.  Products are split into 32 x 32 output
+// blocks, block b of a product going to wave b % 4; a wave keeps the
+// iterate's blocks it updates, and the Gram blocks it later combines with
+// A*A, in registers.  LDS holds the operands in the products' type T: X (two
+// buffers: one read by this iteration's products, the other receiving X'),
+// A and B, so an iteration needs three barriers.  The roundings are those of
+// the other paths of the same type: operands in T, fp32 accumulation, and
+// on the bf16 path the iterate rounded to bf16 between iterations.  gk: 0
+// bf16 gradient, 1 fp32 gradient, 2 NS only.  err: the call's status words
+// when this is its first launch, else null.
 
-template <int BS, int BL>
+// Operand access of the one-launch kernel per product type.  bf16: rows of
+// 128 elements swizzled by sb_at, K-major fragments by the transposing read,
+// 16 K per fragment.  fp32: rows of 132 floats (the padding spreads 16
+// consecutive rows over the banks), K-major fragments as four column reads,
+// 8 K per fragment (lane half h holds k = 8kk + 4h .. +3, the order in which
+// mfma_one<float> feeds its four K = 2 steps).
+template <typename T>
+struct SmallOps;
+
+template <>
+struct SmallOps<__bf16> {
+  typedef uint16_t E;
+  static constexpr int kPitch = kSmall;
+  static constexpr int kK = 16;
+  static __device__ __forceinline__ u32x4 rows(const E* L, int r0, int kk, int lane) {
+    return sb_rows(L, r0, kk, lane);
+  }
+  static __device__ __forceinline__ u32x4 cols(const E* L, int c0, int kk, int lane) {
+    return sb_cols(L, c0, kk, lane);
+  }
+  static __device__ __forceinline__ void put(E* L, const float (&v)[16], int r0, int c0, int lane) {
+    sb_put(L, v, r0, c0, lane);
+  }
+  static __device__ __forceinline__ float iterate(float x) { return bf16_round(x); }
+};
+
+template <>
+struct SmallOps<float> {
+  typedef float E;
+  static constexpr int kPitch = kSmall + 4;
+  static constexpr int kK = 8;
+  static __device__ __forceinline__ u32x4 rows(const E* L, int r0, int kk, int lane) {
+    const int r = r0 + (lane & 31);
+    return *reinterpret_cast<const u32x4*>(L + r * kPitch + 8 * kk + 4 * (lane >> 5));
+  }
+  static __device__ __forceinline__ u32x4 cols(const E* L, int c0, int kk, int lane) {
+    const E* q = L + (8 * kk + 4 * (lane >> 5)) * kPitch + c0 + (lane & 31);
+    return u32x4{__builtin_bit_cast(uint32_t, q[0]), __builtin_bit_cast(uint32_t, q[kPitch]),
+                 __builtin_bit_cast(uint32_t, q[2 * kPitch]), __builtin_bit_cast(uint32_t, q[3 * kPitch])};
+  }
+  static __device__ __forceinline__ void put(E* L, const float (&v)[16], int r0, int c0, int lane) {
+    const int row = r0 + (lane & 31), half = lane >> 5;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<float4*>(L + row * kPitch + c0 + 8 * q + 4 * half) =
+          make_float4(v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+  }
+  static __device__ __forceinline__ float iterate(float x) { return x; }
+};
+
+template <typename T, int BS, int BL>
 __global__ __launch_bounds__(kThreads) void k_ns_small_step(NsSmallArgs p, ChunkArgs ca, int gk,
                                                              uint32_t* __restrict__ err) {
+  typedef SmallOps<T> Op;
+  typedef typename Op::E E;
   constexpr int R = 32 * BS;                // rows of every LDS operand
   constexpr int NA = BS * BS, NX = BS * BL;  // 32 x 32 blocks of A (and B), of X
   constexpr int TA = (NA + 3) / 4, TX = (NX + 3) / 4;  // blocks per wave, at most
-  __shared__ __attribute__((aligned(16))) uint16_t LX[2][R * kSmall];
-  __shared__ __attribute__((aligned(16))) uint16_t LA[R * kSmall];
-  __shared__ __attribute__((aligned(16))) uint16_t LB[R * kSmall];
+  __shared__ __attribute__((aligned(16))) E LX[2][R * Op::kPitch];
+  __shared__ __attribute__((aligned(16))) E LA[R * Op::kPitch];
+  __shared__ __attribute__((aligned(16))) E LB[R * Op::kPitch];
   __shared__ double wsum[kThreads / 64];
   const int u = blockIdx.x;
   const int lane = threadIdx.x & 63;
@@ -1684,9 +1737,9 @@ __global__ __launch_bounds__(kThreads) void k_ns_small_step(NsSmallArgs p, Chunk
 #pragma unroll
   for (int t = 0; t < TX; ++t) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) xv[t][r] = bf16_round(xv[t][r] * inv);
+    for (int r = 0; r < 16; ++r) xv[t][r] = Op::iterate(xv[t][r] * inv);
     const int b = w + 4 * t;
-    if (b < NX) sb_put(LX[0], xv[t], 32 * (b / BL), 32 * (b % BL), lane);
+    if (b < NX) Op::put(LX[0], xv[t], 32 * (b / BL), 32 * (b % BL), lane);
   }
   __syncthreads();
 
@@ -1702,26 +1755,26 @@ __global__ __launch_bounds__(kThreads) void k_ns_small_step(NsSmallArgs p, Chunk
         cb = p.sb[st];
         cc = p.sc[st];
       }
-    const uint16_t* const X = LX[it & 1];
+    const E* const X = LX[it & 1];
     // A = X X^T over K = 32 BL; block b: rows 32(b / BS), columns 32(b % BS).
 #pragma unroll
     for (int t = 0; t < TA; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
 #pragma unroll
-    for (int kk = 0; kk < 2 * BL; ++kk)
+    for (int kk = 0; kk < 32 * BL / Op::kK; ++kk)
 #pragma unroll
       for (int t = 0; t < TA; ++t) {
         const int b = w + 4 * t;
         if (b < NA)
-          mfma_one<__bf16>(sb_rows(X, 32 * (b / BS), kk, lane), sb_rows(X, 32 * (b % BS), kk, lane), acc[t]);
+          mfma_one<T>(Op::rows(X, 32 * (b / BS), kk, lane), Op::rows(X, 32 * (b % BS), kk, lane), acc[t]);
       }
 #pragma unroll
     for (int t = 0; t < TA; ++t) {
       const int b = w + 4 * t;
 #pragma unroll
       for (int r = 0; r < 16; ++r) av[t][r] = acc[t][r];
-      if (b < NA) sb_put(LA, av[t], 32 * (b / BS), 32 * (b % BS), lane);
+      if (b < NA) Op::put(LA, av[t], 32 * (b / BS), 32 * (b % BS), lane);
     }
     __syncthreads();
     // B = b*A + c*A*A (A symmetric: both operands read rows of A).
@@ -1730,19 +1783,19 @@ __global__ __launch_bounds__(kThreads) void k_ns_small_step(NsSmallArgs p, Chunk
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
 #pragma unroll
-    for (int kk = 0; kk < 2 * BS; ++kk)
+    for (int kk = 0; kk < 32 * BS / Op::kK; ++kk)
 #pragma unroll
       for (int t = 0; t < TA; ++t) {
         const int b = w + 4 * t;
         if (b < NA)
-          mfma_one<__bf16>(sb_rows(LA, 32 * (b / BS), kk, lane), sb_rows(LA, 32 * (b % BS), kk, lane), acc[t]);
+          mfma_one<T>(Op::rows(LA, 32 * (b / BS), kk, lane), Op::rows(LA, 32 * (b % BS), kk, lane), acc[t]);
       }
 #pragma unroll
     for (int t = 0; t < TA; ++t) {
       const int b = w + 4 * t;
 #pragma unroll
       for (int r = 0; r < 16; ++r) av[t][r] = cb * av[t][r] + cc * acc[t][r];
-      if (b < NA) sb_put(LB, av[t], 32 * (b / BS), 32 * (b % BS), lane);
+      if (b < NA) Op::put(LB, av[t], 32 * (b / BS), 32 * (b % BS), lane);
     }
     __syncthreads();
     // X' = a*X + B*X over K = 32 BS.
@@ -1751,12 +1804,12 @@ __global__ __launch_bounds__(kThreads) void k_ns_small_step(NsSmallArgs p, Chunk
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
 #pragma unroll
-    for (int kk = 0; kk < 2 * BS; ++kk)
+    for (int kk = 0; kk < 32 * BS / Op::kK; ++kk)
 #pragma unroll
       for (int t = 0; t < TX; ++t) {
         const int b = w + 4 * t;
         if (b < NX)
-          mfma_one<__bf16>(sb_rows(LB, 32 * (b / BL), kk, lane), sb_cols(X, 32 * (b % BL), kk, lane), acc[t]);
+          mfma_one<T>(Op::rows(LB, 32 * (b / BL), kk, lane), Op::cols(X, 32 * (b % BL), kk, lane), acc[t]);
       }
 #pragma unroll
     for (int t = 0; t < TX; ++t)
@@ -1766,9 +1819,9 @@ __global__ __launch_bounds__(kThreads) void k_ns_small_step(NsSmallArgs p, Chunk
 #pragma unroll
     for (int t = 0; t < TX; ++t) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) xv[t][r] = bf16_round(xv[t][r]);
+      for (int r = 0; r < 16; ++r) xv[t][r] = Op::iterate(xv[t][r]);
       const int b = w + 4 * t;
-      if (b < NX) sb_put(LX[(it & 1) ^ 1], xv[t], 32 * (b / BL), 32 * (b % BL), lane);
+      if (b < NX) Op::put(LX[(it & 1) ^ 1], xv[t], 32 * (b / BL), 32 * (b % BL), lane);
     }
     __syncthreads();
   }

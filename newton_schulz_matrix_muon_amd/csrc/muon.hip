@@ -98,15 +98,17 @@ constexpr int kMaxQueues = 16;   // persistent schedule: at most one queue per X
 // also looks at the unit count and the CUs).  Only that kernel reads N in
 // fp32 on the bf16 path.
 bool small_possible(const Chunk& c, const muon_hyper* h) {
-  return h->schedule == MUON_SCHEDULE_AUTO && h->ns_precision == MUON_NS_BF16 && !c.tall &&
-         c.rows_u <= kSmall && c.rows_pad == kSmall;
+  if (h->schedule != MUON_SCHEDULE_AUTO || c.tall || c.rows_u > kSmall || c.rows_pad != kSmall) return false;
+  // fp32 products: one-block units of at most 64 rows (their operands in
+  // fp32 fill the LDS at 64 rows)
+  return h->ns_precision == MUON_NS_BF16 || (c.rows_u <= 64 && c.cols_pad == kSmall);
 }
 
-// A unit that the on-chip kernel may run keeps its own (wide) form; every
+// A unit that the on-chip kernels may run keeps its own (wide) form; every
 // other unit takes the tall form.
 bool unit_small_possible(int64_t rows_u, int64_t cols, const muon_hyper* h) {
-  return h->schedule == MUON_SCHEDULE_AUTO && h->ns_precision == MUON_NS_BF16 && rows_u < cols &&
-         rows_u <= kSmall;
+  if (h->schedule != MUON_SCHEDULE_AUTO || rows_u >= cols || rows_u > kSmall) return false;
+  return h->ns_precision == MUON_NS_BF16 || (rows_u <= 64 && cols <= kSmall);
 }
 
 // Words of persistent-schedule completion counts per unit: three per tile
@@ -561,12 +563,12 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
   int32_t* flag = reinterpret_cast<int32_t*>(ws + L.flag);
 
   const int U = (int)c.n_units;
-  // Small wide units (at most 128 rows, bf16 products, AUTO schedule): the
-  // whole NS in one workgroup per unit.  A unit's workgroup walks its
-  // column blocks in sequence, so the
-  // path is taken for short units (up to eight 128-column blocks) or when
-  // the units number at least half the CUs; a few long units go to the
-  // tiled products, which spread each unit over many CUs.
+  // Small wide units (AUTO schedule; at most 128 rows with bf16 products,
+  // at most 64 rows and 128 columns with fp32 ones): the whole NS in one
+  // workgroup per unit.  A unit's workgroup walks its column blocks in
+  // sequence, so the path is taken for short units (up to eight 128-column
+  // blocks) or when the units number at least half the CUs; a few long
+  // units go to the tiled products, which spread each unit over many CUs.
   bool small = small_possible(c, h);
   if (small && c.cols_pad / kSmall > 8) {
     DeviceInfo di;
@@ -605,17 +607,27 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
     const int bs = (int)((c.rows_u + 31) / 32), bl = (int)((c.cols + 31) / 32);
     tr.before(MUON_KERNEL_NS_SMALL);
     const dim3 grid(U), block(kThreads);
-#define MUON_SMALL_STEP(BS, BL) \
-  case BS * 8 + BL:             \
-    hipLaunchKernelGGL((k_ns_small_step<BS, BL>), grid, block, 0, s, p, ca, gk, err); \
+#define MUON_SMALL_STEP(T, BS, BL) \
+  case BS * 8 + BL:                \
+    hipLaunchKernelGGL((k_ns_small_step<T, BS, BL>), grid, block, 0, s, p, ca, gk, err); \
     break;
-    switch (bs * 8 + bl) {
-      MUON_SMALL_STEP(1, 1) MUON_SMALL_STEP(1, 2) MUON_SMALL_STEP(1, 3) MUON_SMALL_STEP(1, 4)
-      MUON_SMALL_STEP(2, 2) MUON_SMALL_STEP(2, 3) MUON_SMALL_STEP(2, 4)
-      MUON_SMALL_STEP(3, 3) MUON_SMALL_STEP(3, 4)
-      MUON_SMALL_STEP(4, 4)
-      default:
-        return MUON_ERR_SHAPE;  // not reached: rows <= cols <= 128
+    if (bf16) {
+      switch (bs * 8 + bl) {
+        MUON_SMALL_STEP(__bf16, 1, 1) MUON_SMALL_STEP(__bf16, 1, 2) MUON_SMALL_STEP(__bf16, 1, 3)
+        MUON_SMALL_STEP(__bf16, 1, 4) MUON_SMALL_STEP(__bf16, 2, 2) MUON_SMALL_STEP(__bf16, 2, 3)
+        MUON_SMALL_STEP(__bf16, 2, 4) MUON_SMALL_STEP(__bf16, 3, 3) MUON_SMALL_STEP(__bf16, 3, 4)
+        MUON_SMALL_STEP(__bf16, 4, 4)
+        default:
+          return MUON_ERR_SHAPE;  // not reached: rows <= cols <= 128
+      }
+    } else {
+      switch (bs * 8 + bl) {
+        MUON_SMALL_STEP(float, 1, 1) MUON_SMALL_STEP(float, 1, 2) MUON_SMALL_STEP(float, 1, 3)
+        MUON_SMALL_STEP(float, 1, 4) MUON_SMALL_STEP(float, 2, 2) MUON_SMALL_STEP(float, 2, 3)
+        MUON_SMALL_STEP(float, 2, 4)
+        default:
+          return MUON_ERR_SHAPE;  // not reached: rows <= 64, rows <= cols <= 128
+      }
     }
 #undef MUON_SMALL_STEP
     tr.after_ns(MUON_KERNEL_NS_SMALL, c);

@@ -216,47 +216,56 @@ def test_step_single_fp32_matrix_workload(gpu_lib, prec):
 
 
 # Every block-count variant of the one-launch small step (rows and columns
-# in 32-blocks: 1 <= BS <= BL <= 4), NS only, bf16 products, two units each.
+# in 32-blocks: 1 <= BS <= BL <= 4 with bf16 products, BS <= 2 with fp32
+# ones; fp32 units of more than 64 rows take the tiled products), NS only,
+# two units each.
 ONE_BLOCK_NS = [(31, 32), (20, 50), (10, 90), (1, 100), (33, 64), (40, 70), (64, 128), (70, 90),
                 (65, 128), (100, 128)]
 
 
+@pytest.mark.parametrize("prec", ["bf16", "fp32"])
 @pytest.mark.parametrize("shape", ONE_BLOCK_NS, ids=[f"{r}x{c}" for r, c in ONE_BLOCK_NS])
-def test_ns_one_block_variants(gpu_lib, shape):
-    say(f"[ns one-block] shape={shape}")
+def test_ns_one_block_variants(gpu_lib, shape, prec):
+    say(f"[ns one-block] shape={shape} prec={prec}")
     x = _seeded((2, *shape), 3300 + shape[0] * 131 + shape[1])
-    outs, _ = gpu_lib.newton_schulz([x], hyper=gpu_lib.Hyper())
+    outs, _ = gpu_lib.newton_schulz([x], hyper=gpu_lib.Hyper(ns_precision=prec))
     torch.cuda.synchronize()
     worst = max(rel(f64(outs[0][i]), oracle.newton_schulz(f64(x[i]))) for i in range(2))
     say(f"   worst rel err {worst:.3e}")
-    assert worst <= TOL_NS["bf16"]
+    assert worst <= TOL_NS[prec]
 
 
 # Units whose wide form fits one 128 x 128 block take the one-launch step
 # (momentum, norm, on-chip Newton-Schulz and update in one workgroup per
-# unit) with bf16 products: 32-row heads, an odd width (the scalar loads and
-# stores), a single row, fp32 and bf16 gradients, both look-ahead styles,
-# and a unit whose gradient stays zero (pure decay).
+# unit): 32-row heads, an odd width (the scalar loads and stores), a single
+# row, fp32 and bf16 gradients, both look-ahead styles, and a unit whose
+# gradient stays zero (pure decay); bf16 products, and fp32 ones where the
+# units have at most 64 rows.
 ONE_BLOCK = [
-    ((3, 96, 128), 32, "bf16", "sgd"),
-    ((5, 100, 125), 0, "fp32", "sgd"),
-    ((2, 1, 7), 0, "fp32", "ema"),
-    ((4, 64, 128), 0, "bf16", "ema"),
+    ((3, 96, 128), 32, "bf16", "sgd", "bf16"),
+    ((5, 100, 125), 0, "fp32", "sgd", "bf16"),
+    ((2, 1, 7), 0, "fp32", "ema", "bf16"),
+    ((4, 64, 128), 0, "bf16", "ema", "bf16"),
+    ((3, 96, 128), 32, "bf16", "sgd", "fp32"),
+    ((5, 60, 125), 0, "fp32", "sgd", "fp32"),
+    ((4, 64, 128), 0, "bf16", "ema", "fp32"),
 ]
 
 
-@pytest.mark.parametrize("case", range(len(ONE_BLOCK)), ids=["heads", "odd-width", "one-row", "ema-zero-unit"])
+@pytest.mark.parametrize("case", range(len(ONE_BLOCK)),
+                         ids=["heads", "odd-width", "one-row", "ema-zero-unit", "heads-fp32",
+                              "odd-width-fp32", "ema-zero-unit-fp32"])
 def test_step_one_block_units(gpu_lib, case):
-    shape, split, gdt, style = ONE_BLOCK[case]
-    say(f"[step one-block] shape={shape} split={split} grads={gdt} style={style}")
+    shape, split, gdt, style, prec = ONE_BLOCK[case]
+    say(f"[step one-block] shape={shape} split={split} grads={gdt} style={style} ns={prec}")
     w0 = _seeded(shape, 61 + case, 0.02)
     grads = []
     for t in range(3):
         g = _seeded(shape, 610 + 10 * case + t, 1e-3)
-        if case == 3:
+        if shape == (4, 64, 128):
             g[1].zero_()
         grads.append(g.to(torch.bfloat16) if gdt == "bf16" else g)
-    h = gpu_lib.Hyper(ns_precision="bf16", nesterov_style=style)
+    h = gpu_lib.Hyper(ns_precision=prec, nesterov_style=style)
     res = _run_steps(gpu_lib, w0, grads, h, split_rows=split)
     w0_64 = f64(w0)
     rows = split or shape[1]
@@ -265,9 +274,9 @@ def test_step_one_block_units(gpu_lib, case):
         for b in range(shape[0]):
             for hd in range(shape[1] // rows):
                 blk = slice(hd * rows, (hd + 1) * rows)
-                check_weight(wg[b, blk], wr[b, blk], w0_64[b, blk], t, h, TOL_NS["bf16"],
+                check_weight(wg[b, blk], wr[b, blk], w0_64[b, blk], t, h, TOL_NS[prec],
                              f"step {t} matrix {b} head {hd}")
-    if case == 3:
+    if shape == (4, 64, 128):
         assert torch.count_nonzero(torch.from_numpy(res[-1][1][1])).item() == 0
 
 

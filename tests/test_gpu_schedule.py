@@ -94,15 +94,17 @@ def test_persistent_trace_brackets_one_launch_per_pass(gpu_lib):
     assert n == 1 and tr.info() == [(4 * 256 * 300, 6 * 4 * 256 * 300, 4, 0)]
 
 
-def test_one_block_units_take_one_launch(gpu_lib):
-    # Wide units of at most 128 x 128 (bf16 products): the whole step is one
-    # launch of the small-unit kernel, with no momentum or norm launches.
-    print("[schedule one-block]", flush=True)
+@pytest.mark.parametrize("prec", ["bf16", "fp32"])
+def test_one_block_units_take_one_launch(gpu_lib, prec):
+    # Wide units of at most 128 x 128 (at most 64 rows with fp32 products):
+    # the whole step is one launch of the small-unit kernel, with no
+    # momentum or norm launches.
+    print(f"[schedule one-block] prec={prec}", flush=True)
     g = torch.Generator(device="cpu").manual_seed(12)
     w = (torch.randn((3, 64, 128), generator=g) * 0.02).to(DEV)
     gr = (torch.randn((3, 64, 128), generator=g) * 1e-3).to(DEV)
     m = torch.zeros_like(w)
-    h = gpu_lib.Hyper()
+    h = gpu_lib.Hyper(ns_precision=prec)
     counts = {}
     for kind in (gpu_lib.KERNEL_MOMENTUM, gpu_lib.KERNEL_NORMALIZE, gpu_lib.KERNEL_NS_SMALL):
         tr = gpu_lib.Trace(kind, 2)
