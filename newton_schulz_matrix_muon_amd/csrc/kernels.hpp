@@ -714,6 +714,56 @@ __device__ __forceinline__ void lds_barrier() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
+// The XCC (accelerator die, with its own L2) the workgroup runs on.
+__device__ __forceinline__ int xcc_id() {
+  return __builtin_amdgcn_readfirstlane(__builtin_amdgcn_s_getreg((3 << 11) | 20)) & 15;
+}
+
+// Atomic add of v at the wave-uniform address p, made by lane 0 alone: the
+// execution mask is narrowed to lane 0 for that one instruction, so the
+// wave makes exactly one request to the L2.  Left to the compiler, a
+// wave's atomic is either rewritten into one atomic of the lanes' sum or
+// issued by all 64 lanes (63 of them adding 0), and which of the two it
+// does changed with unrelated edits elsewhere in the kernel; 64-lane
+// atomics on the one queue line made the whole schedule about five times
+// slower.  The leading s_nop covers an address the compiler has just
+// moved into scalar registers from a vector one, the trailing one the
+// execution-mask write the compiler does not see (an instruction that
+// reads the mask through DPP must not follow it at once).  The returning
+// form waits for its result (and so for every older vector-memory access
+// of the wave) and gives every lane the old value; the other form does not
+// wait.  Both are called in wave-uniform code with every lane active: lane
+// 0 must hold v and the zero offset when the mask is narrowed.
+__device__ __forceinline__ uint32_t lane0_atomic_add(uint32_t* p, uint32_t v) {
+  uint32_t old;
+  uint64_t saved;
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b64 %[sv], exec\n\t"
+      "s_mov_b64 exec, 1\n\t"
+      "global_atomic_add %[old], %[zero], %[v], %[base] sc0\n\t"
+      "s_waitcnt vmcnt(0)\n\t"
+      "s_mov_b64 exec, %[sv]\n\t"
+      "s_nop 4"
+      : [old] "=&v"(old), [sv] "=&s"(saved)
+      : [zero] "v"(0u), [v] "v"(v), [base] "s"(p)
+      : "memory");
+  return __builtin_amdgcn_readfirstlane(old);
+}
+__device__ __forceinline__ void lane0_atomic_add_noret(uint32_t* p, uint32_t v) {
+  uint64_t saved;
+  asm volatile(
+      "s_nop 4\n\t"
+      "s_mov_b64 %[sv], exec\n\t"
+      "s_mov_b64 exec, 1\n\t"
+      "global_atomic_add %[zero], %[v], %[base]\n\t"
+      "s_mov_b64 exec, %[sv]\n\t"
+      "s_nop 4"
+      : [sv] "=&s"(saved)
+      : [zero] "v"(0u), [v] "v"(v), [base] "s"(p)
+      : "memory");
+}
+
 // LDS of the GEMM tile: a ring of kSlots half-stages, each TILE rows of
 // one operand x 128 bytes of K (160 KB at TILE 256).  Declared once per tile
 // size, so a kernel that runs several tile phases holds a single ring; the
@@ -1272,9 +1322,20 @@ struct NsSmallArgs {
   int32_t final_mode;     // FINAL_STEP or FINAL_NSOUT
   const float* inv_nu;    // per unit: first-iteration scale (k_norm_finish)
   const int32_t* flag;    // per unit: nonzero norm
+  // Split units (k_ns_small with groups > 1): each unit's column blocks are
+  // shared by `groups` workgroups that sum their partial Grams through
+  // memory once per iteration.
+  int32_t groups;
+  int32_t cnt_stride;     // words between the units' counters
+  float* part;            // per unit: 2 x groups partial Grams of 128 x 128
+  uint32_t* cnt;          // per unit: partial Grams published (cleared per call)
+  uint32_t* err;          // the call's stop flag
+  uint64_t timeout_ticks; // bound of one wait for the other workgroups
 };
 
 constexpr int kSmall = 128;  // padded rows (= Gram size) of the small path
+constexpr int kSplitMax = 8;         // workgroups per split unit, at most
+constexpr int kSplitWgMax = 256;     // workgroups of one split launch, at most
 
 // Element (row, k) of a bf16 operand with 128-element rows in LDS: 16 chunks
 // of 8 per row, the chunk index XOR-ed with a permutation of the row's low
@@ -1340,21 +1401,39 @@ __device__ __forceinline__ void sb_put(uint16_t* L, const float (&v)[16], int r0
 // or 1 for a unit it rescaled): the first Gram is scaled by s^2 and the first
 // X' by s.  Roundings as on the tiled bf16 path: bf16 operands, fp32
 // accumulation, the iterate held in bf16.
+//
+// A few long units (fewer than the CUs can keep busy) are split: workgroup
+// g of a unit's `groups` takes column blocks [g nb / groups, (g + 1) nb /
+// groups), and the Gram of the whole iterate is the sum of the groups'
+// partial Grams.  Each workgroup publishes its partial (fp32, in its waves'
+// accumulator layout) and a count, waits until every group of the unit has
+// counted (bounded by a wall-clock limit, after which it reports through
+// `err` and stops), and sums the partials in group order, so every
+// workgroup of the unit holds the same A.  Partials alternate between two
+// buffers: a group writes phase k + 1's partial only after every group has
+// counted phase k, which each does after reading phase k - 1's.  The launch
+// has at most as many workgroups as the CUs, one per CU, so all groups of a
+// unit run at once.
 __global__ __launch_bounds__(kThreads) void k_ns_small(NsSmallArgs p, ChunkArgs ca) {
   __shared__ __attribute__((aligned(16))) uint16_t LS[2][kSmall * kSmall];  // X_j, row-major
   __shared__ __attribute__((aligned(16))) uint16_t LR[kSmall * kSmall];     // A, B', then X'_j
-  const int u = blockIdx.x;
+  __shared__ int s_go;
+  const int G = p.groups;
+  const int u = blockIdx.x / G;
+  const int g = blockIdx.x - u * G;
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   const int wm = w >> 1, wn = w & 1;
   const int m = lane & 31, half = lane >> 5;
   const int nb = p.ldx / kSmall;
+  const int j0 = g * nb / G, j1 = (g + 1) * nb / G;  // this workgroup's column blocks
 
   const SegView sg = find_seg(ca, u);
   float* const wout = sg.w + (int64_t)(u - sg.first) * ca.unit_elems;
   if (!p.flag[u]) {
     // Zero unit: O' = 0, so the weight only decays / the output is zero.
-    for (int64_t e = threadIdx.x; e < ca.unit_elems; e += kThreads)
+    const int64_t e0 = ca.unit_elems * g / G, e1 = ca.unit_elems * (g + 1) / G;
+    for (int64_t e = e0 + threadIdx.x; e < e1; e += kThreads)
       wout[e] = (p.final_mode == FINAL_STEP) ? wout[e] * ca.decay : 0.0f;
     return;
   }
@@ -1403,16 +1482,98 @@ __global__ __launch_bounds__(kThreads) void k_ns_small(NsSmallArgs p, ChunkArgs 
   };
 
   f32x16 accA[2][2], accC[2][2];
+  // Split units: publish this group's partial Gram of phase `ph` (accA),
+  // wait for the unit's other groups, and replace accA by the sum of all
+  // partials.  False when the wait gave up (the launch stops).
+  uint32_t* const cnt = p.cnt ? p.cnt + (int64_t)u * p.cnt_stride : nullptr;
+  auto reduce = [&](int ph) -> bool {
+    float* const base = p.part + ((int64_t)u * 2 + (ph & 1)) * G * (kSmall * kSmall);
+    float* const mine = base + (int64_t)g * (kSmall * kSmall);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mine[((w * 4 + i * 2 + jj) * 16 + r) * 64 + lane] = accA[i][jj][r];
+    __syncthreads();  // every wave's stores are complete
+    if (w == 0) {
+      // The unit's other groups may run on other XCCs: write this L2 back
+      // before the count.
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+      wait_vmcnt<0>();
+      lane0_atomic_add_noret(cnt, 1u);
+      const uint32_t need = (uint32_t)(G * (ph + 1));
+      int go = 1;
+      const uint64_t t0 = wall_clock64();
+      for (;;) {
+        const uint32_t c = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(cnt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        if (c >= need) break;
+        const uint32_t e = __builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(p.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        if (e != 0u || wall_clock64() - t0 > p.timeout_ticks) {
+          __hip_atomic_store(p.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          go = 0;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
+      if (go) {
+        // drop this CU's L1 and this L2's copies of other XCCs' lines (one
+        // acquire for every wave of the workgroup)
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        wait_vmcnt<0>();
+      }
+      s_go = go;
+    }
+    __syncthreads();
+    if (__builtin_amdgcn_readfirstlane(s_go) == 0) return false;
+    // Sum the partials element-wise in group order into LDS (the two X
+    // slots, free between passes: 64 KB), each thread 16 float4 positions
+    // with every group's load in flight at once, then read this wave's
+    // quadrant back.
+    float4* const S = reinterpret_cast<float4*>(&LS[0][0]);
+    const float4* const P = reinterpret_cast<const float4*>(base);
+    constexpr int kQ = kSmall * kSmall / 4;  // float4 per partial
+#pragma unroll 2
+    for (int k = 0; k < kQ / kThreads; ++k) {
+      const int idx = threadIdx.x + kThreads * k;
+      float4 v[kSplitMax];
+#pragma unroll
+      for (int q = 0; q < kSplitMax; ++q) v[q] = P[(int64_t)(q < G ? q : 0) * kQ + idx];
+      float4 t = v[0];
+#pragma unroll
+      for (int q = 1; q < kSplitMax; ++q)
+        if (q < G) {
+          t.x += v[q].x;
+          t.y += v[q].y;
+          t.z += v[q].z;
+          t.w += v[q].w;
+        }
+      S[idx] = t;
+    }
+    lds_barrier();
+    const float* const Sf = reinterpret_cast<const float*>(S);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) accA[i][jj][r] = Sf[((w * 4 + i * 2 + jj) * 16 + r) * 64 + lane];
+    return true;
+  };
+
   const uint16_t* const X0 = p.xb[0] + (int64_t)u * p.x_stride;
   // Gram of the entry iterate, scaled by s^2.
   zero(accA);
-  fetch(X0, 0);
-  for (int j = 0; j < nb; ++j) {
+  fetch(X0, j0);
+  for (int j = j0; j < j1; ++j) {
     stage(LS[j & 1]);
-    if (j + 1 < nb) fetch(X0, j + 1);
+    if (j + 1 < j1) fetch(X0, j + 1);
     lds_barrier();  // block j staged; every wave is done with block j - 1
     gram(LS[j & 1], accA);
   }
+  if (G > 1 && !reduce(0)) return;
   {
     const float s2 = s0 * s0;
 #pragma unroll
@@ -1451,7 +1612,7 @@ __global__ __launch_bounds__(kThreads) void k_ns_small(NsSmallArgs p, ChunkArgs 
     // iteration's stores of X (the barrier's fence drains them) are visible
     // to the whole workgroup before it reads X.
     __syncthreads();
-    fetch(X, 0);
+    fetch(X, j0);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -1482,9 +1643,9 @@ __global__ __launch_bounds__(kThreads) void k_ns_small(NsSmallArgs p, ChunkArgs 
       for (int kk = 0; kk < kSmall / 16; ++kk) bfr[i][kk] = sb_rows(LR, wm * 64 + i * 32, kk, lane);
 
     zero(accA);
-    for (int j = 0; j < nb; ++j) {
+    for (int j = j0; j < j1; ++j) {
       stage(LS[j & 1]);
-      if (j + 1 < nb) fetch(X, j + 1);
+      if (j + 1 < j1) fetch(X, j + 1);
       lds_barrier();  // block j staged; every wave is done with LR and block j - 1
       // X'_j = a*X_j + B'*X_j over this wave's quadrant.
       zero(accC);
@@ -1554,6 +1715,7 @@ __global__ __launch_bounds__(kThreads) void k_ns_small(NsSmallArgs p, ChunkArgs 
       }
       gram(LR, accA);
     }
+    if (!last && G > 1 && !reduce(it + 1)) return;
   }
 }
 
@@ -1904,56 +2066,6 @@ struct NsSched {
   uint32_t* err;                  // set when a wait timed out
   uint64_t timeout_ticks;         // wall-clock ticks
 };
-
-// The XCC (accelerator die, with its own L2) the workgroup runs on.
-__device__ __forceinline__ int xcc_id() {
-  return __builtin_amdgcn_readfirstlane(__builtin_amdgcn_s_getreg((3 << 11) | 20)) & 15;
-}
-
-// Atomic add of v at the wave-uniform address p, made by lane 0 alone: the
-// execution mask is narrowed to lane 0 for that one instruction, so the
-// wave makes exactly one request to the L2.  Left to the compiler, a
-// wave's atomic is either rewritten into one atomic of the lanes' sum or
-// issued by all 64 lanes (63 of them adding 0), and which of the two it
-// does changed with unrelated edits elsewhere in the kernel; 64-lane
-// atomics on the one queue line made the whole schedule about five times
-// slower.  The leading s_nop covers an address the compiler has just
-// moved into scalar registers from a vector one, the trailing one the
-// execution-mask write the compiler does not see (an instruction that
-// reads the mask through DPP must not follow it at once).  The returning
-// form waits for its result (and so for every older vector-memory access
-// of the wave) and gives every lane the old value; the other form does not
-// wait.  Both are called in wave-uniform code with every lane active: lane
-// 0 must hold v and the zero offset when the mask is narrowed.
-__device__ __forceinline__ uint32_t lane0_atomic_add(uint32_t* p, uint32_t v) {
-  uint32_t old;
-  uint64_t saved;
-  asm volatile(
-      "s_nop 4\n\t"
-      "s_mov_b64 %[sv], exec\n\t"
-      "s_mov_b64 exec, 1\n\t"
-      "global_atomic_add %[old], %[zero], %[v], %[base] sc0\n\t"
-      "s_waitcnt vmcnt(0)\n\t"
-      "s_mov_b64 exec, %[sv]\n\t"
-      "s_nop 4"
-      : [old] "=&v"(old), [sv] "=&s"(saved)
-      : [zero] "v"(0u), [v] "v"(v), [base] "s"(p)
-      : "memory");
-  return __builtin_amdgcn_readfirstlane(old);
-}
-__device__ __forceinline__ void lane0_atomic_add_noret(uint32_t* p, uint32_t v) {
-  uint64_t saved;
-  asm volatile(
-      "s_nop 4\n\t"
-      "s_mov_b64 %[sv], exec\n\t"
-      "s_mov_b64 exec, 1\n\t"
-      "global_atomic_add %[zero], %[v], %[base]\n\t"
-      "s_mov_b64 exec, %[sv]\n\t"
-      "s_nop 4"
-      : [sv] "=&s"(saved)
-      : [zero] "v"(0u), [v] "v"(v), [base] "s"(p)
-      : "memory");
-}
 
 // KMODE: 0 = every operand row-major (fp32 path: X^T is kept); 1 = wide
 // bf16 units, B'*X reads X K-major; 2 = tall bf16 units, X^T X reads X

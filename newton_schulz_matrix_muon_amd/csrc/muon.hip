@@ -77,7 +77,7 @@ struct Chunk {
 
 // Workspace carve-up of one chunk (byte offsets).
 struct Layout {
-  size_t x32[2], xb[2], xt[2], a32, ab, bop, partials, inv_nu, flag, done, queue, total;
+  size_t x32[2], xb[2], xt[2], a32, ab, bop, partials, inv_nu, flag, done, queue, split, total;
 };
 
 constexpr size_t kHeader = 256;  // status header at the start of the workspace
@@ -111,6 +111,17 @@ bool unit_small_possible(int64_t rows_u, int64_t cols, const muon_hyper* h) {
   return h->ns_precision == MUON_NS_BF16 || (rows_u <= 64 && cols <= kSmall);
 }
 
+// Long small units (more than eight 128-column blocks) too few to fill the
+// GPU one workgroup each are split over several workgroups (at most
+// kSplitMax per unit, kSplitWgMax per launch): the largest split a chunk may
+// take, 1 if none.
+int split_groups_max(const Chunk& c, const muon_hyper* h) {
+  if (!small_possible(c, h) || h->ns_precision != MUON_NS_BF16) return 1;
+  const int64_t nb = c.cols_pad / kSmall;
+  if (nb <= 8 || 2 * c.n_units >= kSplitWgMax) return 1;
+  return (int)std::max<int64_t>(1, std::min<int64_t>({nb, (int64_t)kSplitMax, kSplitWgMax / c.n_units}));
+}
+
 // Words of persistent-schedule completion counts per unit: three per tile
 // panel on the small side.
 int64_t done_words(const Chunk& c) { return 3 * (c.s_pad / c.tile); }
@@ -123,10 +134,8 @@ Layout layout_of(const Chunk& c, const muon_hyper* h) {
   const size_t ss = (size_t)(c.s_pad * c.s_pad);
   size_t off = kHeader;
   auto take = [&](size_t bytes) { size_t o = off; off = align_up(off + bytes, kAlign); return o; };
-  // fp32 iterates: N (and X0) in the first, on the fp32 path and for the
-  // small-unit kernel; the second only on the fp32 path (the bf16 path keeps
-  // the iterate in bf16, and its tiled products start from N written
-  // straight into it).
+  // fp32 iterates, fp32 path only (the bf16 path keeps the iterate in bf16,
+  // and its products start from N written straight into it).
   if (!bf16) L.x32[0] = take(U * xs * 4);
   if (!bf16) L.x32[1] = take(U * xs * 4);
   if (bf16) {
@@ -152,6 +161,9 @@ Layout layout_of(const Chunk& c, const muon_hyper* h) {
   // of the three products
   L.done = take(U * done_words(c) * 4);
   L.queue = take(4 * (kMaxQueues + 1));  // persistent schedule: claim counters, leavers
+  // split small units: two buffers of partial Grams per group
+  const int gmax = split_groups_max(c, h);
+  if (gmax > 1) L.split = take(U * 2 * (size_t)gmax * kSmall * kSmall * 4);
   L.total = off;
   return L;
 }
@@ -517,7 +529,7 @@ void launch_phase(bool bf16, int tile, int km, const GemmArgs& g, const ChunkArg
 int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs,
               const void* const* ins, float* const* moms, const muon_matrix_desc* mats,
               unsigned char* ws, hipStream_t s, Tracer& tr, bool first_chunk,
-              bool allow_persistent) {
+              bool allow_waits) {
   const bool bf16 = h->ns_precision == MUON_NS_BF16;
   const Layout L = layout_of(c, h);
   ChunkArgs ca;
@@ -570,11 +582,22 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
   // blocks) or when the units number at least half the CUs; a few long
   // units go to the tiled products, which spread each unit over many CUs.
   bool small = small_possible(c, h);
+  int groups = 1;            // workgroups per unit on the on-chip path
+  uint64_t wait_ticks = 0;
   if (small && c.cols_pad / kSmall > 8) {
     DeviceInfo di;
     const int dst = device_info(&di);
     if (dst != MUON_OK) return dst;
-    small = 2 * U >= di.cus;
+    if (2 * U < di.cus) {
+      // Too few to fill the GPU one workgroup each: split each unit over
+      // several (their groups wait on each other, so only where waits are
+      // allowed and every workgroup of the launch gets a CU of its own),
+      // else the tiled products.
+      const int gmax = split_groups_max(c, h);
+      groups = std::min(gmax, di.cus / U);
+      small = allow_waits && groups > 1;
+      wait_ticks = wait_limit_ticks(di.wall_khz);
+    }
   }
   const int gk = !step ? 2 : (c.gdtype == MUON_DTYPE_BF16 ? 0 : 1);
   auto small_args = [&]() {
@@ -597,6 +620,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
     p.final_mode = step ? FINAL_STEP : FINAL_NSOUT;
     p.inv_nu = reinterpret_cast<float*>(ws + L.inv_nu);
     p.flag = reinterpret_cast<int32_t*>(ws + L.flag);
+    p.groups = 1;
     return p;
   };
   // Units of one 128 x 128 block: the whole step in one launch, over the
@@ -683,10 +707,18 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
                      first_chunk ? err : nullptr, nb,
                      (int64_t)(c.rows_pad * c.cols_pad));
   if (small) {
-    const NsSmallArgs p = small_args();
+    NsSmallArgs p = small_args();
+    if (groups > 1) {
+      p.groups = groups;
+      p.cnt = done;
+      p.cnt_stride = (int32_t)done_words(c);
+      p.part = reinterpret_cast<float*>(ws + L.split);
+      p.err = err;
+      p.timeout_ticks = wait_ticks;
+    }
     tr.after(MUON_KERNEL_NORMALIZE, c.n_units);
     tr.before(MUON_KERNEL_NS_SMALL);
-    hipLaunchKernelGGL(k_ns_small, dim3(U), dim3(kThreads), 0, s, p, ca);
+    hipLaunchKernelGGL(k_ns_small, dim3(U * groups), dim3(kThreads), 0, s, p, ca);
     tr.after_ns(MUON_KERNEL_NS_SMALL, c);
     return hipGetLastError() == hipSuccess ? MUON_OK : MUON_ERR_HIP;
   }
@@ -718,7 +750,7 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
   const int64_t n_items = (int64_t)total * U * (2 * tg + ta);
   // AUTO: persistent for 256-tile passes; 128-tile passes (short K) run
   // faster as separate launches than as claimed tiles.
-  const bool persistent = allow_persistent && (h->schedule == MUON_SCHEDULE_PERSISTENT ||
+  const bool persistent = allow_waits && (h->schedule == MUON_SCHEDULE_PERSISTENT ||
                                                (h->schedule == MUON_SCHEDULE_AUTO && T == 256));
   if (persistent && n_items < INT32_MAX / 2) {
     DeviceInfo di;

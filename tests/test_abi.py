@@ -81,10 +81,17 @@ def test_bf16_workspace_holds_only_bf16_iterates():
     # The bf16 paths (tiled and on chip) fold 1/||N|| into the first
     # iteration, so no fp32 copy of N exists: two bf16 iterates (2 x 2 bytes
     # per element of the 128 x 4096 iterate) plus two 128 x 128 bf16
-    # matrices per unit, under any schedule.
+    # matrices per unit, under any schedule.  Under AUTO, 48 such units (too
+    # few to fill 256 CUs) may be split over min(32 blocks, 8, 256 / 48) = 5
+    # workgroups each, with two buffers of fp32 128 x 128 partial Grams per
+    # workgroup.
     per_unit = 128 * 4096 * 4 + 2 * 128 * 128 * 2
+    split = 2 * 5 * 128 * 128 * 4
     st, n = ws_size([(48, 128, 4096, 0)])
-    assert st == 0 and 48 * per_unit <= n < 48 * per_unit + (1 << 20)
+    assert st == 0 and 48 * (per_unit + split) <= n < 48 * (per_unit + split) + (1 << 20)
+    # 128 such units fill the CUs one workgroup each: no partials
+    st, n128 = ws_size([(128, 128, 4096, 0)])
+    assert st == 0 and 128 * per_unit <= n128 < 128 * per_unit + (1 << 20)
     h = muon.default_hyper_c()
     h.schedule = muon.SCHEDULE_PERSISTENT
     st, nt = ws_size([(48, 128, 4096, 0)], h)

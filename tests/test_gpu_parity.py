@@ -58,8 +58,9 @@ def test_ns_only_matches_oracle(gpu_lib, shape, prec):
 
 
 # Wide units of at most 128 rows and more than eight 128-column blocks: the
-# default schedule runs a few of them as tiled products and many of them
-# (at least half the CUs) on chip; the forced schedules always tile.
+# default schedule runs many of them (at least half the CUs) on chip one
+# workgroup each and a few of them on chip split over several workgroups
+# (partial Grams summed through memory); the forced schedules always tile.
 @pytest.mark.parametrize("sched", ["auto", "persistent", "launches"])
 @pytest.mark.parametrize("batch,rows,cols", [(12, 128, 1100), (160, 96, 1100)],
                          ids=["few-long", "many-long"])

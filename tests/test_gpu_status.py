@@ -74,3 +74,28 @@ def test_stop_report_kept_through_a_one_launch_call(gpu_lib, monkeypatch):
         gpu_lib.workspace_status(ws)
     assert e.value.status == -9
     gpu_lib.newton_schulz([small], [out_s], hyper=hs, ws=ws, check=True)
+
+
+def test_split_unit_stop_is_reported_and_the_next_call_is_clean(gpu_lib, monkeypatch):
+    # 12 wide 128 x 4096 units are split over 8 workgroups each, which wait
+    # for each other's partial Grams once per iteration.  With a zero wait
+    # limit the first group to publish gives up at once (the other seven are
+    # still in their column blocks): the call reports the stop, and the
+    # counters it left do not disturb the next call, which matches a clean
+    # run bit for bit.
+    print("[status] split units, zero wait limit", flush=True)
+    g = torch.Generator(device="cpu").manual_seed(8)
+    x = torch.randn((12, 128, 4096), generator=g).to(DEV)
+    h = gpu_lib.Hyper()
+    ws = gpu_lib.workspace(gpu_lib.workspace_size([x], h), torch.device(DEV))
+    ref, out = torch.empty_like(x), torch.empty_like(x)
+    gpu_lib.newton_schulz([x], [ref], hyper=h, ws=ws, check=True)
+    monkeypatch.setenv("MUON_WAIT_LIMIT_US", "0")
+    gpu_lib.newton_schulz([x], [out], hyper=h, ws=ws, check=False)
+    monkeypatch.delenv("MUON_WAIT_LIMIT_US")
+    with pytest.raises(gpu_lib.MuonError) as e:
+        gpu_lib.workspace_status(ws)
+    assert e.value.status == -9
+    gpu_lib.newton_schulz([x], [out], hyper=h, ws=ws, check=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
