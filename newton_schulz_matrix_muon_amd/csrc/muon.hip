@@ -748,10 +748,14 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
   const int tg = (int)((sp / T) * (sp / T + 1) / 2);
   const int ta = (int)((c.rows_pad / T) * (c.cols_pad / T));
   const int64_t n_items = (int64_t)total * U * (2 * tg + ta);
-  // AUTO: persistent for 256-tile passes; 128-tile passes (short K) run
-  // faster as separate launches than as claimed tiles.
+  // AUTO: persistent for 256-tile passes of two units or more.  128-tile
+  // passes (short K) run faster as separate launches than as claimed
+  // tiles, and so does a pass of one unit, whose phases cannot overlap
+  // another unit's and whose single claim queue publishes every tile
+  // through memory (one 4096 x 4096 unit: 3.1 ms as launches, 3.6-3.9 ms
+  // persistent; two units: 6.4 ms against 5.4 ms).
   const bool persistent = allow_waits && (h->schedule == MUON_SCHEDULE_PERSISTENT ||
-                                               (h->schedule == MUON_SCHEDULE_AUTO && T == 256));
+                                          (h->schedule == MUON_SCHEDULE_AUTO && T == 256 && U >= 2));
   if (persistent && n_items < INT32_MAX / 2) {
     DeviceInfo di;
     const int dst = device_info(&di);
