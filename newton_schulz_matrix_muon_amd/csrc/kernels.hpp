@@ -435,7 +435,7 @@ __device__ __forceinline__ void status_fold(uint32_t* err) {
   err[0] = 0u;
 }
 
-// One workgroup per unit: fixed-order sum of the partials (first wave).
+// One workgroup per unit: fixed-order sum of the partials.
 // It also clears the persistent schedule's counts of the unit and claim
 // counter (when given), and, on the first pass of a call (err given), moves
 // the previous call's stop flag into the sticky word and clears it.  With nb (the
@@ -454,12 +454,15 @@ __global__ __launch_bounds__(kThreads) void k_norm_finish(const double* __restri
                                                           uint16_t* __restrict__ nb,
                                                           int64_t x_stride) {
   __shared__ double total;
+  __shared__ double sh[kThreads / 64];
   const int u = blockIdx.x;
-  if (threadIdx.x < 64) {
+  {
+    // every thread a strided share (a long unit has thousands of partials),
+    // then the fixed-order block sum
     double s = 0.0;
-    for (int i = threadIdx.x; i < blocks_per_unit; i += 64)
+    for (int i = threadIdx.x; i < blocks_per_unit; i += kThreads)
       s += partials[(int64_t)u * blocks_per_unit + i];
-    s = wave_sum(s);
+    s = block_sum(s, sh);
     if (threadIdx.x == 0) total = s;
   }
   __syncthreads();
