@@ -67,9 +67,11 @@ typedef enum {
   MUON_ERR_HYPER = -6,     /* invalid hyper-parameters (non-finite, bad stage table) */
   MUON_ERR_HIP = -7,       /* a HIP call failed; outputs are undefined */
   MUON_ERR_ALIAS = -8,     /* overlapping input/output buffers where not allowed */
-  MUON_ERR_SCHEDULE = -9   /* a persistent NS launch stopped: a dependency wait ran
-                              out of time (reported only by muon_workspace_status,
-                              never by the step calls); outputs are undefined */
+  MUON_ERR_SCHEDULE = -9   /* an NS launch whose workgroups wait on each other
+                              (persistent, or small units split on chip) stopped:
+                              a wait ran out of time (reported only by
+                              muon_workspace_status, never by the step calls);
+                              outputs are undefined */
 } muon_status;
 
 typedef enum { MUON_DTYPE_F32 = 0, MUON_DTYPE_BF16 = 1 } muon_dtype;
@@ -96,13 +98,22 @@ typedef enum { MUON_NS_FP32 = 0, MUON_NS_BF16 = 1 } muon_ns_precision;
  *   of wall clock); if one ever runs out the launch stops and
  *   muon_workspace_status reports MUON_ERR_SCHEDULE.
  * LAUNCHES: one launch per product and iteration, in stream order.
- * AUTO (default): per pass, whichever is faster on the MI355X.  Wide units
- *   with at most 128 rows and bf16 products run their whole NS in one
- *   workgroup each (A and B on chip, one pass over X per iteration) when
- *   they span at most eight 128-column blocks or number at least half the
- *   CUs; other passes of units with min(rows, cols) < 256 use LAUNCHES,
- *   the rest PERSISTENT.  The on-chip path rounds like the tiled one except
- *   that b*A uses A's fp32 accumulator, so results agree to rounding. */
+ * AUTO (default): per pass, whichever is faster on the MI355X.
+ *   - Wide units (rows < cols) of at most 128 x 128 (fp32 products: at most
+ *     64 rows) take the whole step, momentum to update, in one launch of
+ *     one workgroup per unit.
+ *   - Other wide units of at most 128 rows with bf16 products run their NS
+ *     on chip (A and B' in the workgroup, one pass over X per iteration):
+ *     one workgroup per unit when the units span at most eight 128-column
+ *     blocks or number at least half the CUs, else each unit split over
+ *     several workgroups that sum their partial Grams through memory
+ *     (those waits are bounded like PERSISTENT's).
+ *   - Other passes of units with min(rows, cols) < 256, and passes of a
+ *     single unit, use LAUNCHES; the rest PERSISTENT.
+ *   The on-chip kernels round like the tiled products (bf16 operands, fp32
+ *   accumulation) but in another order (b*A from A's fp32 accumulator; the
+ *   one-launch step also adds a*X from the fp32 iterate), so results agree
+ *   with a forced schedule to rounding. */
 typedef enum {
   MUON_SCHEDULE_AUTO = 0,
   MUON_SCHEDULE_PERSISTENT = 1,
@@ -266,7 +277,8 @@ int muon_newton_schulz_batched_traced(const float* const* x_in, float* const* o_
 
 /* Waits for `stream`, then reports whether any call on this workspace since
  * the previous muon_workspace_status (or since the workspace's first call)
- * had a persistent NS launch stop early: MUON_OK, or MUON_ERR_SCHEDULE, after
+ * had an NS launch stop early (a persistent one, or small units split on
+ * chip, whose workgroups wait on each other): MUON_OK, or MUON_ERR_SCHEDULE, after
  * which the outputs of the calls in question are undefined.  The report is
  * sticky across calls and cleared by this function, so one check after a
  * series of steps covers all of them.  The step entry points return before

@@ -1131,7 +1131,7 @@ const char* muon_status_string(int status) {
     case MUON_ERR_HYPER: return "invalid hyper-parameters";
     case MUON_ERR_HIP: return "HIP launch failed";
     case MUON_ERR_ALIAS: return "input and output buffers overlap";
-    case MUON_ERR_SCHEDULE: return "a persistent NS launch stopped: a dependency wait ran out of time";
+    case MUON_ERR_SCHEDULE: return "an NS launch stopped: a wait on other workgroups ran out of time";
     default: return "unknown status";
   }
 }

@@ -263,8 +263,9 @@ def workspace(nbytes: int, device: torch.device, stream=None) -> torch.Tensor:
 
 def workspace_status(ws: torch.Tensor, stream=None) -> None:
     """Waits for the stream and raises MuonError(MUON_ERR_SCHEDULE) if any
-    call on `ws` since the previous check had a persistent NS launch stop
-    early (muon_workspace_status; the report is sticky until read)."""
+    call on `ws` since the previous check had an NS launch (persistent, or
+    small units split on chip) stop early (muon_workspace_status; the report
+    is sticky until read)."""
     st = LIB.muon_workspace_status(ctypes.c_void_p(ws.data_ptr()), ctypes.c_size_t(ws.numel()),
                                    ctypes.c_void_p(_stream_ptr(stream)))
     if st != MUON_OK:
@@ -362,11 +363,11 @@ def step(
     params/momenta: fp32 (rows, cols) or (batch, rows, cols) banks;
     grads: bf16 or fp32 of the same shapes; split_rows: per bank, 0 or the
     head size.  `trace` (a Trace) brackets every launch of one kernel
-    class.  `check` (default:
-    `check_default`) waits for the stream afterwards and raises MuonError if
-    a persistent NS launch stopped, in which case params and momenta are
-    undefined.  Returns the number of launches of the traced class (0
-    without a trace)."""
+    class.  `check` (default: `check_default`) waits for the stream
+    afterwards and raises MuonError if an NS launch whose workgroups wait on
+    each other stopped, in which case params and momenta are undefined.
+    Returns the number of launches of the traced class (0 without a
+    trace)."""
     hyper = hyper or Hyper()
     n = len(params)
     if not (len(grads) == len(momenta) == n):
