@@ -1273,16 +1273,49 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
   }
 }
 
-// Upper-triangle tile t (row by row: row r holds tiles (r, r..T-1)) of a
-// T x T tile grid.
-__device__ __forceinline__ void sym_tile(int t, int T, int& tm, int& tn) {
-  int r = 0;
-  while (t >= T - r) {
-    t -= T - r;
-    ++r;
+// Tile orders that keep the tiles claimed together on few operand panels
+// (32 CUs of an XCC run 32 consecutive tiles of a unit at once, and the L2
+// serves a panel's K-slice to every tile reading it at about the same time).
+// Upper triangle of a T x T grid in block rows of G tile rows: block row by
+// block row, inside one column by column (rows r0 .. min(c, r0 + G - 1) of
+// column c): 32 consecutive tiles read G row panels and about 32 / G column
+// panels.
+constexpr int kGroupRows = 8;
+__device__ __forceinline__ void sym_tile_grouped(int t, int T, int& tm, int& tn) {
+  int r0 = 0, h = min(kGroupRows, T);
+  for (;;) {
+    const int n = h * (h + 1) / 2 + h * (T - r0 - h);  // tiles of this block row
+    if (t < n) break;
+    t -= n;
+    r0 += h;
+    h = min(kGroupRows, T - r0);
   }
-  tm = r;
-  tn = r + t;
+  if (t < h * (h + 1) / 2) {  // the block row's own triangle: column c has c + 1 tiles
+    int c = 0;
+    while (t > c) {
+      t -= c + 1;
+      ++c;
+    }
+    tm = r0 + t;
+    tn = r0 + c;
+  } else {  // full columns of h tiles
+    t -= h * (h + 1) / 2;
+    const int c = t / h;
+    tm = r0 + (t - c * h);
+    tn = r0 + h + c;
+  }
+}
+
+// A full tiles_m x tiles_n grid in groups of kGroupRows tile rows, column by
+// column inside a group.
+__device__ __forceinline__ void grid_tile_grouped(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int per_group = kGroupRows * tiles_n;
+  const int g = t / per_group;
+  const int r0 = g * kGroupRows;
+  const int h = min(kGroupRows, tiles_m - r0);
+  const int w = t - g * per_group;
+  tn = w / h;
+  tm = r0 + (w - tn * h);
 }
 
 // One launch per product: workgroup -> (unit, tile), XCD-aware.
@@ -1293,12 +1326,10 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_gemm(GemmArgs g, Chun
   const int u = logical / tiles_per_unit;
   const int tt = logical - u * tiles_per_unit;
   int tm, tn;
-  if (g.sym) {
-    sym_tile(tt, g.tiles_m, tm, tn);
-  } else {
-    tm = tt / g.tiles_n;
-    tn = tt - tm * g.tiles_n;
-  }
+  if (g.sym)
+    sym_tile_grouped(tt, g.tiles_m, tm, tn);
+  else
+    grid_tile_grouped(tt, g.tiles_m, g.tiles_n, tm, tn);
   if (!g.flag[u]) {
     if (PHASE == APPLY && g.final_mode != FINAL_NONE)
       zero_unit_tile<TILE>(ca, g.final_mode, u, tm * TILE, tn * TILE);
@@ -2215,12 +2246,10 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
     u = q + nq * u;
     const bool live = __builtin_amdgcn_readfirstlane(p.gram.flag[u]) != 0;
     int tm, tn;
-    if (phase == APPLY) {
-      tm = t / p.apply.tiles_n;
-      tn = t - tm * p.apply.tiles_n;
-    } else {
-      sym_tile(t, ts, tm, tn);
-    }
+    if (phase == APPLY)
+      grid_tile_grouped(t, p.apply.tiles_m, p.apply.tiles_n, tm, tn);
+    else
+      sym_tile_grouped(t, ts, tm, tn);
     // Small-side panels the tile reads and completes, and the counts it
     // waits for (a zero unit computes nothing, so its items wait for
     // nothing).
