@@ -77,6 +77,39 @@ def test_ns_long_small_units_every_schedule(gpu_lib, sched, batch, rows, cols):
     assert worst <= TOL_NS["bf16"]
 
 
+def test_step_split_small_units_with_a_zero_unit(gpu_lib):
+    # 12 units of 128 x 1100 are too few to fill the GPU one workgroup each:
+    # each is split over several workgroups that sum their partial Grams.
+    # Unit 5's gradient stays zero (its groups only decay the weight and
+    # never wait on each other); two steps against the oracle.
+    say("[step split small units]")
+    shape = (12, 128, 1100)
+    w0 = _seeded(shape, 71, 0.02)
+    grads = []
+    for t in range(2):
+        g = _seeded(shape, 720 + t, 1e-3)
+        g[5].zero_()
+        grads.append(g.to(torch.bfloat16))
+    h = gpu_lib.Hyper()
+    tr = gpu_lib.Trace(gpu_lib.KERNEL_NS_SMALL, 2)
+    gpu_lib.step([w0.clone()], [grads[0]], [torch.zeros_like(w0)], hyper=h, trace=tr)
+    torch.cuda.synchronize()
+    assert tr.info() == [(128, 1100, 12, 128)]  # one on-chip launch for the pass
+    w = w0.clone()
+    m = torch.zeros_like(w0)
+    hw = oracle_hyper(h)
+    w_ref = {i: f64(w0[i]) for i in (0, 5, 11)}
+    m_ref = {i: np.zeros((128, 1100)) for i in (0, 5, 11)}
+    for t, g in enumerate(grads, start=1):
+        gpu_lib.step([w], [g], [m], hyper=h)
+        torch.cuda.synchronize()
+        for i in w_ref:
+            w_ref[i], m_ref[i], _ = oracle.muon_step(w_ref[i], f64(g[i]), m_ref[i], hw, 0, t)
+            assert rel(f64(m[i]), m_ref[i]) <= TOL_M
+            check_weight(f64(w[i]), w_ref[i], f64(w0[i]), t, h, TOL_NS["bf16"], f"step {t} unit {i}")
+    assert torch.count_nonzero(m[5]).item() == 0
+
+
 # The tiled bf16 path folds 1/||N|| into the first iteration (its fp32 Gram
 # accumulates products of N's raw entries) inside a range of norms and
 # scales the iterate first outside it; NS is scale invariant, so every scale
