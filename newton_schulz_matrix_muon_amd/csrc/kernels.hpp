@@ -7,14 +7,15 @@
 //                   for the SGD style's 1s), per-block fp64 partial sums of
 //                   N^2 (DeepSeek tech notes "Muon 优化器" section 1
 //                   Algorithm 1; RFC-0023 方案 1).  N goes to the fp32
-//                   buffer, or on the tiled bf16 path straight into the bf16
-//                   iterate with its padding zeroed.
+//                   buffer, or on the bf16 paths straight into the bf16
+//                   iterate with its padding zeroed (k_momentum_t: units a
+//                   pass holds transposed).
 //   k_norm_finish   per unit: fixed-order fp64 sum of the partials, 1/||N||_F
 //                   and the non-zero flag (notes section 2: Frobenius
 //                   normalisation, a zero matrix stays zero).
 //   k_normalize     fp32 path: X0 = N/||N||_F over the padded iterate (zeros
 //                   in the padding) and X0^T, transposed through LDS.  The
-//                   tiled bf16 path has no such pass: its first iteration
+//                   bf16 paths have no such pass: their first iteration
 //                   reads N and scales the Gram by 1/nu^2, the apply by 1/nu.
 //   ns_gemm<GRAM>   A = X X^T (or X^T X for a tall unit: the smaller side).
 //   ns_gemm<POLY>   B' = a*I + b*A + c*A*A (on the bf16 path A is kept only
@@ -27,9 +28,14 @@
 //                   exists only in bf16.  In the last iteration the
 //                   epilogue writes W <- W*(1 - lr*wd) - lr*scale*X' instead
 //                   (Algorithm 1's decoupled update) or the NS output.
-//   k_ns_small      the whole NS of a wide unit with at most 128 rows in one
-//                   workgroup, A and B on chip, one pass over X per
-//                   iteration (bf16 products).
+//   k_ns_small      the whole NS of a wide unit with at most 128 rows and
+//                   more than 128 columns on chip: A and B' in the
+//                   workgroup, one pass over X per iteration (bf16
+//                   products); a few long units split over several
+//                   workgroups that sum their partial Grams through memory.
+//   k_ns_small_step the whole step (momentum to update) of a wide unit of
+//                   at most 128 x 128 in one launch, the iterate in
+//                   registers (bf16, or fp32 up to 64 rows).
 //   ns_persistent   the three products of every iteration in one launch:
 //                   workgroups claim tiles in order and wait on per-panel
 //                   completion counts, so tiles of different units and
@@ -201,7 +207,7 @@ __device__ __forceinline__ float bf16_round(float f) {
 // ------------------------------------------------------------- momentum ----
 // GK: 0 = bf16 gradient, 1 = fp32 gradient, 2 = NS-only (copy fp32 input).
 // N goes to the fp32 buffer x32, or, when nb is given, to the bf16 iterate
-// nb itself (the tiled bf16 path, which folds 1/nu into its first
+// nb itself (the bf16 paths, which fold 1/nu into their first
 // iteration), padding included: each block clears its rows' padded columns
 // and a unit's last block its padded rows.
 // Units u0, u0 + 1, ... (not transposed) take blocks_per_unit blocks each;
@@ -1419,7 +1425,8 @@ __device__ __forceinline__ void sb_put(uint16_t* L, const float (&v)[16], int r0
   }
 }
 
-// Multi-block units (more than 128 columns), one workgroup per unit.  Per
+// Multi-block units (more than 128 columns), one workgroup per unit or, for
+// a few long units, several (see below).  Per
 // iteration the bf16 iterate streams through LDS in 128-column blocks X_j
 // (row-major, the next block's loads in flight while one is used), and for
 // each block
@@ -1433,8 +1440,9 @@ __device__ __forceinline__ void sb_put(uint16_t* L, const float (&v)[16], int r0
 // The iterate is the folded look-ahead on entry (k_momentum wrote bf16 N,
 // padding zeroed; k_norm_finish left the first iteration's scale s = 1/nu,
 // or 1 for a unit it rescaled): the first Gram is scaled by s^2 and the first
-// X' by s.  Roundings as on the tiled bf16 path: bf16 operands, fp32
-// accumulation, the iterate held in bf16.
+// X' by s.  Roundings as on the tiled bf16 path (bf16 operands, fp32
+// accumulation, the iterate held in bf16) except that b*A takes A's fp32
+// accumulator.
 //
 // A few long units (fewer than the CUs can keep busy) are split: workgroup
 // g of a unit's `groups` takes column blocks [g nb / groups, (g + 1) nb /

@@ -524,8 +524,9 @@ void launch_phase(bool bf16, int tile, int km, const GemmArgs& g, const ChunkArg
 }
 
 // Runs one chunk: momentum (or NS-input copy), norms, normalisation (folded
-// into the first iteration on the tiled bf16 path) and the NS iterations
-// with the fused final epilogue.
+// into the first iteration on the bf16 paths) and the NS iterations with the
+// fused final epilogue; units of one 128 x 128 block take all of it in one
+// launch.
 int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs,
               const void* const* ins, float* const* moms, const muon_matrix_desc* mats,
               unsigned char* ws, hipStream_t s, Tracer& tr, bool first_chunk,
