@@ -173,9 +173,13 @@ def launch_flops(cls, info, groups, iters):
     n = units * (live / total if total else 1.0)
     gram, poly, apply = 2.0 * s * s * l, 2.0 * s**3, 2.0 * s * s * l
     if cls == "ns_small":
-        # whole products on rows padded to 128 and columns to 128-multiples
-        lp = -(-l // 128) * 128
-        exe = 2.0 * 128 * 128 * lp * 2 + 2.0 * 128**3
+        if l <= 128:
+            # one launch per step: products over the unit's 32-blocks
+            sp, lp = -(-s // 32) * 32, -(-l // 32) * 32
+        else:
+            # streamed: whole products on rows padded to 128, columns to 128-multiples
+            sp, lp = 128, -(-l // 128) * 128
+        exe = 2.0 * sp * sp * lp * 2 + 2.0 * sp**3
         return n * iters * (gram + poly + apply), n * iters * exe
     f = executed_fraction(s, tile)
     if cls == "ns":
@@ -314,7 +318,26 @@ def measure(wl, ns, steps, warmup, dev, inputs, schedule="auto", trace_classes=T
     }
     out["dominant_kernel"] = roof["kernel"]
     out["dominant_frac"] = roof["frac"]
+    out["dominant_passes"] = pass_breakdown(dominant, launch_ms, launch_info, groups, iters, peak)
     return out, roof
+
+
+def pass_breakdown(cls, launch_ms, launch_info, groups, iters, peak):
+    """The dominant class's timed launches grouped by the pass they ran
+    (unit shape and count): launches, mean ms and nominal TFLOP/s each."""
+    by = {}
+    for ms, info in zip(launch_ms, launch_info):
+        key = tuple(info[:3])
+        nom, _ = launch_flops(cls, info, groups, iters)
+        e = by.setdefault(key, [0, 0.0, 0.0])
+        e[0] += 1
+        e[1] += ms
+        e[2] += nom
+    out = []
+    for (s, l, units), (n, ms, nom) in sorted(by.items(), key=lambda kv: -kv[1][1]):
+        out.append({"pass": f"{units} x {s}x{l}", "launches": n, "ms_per_launch": ms / n,
+                    "tflops": nom / (ms * 1e-3) / 1e12, "frac": nom / (ms * 1e-3) / 1e12 / peak})
+    return out
 
 
 def hbm_copy_rate(dev, mib=1024, reps=5):
@@ -495,7 +518,8 @@ def main(argv=None):
             "parallelism": "single GPU",
         },
         **{k: head[k] for k in ("ns_tflops", "ns_frac_of_peak", "ns_ms_per_step", "ns_tflops_step",
-                                "kernel_ms_per_step", "elementwise_gbs", "elementwise_frac_of_hbm")
+                                "kernel_ms_per_step", "elementwise_gbs", "elementwise_frac_of_hbm",
+                                "dominant_passes")
            if k in head},
         "hbm_copy_gbs": copy_gbs,
         "roofline": roof,

@@ -51,10 +51,27 @@ def test_launch_flops():
     # only units with a non-zero gradient count
     nom, _ = bench.launch_flops("ns", (2048, 7168, 384, 256), groups, 10)
     assert nom == pytest.approx(345 * 10 * (4 * 2048**2 * 7168 + 2 * 2048**3))
-    # the on-chip kernel: whole 128-row products
+    # the one-launch kernel: products over the unit's 32-blocks (64 x 128
+    # is exact); the streaming kernel: whole 128-row products
     nom, exe = bench.launch_flops("ns_small", (64, 128, 1, 128), {}, 10)
-    assert nom == 10 * (4 * 64 * 64 * 128 + 2 * 64**3)
-    assert exe == 10 * (4 * 128**3 + 2 * 128**3)
+    assert nom == exe == 10 * (4 * 64 * 64 * 128 + 2 * 64**3)
+    nom, exe = bench.launch_flops("ns_small", (100, 125, 2, 128), {}, 10)
+    assert exe == 2 * 10 * (4 * 128 * 128 * 128 + 2 * 128**3)
+    nom, exe = bench.launch_flops("ns_small", (128, 4096, 48, 128), {}, 10)
+    assert nom == exe == 48 * 10 * (4 * 128 * 128 * 4096 + 2 * 128**3)
+    nom, exe = bench.launch_flops("ns_small", (96, 1100, 3, 128), {}, 10)
+    assert exe == 3 * 10 * (4 * 128 * 128 * 1152 + 2 * 128**3)
+
+
+def test_pass_breakdown_groups_launches_by_pass():
+    groups = {(4096, 4096): (32, 32), (4096, 14336): (96, 96)}
+    ms = [80.0, 680.0, 82.0, 682.0]
+    info = [(4096, 4096, 32, 256), (4096, 14336, 96, 256)] * 2
+    rows = bench.pass_breakdown("ns", ms, info, groups, 10, 2516.6)
+    assert [r["pass"] for r in rows] == ["96 x 4096x14336", "32 x 4096x4096"]
+    assert rows[0]["launches"] == 2 and rows[0]["ms_per_launch"] == pytest.approx(681.0)
+    nom = 96 * 10 * (4 * 4096**2 * 14336 + 2 * 4096**3)
+    assert rows[0]["tflops"] == pytest.approx(nom / 0.681 / 1e12)
 
 
 def test_cpu_baseline_extrapolates_over_shapes(monkeypatch):
