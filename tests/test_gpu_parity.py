@@ -200,12 +200,17 @@ def test_batch_vs_single_bitwise(gpu_lib, prec):
         assert torch.equal(stacked[0][i], singles[i])
 
 
-def test_ns_in_place(gpu_lib):
-    x = _seeded((96, 160), 21)
+# The NS-only entry may write its output over its input: tiled (96 x 160),
+# and the one-launch step, which reads the whole unit before it writes any
+# of it (64 x 128 bf16, 48 x 100 fp32).
+@pytest.mark.parametrize("shape,prec", [((96, 160), "fp32"), ((64, 128), "bf16"), ((48, 100), "fp32")],
+                         ids=["tiled", "one-launch-bf16", "one-launch-fp32"])
+def test_ns_in_place(gpu_lib, shape, prec):
+    x = _seeded(shape, 21)
     ref = oracle.newton_schulz(f64(x))
-    gpu_lib.newton_schulz([x], outs=[x], hyper=gpu_lib.Hyper(ns_precision="fp32"))
+    gpu_lib.newton_schulz([x], outs=[x], hyper=gpu_lib.Hyper(ns_precision=prec))
     torch.cuda.synchronize()
-    assert rel(f64(x), ref) <= TOL_NS["fp32"]
+    assert rel(f64(x), ref) <= TOL_NS[prec]
 
 
 # -------------------------------------------------------------- step --------
