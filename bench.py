@@ -167,7 +167,19 @@ def launch_flops(cls, info, groups, iters):
     reports it covered (s, l, units, tile), counting only the share of
     units with a non-zero gradient in that unit shape.  One launch of class
     "ns" or "ns_small" runs every iteration; one of "gram", "poly" or
-    "apply" runs one."""
+    "apply" runs one.  A persistent launch that also ran a single-unit pass
+    reports both passes (muon.ns_passes); their FLOPs add."""
+    from newton_schulz_matrix_muon_amd.muon import ns_passes
+
+    nom = exe = 0.0
+    for one in ns_passes(info):
+        a, b = _pass_flops(cls, one, groups, iters)
+        nom += a
+        exe += b
+    return nom, exe
+
+
+def _pass_flops(cls, info, groups, iters):
     s, l, units, tile = info
     total, live = groups.get((s, l), (units, units))
     n = units * (live / total if total else 1.0)
@@ -301,9 +313,16 @@ def measure(wl, ns, steps, warmup, dev, inputs, schedule="auto", trace_classes=T
         nom += a
         exe += b
     t = sum(launch_ms) * 1e-3
+    kernel = KERNEL_NAMES[dominant]
+    if dominant == "ns":
+        # launches that also ran a single-unit pass are ns_persistent2's
+        from newton_schulz_matrix_muon_amd.muon import ns_passes
+
+        two = [len(ns_passes(i)) > 1 for i in launch_info]
+        kernel = " + ".join(k for k, on in (("ns_persistent", not all(two)), ("ns_persistent2", any(two))) if on)
     roof = {
         "bound": "mfma",
-        "kernel": KERNEL_NAMES[dominant],
+        "kernel": kernel,
         "achieved": nom / t / 1e12,
         "peak": peak,
         "unit": "TFLOP/s",
@@ -325,17 +344,19 @@ def measure(wl, ns, steps, warmup, dev, inputs, schedule="auto", trace_classes=T
 def pass_breakdown(cls, launch_ms, launch_info, groups, iters, peak):
     """The dominant class's timed launches grouped by the pass they ran
     (unit shape and count): launches, mean ms and nominal TFLOP/s each."""
+    from newton_schulz_matrix_muon_amd.muon import ns_passes
+
     by = {}
     for ms, info in zip(launch_ms, launch_info):
-        key = tuple(info[:3])
+        key = " + ".join(f"{u} x {s}x{l}" for s, l, u, _ in ns_passes(info))
         nom, _ = launch_flops(cls, info, groups, iters)
         e = by.setdefault(key, [0, 0.0, 0.0])
         e[0] += 1
         e[1] += ms
         e[2] += nom
     out = []
-    for (s, l, units), (n, ms, nom) in sorted(by.items(), key=lambda kv: -kv[1][1]):
-        out.append({"pass": f"{units} x {s}x{l}", "launches": n, "ms_per_launch": ms / n,
+    for key, (n, ms, nom) in sorted(by.items(), key=lambda kv: -kv[1][1]):
+        out.append({"pass": key, "launches": n, "ms_per_launch": ms / n,
                     "tflops": nom / (ms * 1e-3) / 1e12, "frac": nom / (ms * 1e-3) / 1e12 / peak})
     return out
 

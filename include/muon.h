@@ -109,7 +109,14 @@ typedef enum { MUON_NS_FP32 = 0, MUON_NS_BF16 = 1 } muon_ns_precision;
  *     several workgroups that sum their partial Grams through memory
  *     (those waits are bounded like PERSISTENT's).
  *   - Other passes of units with min(rows, cols) < 256, and passes of a
- *     single unit, use LAUNCHES; the rest PERSISTENT.
+ *     single unit, use LAUNCHES; the rest PERSISTENT.  A single-unit pass
+ *     with min(rows, cols) >= 256 instead runs inside the PERSISTENT
+ *     launch of another pass of the call whose units have the same
+ *     orientation (with bf16 products; any with fp32 ones), when that pass
+ *     takes one claim queue on the device (fewer units than XCCs, or
+ *     units that do not spread evenly over them); its tiles then fill the
+ *     CUs that the other pass leaves idle.  The workspace holds both
+ *     passes' buffers for such a pair.
  *   The on-chip kernels round like the tiled products (bf16 operands, fp32
  *   accumulation) but in another order (b*A from A's fp32 accumulator; the
  *   one-launch step also adds a*X from the fp32 iterate), so results agree
@@ -249,7 +256,10 @@ typedef enum {
  * only the first `capacity` are recorded).  When `info` is not NULL, the
  * four values info[4k .. 4k+3] describe what launch k covered:
  *   NS classes (GRAM, POLY, APPLY, NS, NS_SMALL): the smaller and the larger
- *     side of the units (unpadded), the number of units, the tile size;
+ *     side of the units (unpadded), the number of units, the tile size; an
+ *     NS launch that also runs a single-unit pass (AUTO) carries that
+ *     pass's smaller side, larger side and unit count in bits 32-63 of the
+ *     first three values (zero otherwise), its own in bits 0-31;
  *   MOMENTUM: elements, algorithmic bytes (gradient or NS input read,
  *     momentum read and written, look-ahead written), units, 0;
  *   NORMALIZE: units, 0, 0, 0.
@@ -291,7 +301,7 @@ int muon_workspace_status(void* workspace, size_t workspace_bytes, hipStream_t s
 /* Static description of a status code (never NULL). */
 const char* muon_status_string(int status);
 
-/* ABI version of this header: 5. */
+/* ABI version of this header: 6. */
 int muon_abi_version(void);
 
 #ifdef __cplusplus

@@ -40,6 +40,8 @@
 //                   workgroups claim tiles in order and wait on per-panel
 //                   completion counts, so tiles of different units and
 //                   phases overlap (no launch boundary between products).
+//   ns_persistent2  the same over two passes of different unit shapes at
+//                   once (a pass of one unit beside a stacked pass).
 // The three products are the quintic step a*X + b*(X X^T)X + c*(X X^T)^2 X of
 // the notes' section 2, grouped as (a*I + b*A + c*A^2)*X: the polynomial's
 // epilogue adds a on the diagonal, so the apply is one plain product and
@@ -146,21 +148,41 @@ struct SegView {
   float lr_scale;
 };
 
-__device__ __forceinline__ SegView find_seg(const ChunkArgs& ca, int u) {
-  SegView v{ca.seg[0].w, ca.seg[0].g, ca.seg[0].m, ca.seg[0].first, ca.seg[0].trans,
-            ca.seg[0].lr_scale};
+template <int NSEG>
+__device__ __forceinline__ SegView find_seg_in(const Seg (&seg)[NSEG], int n_seg, int u) {
+  SegView v{seg[0].w, seg[0].g, seg[0].m, seg[0].first, seg[0].trans, seg[0].lr_scale};
 #pragma unroll
-  for (int s = 1; s < kMaxSeg; ++s) {
-    if (s < ca.n_seg && ca.seg[s].first <= u) {
-      v.w = ca.seg[s].w;
-      v.g = ca.seg[s].g;
-      v.m = ca.seg[s].m;
-      v.first = ca.seg[s].first;
-      v.trans = ca.seg[s].trans;
-      v.lr_scale = ca.seg[s].lr_scale;
+  for (int s = 1; s < NSEG; ++s) {
+    if (s < n_seg && seg[s].first <= u) {
+      v.w = seg[s].w;
+      v.g = seg[s].g;
+      v.m = seg[s].m;
+      v.first = seg[s].first;
+      v.trans = seg[s].trans;
+      v.lr_scale = seg[s].lr_scale;
     }
   }
   return v;
+}
+
+__device__ __forceinline__ SegView find_seg(const ChunkArgs& ca, int u) {
+  return find_seg_in(ca.seg, ca.n_seg, u);
+}
+
+// Where a final epilogue writes unit u: its weight (step) or NS output in
+// the caller's layout, and the shape its stores are masked to.
+struct UnitOut {
+  float* w;          // the unit's first element
+  int32_t trans;     // stored transposed relative to the shape below
+  float lr_scale;    // lr * the unit's update scale
+  int32_t rows, cols;
+  float decay;
+};
+
+__device__ __forceinline__ UnitOut unit_out(const ChunkArgs& ca, int u) {
+  const SegView sg = find_seg(ca, u);
+  return UnitOut{sg.w + (int64_t)(u - sg.first) * ca.unit_elems, sg.trans, sg.lr_scale,
+                 ca.rows, ca.cols, ca.decay};
 }
 
 // ----------------------------------------------------------------- utils ---
@@ -783,18 +805,15 @@ __shared__ u32x4 lds_ring[kSlots * TILE * kRowChunks];
 // Zero unit in the last iteration: O' = 0, so the weight only decays (step)
 // or the NS output is zero, over the TILE x TILE block at (m0, n0).
 template <int TILE>
-__device__ __forceinline__ void zero_unit_tile(const ChunkArgs& ca, int final_mode, int u, int m0,
-                                               int n0) {
-  const SegView sg = find_seg(ca, u);
-  float* wout = sg.w + (int64_t)(u - sg.first) * ca.unit_elems;
+__device__ __forceinline__ void zero_unit_tile(const UnitOut& o, int final_mode, int m0, int n0) {
   for (int idx = threadIdx.x; idx < TILE * TILE; idx += gemm_threads<TILE>()) {
     // a transposed unit's caller element (nn, mm) is the chunk's (mm, nn);
     // walk the tile so that consecutive threads touch consecutive elements
     const int a = idx / TILE, b = idx % TILE;
-    const int mm = m0 + (sg.trans ? b : a), nn = n0 + (sg.trans ? a : b);
-    if (mm < ca.rows && nn < ca.cols) {
-      float* p = wout + (sg.trans ? (int64_t)nn * ca.rows + mm : (int64_t)mm * ca.cols + nn);
-      *p = (final_mode == FINAL_STEP) ? (*p) * ca.decay : 0.0f;
+    const int mm = m0 + (o.trans ? b : a), nn = n0 + (o.trans ? a : b);
+    if (mm < o.rows && nn < o.cols) {
+      float* p = o.w + (o.trans ? (int64_t)nn * o.rows + mm : (int64_t)mm * o.cols + nn);
+      *p = (final_mode == FINAL_STEP) ? (*p) * o.decay : 0.0f;
     }
   }
 }
@@ -807,15 +826,16 @@ struct NoHook {
   __device__ __forceinline__ void operator()() const {}
 };
 
+// `out_of()` gives the unit's UnitOut; the final apply epilogue calls it.
 // `issued` runs once the prologue's first copies are in flight (the
 // persistent schedule claims its next item there, so that the claim's round
 // trip overlaps the copies' latency); `ready` runs after the prologue's
 // barrier, when every wave's older memory accesses are complete.
 //
 // KM: bit 0 = the A operand is K-major, bit 1 = the B operand is.
-template <int PHASE, typename T, int TILE, int KM = 0, bool FOLD = false, typename Hook = NoHook,
-          typename Hook2 = NoHook>
-__device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca, int u, int tm,
+template <int PHASE, typename T, int TILE, int KM = 0, bool FOLD = false, typename OutFn = NoHook,
+          typename Hook = NoHook, typename Hook2 = NoHook>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, const OutFn& out_of, int u, int tm,
                                           int tn, const Hook& issued = Hook(),
                                           const Hook2& ready = Hook2()) {
   constexpr int NW = gemm_waves<TILE>();
@@ -1068,16 +1088,16 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
   wait_lgkm0();
   __builtin_amdgcn_s_barrier();  // every wave is done with the stage buffers
   float* ep = reinterpret_cast<float*>(ring) + wid * (32 * LDW);
-  float* wout = nullptr;
-  bool wtrans = false;  // the unit's weight is the chunk shape transposed
-  float lrs = 0.0f;     // lr * the unit's update scale
-  if (PHASE == APPLY && g.final_mode != FINAL_NONE) {
-    const SegView sg = find_seg(ca, u);
-    wout = sg.w + (int64_t)(u - sg.first) * ca.unit_elems;
-    wtrans = sg.trans != 0;
-    lrs = sg.lr_scale;
+  UnitOut uo{nullptr, 0, 0.0f, 0, 0, 1.0f};
+  if constexpr (PHASE == APPLY) {
+    if (g.final_mode != FINAL_NONE) uo = out_of();
   }
-  const bool vec_w = (ca.cols & 3) == 0;
+  float* const wout = uo.w;
+  const bool wtrans = uo.trans != 0;  // the unit's weight is the chunk shape transposed
+  const float lrs = uo.lr_scale;      // lr * the unit's update scale
+  const int wrows = uo.rows, wcols = uo.cols;
+  const float wdecay = uo.decay;
+  const bool vec_w = (wcols & 3) == 0;
   // FOLD (first iteration of the folded path): X = N, so A = (N N^T)/nu^2
   // and X' = (B' N)/nu; the accumulators take the scale as they are staged.
   // A separate instantiation, so that the other tiles' epilogues carry
@@ -1175,17 +1195,17 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
             store_bf16x4(g.out16, o, v0, v1, v2, v3);
           else
             *reinterpret_cast<float4*>(g.out32 + o) = make_float4(v0, v1, v2, v3);
-        } else if (!wtrans && m < ca.rows && ncol < ca.cols) {
+        } else if (!wtrans && m < wrows && ncol < wcols) {
           const int n = ncol;
-          float* p = wout + (int64_t)m * ca.cols + n;
+          float* p = wout + (int64_t)m * wcols + n;
           const bool step = g.final_mode == FINAL_STEP;
-          if (vec_w && n + 3 < ca.cols) {
+          if (vec_w && n + 3 < wcols) {
             float4 wv = step ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
             if (step) {
-              wv.x = __builtin_fmaf(-lrs, v0, wv.x * ca.decay);
-              wv.y = __builtin_fmaf(-lrs, v1, wv.y * ca.decay);
-              wv.z = __builtin_fmaf(-lrs, v2, wv.z * ca.decay);
-              wv.w = __builtin_fmaf(-lrs, v3, wv.w * ca.decay);
+              wv.x = __builtin_fmaf(-lrs, v0, wv.x * wdecay);
+              wv.y = __builtin_fmaf(-lrs, v1, wv.y * wdecay);
+              wv.z = __builtin_fmaf(-lrs, v2, wv.z * wdecay);
+              wv.w = __builtin_fmaf(-lrs, v3, wv.w * wdecay);
             } else {
               wv = make_float4(v0, v1, v2, v3);
             }
@@ -1194,8 +1214,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
             const float vv[4] = {v0, v1, v2, v3};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              if (n + e < ca.cols)
-                p[e] = step ? __builtin_fmaf(-lrs, vv[e], p[e] * ca.decay) : vv[e];
+              if (n + e < wcols)
+                p[e] = step ? __builtin_fmaf(-lrs, vv[e], p[e] * wdecay) : vv[e];
             }
           }
         }
@@ -1230,22 +1250,22 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
         // per caller row, 4 consecutive elements each)
         const int cm = (lane & 7) * 4;
         const bool step = g.final_mode == FINAL_STEP;
-        const bool vec_t = (ca.rows & 3) == 0;
+        const bool vec_t = (wrows & 3) == 0;
 #pragma unroll
         for (int it = 0; it < WN / 8; ++it) {
           const int nn = it * 8 + (lane >> 3);
           const int crow = n0 + wn * WN + nn, ccol = mrow0 + cm;
-          if (crow < ca.cols && ccol < ca.rows) {
+          if (crow < wcols && ccol < wrows) {
             const float vv[4] = {ep[(cm + 0) * LDW + nn], ep[(cm + 1) * LDW + nn],
                                  ep[(cm + 2) * LDW + nn], ep[(cm + 3) * LDW + nn]};
-            float* p = wout + (int64_t)crow * ca.rows + ccol;
-            if (vec_t && ccol + 3 < ca.rows) {
+            float* p = wout + (int64_t)crow * wrows + ccol;
+            if (vec_t && ccol + 3 < wrows) {
               float4 wv = step ? *reinterpret_cast<const float4*>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
               if (step) {
-                wv.x = __builtin_fmaf(-lrs, vv[0], wv.x * ca.decay);
-                wv.y = __builtin_fmaf(-lrs, vv[1], wv.y * ca.decay);
-                wv.z = __builtin_fmaf(-lrs, vv[2], wv.z * ca.decay);
-                wv.w = __builtin_fmaf(-lrs, vv[3], wv.w * ca.decay);
+                wv.x = __builtin_fmaf(-lrs, vv[0], wv.x * wdecay);
+                wv.y = __builtin_fmaf(-lrs, vv[1], wv.y * wdecay);
+                wv.z = __builtin_fmaf(-lrs, vv[2], wv.z * wdecay);
+                wv.w = __builtin_fmaf(-lrs, vv[3], wv.w * wdecay);
               } else {
                 wv = make_float4(vv[0], vv[1], vv[2], vv[3]);
               }
@@ -1253,8 +1273,8 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const ChunkArgs& ca
             } else {
 #pragma unroll
               for (int e = 0; e < 4; ++e)
-                if (ccol + e < ca.rows)
-                  p[e] = step ? __builtin_fmaf(-lrs, vv[e], p[e] * ca.decay) : vv[e];
+                if (ccol + e < wrows)
+                  p[e] = step ? __builtin_fmaf(-lrs, vv[e], p[e] * wdecay) : vv[e];
             }
           }
         }
@@ -1338,13 +1358,14 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_gemm(GemmArgs g, Chun
     grid_tile_grouped(tt, g.tiles_m, g.tiles_n, tm, tn);
   if (!g.flag[u]) {
     if (PHASE == APPLY && g.final_mode != FINAL_NONE)
-      zero_unit_tile<TILE>(ca, g.final_mode, u, tm * TILE, tn * TILE);
+      zero_unit_tile<TILE>(unit_out(ca, u), g.final_mode, tm * TILE, tn * TILE);
     return;
   }
+  auto out_of = [&]() { return unit_out(ca, u); };
   if (PHASE != POLY && g.fold)
-    gemm_tile<PHASE, T, TILE, KM, PHASE != POLY>(g, ca, u, tm, tn);
+    gemm_tile<PHASE, T, TILE, KM, PHASE != POLY>(g, out_of, u, tm, tn);
   else
-    gemm_tile<PHASE, T, TILE, KM>(g, ca, u, tm, tn);
+    gemm_tile<PHASE, T, TILE, KM>(g, out_of, u, tm, tn);
 }
 
 // -------------------------------------------------------- small-s NS -------
@@ -2074,16 +2095,26 @@ __global__ __launch_bounds__(kThreads) void k_ns_small_step(NsSmallArgs p, Chunk
 // wait is still bounded by a wall-clock limit, after which the launch stops
 // and reports through `err`.
 //
+// A launch may carry a second pass (ns_persistent2): units of another
+// shape with the same tile size and operand layout, with their own buffers
+// and completion counts.  Its items follow the first pass's within each
+// phase (Gram of the first pass, Gram of the second, polynomial of the
+// first, ...), so every item still waits only for earlier ones; the second
+// pass's tiles fill the CUs that the first pass's leaves idle.
+//
 // Queues.  With one queue any workgroup may run any tile, so a tile's
 // results are published at agent scope (the L2 written back before the
-// count).  With one queue per XCC, unit u belongs to queue u % n_queues and
-// only workgroups running on that XCC claim from it: every tile of a unit
-// is then produced and consumed through the same L2, so publishing only
-// needs the stores to have completed.  Before a tile's first load, wave 0
-// of the reading workgroup acquires at agent scope once for all its waves
-// (in both cases).  The last workgroup to leave runs, on its own, any queue
-// that no workgroup ever claimed from (an XCC that received none).
-struct NsSched {
+// count).  With one queue per XCC, unit u of a pass belongs to queue
+// u % n_queues and only workgroups running on that XCC claim from it:
+// every tile of a unit is then produced and consumed through the same L2,
+// so publishing only needs the stores to have completed.  Before a tile's
+// first load, wave 0 of the reading workgroup acquires at agent scope once
+// for all its waves (in both cases).  The last workgroup to leave runs, on
+// its own, any queue that no workgroup ever claimed from (an XCC that
+// received none).
+
+// One pass: the products of its units and where their tiles are counted.
+struct NsPass {
   GemmArgs gram, poly, apply;     // cur-independent fields of each product
   const void* gram_op[2];         // Gram operand (both sides) for X in buffer cur
   const void* app_a[2];           // apply operands for X in buffer cur
@@ -2091,29 +2122,99 @@ struct NsSched {
   float* app_out32[2];            // apply outputs (buffer cur ^ 1)
   void* app_out16[2];
   void* app_outt[2];
+  uint32_t* done;                 // per unit: finished tiles per small-side
+                                  // panel, for each of the three products
+  int32_t n_units;
+  int32_t tg;                     // tiles per unit of a symmetric product
+  int32_t ta;                     // tiles per unit of the apply product
+  int32_t apply_s_m;              // 1: an apply tile's small-side panel is its
+                                  // row (wide units), 0: its column (tall)
+};
+
+struct NsSched {
+  NsPass a;                       // the first pass (its units: the ChunkArgs)
   int32_t final_mode;             // of the last iteration's apply
   int32_t n_iter;
   int32_t n_stages;
   int32_t stage_begin[4];         // first iteration of each stage
   float sa[4], sb[4], sc[4];      // coefficients of each stage
-  int32_t tg;                     // tiles per unit of a symmetric product
-  int32_t ta;                     // tiles per unit of the apply product
-  int32_t apply_s_m;              // 1: an apply tile's small-side panel is its
-                                  // row (wide units), 0: its column (tall)
-  int32_t n_queues;               // 1, or one queue per XCC (see below)
+  int32_t n_queues;               // 1, or one queue per XCC (see above)
   uint32_t* queue;                // per queue: next item to claim; then the
                                   // count of workgroups that have left
-  uint32_t* done;                 // per unit: finished tiles per small-side
-                                  // panel, for each of the three products
   uint32_t* err;                  // set when a wait timed out
   uint64_t timeout_ticks;         // wall-clock ticks
 };
 
+// The second pass of a two-pass launch, with what its final epilogue needs
+// of its chunk (the first pass takes that from the kernel's ChunkArgs).
+constexpr int kMaxSegB = 4;
+struct NsPassB {
+  NsPass b;
+  int32_t rows, cols;             // unit shape
+  int64_t unit_elems;
+  float decay;
+  int32_t n_seg;
+  Seg seg[kMaxSegB];
+};
+
+// The pass an item belongs to, picked field by field as values: sel()
+// takes both fields by value, so each pick selects between two loaded
+// kernel-argument values.  (c ? x.f : y.f on two lvalues is itself an
+// lvalue: the compiler selects the addresses and loads through them, and
+// then keeps both kernel arguments in scratch memory and loads every field
+// per lane.)
+template <typename V>
+__device__ __forceinline__ V sel(bool c, V x, V y) {
+  return c ? x : y;
+}
+
+__device__ __forceinline__ GemmArgs pick(bool c, const GemmArgs& x, const GemmArgs& y) {
+  static_assert(sizeof(GemmArgs) == 176, "every GemmArgs field is picked below");
+  GemmArgs g;
+  g.a = sel(c, x.a, y.a);
+  g.b = sel(c, x.b, y.b);
+  g.a_ustride = sel(c, x.a_ustride, y.a_ustride);
+  g.b_ustride = sel(c, x.b_ustride, y.b_ustride);
+  g.lda = sel(c, x.lda, y.lda);
+  g.ldb = sel(c, x.ldb, y.ldb);
+  g.M = sel(c, x.M, y.M);
+  g.N = sel(c, x.N, y.N);
+  g.K = sel(c, x.K, y.K);
+  g.tiles_m = sel(c, x.tiles_m, y.tiles_m);
+  g.tiles_n = sel(c, x.tiles_n, y.tiles_n);
+  g.n_units = sel(c, x.n_units, y.n_units);
+  g.out32 = sel(c, x.out32, y.out32);
+  g.out16 = sel(c, x.out16, y.out16);
+  g.out_ustride = sel(c, x.out_ustride, y.out_ustride);
+  g.ldo = sel(c, x.ldo, y.ldo);
+  g.outt = sel(c, x.outt, y.outt);
+  g.ldt = sel(c, x.ldt, y.ldt);
+  g.sym = sel(c, x.sym, y.sym);
+  g.final_mode = sel(c, x.final_mode, y.final_mode);
+  g.aux = sel(c, x.aux, y.aux);
+  g.aux16 = sel(c, x.aux16, y.aux16);
+  g.aux_ustride = sel(c, x.aux_ustride, y.aux_ustride);
+  g.ldaux = sel(c, x.ldaux, y.ldaux);
+  g.ca = sel(c, x.ca, y.ca);
+  g.cb = sel(c, x.cb, y.cb);
+  g.cc = sel(c, x.cc, y.cc);
+  g.flag = sel(c, x.flag, y.flag);
+  g.fold = sel(c, x.fold, y.fold);
+  return g;
+}
+
+__device__ __forceinline__ UnitOut unit_out(const NsPassB& pb, int u) {
+  const SegView sg = find_seg_in(pb.seg, pb.n_seg, u);
+  return UnitOut{sg.w + (int64_t)(u - sg.first) * pb.unit_elems, sg.trans, sg.lr_scale,
+                 pb.rows, pb.cols, pb.decay};
+}
+
 // KMODE: 0 = every operand row-major (fp32 path: X^T is kept); 1 = wide
 // bf16 units, B'*X reads X K-major; 2 = tall bf16 units, X^T X reads X
-// K-major on both sides.
-template <typename T, int TILE, int KMODE>
-__global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p, ChunkArgs ca) {
+// K-major on both sides.  TWO: the launch carries a second pass (`second`).
+template <typename T, int TILE, int KMODE, bool TWO>
+__device__ __forceinline__ void ns_persistent_run(const NsSched& p, const ChunkArgs& ca,
+                                                  const NsPassB* second) {
   // Every branch below is uniform across the workgroup or across a wave:
   // the scheduling work (claim, completion count, dependency wait) is done
   // by all of wave 0, whose atomics lane 0 makes alone (lane0_atomic_add),
@@ -2126,15 +2227,19 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
   // follows their last read comes before the next tile's first copy.
   int& s_item = reinterpret_cast<int*>(lds_ring<TILE>)[0];
   int& s_go = reinterpret_cast<int*>(lds_ring<TILE>)[1];
-  const int per_unit = 2 * p.tg + p.ta;
+  const int per_unit_a = 2 * p.a.tg + p.a.ta;
+  const int per_unit_b = TWO ? 2 * second->b.tg + second->b.ta : 0;
   const int nq = p.n_queues;
   const bool local = nq > 1;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   uint32_t* const left = p.queue + nq;                    // workgroups that have left
-  // units of queue qq: qq, qq + nq, ...
-  auto units_of = [&](int qq) { return ca.n_units > qq ? (ca.n_units - qq + nq - 1) / nq : 0; };
+  // units of a pass of n units in queue qq: qq, qq + nq, ...
+  auto units_of = [&](int qq, int n) { return n > qq ? (n - qq + nq - 1) / nq : 0; };
+  const int na = p.a.n_units;
+  const int nb = TWO ? second->b.n_units : 0;
   int q = local ? xcc_id() % nq : 0;
-  int uq = units_of(q);
+  int uqa = units_of(q, na);
+  int uqb = TWO ? units_of(q, nb) : 0;
   // Completion counts, per unit three arrays of ts words (Gram, polynomial,
   // apply), indexed by tile panel on the small side: a Gram or polynomial
   // tile (r, c) counts in panels r and c (once when r == c), an apply tile
@@ -2155,8 +2260,6 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
   // item that runs no tile and on every exit, so no workgroup ever blocks
   // while holding an uncounted tile.  With one queue the release also
   // writes the L2 back, and tiles are flushed as they end.
-  const int ts = p.gram.tiles_m;
-  const int tl = p.ta / ts;
   uint32_t* pend_a = nullptr;  // counts of the finished tile not yet made
   uint32_t* pend_b = nullptr;
   bool alone = false;  // running unclaimed queues after every other workgroup left
@@ -2207,7 +2310,7 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
     have_next = false;
     lds_barrier();
     const int item = __builtin_amdgcn_readfirstlane(s_item);
-    const int per_iter = uq * per_unit;
+    const int per_iter = uqa * per_unit_a + uqb * per_unit_b;
     if (item < 0 || item >= p.n_iter * per_iter) flush();
     if (item < 0) break;  // stopped
     if (item >= p.n_iter * per_iter) {
@@ -2228,42 +2331,70 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
       for (int qq = 0; qq < nq; ++qq) {
         const uint32_t head = __builtin_amdgcn_readfirstlane(
             __hip_atomic_load(p.queue + qq, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-        if (next < 0 && head == 0u && units_of(qq) > 0) next = qq;
+        if (next < 0 && head == 0u && units_of(qq, na) + (TWO ? units_of(qq, nb) : 0) > 0)
+          next = qq;
       }
       if (next < 0) break;
       q = next;
-      uq = units_of(q);
+      uqa = units_of(q, na);
+      uqb = TWO ? units_of(q, nb) : 0;
       continue;
     }
-    const int ug = uq * p.tg;
+    // Within an iteration: Gram of pass a, Gram of pass b, polynomial of
+    // a, of b, apply of a, of b.
+    const int ga = uqa * p.a.tg;
+    const int gb = TWO ? uqb * second->b.tg : 0;
     const int it = item / per_iter;
     int r = item - it * per_iter;
-    int phase, u, t;
-    if (r < ug) {
+    int phase;
+    bool in_b = false;
+    if (r < ga) {
       phase = GRAM;
-    } else if (r < 2 * ug) {
+    } else if (TWO && r < ga + gb) {
+      phase = GRAM;
+      in_b = true;
+      r -= ga;
+    } else if (r < 2 * ga + gb) {
       phase = POLY;
-      r -= ug;
+      r -= ga + gb;
+    } else if (TWO && r < 2 * ga + 2 * gb) {
+      phase = POLY;
+      in_b = true;
+      r -= 2 * ga + gb;
     } else {
       phase = APPLY;
-      r -= 2 * ug;
+      r -= 2 * ga + 2 * gb;
+      if (TWO && r >= uqa * p.a.ta) {
+        in_b = true;
+        r -= uqa * p.a.ta;
+      }
     }
-    const int tpu = phase == APPLY ? p.ta : p.tg;
-    u = r / tpu;
-    t = r - u * tpu;
+    // the item's pass (b: the second one; always the first without TWO)
+    const NsPass& PB = TWO ? second->b : p.a;
+    const bool b = TWO && in_b;
+    const int tg = sel(b, PB.tg, p.a.tg);
+    const int ta = sel(b, PB.ta, p.a.ta);
+    const int tpu = phase == APPLY ? ta : tg;
+    int u = r / tpu;
+    const int t = r - u * tpu;
     u = q + nq * u;
-    const bool live = __builtin_amdgcn_readfirstlane(p.gram.flag[u]) != 0;
+    const int32_t* const flag = sel(b, PB.gram.flag, p.a.gram.flag);
+    const bool live = __builtin_amdgcn_readfirstlane(flag[u]) != 0;
+    const int ts = sel(b, PB.gram.tiles_m, p.a.gram.tiles_m);
+    const int tl = ta / ts;
     int tm, tn;
     if (phase == APPLY)
-      grid_tile_grouped(t, p.apply.tiles_m, p.apply.tiles_n, tm, tn);
+      grid_tile_grouped(t, sel(b, PB.apply.tiles_m, p.a.apply.tiles_m),
+                        sel(b, PB.apply.tiles_n, p.a.apply.tiles_n), tm, tn);
     else
       sym_tile_grouped(t, ts, tm, tn);
     // Small-side panels the tile reads and completes, and the counts it
     // waits for (a zero unit computes nothing, so its items wait for
     // nothing).
-    const int pa = phase == APPLY ? (p.apply_s_m ? tm : tn) : tm;
+    const int apply_s_m = sel(b, PB.apply_s_m, p.a.apply_s_m);
+    const int pa = phase == APPLY ? (apply_s_m ? tm : tn) : tm;
     const int pb = phase == APPLY ? pa : tn;
-    uint32_t* const cnt = p.done + (int64_t)u * 3 * ts;  // Gram | polynomial | apply
+    uint32_t* const cnt = sel(b, PB.done, p.a.done) + (int64_t)u * 3 * ts;  // Gram | polynomial | apply
     uint32_t* dep = nullptr;  // the counts waited for: dep[pa] and dep[pb]
     uint32_t need = 0;
     if (phase == GRAM) {
@@ -2340,20 +2471,29 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
         have_next = true;
       }
     };
+    // the final epilogue's view of the unit, from its own pass's chunk
+    auto out_of = [&]() {
+      if constexpr (TWO) {
+        if (in_b) return unit_out(*second, u);
+      }
+      return unit_out(ca, u);
+    };
     const int cur = it & 1;
     if (phase == GRAM) {
       if (live) {
-        GemmArgs g = p.gram;
-        g.a = g.b = cur ? p.gram_op[1] : p.gram_op[0];
+        GemmArgs g = pick(b, PB.gram, p.a.gram);
+        g.a = g.b = sel(cur != 0, sel(b, PB.gram_op[1], p.a.gram_op[1]),
+                        sel(b, PB.gram_op[0], p.a.gram_op[0]));
         if (it == 0 && g.fold)
-          gemm_tile<GRAM, T, TILE, KMODE == 2 ? 3 : 0, true>(g, ca, u, tm, tn, claim_next,
+          gemm_tile<GRAM, T, TILE, KMODE == 2 ? 3 : 0, true>(g, out_of, u, tm, tn, claim_next,
                                                             count_pending);
         else
-          gemm_tile<GRAM, T, TILE, KMODE == 2 ? 3 : 0>(g, ca, u, tm, tn, claim_next, count_pending);
+          gemm_tile<GRAM, T, TILE, KMODE == 2 ? 3 : 0>(g, out_of, u, tm, tn, claim_next,
+                                                       count_pending);
       }
     } else if (phase == POLY) {
       if (live) {
-        GemmArgs g = p.poly;
+        GemmArgs g = pick(b, PB.poly, p.a.poly);
         float a = p.sa[0], cb = p.sb[0], cc = p.sc[0];
 #pragma unroll
         for (int s = 1; s < 4; ++s)
@@ -2365,26 +2505,28 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
         g.ca = a;
         g.cb = cb;
         g.cc = cc;
-        gemm_tile<POLY, T, TILE, 0>(g, ca, u, tm, tn, claim_next, count_pending);
+        gemm_tile<POLY, T, TILE, 0>(g, out_of, u, tm, tn, claim_next, count_pending);
       }
     } else {
       const int fm = it == p.n_iter - 1 ? p.final_mode : (int)FINAL_NONE;
       if (live) {
-        GemmArgs g = p.apply;
+        GemmArgs g = pick(b, PB.apply, p.a.apply);
         g.final_mode = fm;
-        g.a = cur ? p.app_a[1] : p.app_a[0];
-        g.b = cur ? p.app_b[1] : p.app_b[0];
-        g.out32 = cur ? p.app_out32[1] : p.app_out32[0];
-        g.out16 = cur ? p.app_out16[1] : p.app_out16[0];
-        g.outt = cur ? p.app_outt[1] : p.app_outt[0];
+        const NsPass& PA = p.a;
+        const bool c1 = cur != 0;
+        g.a = sel(c1, sel(b, PB.app_a[1], PA.app_a[1]), sel(b, PB.app_a[0], PA.app_a[0]));
+        g.b = sel(c1, sel(b, PB.app_b[1], PA.app_b[1]), sel(b, PB.app_b[0], PA.app_b[0]));
+        g.out32 = sel(c1, sel(b, PB.app_out32[1], PA.app_out32[1]), sel(b, PB.app_out32[0], PA.app_out32[0]));
+        g.out16 = sel(c1, sel(b, PB.app_out16[1], PA.app_out16[1]), sel(b, PB.app_out16[0], PA.app_out16[0]));
+        g.outt = sel(c1, sel(b, PB.app_outt[1], PA.app_outt[1]), sel(b, PB.app_outt[0], PA.app_outt[0]));
         if (it == 0 && g.fold)
-          gemm_tile<APPLY, T, TILE, KMODE == 1 ? 2 : 0, true>(g, ca, u, tm, tn, claim_next,
+          gemm_tile<APPLY, T, TILE, KMODE == 1 ? 2 : 0, true>(g, out_of, u, tm, tn, claim_next,
                                                              count_pending);
         else
-          gemm_tile<APPLY, T, TILE, KMODE == 1 ? 2 : 0>(g, ca, u, tm, tn, claim_next,
+          gemm_tile<APPLY, T, TILE, KMODE == 1 ? 2 : 0>(g, out_of, u, tm, tn, claim_next,
                                                        count_pending);
       } else if (fm != FINAL_NONE) {
-        zero_unit_tile<TILE>(ca, fm, u, tm * TILE, tn * TILE);
+        zero_unit_tile<TILE>(out_of(), fm, tm * TILE, tn * TILE);
       }
     }
     if (live) {
@@ -2396,6 +2538,17 @@ __global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p,
     // epilogue staged through; the barrier after the next claim orders them.
   }
   // Every exit flushes the pending tile first.
+}
+
+template <typename T, int TILE, int KMODE>
+__global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent(NsSched p, ChunkArgs ca) {
+  ns_persistent_run<T, TILE, KMODE, false>(p, ca, nullptr);
+}
+
+template <typename T, int TILE, int KMODE>
+__global__ __launch_bounds__(gemm_threads<TILE>()) void ns_persistent2(NsSched p, ChunkArgs ca,
+                                                                       NsPassB second) {
+  ns_persistent_run<T, TILE, KMODE, true>(p, ca, &second);
 }
 
 }  // namespace muon_dev

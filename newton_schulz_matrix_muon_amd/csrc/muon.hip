@@ -17,8 +17,11 @@
 //  3. A chunk is one stacked pass: every kernel of the step runs once over
 //     all of its units (and the ten NS iterations run back to back), with the
 //     iterates laid out at a fixed stride in the caller's workspace.
+//  4. AUTO: a pass of one 256-tile unit may ride along in a stacked pass's
+//     persistent launch (pair_passes).
 // The workspace is a 256-byte status header (word 0: the schedule error
-// word) followed by the carve-up of the largest chunk, reused by every chunk.
+// word) followed by the carve-up of the largest chunk, reused by every chunk
+// (a pass with a riding pass: the two carve-ups one after the other).
 #include "../../include/muon.h"
 
 #include <algorithm>
@@ -73,6 +76,9 @@ struct Chunk {
   int tiles_t;                           // momentum kernel of transposed units: 64x64 tiles
   int partials_per_unit;                 // max of the two
   int norm_blocks_per_unit;              // 64x64 tiles of the padded iterate
+  int rider = -1;  // AUTO: a one-unit pass that may run inside this pass's
+                   // persistent launch (pair_passes)
+  int host = -1;   // this pass may run inside pass `host`'s launch
 };
 
 // Workspace carve-up of one chunk (byte offsets).
@@ -222,6 +228,45 @@ int pick_tile(int64_t rows_u, int64_t cols) {
   return std::min(rows_u, cols) >= 256 ? 256 : 128;
 }
 
+// AUTO: a pass of one 256-tile unit runs its three products as separate
+// launches (faster than a persistent launch of its own), which leave CUs
+// idle (the Gram of a 4096 x 4096 unit has 136 tiles).  It may instead
+// ride along in the persistent launch of a stacked pass with the same tile
+// size and operand layout (ns_persistent2), the larger such pass first,
+// each stacked pass taking at most one.  Whether it does is decided per
+// call on the device (run): the stacked pass must take one claim queue.
+// Sides of unit shapes stay below 2^31 (validate_descs), so the trace's
+// packed values hold both passes.
+void pair_passes(std::vector<Chunk>* cs, const muon_hyper* h) {
+  const bool bf16 = h->ns_precision == MUON_NS_BF16;
+  for (size_t j = 0; j < cs->size(); ++j) {
+    Chunk& q = (*cs)[j];
+    if (q.tile != 256 || q.n_units != 1 || small_possible(q, h) || q.segs.size() > (size_t)kMaxSegB)
+      continue;
+    int best = -1;
+    double best_work = 0.0;
+    for (size_t i = 0; i < cs->size(); ++i) {
+      const Chunk& p = (*cs)[i];
+      if (i == j || p.tile != 256 || p.n_units < 2 || small_possible(p, h) || p.rider >= 0 ||
+          p.host >= 0)
+        continue;
+      // one operand layout per launch: bf16 wide and tall units read X
+      // differently (fp32 units all read rows of X and X^T)
+      if (bf16 && p.tall != q.tall) continue;
+      const double work = (double)p.n_units * (double)p.s_pad * (double)p.s_pad *
+                          (double)std::max(p.rows_pad, p.cols_pad);
+      if (work > best_work) {
+        best = (int)i;
+        best_work = work;
+      }
+    }
+    if (best >= 0) {
+      (*cs)[best].rider = (int)j;
+      q.host = best;
+    }
+  }
+}
+
 // Group the banks' units by shape and cut the groups into chunks.
 int plan(const muon_matrix_desc* mats, int64_t n, const muon_hyper* h, bool step,
          std::vector<Chunk>* chunks) {
@@ -330,12 +375,18 @@ int plan(const muon_matrix_desc* mats, int64_t n, const muon_hyper* h, bool step
     // a K-major bf16 operand tile spans every row of the iterate
     if (c.rows_pad * c.cols_pad * 2 >= ((int64_t)1 << 31)) return MUON_ERR_SHAPE;
   }
+  if (h->schedule == MUON_SCHEDULE_AUTO) pair_passes(chunks, h);
   return MUON_OK;
 }
 
 size_t workspace_of(const std::vector<Chunk>& chunks, const muon_hyper* h) {
   size_t need = kHeader;
-  for (const Chunk& c : chunks) need = std::max(need, layout_of(c, h).total);
+  for (const Chunk& c : chunks) {
+    size_t t = layout_of(c, h).total;
+    // a riding pass's buffers follow the stacked pass's
+    if (c.rider >= 0) t += layout_of(chunks[(size_t)c.rider], h).total - kHeader;
+    need = std::max(need, t);
+  }
   return need;
 }
 
@@ -410,9 +461,14 @@ struct Tracer {
       t->count++;
     }
   }
-  // an NS launch over a chunk: smaller and larger unit side, units, tile
-  void after_ns(int kind, const Chunk& c) {
-    after(kind, std::min(c.rows_u, c.cols), std::max(c.rows_u, c.cols), c.n_units, c.tile);
+  // an NS launch over a chunk: smaller and larger unit side, units, tile;
+  // a launch that also runs a riding pass carries that pass's three values
+  // in the upper 32 bits of each (muon.h, muon_trace)
+  void after_ns(int kind, const Chunk& c, const Chunk* r = nullptr) {
+    auto pack = [](int64_t lo, int64_t hi) { return lo | (hi << 32); };
+    after(kind, pack(std::min(c.rows_u, c.cols), r ? std::min(r->rows_u, r->cols) : 0),
+          pack(std::max(c.rows_u, c.cols), r ? std::max(r->rows_u, r->cols) : 0),
+          pack(c.n_units, r ? r->n_units : 0), c.tile);
   }
 };
 
@@ -523,57 +579,273 @@ void launch_phase(bool bf16, int tile, int km, const GemmArgs& g, const ChunkArg
     launch_gemm<PHASE, __bf16, 0>(tile, g, ca, s);
 }
 
-// Runs one chunk: momentum (or NS-input copy), norms, normalisation (folded
-// into the first iteration on the bf16 paths) and the NS iterations with the
-// fused final epilogue; units of one 128 x 128 block take all of it in one
-// launch.
-int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs,
-              const void* const* ins, float* const* moms, const muon_matrix_desc* mats,
-              unsigned char* ws, hipStream_t s, Tracer& tr, bool first_chunk,
-              bool allow_waits) {
-  const bool bf16 = h->ns_precision == MUON_NS_BF16;
-  const Layout L = layout_of(c, h);
-  ChunkArgs ca;
-  std::memset(&ca, 0, sizeof(ca));
-  ca.n_seg = (int32_t)c.segs.size();
-  ca.n_units = (int32_t)c.n_units;
-  ca.rows = (int32_t)c.rows_u;
-  ca.cols = (int32_t)c.cols;
-  ca.rows_pad = (int32_t)c.rows_pad;
-  ca.cols_pad = (int32_t)c.cols_pad;
-  ca.unit_elems = c.rows_u * c.cols;
-  ca.x_stride = c.rows_pad * c.cols_pad;
-  momentum_coefficients(h, &ca.ma, &ca.mb, &ca.la, &ca.lb);
-  ca.decay = (float)(1.0 - (double)h->lr * (double)h->weight_decay);
-  ca.lr_scale = (float)((double)h->lr * unit_scale(c.rows_u, c.cols, h));
+// The chunk's kernel arguments: its shape, the momentum coefficients and
+// the caller matrices of its units.
+void fill_chunk_args(ChunkArgs* ca, const Chunk& c, const muon_hyper* h, bool step,
+                     float* const* outs, const void* const* ins, float* const* moms,
+                     const muon_matrix_desc* mats) {
+  std::memset(ca, 0, sizeof(*ca));
+  ca->n_seg = (int32_t)c.segs.size();
+  ca->n_units = (int32_t)c.n_units;
+  ca->rows = (int32_t)c.rows_u;
+  ca->cols = (int32_t)c.cols;
+  ca->rows_pad = (int32_t)c.rows_pad;
+  ca->cols_pad = (int32_t)c.cols_pad;
+  ca->unit_elems = c.rows_u * c.cols;
+  ca->x_stride = c.rows_pad * c.cols_pad;
+  momentum_coefficients(h, &ca->ma, &ca->mb, &ca->la, &ca->lb);
+  ca->decay = (float)(1.0 - (double)h->lr * (double)h->weight_decay);
+  ca->lr_scale = (float)((double)h->lr * unit_scale(c.rows_u, c.cols, h));
   const float lr_scale_t = (float)((double)h->lr * unit_scale(c.cols, c.rows_u, h));
   int32_t first = 0;
   for (size_t i = 0; i < c.segs.size(); ++i) {
     const SegRef& r = c.segs[i];
     const int64_t off = r.unit_begin * c.rows_u * c.cols;  // elements
-    ca.seg[i].w = outs[r.desc] + off;
+    ca->seg[i].w = outs[r.desc] + off;
     const size_t gsz = (step && mats[r.desc].grad_dtype == MUON_DTYPE_BF16) ? 2 : 4;
-    ca.seg[i].g = static_cast<const unsigned char*>(ins[r.desc]) + off * (int64_t)gsz;
-    ca.seg[i].m = step ? moms[r.desc] + off : nullptr;
-    ca.seg[i].first = first;
-    ca.seg[i].count = (int32_t)r.count;
-    ca.seg[i].trans = r.trans ? 1 : 0;
+    ca->seg[i].g = static_cast<const unsigned char*>(ins[r.desc]) + off * (int64_t)gsz;
+    ca->seg[i].m = step ? moms[r.desc] + off : nullptr;
+    ca->seg[i].first = first;
+    ca->seg[i].count = (int32_t)r.count;
+    ca->seg[i].trans = r.trans ? 1 : 0;
     // a transposed unit's fan_out is the chunk's cols
-    ca.seg[i].lr_scale = r.trans ? lr_scale_t : ca.lr_scale;
+    ca->seg[i].lr_scale = r.trans ? lr_scale_t : ca->lr_scale;
     first += (int32_t)r.count;
   }
+}
 
-  float* x32[2] = {L.x32[0] ? reinterpret_cast<float*>(ws + L.x32[0]) : nullptr,
-                   bf16 ? nullptr : reinterpret_cast<float*>(ws + L.x32[1])};
-  uint16_t* xb[2] = {bf16 ? reinterpret_cast<uint16_t*>(ws + L.xb[0]) : nullptr,
-                     bf16 ? reinterpret_cast<uint16_t*>(ws + L.xb[1]) : nullptr};
-  void* xt[2] = {bf16 ? nullptr : ws + L.xt[0], bf16 ? nullptr : ws + L.xt[1]};
-  float* a32 = bf16 ? nullptr : reinterpret_cast<float*>(ws + L.a32);
-  uint16_t* ab = bf16 ? reinterpret_cast<uint16_t*>(ws + L.ab) : nullptr;
-  void* bop = ws + L.bop;
-  double* partials = reinterpret_cast<double*>(ws + L.partials);
-  float* inv_nu = reinterpret_cast<float*>(ws + L.inv_nu);
-  int32_t* flag = reinterpret_cast<int32_t*>(ws + L.flag);
+// A chunk's buffers in the workspace.  `base` is where its layout's offsets
+// count from: the workspace itself, or, for a pass riding along in another
+// pass's launch, the end of that pass's buffers (less the header).
+struct ChunkBufs {
+  Layout L;
+  float* x32[2];
+  uint16_t* xb[2];
+  void* xt[2];
+  float* a32;
+  uint16_t* ab;
+  void* bop;
+  double* partials;
+  float* inv_nu;
+  int32_t* flag;
+  uint32_t* done;
+  uint32_t* queue;
+  void* split;
+};
+
+ChunkBufs chunk_bufs(const Chunk& c, const muon_hyper* h, unsigned char* base) {
+  const bool bf16 = h->ns_precision == MUON_NS_BF16;
+  ChunkBufs B;
+  B.L = layout_of(c, h);
+  const Layout& L = B.L;
+  B.x32[0] = L.x32[0] ? reinterpret_cast<float*>(base + L.x32[0]) : nullptr;
+  B.x32[1] = bf16 ? nullptr : reinterpret_cast<float*>(base + L.x32[1]);
+  B.xb[0] = bf16 ? reinterpret_cast<uint16_t*>(base + L.xb[0]) : nullptr;
+  B.xb[1] = bf16 ? reinterpret_cast<uint16_t*>(base + L.xb[1]) : nullptr;
+  B.xt[0] = bf16 ? nullptr : base + L.xt[0];
+  B.xt[1] = bf16 ? nullptr : base + L.xt[1];
+  B.a32 = bf16 ? nullptr : reinterpret_cast<float*>(base + L.a32);
+  B.ab = bf16 ? reinterpret_cast<uint16_t*>(base + L.ab) : nullptr;
+  B.bop = base + L.bop;
+  B.partials = reinterpret_cast<double*>(base + L.partials);
+  B.inv_nu = reinterpret_cast<float*>(base + L.inv_nu);
+  B.flag = reinterpret_cast<int32_t*>(base + L.flag);
+  B.done = reinterpret_cast<uint32_t*>(base + L.done);
+  B.queue = reinterpret_cast<uint32_t*>(base + L.queue);
+  B.split = L.split ? base + L.split : nullptr;
+  return B;
+}
+
+// Steps 1 and 2 of a tiled or streamed pass: momentum (or the NS-input
+// copy) with the partial sums of squares, the norm finish, and, off the
+// folded path, X0 = N / ||N||_F.  `err`: the call's status word when this
+// is the first pass of the call (the norm finish clears it), else nullptr.
+void launch_prologue(const Chunk& c, const ChunkArgs& ca, const ChunkBufs& B, const muon_hyper* h,
+                     bool step, uint32_t* err, hipStream_t s, Tracer& tr) {
+  const bool bf16 = h->ns_precision == MUON_NS_BF16;
+  // The bf16 paths fold 1/nu into the first iteration: momentum writes N
+  // straight into the bf16 iterate (padding zeroed) and no normalisation
+  // pass runs.
+  uint16_t* const nb = bf16 ? B.xb[0] : nullptr;
+  const int gk = !step ? 2 : (c.gdtype == MUON_DTYPE_BF16 ? 0 : 1);
+  // Units in their own form (0 .. n_plain - 1), then transposed ones; each
+  // launch's algorithmic bytes: G (or the NS input) read, M read and
+  // written (step), N written into the bf16 iterate (2 B) or in fp32 (4 B).
+  const int64_t pp = c.partials_per_unit;
+  auto mom_info = [&](int64_t units) {
+    const int64_t elems = units * c.rows_u * c.cols;
+    const int64_t gsz = (step && c.gdtype == MUON_DTYPE_BF16) ? 2 : 4;
+    const int64_t per = gsz + (step ? 8 : 0) + (nb ? 2 : 4);
+    tr.after(MUON_KERNEL_MOMENTUM, elems, elems * per, units, 0);
+  };
+  float* const x0 = B.x32[0];
+  double* const partials = B.partials;
+  if (c.n_plain > 0) {
+    tr.before(MUON_KERNEL_MOMENTUM);
+    const dim3 grid((unsigned)(c.n_plain * c.blocks_per_unit));
+    const int bpu = c.blocks_per_unit, rpb = c.rows_per_block;
+    if (gk == 2)
+      hipLaunchKernelGGL(k_momentum<2>, grid, dim3(kThreads), 0, s, ca, x0, nb, partials, rpb, bpu, 0, (int)pp);
+    else if (gk == 0)
+      hipLaunchKernelGGL(k_momentum<0>, grid, dim3(kThreads), 0, s, ca, x0, nb, partials, rpb, bpu, 0, (int)pp);
+    else
+      hipLaunchKernelGGL(k_momentum<1>, grid, dim3(kThreads), 0, s, ca, x0, nb, partials, rpb, bpu, 0, (int)pp);
+    mom_info(c.n_plain);
+  }
+  if (c.n_units > c.n_plain) {
+    tr.before(MUON_KERNEL_MOMENTUM);
+    const dim3 grid((unsigned)((c.n_units - c.n_plain) * c.tiles_t));
+    const int u0 = (int)c.n_plain;
+    if (gk == 2)
+      hipLaunchKernelGGL(k_momentum_t<2>, grid, dim3(kThreads), 0, s, ca, x0, nb, partials, u0, (int)pp);
+    else if (gk == 0)
+      hipLaunchKernelGGL(k_momentum_t<0>, grid, dim3(kThreads), 0, s, ca, x0, nb, partials, u0, (int)pp);
+    else
+      hipLaunchKernelGGL(k_momentum_t<1>, grid, dim3(kThreads), 0, s, ca, x0, nb, partials, u0, (int)pp);
+    mom_info(c.n_units - c.n_plain);
+  }
+  // norms (and, off the folded path, X0 = N / ||N||_F)
+  tr.before(MUON_KERNEL_NORMALIZE);
+  hipLaunchKernelGGL(k_norm_finish, dim3((unsigned)c.n_units), dim3(kThreads), 0, s, partials,
+                     (int)pp, B.inv_nu, B.flag, B.done, (int)done_words(c), B.queue,
+                     kMaxQueues + 1, err, nb, (int64_t)(c.rows_pad * c.cols_pad));
+  if (!bf16)
+    hipLaunchKernelGGL(k_normalize, dim3((unsigned)(c.n_units * c.norm_blocks_per_unit)),
+                       dim3(kThreads), 0, s, ca, x0, static_cast<float*>(B.xt[0]), B.inv_nu,
+                       (int)(c.cols_pad / 64), c.norm_blocks_per_unit);
+  tr.after(MUON_KERNEL_NORMALIZE, c.n_units);
+}
+
+// Symmetric tiles per unit (upper triangle) and apply tiles per unit.
+int sym_tiles(const Chunk& c) {
+  const int64_t t = c.s_pad / c.tile;
+  return (int)(t * (t + 1) / 2);
+}
+int apply_tiles(const Chunk& c) { return (int)((c.rows_pad / c.tile) * (c.cols_pad / c.tile)); }
+
+// The persistent schedule's description of one pass: its three products
+// and where its tiles are counted.
+void fill_pass(NsPass* P, const Chunk& c, const ChunkBufs& B, const muon_hyper* h) {
+  const bool bf16 = h->ns_precision == MUON_NS_BF16;
+  std::memset(P, 0, sizeof(*P));
+  const int U = (int)c.n_units;
+  const int T = c.tile;
+  const int64_t xs = c.rows_pad * c.cols_pad;
+  const int64_t ss = c.s_pad * c.s_pad;
+  const int64_t sp = c.s_pad;
+  // Operand copies of the iterate: X as is (bf16, or the fp32 iterate
+  // itself) and, on the fp32 path only, X^T (cols_pad x rows_pad); the bf16
+  // products read X K-major instead.
+  const void* xop[2] = {bf16 ? (const void*)B.xb[0] : (const void*)B.x32[0],
+                        bf16 ? (const void*)B.xb[1] : (const void*)B.x32[1]};
+  const void* aop = bf16 ? (const void*)B.ab : (const void*)B.a32;
+  // First iteration's scale on the folded path (inv_nu as k_norm_finish
+  // left it): Gram by its square, apply by itself.
+  const float* const fold_scale = bf16 ? B.inv_nu : nullptr;
+  // Gram: A = X X^T (wide, rows of X) or X^T X (tall, rows of X^T).
+  // bf16: a tall unit's X^T X reads X K-major; fp32: rows of X^T.
+  GemmArgs& gg = P->gram;
+  gg.n_units = U;
+  gg.flag = B.flag;
+  gg.fold = fold_scale;  // the kernel keeps it for the first iteration only
+  gg.a_ustride = gg.b_ustride = xs;
+  gg.lda = gg.ldb = (int32_t)(c.tall && !bf16 ? c.rows_pad : c.cols_pad);
+  gg.M = gg.N = (int32_t)sp;
+  gg.K = (int32_t)(c.tall ? c.rows_pad : c.cols_pad);
+  gg.tiles_m = gg.tiles_n = (int32_t)(sp / T);
+  gg.sym = 1;
+  gg.out32 = B.a32;
+  gg.out16 = B.ab;
+  gg.out_ustride = ss;
+  gg.ldo = (int32_t)sp;
+  for (int k = 0; k < 2; ++k) P->gram_op[k] = c.tall && !bf16 ? (const void*)B.xt[k] : xop[k];
+  // Polynomial: B' = a*I + b*A + c*A*A (the apply's a*X term on its
+  // diagonal; a comes per iteration).
+  GemmArgs& gp = P->poly;
+  gp.n_units = U;
+  gp.flag = B.flag;
+  gp.a = gp.b = aop;
+  gp.a_ustride = gp.b_ustride = ss;
+  gp.lda = gp.ldb = (int32_t)sp;
+  gp.M = gp.N = gp.K = (int32_t)sp;
+  gp.tiles_m = gp.tiles_n = (int32_t)(sp / T);
+  gp.sym = 1;
+  gp.out32 = bf16 ? nullptr : static_cast<float*>(B.bop);
+  gp.out16 = bf16 ? B.bop : nullptr;
+  gp.out_ustride = ss;
+  gp.ldo = (int32_t)sp;
+  gp.aux = B.a32;
+  gp.aux16 = B.ab;
+  gp.aux_ustride = ss;
+  gp.ldaux = (int32_t)sp;
+  // Apply: X' = B'*X (wide) or X*B' (tall).
+  GemmArgs& ga = P->apply;
+  ga.n_units = U;
+  ga.flag = B.flag;
+  ga.fold = fold_scale;
+  ga.M = (int32_t)c.rows_pad;
+  ga.N = (int32_t)c.cols_pad;
+  ga.K = (int32_t)sp;
+  ga.tiles_m = (int32_t)(c.rows_pad / T);
+  ga.tiles_n = (int32_t)(c.cols_pad / T);
+  if (!c.tall) {
+    ga.a_ustride = ss;
+    ga.lda = (int32_t)sp;
+    ga.b_ustride = xs;
+    ga.ldb = (int32_t)(bf16 ? c.cols_pad : c.rows_pad);  // X K-major, or rows of X^T
+  } else {
+    ga.a_ustride = xs;
+    ga.lda = (int32_t)c.cols_pad;
+    ga.b_ustride = ss;
+    ga.ldb = (int32_t)sp;
+  }
+  ga.out_ustride = xs;
+  ga.ldo = (int32_t)c.cols_pad;
+  ga.ldt = (int32_t)c.rows_pad;
+  for (int k = 0; k < 2; ++k) {
+    const int nx = k ^ 1;
+    P->app_a[k] = c.tall ? xop[k] : (const void*)B.bop;
+    P->app_b[k] = c.tall ? (const void*)B.bop : (bf16 ? xop[k] : (const void*)B.xt[k]);
+    P->app_out32[k] = bf16 ? nullptr : B.x32[nx];
+    P->app_out16[k] = bf16 ? (void*)B.xb[nx] : nullptr;
+    P->app_outt[k] = B.xt[nx];  // nullptr on the bf16 path
+  }
+  P->done = B.done;
+  P->n_units = U;
+  P->tg = sym_tiles(c);
+  P->ta = apply_tiles(c);
+  P->apply_s_m = c.tall ? 0 : 1;
+}
+
+// Claim queues of a persistent launch over `units` units: one per XCC when
+// the units spread over the XCCs with at most an eighth of the slots idle,
+// one otherwise.
+int queues_for(int64_t units, int xccs) {
+  const int64_t slots = (units + xccs - 1) / xccs * (int64_t)xccs;
+  return (xccs > 1 && units >= xccs && 8 * (slots - units) <= slots) ? xccs : 1;
+}
+
+// Work items of a pass's persistent schedule.
+int64_t persistent_items(const Chunk& c, int n_iter) {
+  return (int64_t)n_iter * c.n_units * (2 * (int64_t)sym_tiles(c) + apply_tiles(c));
+}
+
+// Runs one chunk: momentum (or NS-input copy), norms, normalisation (folded
+// into the first iteration on the bf16 paths) and the NS iterations with the
+// fused final epilogue; units of one 128 x 128 block take all of it in one
+// launch.  `rider`: a one-unit pass whose products run inside this chunk's
+// persistent launch (pair_passes; its buffers follow this chunk's in the
+// workspace).
+int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs,
+              const void* const* ins, float* const* moms, const muon_matrix_desc* mats,
+              unsigned char* ws, hipStream_t s, Tracer& tr, bool first_chunk,
+              bool allow_waits, const Chunk* rider = nullptr) {
+  const bool bf16 = h->ns_precision == MUON_NS_BF16;
+  ChunkArgs ca;
+  fill_chunk_args(&ca, c, h, step, outs, ins, moms, mats);
+  const ChunkBufs B = chunk_bufs(c, h, ws);
+  const Layout& L = B.L;
+  uint16_t* const* xb = B.xb;
 
   const int U = (int)c.n_units;
   // Small wide units (AUTO schedule; at most 128 rows with bf16 products,
@@ -619,8 +891,8 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
     }
     p.n_iter = begin;
     p.final_mode = step ? FINAL_STEP : FINAL_NSOUT;
-    p.inv_nu = reinterpret_cast<float*>(ws + L.inv_nu);
-    p.flag = reinterpret_cast<int32_t*>(ws + L.flag);
+    p.inv_nu = B.inv_nu;
+    p.flag = B.flag;
     p.groups = 1;
     return p;
   };
@@ -658,179 +930,61 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
     tr.after_ns(MUON_KERNEL_NS_SMALL, c);
     return hipGetLastError() == hipSuccess ? MUON_OK : MUON_ERR_HIP;
   }
-  // The bf16 paths fold 1/nu into the first iteration: momentum writes N
-  // straight into the bf16 iterate (padding zeroed) and no normalisation
-  // pass runs.
-  const bool fold = bf16;
-  uint16_t* const nb = fold ? xb[0] : nullptr;
-  // 1. momentum + Nesterov + partial sums of squares.
-  // Units in their own form (0 .. n_plain - 1), then transposed ones; each
-  // launch's algorithmic bytes: G (or the NS input) read, M read and
-  // written (step), N written into the bf16 iterate (2 B) or in fp32 (4 B).
-  const int64_t pp = c.partials_per_unit;
-  auto mom_info = [&](int64_t units) {
-    const int64_t elems = units * c.rows_u * c.cols;
-    const int64_t gsz = (step && c.gdtype == MUON_DTYPE_BF16) ? 2 : 4;
-    const int64_t per = gsz + (step ? 8 : 0) + (nb ? 2 : 4);
-    tr.after(MUON_KERNEL_MOMENTUM, elems, elems * per, units, 0);
-  };
-  if (c.n_plain > 0) {
-    tr.before(MUON_KERNEL_MOMENTUM);
-    const dim3 grid((unsigned)(c.n_plain * c.blocks_per_unit));
-    const int bpu = c.blocks_per_unit, rpb = c.rows_per_block;
-    if (gk == 2)
-      hipLaunchKernelGGL(k_momentum<2>, grid, dim3(kThreads), 0, s, ca, x32[0], nb, partials, rpb, bpu, 0, (int)pp);
-    else if (gk == 0)
-      hipLaunchKernelGGL(k_momentum<0>, grid, dim3(kThreads), 0, s, ca, x32[0], nb, partials, rpb, bpu, 0, (int)pp);
-    else
-      hipLaunchKernelGGL(k_momentum<1>, grid, dim3(kThreads), 0, s, ca, x32[0], nb, partials, rpb, bpu, 0, (int)pp);
-    mom_info(c.n_plain);
+  // 1-2. momentum, norms (and X0 on the fp32 path); the riding pass's too.
+  uint32_t* const err = reinterpret_cast<uint32_t*>(ws);
+  launch_prologue(c, ca, B, h, step, first_chunk ? err : nullptr, s, tr);
+  ChunkArgs ca_r;
+  ChunkBufs B_r{};
+  if (rider) {
+    fill_chunk_args(&ca_r, *rider, h, step, outs, ins, moms, mats);
+    B_r = chunk_bufs(*rider, h, ws + (L.total - kHeader));
+    launch_prologue(*rider, ca_r, B_r, h, step, nullptr, s, tr);
   }
-  if (c.n_units > c.n_plain) {
-    tr.before(MUON_KERNEL_MOMENTUM);
-    const dim3 grid((unsigned)((c.n_units - c.n_plain) * c.tiles_t));
-    const int u0 = (int)c.n_plain;
-    if (gk == 2)
-      hipLaunchKernelGGL(k_momentum_t<2>, grid, dim3(kThreads), 0, s, ca, x32[0], nb, partials, u0, (int)pp);
-    else if (gk == 0)
-      hipLaunchKernelGGL(k_momentum_t<0>, grid, dim3(kThreads), 0, s, ca, x32[0], nb, partials, u0, (int)pp);
-    else
-      hipLaunchKernelGGL(k_momentum_t<1>, grid, dim3(kThreads), 0, s, ca, x32[0], nb, partials, u0, (int)pp);
-    mom_info(c.n_units - c.n_plain);
-  }
-  // 2. norms (and, off the folded path, X0 = N / ||N||_F).
-  tr.before(MUON_KERNEL_NORMALIZE);
-  uint32_t* done = reinterpret_cast<uint32_t*>(ws + L.done);
-  uint32_t* queue = reinterpret_cast<uint32_t*>(ws + L.queue);
-  uint32_t* err = reinterpret_cast<uint32_t*>(ws);
-  hipLaunchKernelGGL(k_norm_finish, dim3(U), dim3(kThreads), 0, s, partials, (int)pp,
-                     inv_nu, flag, done, (int)done_words(c), queue, kMaxQueues + 1,
-                     first_chunk ? err : nullptr, nb,
-                     (int64_t)(c.rows_pad * c.cols_pad));
   if (small) {
     NsSmallArgs p = small_args();
     if (groups > 1) {
       p.groups = groups;
-      p.cnt = done;
+      p.cnt = B.done;
       p.cnt_stride = (int32_t)done_words(c);
-      p.part = reinterpret_cast<float*>(ws + L.split);
+      p.part = static_cast<float*>(B.split);
       p.err = err;
       p.timeout_ticks = wait_ticks;
     }
-    tr.after(MUON_KERNEL_NORMALIZE, c.n_units);
     tr.before(MUON_KERNEL_NS_SMALL);
     hipLaunchKernelGGL(k_ns_small, dim3(U * groups), dim3(kThreads), 0, s, p, ca);
     tr.after_ns(MUON_KERNEL_NS_SMALL, c);
     return hipGetLastError() == hipSuccess ? MUON_OK : MUON_ERR_HIP;
   }
-  const int tiles_c = (int)(c.cols_pad / 64);
-  if (!fold)
-    hipLaunchKernelGGL(k_normalize, dim3(U * c.norm_blocks_per_unit), dim3(kThreads), 0, s, ca,
-                       x32[0], static_cast<float*>(xt[0]), inv_nu, tiles_c, c.norm_blocks_per_unit);
-  tr.after(MUON_KERNEL_NORMALIZE, c.n_units);
-  // First iteration's scale on the folded path (inv_nu as k_norm_finish
-  // left it): Gram by its square, apply by itself.
-  const float* const fold_scale = fold ? inv_nu : nullptr;
 
   // 3. Newton-Schulz iterations.
   const int T = c.tile;
   const int64_t xs = c.rows_pad * c.cols_pad;
   const int64_t ss = c.s_pad * c.s_pad;
   const int64_t sp = c.s_pad;
-  // Operand copies of the iterate: X as is (bf16, or the fp32 iterate
-  // itself) and, on the fp32 path only, X^T (cols_pad x rows_pad); the bf16
-  // products read X K-major instead.
-  const void* xop[2] = {bf16 ? (const void*)xb[0] : (const void*)x32[0],
-                        bf16 ? (const void*)xb[1] : (const void*)x32[1]};
-  const void* aop = bf16 ? (const void*)ab : (const void*)a32;
+  const void* xop[2] = {bf16 ? (const void*)xb[0] : (const void*)B.x32[0],
+                        bf16 ? (const void*)xb[1] : (const void*)B.x32[1]};
+  const void* aop = bf16 ? (const void*)B.ab : (const void*)B.a32;
+  const float* const fold_scale = bf16 ? B.inv_nu : nullptr;
   int total = 0;
   for (int i = 0; i < h->n_stages; ++i) total += h->stages[i].steps;
-  if (total == 0) return hipGetLastError() == hipSuccess ? MUON_OK : MUON_ERR_HIP;
-  const int tg = (int)((sp / T) * (sp / T + 1) / 2);
-  const int ta = (int)((c.rows_pad / T) * (c.cols_pad / T));
-  const int64_t n_items = (int64_t)total * U * (2 * tg + ta);
+  const int64_t n_items = persistent_items(c, total) + (rider ? persistent_items(*rider, total) : 0);
   // AUTO: persistent for 256-tile passes of two units or more.  128-tile
   // passes (short K) run faster as separate launches than as claimed
-  // tiles, and so does a pass of one unit, whose phases cannot overlap
-  // another unit's and whose single claim queue publishes every tile
-  // through memory (one 4096 x 4096 unit: 3.1 ms as launches, 3.6-3.9 ms
-  // persistent; two units: 6.4 ms against 5.4 ms).
+  // tiles, and so does a pass of one unit on its own, whose phases cannot
+  // overlap another unit's and whose single claim queue publishes every
+  // tile through memory (one 4096 x 4096 unit: 3.1 ms as launches, 3.6-3.9
+  // ms persistent; two units: 6.4 ms against 5.4 ms).  Such a pass runs
+  // inside a stacked pass's launch instead where one fits (`rider`).
   const bool persistent = allow_waits && (h->schedule == MUON_SCHEDULE_PERSISTENT ||
                                           (h->schedule == MUON_SCHEDULE_AUTO && T == 256 && U >= 2));
+  if (rider && !(persistent && n_items < INT32_MAX / 2)) return MUON_ERR_SCHEDULE;  // not reached
   if (persistent && n_items < INT32_MAX / 2) {
     DeviceInfo di;
     const int dst = device_info(&di);
     if (dst != MUON_OK) return dst;
     NsSched p;
     std::memset(&p, 0, sizeof(p));
-    // Gram: A = X X^T (wide, rows of X) or X^T X (tall, rows of X^T).
-    // bf16: a tall unit's X^T X reads X K-major; fp32: rows of X^T.
-    GemmArgs& gg = p.gram;
-    gg.n_units = U;
-    gg.flag = flag;
-    gg.fold = fold_scale;  // the kernel keeps it for the first iteration only
-    gg.a_ustride = gg.b_ustride = xs;
-    gg.lda = gg.ldb = (int32_t)(c.tall && !bf16 ? c.rows_pad : c.cols_pad);
-    gg.M = gg.N = (int32_t)sp;
-    gg.K = (int32_t)(c.tall ? c.rows_pad : c.cols_pad);
-    gg.tiles_m = gg.tiles_n = (int32_t)(sp / T);
-    gg.sym = 1;
-    gg.out32 = a32;
-    gg.out16 = ab;
-    gg.out_ustride = ss;
-    gg.ldo = (int32_t)sp;
-    for (int k = 0; k < 2; ++k) p.gram_op[k] = c.tall && !bf16 ? (const void*)xt[k] : xop[k];
-    // Polynomial: B' = a*I + b*A + c*A*A (the apply's a*X term on its
-    // diagonal; a comes per iteration).
-    GemmArgs& gp = p.poly;
-    gp.n_units = U;
-    gp.flag = flag;
-    gp.a = gp.b = aop;
-    gp.a_ustride = gp.b_ustride = ss;
-    gp.lda = gp.ldb = (int32_t)sp;
-    gp.M = gp.N = gp.K = (int32_t)sp;
-    gp.tiles_m = gp.tiles_n = (int32_t)(sp / T);
-    gp.sym = 1;
-    gp.out32 = bf16 ? nullptr : static_cast<float*>(bop);
-    gp.out16 = bf16 ? bop : nullptr;
-    gp.out_ustride = ss;
-    gp.ldo = (int32_t)sp;
-    gp.aux = a32;
-    gp.aux16 = ab;
-    gp.aux_ustride = ss;
-    gp.ldaux = (int32_t)sp;
-    // Apply: X' = B'*X (wide) or X*B' (tall).
-    GemmArgs& ga = p.apply;
-    ga.n_units = U;
-    ga.flag = flag;
-    ga.fold = fold_scale;
-    ga.M = (int32_t)c.rows_pad;
-    ga.N = (int32_t)c.cols_pad;
-    ga.K = (int32_t)sp;
-    ga.tiles_m = (int32_t)(c.rows_pad / T);
-    ga.tiles_n = (int32_t)(c.cols_pad / T);
-    if (!c.tall) {
-      ga.a_ustride = ss;
-      ga.lda = (int32_t)sp;
-      ga.b_ustride = xs;
-      ga.ldb = (int32_t)(bf16 ? c.cols_pad : c.rows_pad);  // X K-major, or rows of X^T
-    } else {
-      ga.a_ustride = xs;
-      ga.lda = (int32_t)c.cols_pad;
-      ga.b_ustride = ss;
-      ga.ldb = (int32_t)sp;
-    }
-    ga.out_ustride = xs;
-    ga.ldo = (int32_t)c.cols_pad;
-    ga.ldt = (int32_t)c.rows_pad;
-    for (int k = 0; k < 2; ++k) {
-      const int nx = k ^ 1;
-      p.app_a[k] = c.tall ? xop[k] : (const void*)bop;
-      p.app_b[k] = c.tall ? (const void*)bop : (bf16 ? xop[k] : (const void*)xt[k]);
-      p.app_out32[k] = bf16 ? nullptr : x32[nx];
-      p.app_out16[k] = bf16 ? (void*)xb[nx] : nullptr;
-      p.app_outt[k] = xt[nx];  // nullptr on the bf16 path
-    }
+    fill_pass(&p.a, c, B, h);
     p.final_mode = step ? FINAL_STEP : FINAL_NSOUT;
     p.n_iter = total;
     p.n_stages = h->n_stages;
@@ -844,16 +998,8 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
     }
     // A stage with zero steps begins where the next one does; the kernel
     // takes the last stage whose beginning it has reached.
-    p.tg = tg;
-    p.ta = ta;
-    p.apply_s_m = c.tall ? 0 : 1;
-    // One queue per XCC when the units spread over the XCCs with at most
-    // an eighth of the slots idle; one queue otherwise.
-    const int nx = di.xccs;
-    const int64_t slots = (U + nx - 1) / nx * (int64_t)nx;
-    p.n_queues = (nx > 1 && U >= nx && 8 * (slots - U) <= slots) ? nx : 1;
-    p.queue = queue;
-    p.done = done;
+    p.n_queues = rider ? 1 : queues_for(U, di.xccs);
+    p.queue = B.queue;
     p.err = err;
     p.timeout_ticks = wait_limit_ticks(di.wall_khz);
     int grid = (int)std::min<int64_t>(n_items, di.resident[bf16 ? 1 : 0][T == 256 ? 1 : 0]);
@@ -864,25 +1010,51 @@ int run_chunk(const Chunk& c, const muon_hyper* h, bool step, float* const* outs
       if (c > 0) grid = std::min(grid, c);
     }
     tr.before(MUON_KERNEL_NS);
-    if (bf16 && !c.tall) {
-      if (T == 256)
-        hipLaunchKernelGGL((ns_persistent<__bf16, 256, 1>), dim3(grid), dim3(gemm_threads<256>()), 0, s, p, ca);
+    if (rider) {
+      NsPassB pb;
+      std::memset(&pb, 0, sizeof(pb));
+      fill_pass(&pb.b, *rider, B_r, h);
+      pb.rows = ca_r.rows;
+      pb.cols = ca_r.cols;
+      pb.unit_elems = ca_r.unit_elems;
+      pb.decay = ca_r.decay;
+      pb.n_seg = ca_r.n_seg;
+      for (int i = 0; i < ca_r.n_seg; ++i) pb.seg[i] = ca_r.seg[i];  // n_seg <= kMaxSegB
+      const dim3 g3(grid), b3(gemm_threads<256>());
+      if (bf16 && !c.tall)
+        hipLaunchKernelGGL((ns_persistent2<__bf16, 256, 1>), g3, b3, 0, s, p, ca, pb);
+      else if (bf16)
+        hipLaunchKernelGGL((ns_persistent2<__bf16, 256, 2>), g3, b3, 0, s, p, ca, pb);
       else
-        hipLaunchKernelGGL((ns_persistent<__bf16, 128, 1>), dim3(grid), dim3(gemm_threads<128>()), 0, s, p, ca);
-    } else if (bf16) {
-      if (T == 256)
-        hipLaunchKernelGGL((ns_persistent<__bf16, 256, 2>), dim3(grid), dim3(gemm_threads<256>()), 0, s, p, ca);
-      else
-        hipLaunchKernelGGL((ns_persistent<__bf16, 128, 2>), dim3(grid), dim3(gemm_threads<128>()), 0, s, p, ca);
+        hipLaunchKernelGGL((ns_persistent2<float, 256, 0>), g3, b3, 0, s, p, ca, pb);
+      tr.after_ns(MUON_KERNEL_NS, c, rider);
     } else {
-      if (T == 256)
-        hipLaunchKernelGGL((ns_persistent<float, 256, 0>), dim3(grid), dim3(gemm_threads<256>()), 0, s, p, ca);
-      else
-        hipLaunchKernelGGL((ns_persistent<float, 128, 0>), dim3(grid), dim3(gemm_threads<128>()), 0, s, p, ca);
+      if (bf16 && !c.tall) {
+        if (T == 256)
+          hipLaunchKernelGGL((ns_persistent<__bf16, 256, 1>), dim3(grid), dim3(gemm_threads<256>()), 0, s, p, ca);
+        else
+          hipLaunchKernelGGL((ns_persistent<__bf16, 128, 1>), dim3(grid), dim3(gemm_threads<128>()), 0, s, p, ca);
+      } else if (bf16) {
+        if (T == 256)
+          hipLaunchKernelGGL((ns_persistent<__bf16, 256, 2>), dim3(grid), dim3(gemm_threads<256>()), 0, s, p, ca);
+        else
+          hipLaunchKernelGGL((ns_persistent<__bf16, 128, 2>), dim3(grid), dim3(gemm_threads<128>()), 0, s, p, ca);
+      } else {
+        if (T == 256)
+          hipLaunchKernelGGL((ns_persistent<float, 256, 0>), dim3(grid), dim3(gemm_threads<256>()), 0, s, p, ca);
+        else
+          hipLaunchKernelGGL((ns_persistent<float, 128, 0>), dim3(grid), dim3(gemm_threads<128>()), 0, s, p, ca);
+      }
+      tr.after_ns(MUON_KERNEL_NS, c);
     }
-    tr.after_ns(MUON_KERNEL_NS, c);
     return hipGetLastError() == hipSuccess ? MUON_OK : MUON_ERR_HIP;
   }
+  float* const* x32 = B.x32;
+  void* const* xt = B.xt;
+  float* const a32 = B.a32;
+  uint16_t* const ab = B.ab;
+  void* const bop = B.bop;
+  int32_t* const flag = B.flag;
   int it = 0;
   for (int st = 0; st < h->n_stages; ++st) {
     const muon_ns_stage& sg = h->stages[st];
@@ -1026,13 +1198,36 @@ int run(bool step, float* const* outs, const void* const* ins, float* const* mom
     if (((uintptr_t)ws & (kAlign - 1)) != 0) return MUON_ERR_ALIGN;
     Tracer tr{trace, stream};
     if (trace) trace->count = 0;
-    for (const Chunk& c : chunks) {
-      // The scratch's status header cannot be read by the callers of the
-      // scratch entry point, so their passes run as one launch per product,
-      // whose kernels never wait (bit-identical to the persistent launch).
+    // The scratch's status header cannot be read by the callers of the
+    // scratch entry point, so their passes run as one launch per product,
+    // whose kernels never wait (bit-identical to the persistent launch).
+    const bool allow_waits = !scratch_ws;
+    // Riding passes that run inside their stacked pass's launch on this
+    // device: the stacked pass takes one claim queue there.
+    std::vector<char> rides(chunks.size(), 0);
+    if (allow_waits) {
+      int total = 0;
+      for (int i = 0; i < h->n_stages; ++i) total += h->stages[i].steps;
+      for (const Chunk& c : chunks) {
+        if (c.rider < 0) continue;
+        DeviceInfo di;
+        st = device_info(&di);
+        if (st != MUON_OK) return st;
+        const Chunk& r = chunks[(size_t)c.rider];
+        if (queues_for(c.n_units, di.xccs) == 1 &&
+            persistent_items(c, total) + persistent_items(r, total) < INT32_MAX / 2)
+          rides[(size_t)c.rider] = 1;
+      }
+    }
+    bool first = true;
+    for (size_t i = 0; i < chunks.size(); ++i) {
+      if (rides[i]) continue;
+      const Chunk& c = chunks[i];
+      const Chunk* rider = c.rider >= 0 && rides[(size_t)c.rider] ? &chunks[(size_t)c.rider] : nullptr;
       st = run_chunk(c, h, step, outs, ins, moms, mats, static_cast<unsigned char*>(ws), stream, tr,
-                     &c == &chunks.front(), !scratch_ws);
+                     first, allow_waits, rider);
       if (st != MUON_OK) return st;
+      first = false;
     }
     return MUON_OK;
   } catch (const std::bad_alloc&) {
@@ -1158,6 +1353,6 @@ int muon_workspace_status(void* workspace, size_t workspace_bytes, hipStream_t s
   return MUON_ERR_SCHEDULE;
 }
 
-int muon_abi_version(void) { return 5; }
+int muon_abi_version(void) { return 6; }
 
 }  // extern "C"

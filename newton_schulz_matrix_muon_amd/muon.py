@@ -337,6 +337,23 @@ class Trace:
     def info(self) -> list[tuple[int, int, int, int]]:
         return [tuple(self._info[4 * i: 4 * i + 4]) for i in range(self.recorded)]
 
+    def passes(self) -> list[list[tuple[int, int, int, int]]]:
+        """For NS classes: the passes each recorded launch ran, as
+        (smaller side, larger side, units, tile) tuples (see ns_passes)."""
+        return [ns_passes(i) for i in self.info()]
+
+
+def ns_passes(info) -> list[tuple[int, int, int, int]]:
+    """The passes one NS launch ran, from its four trace values: its own
+    pass, and a single-unit pass it ran beside it, whose values sit in bits
+    32-63 of the first three (muon.h, muon_trace)."""
+    s, l, units, tile = (int(v) for v in info)
+    lo = (1 << 32) - 1
+    out = [(s & lo, l & lo, units & lo, tile)]
+    if units >> 32:
+        out.append((s >> 32, l >> 32, units >> 32, tile))
+    return out
+
 
 def _run_traced(fn, args, trace: Trace | None):
     if trace is None:

@@ -103,6 +103,40 @@ def test_bf16_workspace_holds_only_bf16_iterates():
     assert st == 0 and nf >= 48 * 128 * 4096 * 16
 
 
+def test_workspace_holds_a_riding_pass():
+    # AUTO: a single 256-tile unit (4096 x 4096) may run inside the
+    # persistent launch of a stacked pass with the same orientation (three
+    # tall 14336 x 4096 units), so the workspace holds both passes' buffers
+    # one after the other; forced schedules run the passes one by one and
+    # reuse one carve-up.
+    mib = 1024 * 1024
+    per_mlp = 14336 * 4096 * 4 + 2 * 4096 * 4096 * 2   # two bf16 iterates, bf16 A and B'
+    per_o = 4096 * 4096 * 8
+    shapes = [(1, 4096, 4096, 0), (2, 14336, 4096, 0), (1, 4096, 14336, 0)]
+    st, n = ws_size(shapes)
+    assert st == 0 and 3 * per_mlp + per_o <= n < 3 * per_mlp + per_o + mib
+    for sched in (muon.SCHEDULE_PERSISTENT, muon.SCHEDULE_LAUNCHES):
+        h = muon.default_hyper_c()
+        h.schedule = sched
+        st, nf = ws_size(shapes, h)
+        assert st == 0 and 3 * per_mlp <= nf < 3 * per_mlp + mib
+    # tiled passes take the tall form (wide units transposed), so wide
+    # units pair as well
+    st, n = ws_size([(1, 4096, 4096, 0), (3, 4096, 14336, 0)])
+    assert st == 0 and 3 * per_mlp + per_o <= n < 3 * per_mlp + per_o + mib
+    # one riding pass per stacked pass: the first in pass order (units in
+    # their own form before transposed ones), here the 4096 x 4096 unit
+    st, n = ws_size([(1, 2048, 4096, 0), (3, 4096, 14336, 0), (1, 4096, 4096, 0)])
+    assert st == 0 and 3 * per_mlp + per_o <= n < 3 * per_mlp + per_o + mib
+    # fp32 products read rows of X and X^T on every pass: any stacked pass
+    h = muon.default_hyper_c()
+    h.ns_precision = muon.NS_FP32
+    st, n = ws_size([(1, 512, 512, 0), (2, 1024, 512, 0)], h)
+    per_a = 1024 * 512 * 16 + 2 * 512 * 512 * 4
+    per_b = 512 * 512 * 16 + 2 * 512 * 512 * 4
+    assert st == 0 and 2 * per_a + per_b <= n < 2 * per_a + per_b + mib
+
+
 @pytest.mark.parametrize(
     "shape,code",
     [
@@ -280,4 +314,4 @@ def test_status_strings():
     for code in range(-9, 1):
         assert muon.status_string(code) != "unknown status"
     assert muon.status_string(12345) == "unknown status"
-    assert muon.LIB.muon_abi_version() == 5
+    assert muon.LIB.muon_abi_version() == 6

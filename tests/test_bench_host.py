@@ -74,6 +74,19 @@ def test_pass_breakdown_groups_launches_by_pass():
     assert rows[0]["tflops"] == pytest.approx(nom / 0.681 / 1e12)
 
 
+def test_two_pass_launch_counts_both_passes():
+    # a persistent launch that ran the layer's MLP units and, beside them,
+    # the O projection: the second pass in bits 32-63 (muon.h, muon_trace)
+    groups = {(4096, 14336): (3, 3), (4096, 4096): (1, 1)}
+    packed = (4096 | 4096 << 32, 14336 | 4096 << 32, 3 | 1 << 32, 256)
+    mlp, mlp_e = bench.launch_flops("ns", (4096, 14336, 3, 256), groups, 10)
+    o, o_e = bench.launch_flops("ns", (4096, 4096, 1, 256), groups, 10)
+    assert bench.launch_flops("ns", packed, groups, 10) == (mlp + o, mlp_e + o_e)
+    rows = bench.pass_breakdown("ns", [22.0, 24.0], [packed] * 2, groups, 10, 2516.6)
+    assert [r["pass"] for r in rows] == ["3 x 4096x14336 + 1 x 4096x4096"]
+    assert rows[0]["tflops"] == pytest.approx((mlp + o) / 0.023 / 1e12)
+
+
 def test_cpu_baseline_extrapolates_over_shapes(monkeypatch):
     import oracle
 

@@ -136,6 +136,99 @@ def test_persistent_with_xccs_left_without_workgroups(gpu_lib, workgroups, monke
     assert torch.equal(out["launches"], out["persistent"])
 
 
+# A single 256-tile unit under AUTO runs inside the persistent launch of a
+# stacked pass (ns_persistent2) when that pass takes one claim queue.
+# (banks, grad dtype, NS precision, index of a bank whose gradient is zero)
+RIDING = [
+    # the transformer layer's O projection beside its MLP units (down transposed)
+    ([(1, 4096, 4096, 0), (2, 14336, 4096, 0), (1, 4096, 14336, 0)], "bf16", "bf16", None),
+    # ragged: s = 300 and 520 on 256 tiles, a zero unit in the stacked pass
+    ([(3, 1100, 300, 0), (1, 700, 520, 0)], "bf16", "bf16", None),
+    # a riding unit with a zero gradient (pure decay in its final epilogue)
+    ([(2, 640, 256, 0), (1, 512, 384, 0)], "fp32", "bf16", 1),
+    # fp32 products; the riding unit is wide, stored transposed
+    ([(2, 640, 256, 0), (1, 300, 700, 0)], "bf16", "fp32", None),
+]
+
+
+def _run_steps(gpu_lib, banks, inputs, sched, prec, trace_kinds=()):
+    splits = [b[3] for b in banks]
+    h = gpu_lib.Hyper(ns_precision=prec, schedule=sched)
+    params = [w.clone() for w, _ in inputs]
+    moms = [torch.zeros_like(w) for w, _ in inputs]
+    ws = gpu_lib.workspace(gpu_lib.workspace_size(params, h, splits), torch.device(DEV))
+    traces = {}
+    for t in range(2):  # the second step starts from a live momentum
+        gpu_lib.step(params, [g for _, g in inputs], moms, hyper=h, split_rows=splits, ws=ws)
+    for kind in trace_kinds:
+        tr = gpu_lib.Trace(kind, 8)
+        n = gpu_lib.step([w.clone() for w in params], [g for _, g in inputs],
+                         [m.clone() for m in moms], hyper=h, split_rows=splits, ws=ws, trace=tr)
+        torch.cuda.synchronize()
+        traces[kind] = (n, tr.info()[:n])
+    gpu_lib.workspace_status(ws)
+    return params, moms, traces
+
+
+@pytest.mark.parametrize("case", range(len(RIDING)))
+def test_riding_pass_agrees_bitwise_with_launches(gpu_lib, case):
+    banks, gdtype, prec, zero = RIDING[case]
+    print(f"[schedule riding] case {case}: {banks} grads {gdtype} products {prec}", flush=True)
+    inputs = [_bank(s, 500 + 13 * i, gdtype) for i, s in enumerate(banks)]
+    if zero is not None:
+        inputs[zero][1].zero_()
+    kinds = (gpu_lib.KERNEL_NS, gpu_lib.KERNEL_GRAM)
+    pa, ma, tra = _run_steps(gpu_lib, banks, inputs, "auto", prec, kinds)
+    pl, ml, _ = _run_steps(gpu_lib, banks, inputs, "launches", prec)
+    for i in range(len(banks)):
+        assert torch.equal(pa[i], pl[i]), f"params of bank {i}"
+        assert torch.equal(ma[i], ml[i]), f"momenta of bank {i}"
+    # one NS launch carries both passes, and no per-product launch runs
+    n_ns, info = tra[gpu_lib.KERNEL_NS]
+    assert n_ns == 1 and tra[gpu_lib.KERNEL_GRAM][0] == 0
+    passes = gpu_lib.ns_passes(info[0])
+    assert len(passes) == 2 and passes[1][2] == 1 and all(p[3] == 256 for p in passes)
+    if zero is not None:
+        w0 = inputs[zero][0]
+        decay = 1.0 - 2.7e-4 * 0.1
+        expect = w0 * decay * decay
+        assert torch.allclose(pa[zero], expect, rtol=1e-6, atol=0)
+
+
+def test_riding_pass_ns_only(gpu_lib):
+    # the NS-only entry: the riding unit's final epilogue writes its output
+    print("[schedule riding ns-only]", flush=True)
+    g = torch.Generator(device="cpu").manual_seed(31)
+    xs = [torch.randn((3, 384, 256), generator=g).to(DEV), torch.randn((1, 300, 520), generator=g).to(DEV)]
+    res = {}
+    for sched in ("auto", "launches"):
+        tr = gpu_lib.Trace(gpu_lib.KERNEL_NS, 4)
+        outs, n = gpu_lib.newton_schulz(xs, hyper=gpu_lib.Hyper(schedule=sched), trace=tr)
+        torch.cuda.synchronize()
+        res[sched] = (outs, n, tr.info()[:n])
+    for a, b in zip(res["auto"][0], res["launches"][0]):
+        assert torch.equal(a, b)
+    assert res["auto"][1] == 1 and gpu_lib.ns_passes(res["auto"][2][0]) == [(256, 384, 3, 256),
+                                                                         (300, 520, 1, 256)]
+    assert res["launches"][1] == 0
+
+
+def test_no_riding_beside_xcc_local_queues(gpu_lib):
+    # A stacked pass that spreads over one queue per XCC keeps them; the
+    # single unit then runs its own launches (results unchanged).
+    print("[schedule riding local queues]", flush=True)
+    banks = [(16, 256, 256, 0), (1, 512, 256, 0)]
+    inputs = [_bank(s, 700 + i, "bf16") for i, s in enumerate(banks)]
+    kinds = (gpu_lib.KERNEL_NS, gpu_lib.KERNEL_GRAM)
+    pa, _, tra = _run_steps(gpu_lib, banks, inputs, "auto", "bf16", kinds)
+    pl, _, _ = _run_steps(gpu_lib, banks, inputs, "launches", "bf16")
+    for a, b in zip(pa, pl):
+        assert torch.equal(a, b)
+    n_ns, info = tra[gpu_lib.KERNEL_NS]
+    assert n_ns == 1 and gpu_lib.ns_passes(info[0]) == [(256, 256, 16, 256)]
+    assert tra[gpu_lib.KERNEL_GRAM][0] == 10
+
+
 _FRESH = r"""
 import sys
 import torch
