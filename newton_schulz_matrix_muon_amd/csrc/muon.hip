@@ -379,12 +379,14 @@ int plan(const muon_matrix_desc* mats, int64_t n, const muon_hyper* h, bool step
   return MUON_OK;
 }
 
-size_t workspace_of(const std::vector<Chunk>& chunks, const muon_hyper* h) {
+// riding: room for riding passes (every call but the scratch entry's,
+// whose passes never ride along).
+size_t workspace_of(const std::vector<Chunk>& chunks, const muon_hyper* h, bool riding = true) {
   size_t need = kHeader;
   for (const Chunk& c : chunks) {
     size_t t = layout_of(c, h).total;
     // a riding pass's buffers follow the stacked pass's
-    if (c.rider >= 0) t += layout_of(chunks[(size_t)c.rider], h).total - kHeader;
+    if (riding && c.rider >= 0) t += layout_of(chunks[(size_t)c.rider], h).total - kHeader;
     need = std::max(need, t);
   }
   return need;
@@ -1187,7 +1189,7 @@ int run(bool step, float* const* outs, const void* const* ins, float* const* mom
     std::vector<Chunk> chunks;
     st = plan(mats, n, h, step, &chunks);
     if (st != MUON_OK) return st;
-    const size_t need = workspace_of(chunks, h);
+    const size_t need = workspace_of(chunks, h, !scratch_ws);
     if (scratch_ws) {
       // the fixed scratch: refuse a step that needs more, before anything runs
       if (need > kScratchBytes) return MUON_ERR_WORKSPACE;

@@ -138,22 +138,27 @@ def test_persistent_with_xccs_left_without_workgroups(gpu_lib, workgroups, monke
 
 # A single 256-tile unit under AUTO runs inside the persistent launch of a
 # stacked pass (ns_persistent2) when that pass takes one claim queue.
-# (banks, grad dtype, NS precision, index of a bank whose gradient is zero)
+# (banks, grad dtype, NS precision, index of a bank whose gradient is zero,
+# other hyperparameters)
+EMA_STAGES = dict(nesterov_style="ema", step=3,
+                  stages=((3, (3.4445, -4.7750, 2.0315)), (0, (1.0, 0.0, 0.0)), (2, (2.0, -1.5, 0.5))))
 RIDING = [
     # the transformer layer's O projection beside its MLP units (down transposed)
-    ([(1, 4096, 4096, 0), (2, 14336, 4096, 0), (1, 4096, 14336, 0)], "bf16", "bf16", None),
+    ([(1, 4096, 4096, 0), (2, 14336, 4096, 0), (1, 4096, 14336, 0)], "bf16", "bf16", None, {}),
     # ragged: s = 300 and 520 on 256 tiles, a zero unit in the stacked pass
-    ([(3, 1100, 300, 0), (1, 700, 520, 0)], "bf16", "bf16", None),
+    ([(3, 1100, 300, 0), (1, 700, 520, 0)], "bf16", "bf16", None, {}),
     # a riding unit with a zero gradient (pure decay in its final epilogue)
-    ([(2, 640, 256, 0), (1, 512, 384, 0)], "fp32", "bf16", 1),
+    ([(2, 640, 256, 0), (1, 512, 384, 0)], "fp32", "bf16", 1, {}),
     # fp32 products; the riding unit is wide, stored transposed
-    ([(2, 640, 256, 0), (1, 300, 700, 0)], "bf16", "fp32", None),
+    ([(2, 640, 256, 0), (1, 300, 700, 0)], "bf16", "fp32", None, {}),
+    # EMA look-ahead, three stages (one of zero steps), unit_rms_norm scale
+    ([(2, 640, 256, 0), (1, 300, 700, 0)], "bf16", "bf16", None, dict(EMA_STAGES, scale="unit_rms_norm")),
 ]
 
 
-def _run_steps(gpu_lib, banks, inputs, sched, prec, trace_kinds=()):
+def _run_steps(gpu_lib, banks, inputs, sched, prec, trace_kinds=(), extra=None):
     splits = [b[3] for b in banks]
-    h = gpu_lib.Hyper(ns_precision=prec, schedule=sched)
+    h = gpu_lib.Hyper(ns_precision=prec, schedule=sched, **(extra or {}))
     params = [w.clone() for w, _ in inputs]
     moms = [torch.zeros_like(w) for w, _ in inputs]
     ws = gpu_lib.workspace(gpu_lib.workspace_size(params, h, splits), torch.device(DEV))
@@ -172,14 +177,14 @@ def _run_steps(gpu_lib, banks, inputs, sched, prec, trace_kinds=()):
 
 @pytest.mark.parametrize("case", range(len(RIDING)))
 def test_riding_pass_agrees_bitwise_with_launches(gpu_lib, case):
-    banks, gdtype, prec, zero = RIDING[case]
-    print(f"[schedule riding] case {case}: {banks} grads {gdtype} products {prec}", flush=True)
+    banks, gdtype, prec, zero, extra = RIDING[case]
+    print(f"[schedule riding] case {case}: {banks} grads {gdtype} products {prec} {extra}", flush=True)
     inputs = [_bank(s, 500 + 13 * i, gdtype) for i, s in enumerate(banks)]
     if zero is not None:
         inputs[zero][1].zero_()
     kinds = (gpu_lib.KERNEL_NS, gpu_lib.KERNEL_GRAM)
-    pa, ma, tra = _run_steps(gpu_lib, banks, inputs, "auto", prec, kinds)
-    pl, ml, _ = _run_steps(gpu_lib, banks, inputs, "launches", prec)
+    pa, ma, tra = _run_steps(gpu_lib, banks, inputs, "auto", prec, kinds, extra)
+    pl, ml, _ = _run_steps(gpu_lib, banks, inputs, "launches", prec, extra=extra)
     for i in range(len(banks)):
         assert torch.equal(pa[i], pl[i]), f"params of bank {i}"
         assert torch.equal(ma[i], ml[i]), f"momenta of bank {i}"

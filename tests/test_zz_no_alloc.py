@@ -28,9 +28,11 @@ def _banks(specs, seed):
 
 CALLS = [
     # 256 tiles (two panels per side), split heads on 128 tiles, a ragged tall
-    # bank with fp32 gradients, and a unit small enough for the on-chip kernel
+    # bank with fp32 gradients, a unit small enough for the on-chip kernel,
+    # and a single 256-tile unit (with a workspace it runs inside the first
+    # bank's persistent launch; the scratch entry runs it on its own)
     [(4, 512, 768, 0, "bf16"), (2, 384, 1024, 128, "bf16"), (3, 300, 200, 0, "fp32"),
-     (1, 64, 128, 0, "fp32")],
+     (1, 64, 128, 0, "fp32"), (1, 640, 512, 0, "bf16")],
     # smaller: fewer, smaller units
     [(2, 256, 300, 0, "bf16"), (1, 64, 128, 0, "fp32")],
 ]
