@@ -98,6 +98,10 @@ constexpr int64_t kMaxChunks = (int64_t)1 << 20;  // stacked passes per call
 constexpr size_t kScratchBytes = (size_t)128 << 20;
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 constexpr int kMaxQueues = 16;   // persistent schedule: at most one queue per XCC
+// Passes whose momentum (fp32, 4 B per element) is larger than this take
+// the non-temporal momentum kernels: the MI355X's last-level cache (the
+// 256 MB Infinity Cache) cannot hold their stream.
+constexpr int64_t kStreamBytes = (int64_t)256 << 20;
 
 // Whether the AUTO schedule may run the pass on the on-chip small-unit
 // kernel (bf16 products, wide units with at most 128 rows; the final choice
@@ -682,28 +686,37 @@ void launch_prologue(const Chunk& c, const ChunkArgs& ca, const ChunkBufs& B, co
   };
   float* const x0 = B.x32[0];
   double* const partials = B.partials;
+  // Non-temporal gradient and momentum accesses for passes whose momentum
+  // (or NS input) outgrows the last-level cache (kernels.hpp, ld_f4).
+  const bool nt = c.n_units * c.rows_u * c.cols * 4 > kStreamBytes;
   if (c.n_plain > 0) {
     tr.before(MUON_KERNEL_MOMENTUM);
     const dim3 grid((unsigned)(c.n_plain * c.blocks_per_unit));
     const int bpu = c.blocks_per_unit, rpb = c.rows_per_block;
+#define MUON_MOMENTUM(GK, NT) \
+  hipLaunchKernelGGL((k_momentum<GK, NT>), grid, dim3(kThreads), 0, s, ca, x0, nb, partials, rpb, bpu, 0, (int)pp)
     if (gk == 2)
-      hipLaunchKernelGGL(k_momentum<2>, grid, dim3(kThreads), 0, s, ca, x0, nb, partials, rpb, bpu, 0, (int)pp);
+      { if (nt) MUON_MOMENTUM(2, true); else MUON_MOMENTUM(2, false); }
     else if (gk == 0)
-      hipLaunchKernelGGL(k_momentum<0>, grid, dim3(kThreads), 0, s, ca, x0, nb, partials, rpb, bpu, 0, (int)pp);
+      { if (nt) MUON_MOMENTUM(0, true); else MUON_MOMENTUM(0, false); }
     else
-      hipLaunchKernelGGL(k_momentum<1>, grid, dim3(kThreads), 0, s, ca, x0, nb, partials, rpb, bpu, 0, (int)pp);
+      { if (nt) MUON_MOMENTUM(1, true); else MUON_MOMENTUM(1, false); }
+#undef MUON_MOMENTUM
     mom_info(c.n_plain);
   }
   if (c.n_units > c.n_plain) {
     tr.before(MUON_KERNEL_MOMENTUM);
     const dim3 grid((unsigned)((c.n_units - c.n_plain) * c.tiles_t));
     const int u0 = (int)c.n_plain;
+#define MUON_MOMENTUM_T(GK, NT) \
+  hipLaunchKernelGGL((k_momentum_t<GK, NT>), grid, dim3(kThreads), 0, s, ca, x0, nb, partials, u0, (int)pp)
     if (gk == 2)
-      hipLaunchKernelGGL(k_momentum_t<2>, grid, dim3(kThreads), 0, s, ca, x0, nb, partials, u0, (int)pp);
+      { if (nt) MUON_MOMENTUM_T(2, true); else MUON_MOMENTUM_T(2, false); }
     else if (gk == 0)
-      hipLaunchKernelGGL(k_momentum_t<0>, grid, dim3(kThreads), 0, s, ca, x0, nb, partials, u0, (int)pp);
+      { if (nt) MUON_MOMENTUM_T(0, true); else MUON_MOMENTUM_T(0, false); }
     else
-      hipLaunchKernelGGL(k_momentum_t<1>, grid, dim3(kThreads), 0, s, ca, x0, nb, partials, u0, (int)pp);
+      { if (nt) MUON_MOMENTUM_T(1, true); else MUON_MOMENTUM_T(1, false); }
+#undef MUON_MOMENTUM_T
     mom_info(c.n_units - c.n_plain);
   }
   // norms (and, off the folded path, X0 = N / ||N||_F)
