@@ -243,31 +243,34 @@ int pick_tile(int64_t rows_u, int64_t cols) {
 // packed values hold both passes.
 void pair_passes(std::vector<Chunk>* cs, const muon_hyper* h) {
   const bool bf16 = h->ns_precision == MUON_NS_BF16;
+  // one operand layout per launch: bf16 wide and tall units read X
+  // differently (fp32 units all read rows of X and X^T)
+  auto layout = [&](const Chunk& c) { return bf16 && c.tall ? 1 : 0; };
+  auto work = [](const Chunk& c) {
+    return (double)c.n_units * (double)c.s_pad * (double)c.s_pad *
+           (double)std::max(c.rows_pad, c.cols_pad);
+  };
+  // Stacked passes that may take a rider, per operand layout, largest
+  // first (ties in pass order); each takes at most one, riders in pass
+  // order.  (Sorting once keeps plans of many passes linear-logarithmic.)
+  std::vector<int> hosts[2];
+  for (size_t i = 0; i < cs->size(); ++i) {
+    const Chunk& p = (*cs)[i];
+    if (p.tile == 256 && p.n_units >= 2 && !small_possible(p, h)) hosts[layout(p)].push_back((int)i);
+  }
+  for (auto& v : hosts)
+    std::stable_sort(v.begin(), v.end(),
+                     [&](int x, int y) { return work((*cs)[(size_t)x]) > work((*cs)[(size_t)y]); });
+  size_t next[2] = {0, 0};
   for (size_t j = 0; j < cs->size(); ++j) {
     Chunk& q = (*cs)[j];
     if (q.tile != 256 || q.n_units != 1 || small_possible(q, h) || q.segs.size() > (size_t)kMaxSegB)
       continue;
-    int best = -1;
-    double best_work = 0.0;
-    for (size_t i = 0; i < cs->size(); ++i) {
-      const Chunk& p = (*cs)[i];
-      if (i == j || p.tile != 256 || p.n_units < 2 || small_possible(p, h) || p.rider >= 0 ||
-          p.host >= 0)
-        continue;
-      // one operand layout per launch: bf16 wide and tall units read X
-      // differently (fp32 units all read rows of X and X^T)
-      if (bf16 && p.tall != q.tall) continue;
-      const double work = (double)p.n_units * (double)p.s_pad * (double)p.s_pad *
-                          (double)std::max(p.rows_pad, p.cols_pad);
-      if (work > best_work) {
-        best = (int)i;
-        best_work = work;
-      }
-    }
-    if (best >= 0) {
-      (*cs)[best].rider = (int)j;
-      q.host = best;
-    }
+    const int k = layout(q);
+    if (next[k] == hosts[k].size()) continue;
+    const int best = hosts[k][next[k]++];
+    (*cs)[(size_t)best].rider = (int)j;
+    q.host = best;
   }
 }
 

@@ -137,6 +137,20 @@ def test_workspace_holds_a_riding_pass():
     assert st == 0 and 2 * per_a + per_b <= n < 2 * per_a + per_b + mib
 
 
+def test_pairing_many_passes_is_fast():
+    # 20000 shapes of three 256-tile units, cut two per pass: 20000 stacked
+    # passes and 20000 single-unit passes to pair (one rider each)
+    import time
+
+    shapes = [(3, 256 + i, 256, 0) for i in range(20000)]
+    h = muon.default_hyper_c()
+    h.batch_update_size = 2
+    t0 = time.perf_counter()
+    st, n = ws_size(shapes, h)
+    assert st == 0 and n > 0
+    assert time.perf_counter() - t0 < 2.0
+
+
 @pytest.mark.parametrize(
     "shape,code",
     [
