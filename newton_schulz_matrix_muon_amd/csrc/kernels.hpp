@@ -230,8 +230,8 @@ __device__ __forceinline__ float bf16_round(float f) {
 // Streaming accesses to the caller's gradient and momentum.  With NT they
 // carry the non-temporal hint, which the host picks for passes whose
 // momentum is larger than the last-level cache (an MoE bank of 5.6G
-// elements: 13.0-13.4 -> 11.6 ms; on 32 x 1024^2, 134 MB of momentum, the
-// hint was 5-10% slower).
+// elements: 13.4 -> 12.9 ms on one box, 13.0 -> 11.6 ms on another; on
+// 32 x 1024^2, 134 MB of momentum, the hint was 5-10% slower).
 typedef unsigned u32x2e __attribute__((ext_vector_type(2)));
 template <bool NT>
 __device__ __forceinline__ uint2 ld_u2(const void* p) {
@@ -2137,7 +2137,7 @@ __global__ __launch_bounds__(kThreads) void k_ns_small_step(NsSmallArgs p, Chunk
 // and completion counts.  Its items follow the first pass's within each
 // phase (Gram of the first pass, Gram of the second, polynomial of the
 // first, ...), so every item still waits only for earlier ones; the second
-// pass's tiles fill the CUs that the first pass's leaves idle.
+// pass's tiles fill the CUs that the first pass leaves idle.
 //
 // Queues.  With one queue any workgroup may run any tile, so a tile's
 // results are published at agent scope (the L2 written back before the
