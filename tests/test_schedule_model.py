@@ -13,6 +13,8 @@ dependency points to an earlier item in claim order (so the schedule makes
 progress) and that every write to a buffer that is rewritten each iteration
 (A, B' and the two iterates) comes after every read of the same region, and
 every read after the write it needs, directly or through other dependencies.
+A launch that runs two passes interleaves their items phase by phase; the
+model checks that every unit keeps its own order inside that interleaving.
 
 Two further models cover how a finished tile reaches its readers: through
 the caches (per-CU L1s, per-XCC write-back L2s, memory; stores, L2
@@ -145,6 +147,44 @@ def test_counts_cannot_run_ahead(ts, tl):
 def test_iteration_zero_reads_no_earlier_item():
     # the first Gram reads N / nu, written before the launch
     assert deps((0, "G", (0, 1)), 2, 3) == []
+
+
+def two_pass_order(passes, n_iter):
+    """Claim order of a two-pass launch (ns_persistent2): per iteration the
+    Gram tiles of the first pass's units (unit-major), then the second
+    pass's, then the polynomial tiles of each pass, then the apply tiles of
+    each.  passes: (units, ts, tl) per pass; items are (pass, unit, item)."""
+    one = [items(ts, tl, n_iter) for _, ts, tl in passes]
+    out = []
+    for it in range(n_iter):
+        for ph in ("G", "P", "A"):
+            for k, (units, _, _) in enumerate(passes):
+                for u in range(units):
+                    out += [(k, u, x) for x in one[k] if x[0] == it and x[1] == ph]
+    return out
+
+
+@pytest.mark.parametrize("passes", [
+    [(3, 4, 14), (1, 4, 4)],     # the layer's MLP units with its O projection (16 x 56 and 16 x 16 panels, scaled down)
+    [(2, 2, 5), (1, 3, 3)],      # ragged: different small sides
+    [(4, 2, 6), (1, 1, 1)],      # a one-tile rider
+])
+def test_two_pass_order_keeps_each_units_order(passes):
+    # Each unit's items keep their own claim order inside the two-pass
+    # order, so every dependency still points to an earlier item and every
+    # property checked above for one unit's order carries over; items of
+    # different units (of either pass) share no buffers.
+    n_iter = 3
+    order = two_pass_order(passes, n_iter)
+    assert len(order) == sum(u * len(items(ts, tl, n_iter)) for u, ts, tl in passes)
+    pos = {x: k for k, x in enumerate(order)}
+    for k, (units, ts, tl) in enumerate(passes):
+        for u in range(units):
+            mine = [x for (kk, uu, x) in order if (kk, uu) == (k, u)]
+            assert mine == items(ts, tl, n_iter)
+            for x in mine:
+                for d in deps(x, ts, tl):
+                    assert pos[(k, u, d)] < pos[(k, u, x)]
 
 
 # ------------------------------------------------------------------------
