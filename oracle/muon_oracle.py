@@ -1,8 +1,8 @@
 """Float64 CPU oracle of the Muon optimizer step.
 
 TEST INFRASTRUCTURE ONLY.  This module is the slow, plain reference that the
-HIP library is checked against.  Only the test suite, the graft smoke check
-and the CPU-baseline leg of the benchmark may import it; the product path
+HIP library is checked against.  Only the test suite, the smoke check in
+__graft_entry__.py and the CPU-baseline leg of the benchmark may import it; the product path
 (the HIP library and its Python binding) never does, and the two share no
 code.  It depends on NumPy alone.
 
