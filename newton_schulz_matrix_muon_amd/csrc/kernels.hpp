@@ -230,7 +230,7 @@ __device__ __forceinline__ float bf16_round(float f) {
 // Streaming accesses to the caller's gradient and momentum.  With NT they
 // carry the non-temporal hint, which the host picks for passes whose
 // momentum is larger than the last-level cache (an MoE bank of 5.6G
-// elements: 13.4 -> 12.9 ms on one box, 13.0 -> 11.6 ms on another; on
+// elements: 13.4 -> 12.9 ms on one machine, 13.0 -> 11.6 ms on another; on
 // 32 x 1024^2, 134 MB of momentum, the hint was 5-10% slower).
 typedef unsigned u32x2e __attribute__((ext_vector_type(2)));
 template <bool NT>
