@@ -153,6 +153,9 @@ RIDING = [
     ([(2, 640, 256, 0), (1, 300, 700, 0)], "bf16", "fp32", None, {}),
     # EMA look-ahead, three stages (one of zero steps), unit_rms_norm scale
     ([(2, 640, 256, 0), (1, 300, 700, 0)], "bf16", "bf16", None, dict(EMA_STAGES, scale="unit_rms_norm")),
+    # batch_update_size cuts one bank into passes of two units and one: the
+    # single unit rides with a pass of its own shape
+    ([(3, 768, 512, 0)], "bf16", "bf16", None, dict(batch_update_size=2)),
 ]
 
 
