@@ -200,6 +200,10 @@ int muon_workspace_size(const muon_matrix_desc* mats, int64_t n_mats, const muon
  * A unit whose Nesterov look-ahead is exactly zero gets O' = 0, i.e. only
  * the weight decay.  Buffers of different banks must not overlap, and a
  * bank's params, grads and momenta must be distinct.  n_mats = 0 is a no-op.
+ * The call only enqueues kernels on `stream` (the first call on a device
+ * also queries the device), and every kernel resets the counters it uses by
+ * its own writes, so a call made while `stream` is being captured into a HIP
+ * graph replays like a fresh call on the same buffers.
  * Errors: every code above. */
 int muon_step_batched(float* const* params, const void* const* grads, float* const* momenta,
                       const muon_matrix_desc* mats, int64_t n_mats, const muon_hyper* h,
