@@ -341,6 +341,40 @@ def measure(wl, ns, steps, warmup, dev, inputs, schedule="auto", trace_classes=T
     return out, roof
 
 
+def graph_step_us(wl, ns, dev, inputs, reps=500):
+    """Microseconds per step of workload `wl` with one step captured in a
+    HIP graph and replayed `reps` times: the step's launches without the
+    host-side work of each call (argument marshalling, planning).  The
+    replays reuse the first gradient set."""
+    import torch
+
+    from newton_schulz_matrix_muon_amd import muon
+
+    params, moms, grads, splits = inputs
+    hyper = muon.Hyper(scale=wl.scale, ns_precision=ns)
+    ws = muon.workspace(muon.workspace_size(params, hyper, splits), dev)
+
+    def one():
+        muon.step(params, grads[0], moms, hyper=hyper, split_rows=splits, ws=ws, check=False)
+
+    one()  # first-call set-up outside the capture
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        one()
+    for _ in range(20):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        graph.replay()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / reps
+    muon.workspace_status(ws)
+    del graph
+    return dt * 1e6
+
+
 def pass_breakdown(cls, launch_ms, launch_info, groups, iters, peak):
     """The dominant class's timed launches grouped by the pass they ran
     (unit shape and count): launches, mean ms and nominal TFLOP/s each."""
@@ -507,6 +541,8 @@ def main(argv=None):
             r, _ = measure(w, ns, steps, warmup, dev, inp, "auto", trace_classes=tc)
             if cfg == 1:
                 r["us_per_step"] = r["ms_per_step"] * 1e3
+                # the same step replayed from a HIP graph (no per-call host work)
+                r["graph_us_per_step"] = graph_step_us(w, ns, dev, inp)
             subs[f"{cfg}_{ns}"] = r
             del inp
             free()
