@@ -221,6 +221,23 @@ def test_riding_pass_ns_only(gpu_lib):
     assert res["launches"][1] == 0
 
 
+@pytest.mark.parametrize("workgroups", [1, 3])
+def test_riding_pass_with_few_workgroups(gpu_lib, workgroups, monkeypatch):
+    # A capped grid: one or three workgroups claim every item of both passes
+    # in order, which still completes (each item waits only for earlier
+    # ones) and gives the per-product launches' result.
+    print(f"[schedule riding] {workgroups} workgroups", flush=True)
+    banks = [(2, 640, 256, 0), (1, 512, 384, 0)]
+    inputs = [_bank(s, 900 + i, "bf16") for i, s in enumerate(banks)]
+    pl, ml, _ = _run_steps(gpu_lib, banks, inputs, "launches", "bf16")
+    monkeypatch.setenv("MUON_PERSISTENT_WORKGROUPS", str(workgroups))
+    pa, ma, tra = _run_steps(gpu_lib, banks, inputs, "auto", "bf16", (gpu_lib.KERNEL_NS,))
+    monkeypatch.delenv("MUON_PERSISTENT_WORKGROUPS")
+    assert tra[gpu_lib.KERNEL_NS][0] == 1 and len(gpu_lib.ns_passes(tra[gpu_lib.KERNEL_NS][1][0])) == 2
+    for i in range(len(banks)):
+        assert torch.equal(pa[i], pl[i]) and torch.equal(ma[i], ml[i]), f"bank {i}"
+
+
 def test_no_riding_beside_xcc_local_queues(gpu_lib):
     # A stacked pass that spreads over one queue per XCC keeps them; the
     # single unit then runs its own launches (results unchanged).
