@@ -1887,6 +1887,37 @@ struct SmallOps<float> {
   static __device__ __forceinline__ float iterate(float x) { return x; }
 };
 
+// acc[t] += the product of fragments fa(t, kk) and fb(t, kk) over kk < KS,
+// t < NT: the fragments of the next D steps are read while a step's MFMAs
+// run (a ring of registers, every index known at compile time), so LDS
+// latency stays off the chain of dependent MFMAs.  D shrinks as a wave's
+// blocks grow, to bound the registers the ring takes.
+template <typename T, int NT, int KS, typename FA, typename FB>
+__device__ __forceinline__ void small_product(f32x16* acc, const FA& fa, const FB& fb) {
+  constexpr int D0 = NT >= 4 ? 1 : (NT >= 2 ? 2 : 4);
+  constexpr int D = D0 < KS ? D0 : KS;
+  u32x4 ra[D][NT], rb[D][NT];
+#pragma unroll
+  for (int k = 0; k < D; ++k)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      ra[k][t] = fa(t, k);
+      rb[k][t] = fb(t, k);
+    }
+#pragma unroll
+  for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) mfma_one<T>(ra[kk % D][t], rb[kk % D][t], acc[t]);
+    if (kk + D < KS) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        ra[kk % D][t] = fa(t, kk + D);
+        rb[kk % D][t] = fb(t, kk + D);
+      }
+    }
+  }
+}
+
 template <typename T, int BS, int BL>
 __global__ __launch_bounds__(kThreads) void k_ns_small_step(NsSmallArgs p, ChunkArgs ca, int gk,
                                                              uint32_t* __restrict__ err) {
@@ -1901,20 +1932,99 @@ __global__ __launch_bounds__(kThreads) void k_ns_small_step(NsSmallArgs p, Chunk
   __shared__ double wsum[kThreads / 64];
   const int u = blockIdx.x;
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  // wave-uniform, so that the per-block conditions below are scalar
+  // branches and the products run as straight-line code
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int m = lane & 31, half = lane >> 5;
   if (err && u == 0 && threadIdx.x == 0) status_fold(err);
 
   const SegView sg = find_seg(ca, u);
   const int64_t uoff = (int64_t)(u - sg.first) * ca.unit_elems;
+  float* const wout = sg.w + uoff;
   const int rows = ca.rows, cols = ca.cols;
   const bool vec = (cols & 3) == 0;
 
+  // The old weights of this wave's blocks (step only), for the update at
+  // the end: loaded with G and M when a wave holds at most two blocks (the
+  // registers stay free enough), else at the end.
+  const float lrs = sg.lr_scale;
+  const bool step = p.final_mode == FINAL_STEP;
+  constexpr bool kEarlyW = TX <= 2;
+  float wo[TX][4][4];
+  auto load_w = [&]() {
+#pragma unroll
+    for (int t = 0; t < TX; ++t) {
+      const int b = w + 4 * t;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wo[t][q][e] = 0.0f;
+        const int row = 32 * (b / BL) + m;
+        const int c0 = 32 * (b % BL) + 8 * q + 4 * half;
+        if (!step || b >= NX || row >= rows || c0 >= cols) continue;
+        const float* const wp = wout + (int64_t)row * cols + c0;
+        if (vec) {
+          const float4 w0 = *reinterpret_cast<const float4*>(wp);
+          wo[t][q][0] = w0.x; wo[t][q][1] = w0.y; wo[t][q][2] = w0.z; wo[t][q][3] = w0.w;
+        } else {
+          const int ne = min(4, cols - c0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (e < ne) wo[t][q][e] = wp[e];
+        }
+      }
+    }
+  };
+  if constexpr (kEarlyW) load_w();
+
   // 1. M = ma*M + mb*G and N = la*M + lb*G for this wave's blocks of X
   // (block b: rows 32(b / BL) .., columns 32(b % BL) ..), zero outside the
-  // matrix; gk == 2 takes the input itself as N.
+  // matrix; gk == 2 takes the input itself as N.  Every group's G and M
+  // are loaded before any is updated, so the loads are in flight together
+  // (a store to M between them would hold each next load back).
   float xv[TX][16];
+  float gv[TX][4][4], mv[TX][4][4];
   double ss = 0.0;
+#pragma unroll
+  for (int t = 0; t < TX; ++t) {
+    const int b = w + 4 * t;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) gv[t][q][e] = mv[t][q][e] = 0.0f;
+      const int row = 32 * (b / BL) + m;
+      const int c0 = 32 * (b % BL) + 8 * q + 4 * half;
+      if (b < NX && row < rows && c0 < cols) {
+        const int64_t base = uoff + (int64_t)row * cols + c0;
+        if (vec) {
+          if (gk == 0) {
+            const uint2 raw = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(sg.g) + base);
+            gv[t][q][0] = bf16_bits_to_f32(raw.x & 0xffffu);
+            gv[t][q][1] = bf16_bits_to_f32(raw.x >> 16);
+            gv[t][q][2] = bf16_bits_to_f32(raw.y & 0xffffu);
+            gv[t][q][3] = bf16_bits_to_f32(raw.y >> 16);
+          } else {
+            const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(sg.g) + base);
+            gv[t][q][0] = v.x; gv[t][q][1] = v.y; gv[t][q][2] = v.z; gv[t][q][3] = v.w;
+          }
+          if (gk != 2) {
+            const float4 v = *reinterpret_cast<const float4*>(sg.m + base);
+            mv[t][q][0] = v.x; mv[t][q][1] = v.y; mv[t][q][2] = v.z; mv[t][q][3] = v.w;
+          }
+        } else {
+          const int ne = min(4, cols - c0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            if (e >= ne) continue;
+            gv[t][q][e] = gk == 0 ? bf16_bits_to_f32(static_cast<const uint16_t*>(sg.g)[base + e])
+                                  : static_cast<const float*>(sg.g)[base + e];
+            if (gk != 2) mv[t][q][e] = sg.m[base + e];
+          }
+        }
+        // lanes past the last column read nothing: g = 0, M = 0, N = 0
+      }
+    }
+  }
 #pragma unroll
   for (int t = 0; t < TX; ++t) {
     const int b = w + 4 * t;
@@ -1926,31 +2036,8 @@ __global__ __launch_bounds__(kThreads) void k_ns_small_step(NsSmallArgs p, Chunk
       if (b < NX && row < rows && c0 < cols) {
         const int64_t base = uoff + (int64_t)row * cols + c0;
         const int ne = vec ? 4 : min(4, cols - c0);
-        float g[4] = {0.0f, 0.0f, 0.0f, 0.0f}, mo[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-        if (vec) {
-          if (gk == 0) {
-            const uint2 raw = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(sg.g) + base);
-            g[0] = bf16_bits_to_f32(raw.x & 0xffffu);
-            g[1] = bf16_bits_to_f32(raw.x >> 16);
-            g[2] = bf16_bits_to_f32(raw.y & 0xffffu);
-            g[3] = bf16_bits_to_f32(raw.y >> 16);
-          } else {
-            const float4 v = *reinterpret_cast<const float4*>(static_cast<const float*>(sg.g) + base);
-            g[0] = v.x; g[1] = v.y; g[2] = v.z; g[3] = v.w;
-          }
-          if (gk != 2) {
-            const float4 v = *reinterpret_cast<const float4*>(sg.m + base);
-            mo[0] = v.x; mo[1] = v.y; mo[2] = v.z; mo[3] = v.w;
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            if (e >= ne) continue;
-            g[e] = gk == 0 ? bf16_bits_to_f32(static_cast<const uint16_t*>(sg.g)[base + e])
-                           : static_cast<const float*>(sg.g)[base + e];
-            if (gk != 2) mo[e] = sg.m[base + e];
-          }
-        }
+        float* const mo = mv[t][q];
+        const float* const g = gv[t][q];
         if (gk == 2) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) n[e] = g[e];
@@ -1968,7 +2055,6 @@ __global__ __launch_bounds__(kThreads) void k_ns_small_step(NsSmallArgs p, Chunk
               if (e < ne) sg.m[base + e] = mo[e];
           }
         }
-        // lanes past the last column read nothing: g = 0, M = 0, N = 0
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -1987,7 +2073,6 @@ __global__ __launch_bounds__(kThreads) void k_ns_small_step(NsSmallArgs p, Chunk
 #pragma unroll
   for (int i = 0; i < kThreads / 64; ++i) s2 += wsum[i];
 
-  float* const wout = sg.w + uoff;
   if (s2 == 0.0) {
     // Zero look-ahead: O' = 0, so the weight only decays / the output is zero.
     for (int64_t e = threadIdx.x; e < ca.unit_elems; e += kThreads)
@@ -2023,14 +2108,12 @@ __global__ __launch_bounds__(kThreads) void k_ns_small_step(NsSmallArgs p, Chunk
     for (int t = 0; t < TA; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
-#pragma unroll
-    for (int kk = 0; kk < 32 * BL / Op::kK; ++kk)
-#pragma unroll
-      for (int t = 0; t < TA; ++t) {
-        const int b = w + 4 * t;
-        if (b < NA)
-          mfma_one<T>(Op::rows(X, 32 * (b / BS), kk, lane), Op::rows(X, 32 * (b % BS), kk, lane), acc[t]);
-      }
+    // (A wave past the last block repeats the last one, in bounds, and
+    // never stores it: no branch around the products, whose operand reads
+    // then go ahead of the MFMAs.)
+    small_product<T, TA, 32 * BL / Op::kK>(
+        acc, [&](int t, int kk) { return Op::rows(X, 32 * (min(w + 4 * t, NA - 1) / BS), kk, lane); },
+        [&](int t, int kk) { return Op::rows(X, 32 * (min(w + 4 * t, NA - 1) % BS), kk, lane); });
 #pragma unroll
     for (int t = 0; t < TA; ++t) {
       const int b = w + 4 * t;
@@ -2044,14 +2127,9 @@ __global__ __launch_bounds__(kThreads) void k_ns_small_step(NsSmallArgs p, Chunk
     for (int t = 0; t < TA; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
-#pragma unroll
-    for (int kk = 0; kk < 32 * BS / Op::kK; ++kk)
-#pragma unroll
-      for (int t = 0; t < TA; ++t) {
-        const int b = w + 4 * t;
-        if (b < NA)
-          mfma_one<T>(Op::rows(LA, 32 * (b / BS), kk, lane), Op::rows(LA, 32 * (b % BS), kk, lane), acc[t]);
-      }
+    small_product<T, TA, 32 * BS / Op::kK>(
+        acc, [&](int t, int kk) { return Op::rows(LA, 32 * (min(w + 4 * t, NA - 1) / BS), kk, lane); },
+        [&](int t, int kk) { return Op::rows(LA, 32 * (min(w + 4 * t, NA - 1) % BS), kk, lane); });
 #pragma unroll
     for (int t = 0; t < TA; ++t) {
       const int b = w + 4 * t;
@@ -2065,14 +2143,9 @@ __global__ __launch_bounds__(kThreads) void k_ns_small_step(NsSmallArgs p, Chunk
     for (int t = 0; t < TX; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[t][r] = 0.0f;
-#pragma unroll
-    for (int kk = 0; kk < 32 * BS / Op::kK; ++kk)
-#pragma unroll
-      for (int t = 0; t < TX; ++t) {
-        const int b = w + 4 * t;
-        if (b < NX)
-          mfma_one<T>(Op::rows(LB, 32 * (b / BL), kk, lane), Op::cols(X, 32 * (b % BL), kk, lane), acc[t]);
-      }
+    small_product<T, TX, 32 * BS / Op::kK>(
+        acc, [&](int t, int kk) { return Op::rows(LB, 32 * (min(w + 4 * t, NX - 1) / BL), kk, lane); },
+        [&](int t, int kk) { return Op::cols(X, 32 * (min(w + 4 * t, NX - 1) % BL), kk, lane); });
 #pragma unroll
     for (int t = 0; t < TX; ++t)
 #pragma unroll
@@ -2088,8 +2161,10 @@ __global__ __launch_bounds__(kThreads) void k_ns_small_step(NsSmallArgs p, Chunk
     __syncthreads();
   }
 
-  // 4. The decoupled update (or the NS output) of this wave's blocks.
-  const float lrs = sg.lr_scale;
+  // 4. The decoupled update (or the NS output) of this wave's blocks, from
+  // the old weights loaded with G and M (or, for a wave of more blocks,
+  // all loaded now, in flight together).
+  if constexpr (!kEarlyW) load_w();
 #pragma unroll
   for (int t = 0; t < TX; ++t) {
     const int b = w + 4 * t;
@@ -2099,22 +2174,18 @@ __global__ __launch_bounds__(kThreads) void k_ns_small_step(NsSmallArgs p, Chunk
       const int c0 = 32 * (b % BL) + 8 * q + 4 * half;
       if (b >= NX || row >= rows || c0 >= cols) continue;
       float* const wp = wout + (int64_t)row * cols + c0;
-      const float o[4] = {xv[t][4 * q], xv[t][4 * q + 1], xv[t][4 * q + 2], xv[t][4 * q + 3]};
+      float o[4] = {xv[t][4 * q], xv[t][4 * q + 1], xv[t][4 * q + 2], xv[t][4 * q + 3]};
+      if (step) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[e] = __builtin_fmaf(-lrs, o[e], wo[t][q][e] * ca.decay);
+      }
       if (vec) {
-        float4 wv = make_float4(o[0], o[1], o[2], o[3]);
-        if (p.final_mode == FINAL_STEP) {
-          const float4 w0 = *reinterpret_cast<const float4*>(wp);
-          wv.x = __builtin_fmaf(-lrs, o[0], w0.x * ca.decay);
-          wv.y = __builtin_fmaf(-lrs, o[1], w0.y * ca.decay);
-          wv.z = __builtin_fmaf(-lrs, o[2], w0.z * ca.decay);
-          wv.w = __builtin_fmaf(-lrs, o[3], w0.w * ca.decay);
-        }
-        *reinterpret_cast<float4*>(wp) = wv;
+        *reinterpret_cast<float4*>(wp) = make_float4(o[0], o[1], o[2], o[3]);
       } else {
         const int ne = min(4, cols - c0);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          if (e < ne) wp[e] = (p.final_mode == FINAL_STEP) ? __builtin_fmaf(-lrs, o[e], wp[e] * ca.decay) : o[e];
+          if (e < ne) wp[e] = o[e];
       }
     }
   }
