@@ -541,8 +541,14 @@ def main(argv=None):
             r, _ = measure(w, ns, steps, warmup, dev, inp, "auto", trace_classes=tc)
             if cfg == 1:
                 r["us_per_step"] = r["ms_per_step"] * 1e3
-                # the same step replayed from a HIP graph (no per-call host work)
-                r["graph_us_per_step"] = graph_step_us(w, ns, dev, inp)
+                # the same step replayed from a HIP graph (no per-call host
+                # work); an extra figure, so a capture failure does not cost
+                # the line
+                try:
+                    r["graph_us_per_step"] = graph_step_us(w, ns, dev, inp)
+                except Exception as e:  # noqa: BLE001
+                    r["graph_us_per_step"] = None
+                    r["graph_error"] = f"{type(e).__name__}: {e}"[:200]
             subs[f"{cfg}_{ns}"] = r
             del inp
             free()
