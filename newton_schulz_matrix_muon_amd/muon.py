@@ -384,7 +384,12 @@ def step(
     afterwards and raises MuonError if an NS launch whose workgroups wait on
     each other stopped, in which case params and momenta are undefined.
     Returns the number of launches of the traced class (0 without a
-    trace)."""
+    trace).
+
+    Under HIP graph capture (torch.cuda.graph), pass a workspace `ws` and
+    check=False, and make one eager call on the device first: the call then
+    only enqueues kernels, and the captured step replays like a fresh one
+    (tests/test_gpu_graph.py)."""
     hyper = hyper or Hyper()
     n = len(params)
     if not (len(grads) == len(momenta) == n):
