@@ -313,13 +313,7 @@ def measure(wl, ns, steps, warmup, dev, inputs, schedule="auto", trace_classes=T
         nom += a
         exe += b
     t = sum(launch_ms) * 1e-3
-    kernel = KERNEL_NAMES[dominant]
-    if dominant == "ns":
-        # launches that also ran a single-unit pass are ns_persistent2's
-        from newton_schulz_matrix_muon_amd.muon import ns_passes
-
-        two = [len(ns_passes(i)) > 1 for i in launch_info]
-        kernel = " + ".join(k for k, on in (("ns_persistent", not all(two)), ("ns_persistent2", any(two))) if on)
+    kernel = kernel_label(dominant, launch_info)
     roof = {
         "bound": "mfma",
         "kernel": kernel,
@@ -373,6 +367,17 @@ def graph_step_us(wl, ns, dev, inputs, reps=500):
     muon.workspace_status(ws)
     del graph
     return dt * 1e6
+
+
+def kernel_label(cls, launch_info):
+    """Name of the kernel a class's timed launches ran: a persistent launch
+    that also ran a single-unit pass is ns_persistent2's."""
+    if cls != "ns":
+        return KERNEL_NAMES[cls]
+    from newton_schulz_matrix_muon_amd.muon import ns_passes
+
+    two = [len(ns_passes(i)) > 1 for i in launch_info]
+    return " + ".join(k for k, on in (("ns_persistent", not all(two)), ("ns_persistent2", any(two))) if on)
 
 
 def pass_breakdown(cls, launch_ms, launch_info, groups, iters, peak):

@@ -87,6 +87,15 @@ def test_two_pass_launch_counts_both_passes():
     assert rows[0]["tflops"] == pytest.approx((mlp + o) / 0.023 / 1e12)
 
 
+def test_kernel_label_names_the_two_pass_launch():
+    packed = (4096 | 4096 << 32, 14336 | 4096 << 32, 3 | 1 << 32, 256)
+    single = (4096, 4096, 32, 256)
+    assert bench.kernel_label("ns", [single, single]) == "ns_persistent"
+    assert bench.kernel_label("ns", [packed] * 3) == "ns_persistent2"
+    assert bench.kernel_label("ns", [single, packed]) == "ns_persistent + ns_persistent2"
+    assert bench.kernel_label("ns_small", [(128, 4096, 48, 128)]) == "k_ns_small"
+
+
 def test_cpu_baseline_extrapolates_over_shapes(monkeypatch):
     import oracle
 
